@@ -1,0 +1,920 @@
+// ddh_build.hip - halo-map builder on gfx950.
+//
+// Source ("the guide"): NVIDIA technical blog "A Practical Guide to
+// GPU-Initiated Communication for Molecular Dynamics at Scale"; the guide
+// shows the maps only as inputs of its pack kernels ("From MPI baseline to
+// optimized GPU-native halo exchange") and states the relay structure
+// ("Accelerating GROMACS using Device-initiated Remote Memory Access") and the
+// split of every map at the dependency offset ("Enabling parallelism across
+// pulses through kernel fusion"). The selection rule implemented here:
+//
+//   1. every atom goes to the domain whose half-open interval [b_d[i],
+//      b_d[i+1]) holds it in each dimension (fp32 compares decide);
+//   2. home atoms of a domain are ordered by sort cell (key cx + ncx * (cy +
+//      ncy * cz)) and then by global id: a counting sort over all cells of
+//      all domains, made deterministic by sorting each cell by id;
+//   3. pulse p along d, sender S: candidates are S's home slots and every
+//      slot it received in earlier pulses (first pulse of d), or the slots it
+//      received in the previous pulse of d (later pulses); slot j is selected
+//      iff fl(x_j[d] - lo_d(S)) < rc, and selected slots are compacted in
+//      increasing order (wavefront ballots + a work-group prefix). Selected
+//      records go to the -d neighbour; a slot is held as (global id, mask of
+//      dimensions whose + L shift it carries), so its fp32 coordinate is
+//      fl(x + L) or x in each component, exactly what the coordinate pass
+//      stores.
+//
+// The builder runs once per neighbour-search step; it waits for the stream
+// after every pulse to learn the sizes.
+#pragma clang fp contract(off)
+
+#include <algorithm>
+#include <cstring>
+
+#include "ddh_internal.h"
+
+namespace ddh {
+
+namespace {
+
+constexpr int kScanBlock = 1024;  // elements per scan block (4 per thread)
+
+struct AGeom {
+    int n[3];
+    float L[3];
+    float inv_c;
+    const float* b;       // boundaries, dimension d at boff[d]
+    int boff[3];
+    const int* ncell;     // cells across domain index i of d, at noff[d]
+    int noff[3];
+    const int* cellbase;  // first bucket of each domain
+};
+
+__global__ __launch_bounds__(256) void assign_kernel(const float* __restrict__ xg, int n_atoms,
+                                                     AGeom g, int* __restrict__ bucket,
+                                                     uint32_t* __restrict__ count,
+                                                     uint32_t* __restrict__ err)
+{
+    const int a = blockIdx.x * 256 + threadIdx.x;
+    if (a >= n_atoms)
+        return;
+    int ci[3], cc[3], nc[3];
+    for (int d = 0; d < 3; d++) {
+        const float v = xg[3ll * a + d];
+        if (!(v >= 0.0f && v < g.L[d])) {
+            atomicOr(err, 1u);
+            bucket[a] = -1;
+            return;
+        }
+        const float* b = g.b + g.boff[d];
+        const int n = g.n[d];
+        int i = (int)(v * ((float)n / g.L[d]));
+        i = i < 0 ? 0 : (i > n - 1 ? n - 1 : i);
+        while (i > 0 && v < b[i])
+            i--;
+        while (i < n - 1 && v >= b[i + 1])
+            i++;
+        ci[d] = i;
+        nc[d] = g.ncell[g.noff[d] + i];
+        int c = 0;
+        if (nc[d] > 1) {
+            const float t = (v - b[i]) * g.inv_c;
+            c = (int)floorf(t);
+            c = c < 0 ? 0 : (c > nc[d] - 1 ? nc[d] - 1 : c);
+        }
+        cc[d] = c;
+    }
+    const int D = ci[0] + g.n[0] * (ci[1] + g.n[1] * ci[2]);
+    const int key = cc[0] + nc[0] * (cc[1] + nc[1] * cc[2]);
+    const int bk = g.cellbase[D] + key;
+    bucket[a] = bk;
+    atomicAdd(count + bk, 1u);
+}
+
+// ---- exclusive scan of uint32 counts: out[i] = sum(in[0..i)), out[n] = total
+
+__device__ uint32_t block_scan_excl(uint32_t v, uint32_t* sh, uint32_t& total)
+{
+    const int t = threadIdx.x;
+    sh[t] = v;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        const uint32_t add = t >= o ? sh[t - o] : 0u;
+        __syncthreads();
+        sh[t] += add;
+        __syncthreads();
+    }
+    total = sh[255];
+    const uint32_t incl = sh[t];
+    __syncthreads();
+    return incl - v;
+}
+
+__global__ __launch_bounds__(256) void scan_sums_kernel(const uint32_t* __restrict__ in, int64_t n,
+                                                        uint32_t* __restrict__ bsum)
+{
+    __shared__ uint32_t sh[256];
+    const int64_t b0 = (int64_t)blockIdx.x * kScanBlock + 4ll * threadIdx.x;
+    uint32_t s = 0;
+    for (int k = 0; k < 4; k++)
+        if (b0 + k < n)
+            s += in[b0 + k];
+    uint32_t total;
+    block_scan_excl(s, sh, total);
+    if (threadIdx.x == 0)
+        bsum[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(256) void scan_top_kernel(uint32_t* bsum, int nblk, uint32_t* out_total)
+{
+    __shared__ uint32_t sh[256];
+    uint32_t carry = 0;
+    for (int base = 0; base < nblk; base += 256) {
+        const int i = base + threadIdx.x;
+        const uint32_t v = i < nblk ? bsum[i] : 0u;
+        uint32_t total;
+        const uint32_t ex = block_scan_excl(v, sh, total);
+        if (i < nblk)
+            bsum[i] = carry + ex;
+        carry += total;
+    }
+    if (threadIdx.x == 0)
+        *out_total = carry;
+}
+
+__global__ __launch_bounds__(256) void scan_apply_kernel(const uint32_t* __restrict__ in, int64_t n,
+                                                         const uint32_t* __restrict__ bsum,
+                                                         uint32_t* __restrict__ out)
+{
+    __shared__ uint32_t sh[256];
+    const int64_t b0 = (int64_t)blockIdx.x * kScanBlock + 4ll * threadIdx.x;
+    uint32_t v[4];
+    uint32_t s = 0;
+    for (int k = 0; k < 4; k++) {
+        v[k] = b0 + k < n ? in[b0 + k] : 0u;
+        s += v[k];
+    }
+    uint32_t total;
+    uint32_t run = bsum[blockIdx.x] + block_scan_excl(s, sh, total);
+    for (int k = 0; k < 4; k++) {
+        if (b0 + k < n)
+            out[b0 + k] = run;
+        run += v[k];
+    }
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ bucket, int n_atoms,
+                                                      const uint32_t* __restrict__ start,
+                                                      uint32_t* __restrict__ fill,
+                                                      int* __restrict__ sorted)
+{
+    const int a = blockIdx.x * 256 + threadIdx.x;
+    if (a >= n_atoms)
+        return;
+    const int bk = bucket[a];
+    const uint32_t pos = start[bk] + atomicAdd(fill + bk, 1u);
+    sorted[pos] = a;
+}
+
+// Order each cell's atoms by global id (cells hold ~10 atoms: insertion sort).
+__global__ __launch_bounds__(256) void sort_cells_kernel(const uint32_t* __restrict__ start, int nb,
+                                                         int* __restrict__ sorted)
+{
+    const int bk = blockIdx.x * 256 + threadIdx.x;
+    if (bk >= nb)
+        return;
+    const uint32_t s = start[bk], e = start[bk + 1];
+    for (uint32_t i = s + 1; i < e; i++) {
+        const int v = sorted[i];
+        uint32_t j = i;
+        while (j > s && sorted[j - 1] > v) {
+            sorted[j] = sorted[j - 1];
+            j--;
+        }
+        sorted[j] = v;
+    }
+}
+
+__global__ void home_start_kernel(const uint32_t* __restrict__ start, const int* __restrict__ cellbase,
+                                  int ndom, int* __restrict__ hs)
+{
+    const int D = blockIdx.x * 256 + threadIdx.x;
+    if (D <= ndom)
+        hs[D] = (int)start[cellbase[D]];
+}
+
+// ---- per-pulse selection
+
+struct SArgs {
+    int p, d, P;
+    float L_d, rc;
+    const float* xg;
+    const int* home_gid;
+    const int* home_start;
+    const int* nhome;
+    const int* roff_at;   // [S * P + q] first slot of S's region q
+    const int* rsize_at;  // [S * P + q] size of S's region q
+    const int* rstart;    // [S * P + q] index of S's region q in pulse q's storage
+    int* const* rgid;     // per pulse q: global ids of received records
+    int* const* rmask;    // per pulse q: shift masks of received records
+    const float* lo;      // per S: lower boundary along d
+    const int* first;     // per S: candidate slot range
+    const int* last;
+    const int* shiftbit;  // per S: 1 if S sits at index 0 of d
+    int* cnt_send;        // per S outputs of the counting kernel
+    int* cnt_split;
+    const int* map_pos;   // per S: first entry of its map in the pulse buffer
+    int* map_out;
+    const int* out_pos;   // per S: first record of its region at R
+    int* out_gid;
+    int* out_mask;
+};
+
+__device__ void resolve(const SArgs& a, int S, int j, int& gid, int& mask)
+{
+    if (j < a.nhome[S]) {
+        gid = a.home_gid[a.home_start[S] + j];
+        mask = 0;
+        return;
+    }
+    for (int q = 0; q < a.p; q++) {
+        const int o = a.roff_at[S * a.P + q];
+        const int n = a.rsize_at[S * a.P + q];
+        if (j >= o && j < o + n) {
+            const int idx = a.rstart[S * a.P + q] + (j - o);
+            gid = a.rgid[q][idx];
+            mask = a.rmask[q][idx];
+            return;
+        }
+    }
+    gid = -1;
+    mask = 0;
+}
+
+__device__ bool selected(const SArgs& a, int S, int j, int& gid, int& mask)
+{
+    resolve(a, S, j, gid, mask);
+    if (gid < 0)
+        return false;
+    float v = a.xg[3ll * gid + a.d];
+    if ((mask >> a.d) & 1)
+        v = v + a.L_d;
+    return (v - a.lo[S]) < a.rc;
+}
+
+__global__ __launch_bounds__(256) void select_count_kernel(SArgs a)
+{
+    __shared__ int s_send, s_split;
+    const int S = blockIdx.x;
+    if (threadIdx.x == 0) {
+        s_send = 0;
+        s_split = 0;
+    }
+    __syncthreads();
+    int c = 0, below = 0;
+    const int nh = a.nhome[S];
+    for (int j = a.first[S] + threadIdx.x; j < a.last[S]; j += 256) {
+        int gid, mask;
+        if (selected(a, S, j, gid, mask)) {
+            c++;
+            below += j < nh;
+        }
+    }
+    atomicAdd(&s_send, c);
+    atomicAdd(&s_split, below);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        a.cnt_send[S] = s_send;
+        a.cnt_split[S] = s_split;
+    }
+}
+
+// Ordered compaction of the selected candidates of sender S.
+__global__ __launch_bounds__(256) void select_write_kernel(SArgs a)
+{
+    __shared__ int wave_tot[4];
+    __shared__ int s_run;
+    const int S = blockIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (threadIdx.x == 0)
+        s_run = 0;
+    __syncthreads();
+    const int first = a.first[S], last = a.last[S];
+    const int sbit = a.shiftbit[S] << a.d;
+    for (int base = first; base < last; base += 256) {
+        const int j = base + threadIdx.x;
+        int gid = -1, mask = 0;
+        const bool pred = j < last && selected(a, S, j, gid, mask);
+        const unsigned long long bal = __ballot(pred);
+        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0)
+            wave_tot[w] = __popcll(bal);
+        __syncthreads();
+        int off = s_run, tot = 0;
+        for (int q = 0; q < 4; q++) {
+            if (q < w)
+                off += wave_tot[q];
+            tot += wave_tot[q];
+        }
+        if (pred) {
+            const int idx = off + pre;
+            a.map_out[a.map_pos[S] + idx] = j;
+            a.out_gid[a.out_pos[S] + idx] = gid;
+            a.out_mask[a.out_pos[S] + idx] = mask | sbit;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_run += tot;
+        __syncthreads();
+    }
+}
+
+// slot_gid / home_slot for the home slots: r -> domain by binary search.
+__global__ __launch_bounds__(256) void fill_home_kernel(const int* __restrict__ home_gid,
+                                                        const int* __restrict__ hs, int ndom,
+                                                        const int* __restrict__ base, int n_atoms,
+                                                        int* __restrict__ slot_gid,
+                                                        int* __restrict__ home_slot)
+{
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= n_atoms)
+        return;
+    int lo = 0, hi = ndom;  // find D with hs[D] <= r < hs[D+1]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (hs[mid] <= r)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const int slot = base[lo] + (r - hs[lo]);
+    slot_gid[slot] = home_gid[r];
+    home_slot[r] = slot;
+}
+
+// slot_gid for the region records of one pulse (stored receiver-major).
+__global__ __launch_bounds__(256) void fill_region_kernel(const int* __restrict__ rgid, int total,
+                                                          const int* __restrict__ rs, int ndom,
+                                                          const int* __restrict__ dst,
+                                                          int* __restrict__ slot_gid)
+{
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total)
+        return;
+    int lo = 0, hi = ndom;  // find R with rs[R] <= idx < rs[R+1]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (rs[mid] <= idx)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    slot_gid[dst[lo] + (idx - rs[lo])] = rgid[idx];
+}
+
+// ---------------------------------------------------------------- host side
+
+// Device allocations that live only during one build.
+struct Scratch {
+    std::vector<void*> ptrs;
+    ~Scratch()
+    {
+        for (void* p : ptrs)
+            (void)hipFree(p);
+    }
+    template <class T>
+    hipError_t alloc(T** out, size_t n)
+    {
+        void* p = nullptr;
+        hipError_t e = hipMalloc(&p, std::max<size_t>(n, 1) * sizeof(T));
+        if (e == hipSuccess)
+            ptrs.push_back(p);
+        *out = (T*)p;
+        return e;
+    }
+};
+
+template <class T>
+hipError_t owned_alloc(Plan* p, T** out, size_t n)
+{
+    void* q = nullptr;
+    hipError_t e = hipMalloc(&q, std::max<size_t>(n, 1) * sizeof(T));
+    if (e == hipSuccess)
+        p->owned.push_back(q);
+    *out = (T*)q;
+    return e;
+}
+
+template <class T>
+hipError_t upload(T* dst, const std::vector<T>& src, hipStream_t s)
+{
+    if (src.empty())
+        return hipSuccess;
+    return hipMemcpyAsync(dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice, s);
+}
+
+int scan_exclusive(Scratch& sc, const uint32_t* in, int64_t n, uint32_t* out, hipStream_t s)
+{
+    const int nblk = (int)((n + kScanBlock - 1) / kScanBlock);
+    uint32_t* bsum;
+    DDH_HIP(sc.alloc(&bsum, (size_t)nblk + 1));
+    if (nblk > 0)
+        hipLaunchKernelGGL(scan_sums_kernel, dim3(nblk), dim3(256), 0, s, in, n, bsum);
+    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, s, bsum, nblk, out + n);
+    if (nblk > 0)
+        hipLaunchKernelGGL(scan_apply_kernel, dim3(nblk), dim3(256), 0, s, in, n, bsum, out);
+    DDH_HIP(hipGetLastError());
+    return DDH_OK;
+}
+
+int blocks(int64_t n) { return (int)((n + 255) / 256); }
+
+}  // namespace
+
+void free_built(Plan* p)
+{
+    for (auto& kv : p->graphs)
+        (void)hipGraphExecDestroy(kv.second);
+    p->graphs.clear();
+    for (void* q : p->owned)
+        (void)hipFree(q);
+    p->owned.clear();
+    p->d_maps = p->d_slot_gid = p->d_home_gid = p->d_home_slot = nullptr;
+    p->d_items = nullptr;
+    p->d_xch_fused = p->d_xch_pulse = p->d_fch = nullptr;
+    p->d_ctrl = p->d_xflag = p->d_fflag = p->d_xcnt = p->d_fcnt = nullptr;
+    p->built = false;
+    p->n_slots = p->n_halo = 0;
+    p->n_atoms = 0;
+    p->items.clear();
+    p->xch_fused.clear();
+    p->xch_pulse.clear();
+    p->fch.clear();
+}
+
+// Chunk tables and per-chunk waits, from the maps (host copies).
+static void make_work_tables(Plan* p, const std::vector<int32_t>& maps)
+{
+    const Geometry& g = p->g;
+    const int D = g.ndom, P = g.P, CH = p->chunk;
+    // per slot: pulse the slot was received in (-1 home), and the set of
+    // pulses whose map holds the slot (as a bit mask)
+    std::vector<int8_t> rid((size_t)p->n_slots, -1);
+    std::vector<uint32_t> inmap((size_t)p->n_slots, 0u);
+    for (int S = 0; S < D; S++)
+        for (int q = 0; q < P; q++) {
+            const int it = S * P + q;
+            const int R = p->recv[it];
+            const int64_t b = p->base[R] + p->roff[it];
+            for (int i = 0; i < p->send[it]; i++)
+                rid[(size_t)(b + i)] = (int8_t)q;
+            const int32_t* m = maps.data() + p->map_off[it];
+            for (int i = 0; i < p->send[it]; i++)
+                inmap[(size_t)(p->base[S] + m[i])] |= 1u << q;
+        }
+
+    struct Cut { int item, begin, end; bool tail; };
+    std::vector<std::vector<Cut>> cuts((size_t)D * P);
+    for (int S = 0; S < D; S++)
+        for (int q = 0; q < P; q++) {
+            const int it = S * P + q;
+            auto& v = cuts[it];
+            const int split = p->split[it], send = p->send[it];
+            for (int b = 0; b < split; b += CH)
+                v.push_back({it, b, std::min(b + CH, split), false});
+            for (int b = split; b < send; b += CH)
+                v.push_back({it, b, std::min(b + CH, send), true});
+            if (v.empty())
+                v.push_back({it, 0, 0, false});
+            p->items[it].nchunks = (int)v.size();
+        }
+
+    auto xwait = [&](const Cut& c) -> uint32_t {
+        if (!c.tail)
+            return 0u;
+        const int S = c.item / P, q = c.item % P;
+        if (!p->refined_waits)
+            return (1u << q) - 1u;
+        uint32_t w = 0;
+        const int32_t* m = maps.data() + p->map_off[c.item];
+        for (int i = c.begin; i < c.end; i++)
+            w |= 1u << rid[(size_t)(p->base[S] + m[i])];
+        return w;
+    };
+    auto fwait = [&](const Cut& c, uint32_t& wa, uint32_t& wb) {
+        const int S = c.item / P, q = c.item % P;
+        const uint32_t later = ~((2u << q) - 1u) & ((1u << P) - 1u);
+        if (!p->refined_waits) {
+            wa = wb = later;
+            return;
+        }
+        wa = wb = 0;
+        const int32_t* m = maps.data() + p->map_off[c.item];
+        for (int i = c.begin; i < c.end; i++)
+            wa |= inmap[(size_t)(p->base[S] + m[i])];
+        const int R = p->recv[c.item];
+        const int64_t b = p->base[R] + p->roff[c.item];
+        for (int i = c.begin; i < c.end; i++)
+            wb |= inmap[(size_t)(b + i)];
+        wa &= later;
+        wb &= later;
+    };
+    auto xchunk = [&](const Cut& c) {
+        DChunk d{};
+        d.item = c.item;
+        d.begin = c.begin;
+        d.end = c.end;
+        d.wait_a = xwait(c);
+        return d;
+    };
+
+    p->xch_fused.clear();
+    p->xch_pulse.clear();
+    p->fch.clear();
+    p->xpulse_begin.assign((size_t)P + 1, 0);
+    p->fpulse_begin.assign((size_t)P + 1, 0);
+    // fused: every independent head first, then the dependent tails, each in
+    // pulse order
+    for (int pass = 0; pass < 2; pass++)
+        for (int q = 0; q < P; q++)
+            for (int S = 0; S < D; S++)
+                for (const Cut& c : cuts[S * P + q])
+                    if (c.tail == (pass == 1))
+                        p->xch_fused.push_back(xchunk(c));
+    // pulse mode: one ticket range per pulse
+    for (int q = 0; q < P; q++) {
+        p->xpulse_begin[q] = (int)p->xch_pulse.size();
+        for (int pass = 0; pass < 2; pass++)
+            for (int S = 0; S < D; S++)
+                for (const Cut& c : cuts[S * P + q])
+                    if (c.tail == (pass == 1))
+                        p->xch_pulse.push_back(xchunk(c));
+    }
+    p->xpulse_begin[P] = (int)p->xch_pulse.size();
+    // forces: decreasing pulse order
+    for (int r = 0; r < P; r++) {
+        const int q = P - 1 - r;
+        p->fpulse_begin[r] = (int)p->fch.size();
+        for (int S = 0; S < D; S++)
+            for (const Cut& c : cuts[S * P + q]) {
+                DChunk d{};
+                d.item = c.item;
+                d.begin = c.begin;
+                d.end = c.end;
+                fwait(c, d.wait_a, d.wait_b);
+                p->fch.push_back(d);
+            }
+    }
+    p->fpulse_begin[P] = (int)p->fch.size();
+}
+
+static int auto_chunk(int64_t n_halo)
+{
+    if (n_halo >= 2048ll * 1024)
+        return 1024;
+    if (n_halo >= 256ll * 512)
+        return 512;
+    return 256;
+}
+
+int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
+{
+    free_built(p);
+    Geometry& g = p->g;
+    const int D = g.ndom, P = g.P;
+    if (n_atoms < 0 || (n_atoms > 0 && !xg))
+        return fail(DDH_EINVAL, "ddh_build_maps: bad positions pointer or count");
+    Scratch sc;
+
+    // ---- geometry tables
+    std::vector<float> bcat;
+    std::vector<int> ncat;
+    AGeom ag{};
+    for (int d = 0; d < 3; d++) {
+        ag.n[d] = g.n[d];
+        ag.L[d] = g.L[d];
+        ag.boff[d] = (int)bcat.size();
+        ag.noff[d] = (int)ncat.size();
+        bcat.insert(bcat.end(), g.b[d].begin(), g.b[d].end());
+        ncat.insert(ncat.end(), g.ncell[d].begin(), g.ncell[d].end());
+    }
+    ag.inv_c = g.inv_c;
+    std::vector<int> cellbase((size_t)D + 1, 0);
+    {
+        int64_t acc = 0;
+        for (int Dm = 0; Dm < D; Dm++) {
+            int c[3];
+            g.coords(Dm, c);
+            cellbase[Dm] = (int)acc;
+            acc += (int64_t)g.ncell[0][c[0]] * g.ncell[1][c[1]] * g.ncell[2][c[2]];
+            if (acc > (1ll << 30))
+                return fail(DDH_EINVAL, "ddh_build_maps: too many sort cells (cell edge too small)");
+        }
+        cellbase[D] = (int)acc;
+    }
+    const int nb = cellbase[D];
+    float* d_b;
+    int *d_ncell, *d_cellbase;
+    DDH_HIP(sc.alloc(&d_b, bcat.size()));
+    DDH_HIP(sc.alloc(&d_ncell, ncat.size()));
+    DDH_HIP(sc.alloc(&d_cellbase, cellbase.size()));
+    DDH_HIP(upload(d_b, bcat, s));
+    DDH_HIP(upload(d_ncell, ncat, s));
+    DDH_HIP(upload(d_cellbase, cellbase, s));
+    ag.b = d_b;
+    ag.ncell = d_ncell;
+    ag.cellbase = d_cellbase;
+
+    // ---- 1-2: home assignment and cell sort
+    int *d_bucket, *d_hs;
+    uint32_t *d_count, *d_start, *d_fill, *d_err;
+    DDH_HIP(sc.alloc(&d_bucket, (size_t)n_atoms));
+    DDH_HIP(sc.alloc(&d_count, (size_t)nb + 1));
+    DDH_HIP(sc.alloc(&d_start, (size_t)nb + 1));
+    DDH_HIP(sc.alloc(&d_fill, (size_t)nb + 1));
+    DDH_HIP(sc.alloc(&d_err, 1));
+    DDH_HIP(sc.alloc(&d_hs, (size_t)D + 1));
+    DDH_HIP(owned_alloc(p, &p->d_home_gid, (size_t)n_atoms));
+    DDH_HIP(hipMemsetAsync(d_count, 0, sizeof(uint32_t) * ((size_t)nb + 1), s));
+    DDH_HIP(hipMemsetAsync(d_fill, 0, sizeof(uint32_t) * ((size_t)nb + 1), s));
+    DDH_HIP(hipMemsetAsync(d_err, 0, sizeof(uint32_t), s));
+    if (n_atoms > 0)
+        hipLaunchKernelGGL(assign_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s, xg, n_atoms, ag,
+                           d_bucket, d_count, d_err);
+    DDH_HIP(hipGetLastError());
+    uint32_t herr = 0;
+    DDH_HIP(hipMemcpyAsync(&herr, d_err, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+    DDH_HIP(hipStreamSynchronize(s));
+    if (herr)
+        return fail(DDH_EINVAL, "ddh_build_maps: a position is outside [0, L) or not a number");
+    int rcode = scan_exclusive(sc, d_count, nb, d_start, s);
+    if (rcode)
+        return rcode;
+    if (n_atoms > 0) {
+        hipLaunchKernelGGL(scatter_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s, d_bucket, n_atoms,
+                           d_start, d_fill, p->d_home_gid);
+        hipLaunchKernelGGL(sort_cells_kernel, dim3(blocks(nb)), dim3(256), 0, s, d_start, nb,
+                           p->d_home_gid);
+    }
+    hipLaunchKernelGGL(home_start_kernel, dim3(blocks(D + 1)), dim3(256), 0, s, d_start, d_cellbase,
+                       D, d_hs);
+    DDH_HIP(hipGetLastError());
+    std::vector<int> hs((size_t)D + 1);
+    DDH_HIP(hipMemcpyAsync(hs.data(), d_hs, sizeof(int) * (D + 1), hipMemcpyDeviceToHost, s));
+    DDH_HIP(hipStreamSynchronize(s));
+
+    p->nhome.assign(D, 0);
+    p->ntotal.assign(D, 0);
+    for (int Dm = 0; Dm < D; Dm++) {
+        p->nhome[Dm] = hs[Dm + 1] - hs[Dm];
+        p->ntotal[Dm] = p->nhome[Dm];
+    }
+    int* d_nhome;
+    DDH_HIP(sc.alloc(&d_nhome, (size_t)D));
+    DDH_HIP(upload(d_nhome, p->nhome, s));
+
+    // ---- 3: pulses
+    const size_t DP = (size_t)D * P;
+    p->send.assign(DP, 0);
+    p->split.assign(DP, 0);
+    p->recv.assign(DP, 0);
+    p->roff.assign(DP, 0);
+    p->shift.assign(DP, 0);
+    std::vector<int> roff_at(DP, 0), rsize_at(DP, 0), rstart(DP, 0);
+    std::vector<int*> rgid((size_t)std::max(P, 1), nullptr), rmask((size_t)std::max(P, 1), nullptr);
+    std::vector<int*> mapp((size_t)std::max(P, 1), nullptr);
+    std::vector<std::vector<int>> mpos((size_t)P), rsprefix((size_t)P);
+    std::vector<int> total((size_t)P, 0);
+    int *d_roff_at, *d_rsize_at, *d_rstart, *d_cnt_send, *d_cnt_split;
+    int *d_first, *d_last, *d_shiftbit, *d_map_pos, *d_out_pos;
+    float* d_lo;
+    int **d_rgid, **d_rmask;
+    DDH_HIP(sc.alloc(&d_roff_at, DP));
+    DDH_HIP(sc.alloc(&d_rsize_at, DP));
+    DDH_HIP(sc.alloc(&d_rstart, DP));
+    DDH_HIP(sc.alloc(&d_cnt_send, (size_t)D));
+    DDH_HIP(sc.alloc(&d_cnt_split, (size_t)D));
+    DDH_HIP(sc.alloc(&d_first, (size_t)D));
+    DDH_HIP(sc.alloc(&d_last, (size_t)D));
+    DDH_HIP(sc.alloc(&d_shiftbit, (size_t)D));
+    DDH_HIP(sc.alloc(&d_map_pos, (size_t)D));
+    DDH_HIP(sc.alloc(&d_out_pos, (size_t)D));
+    DDH_HIP(sc.alloc(&d_lo, (size_t)D));
+    DDH_HIP(sc.alloc(&d_rgid, (size_t)std::max(P, 1)));
+    DDH_HIP(sc.alloc(&d_rmask, (size_t)std::max(P, 1)));
+
+    for (int q = 0; q < P; q++) {
+        const int d = g.pdim[q], k = g.pk[q];
+        std::vector<float> lo(D);
+        std::vector<int> first(D), last(D), sbit(D), rcv(D);
+        for (int S = 0; S < D; S++) {
+            int c[3];
+            g.coords(S, c);
+            lo[S] = g.b[d][c[d]];
+            sbit[S] = c[d] == 0;
+            int cr[3] = {c[0], c[1], c[2]};
+            cr[d] = (c[d] - 1 + g.n[d]) % g.n[d];
+            rcv[S] = g.index(cr);
+            if (k == 0) {
+                first[S] = 0;
+                last[S] = p->ntotal[S];
+            } else {
+                first[S] = roff_at[S * P + q - 1];
+                last[S] = first[S] + rsize_at[S * P + q - 1];
+            }
+        }
+        DDH_HIP(upload(d_lo, lo, s));
+        DDH_HIP(upload(d_first, first, s));
+        DDH_HIP(upload(d_last, last, s));
+        DDH_HIP(upload(d_shiftbit, sbit, s));
+        DDH_HIP(upload(d_roff_at, roff_at, s));
+        DDH_HIP(upload(d_rsize_at, rsize_at, s));
+        DDH_HIP(upload(d_rstart, rstart, s));
+        DDH_HIP(upload(d_rgid, rgid, s));
+        DDH_HIP(upload(d_rmask, rmask, s));
+
+        SArgs a{};
+        a.p = q;
+        a.d = d;
+        a.P = P;
+        a.L_d = g.L[d];
+        a.rc = g.rc;
+        a.xg = xg;
+        a.home_gid = p->d_home_gid;
+        a.home_start = d_hs;
+        a.nhome = d_nhome;
+        a.roff_at = d_roff_at;
+        a.rsize_at = d_rsize_at;
+        a.rstart = d_rstart;
+        a.rgid = d_rgid;
+        a.rmask = d_rmask;
+        a.lo = d_lo;
+        a.first = d_first;
+        a.last = d_last;
+        a.shiftbit = d_shiftbit;
+        a.cnt_send = d_cnt_send;
+        a.cnt_split = d_cnt_split;
+        hipLaunchKernelGGL(select_count_kernel, dim3(D), dim3(256), 0, s, a);
+        DDH_HIP(hipGetLastError());
+        std::vector<int> cs(D), cp(D);
+        DDH_HIP(hipMemcpyAsync(cs.data(), d_cnt_send, sizeof(int) * D, hipMemcpyDeviceToHost, s));
+        DDH_HIP(hipMemcpyAsync(cp.data(), d_cnt_split, sizeof(int) * D, hipMemcpyDeviceToHost, s));
+        DDH_HIP(hipStreamSynchronize(s));
+
+        // sizes -> offsets; region q of R lands after R's current slots
+        mpos[q].assign(D, 0);
+        int64_t mt = 0;
+        for (int S = 0; S < D; S++) {
+            const int it = S * P + q;
+            p->send[it] = cs[S];
+            p->split[it] = cp[S];
+            p->recv[it] = rcv[S];
+            p->shift[it] = sbit[S];
+            mpos[q][S] = (int)mt;
+            mt += cs[S];
+        }
+        for (int S = 0; S < D; S++) {
+            const int R = rcv[S];
+            p->roff[S * P + q] = p->ntotal[R];
+            roff_at[R * P + q] = p->ntotal[R];
+            rsize_at[R * P + q] = cs[S];
+            if ((int64_t)p->ntotal[R] + cs[S] > INT32_MAX)
+                return fail(DDH_ECAPACITY, "ddh_build_maps: a domain exceeds 2^31 slots");
+            p->ntotal[R] += cs[S];
+        }
+        rsprefix[q].assign((size_t)D + 1, 0);
+        for (int R = 0; R < D; R++) {
+            rstart[R * P + q] = rsprefix[q][R];
+            rsprefix[q][R + 1] = rsprefix[q][R] + rsize_at[R * P + q];
+        }
+        total[q] = (int)mt;
+        if (mt > INT32_MAX)
+            return fail(DDH_ECAPACITY, "ddh_build_maps: a pulse exceeds 2^31 entries");
+        DDH_HIP(sc.alloc(&rgid[q], (size_t)mt));
+        DDH_HIP(sc.alloc(&rmask[q], (size_t)mt));
+        DDH_HIP(sc.alloc(&mapp[q], (size_t)mt));
+        std::vector<int> opos(D);
+        for (int S = 0; S < D; S++)
+            opos[S] = rstart[rcv[S] * P + q];
+        DDH_HIP(upload(d_map_pos, mpos[q], s));
+        DDH_HIP(upload(d_out_pos, opos, s));
+        a.map_pos = d_map_pos;
+        a.map_out = mapp[q];
+        a.out_pos = d_out_pos;
+        a.out_gid = rgid[q];
+        a.out_mask = rmask[q];
+        hipLaunchKernelGGL(select_write_kernel, dim3(D), dim3(256), 0, s, a);
+        DDH_HIP(hipGetLastError());
+        DDH_HIP(hipStreamSynchronize(s));  // per-pulse host arrays are reused
+    }
+
+    // ---- 4: final layout
+    p->base.assign(D, 0);
+    int64_t acc = 0;
+    for (int Dm = 0; Dm < D; Dm++) {
+        p->base[Dm] = acc;
+        acc += p->ntotal[Dm];
+    }
+    if (acc > INT32_MAX / 3)
+        return fail(DDH_ECAPACITY, "ddh_build_maps: layout exceeds the int32 slot range");
+    p->n_slots = acc;
+    p->n_atoms = n_atoms;
+    int64_t nh = 0;
+    for (int q = 0; q < P; q++)
+        nh += total[q];
+    p->n_halo = nh;
+
+    // maps, pulse-major
+    DDH_HIP(owned_alloc(p, &p->d_maps, (size_t)nh));
+    p->map_off.assign(DP, 0);
+    {
+        int64_t pb = 0;
+        for (int q = 0; q < P; q++) {
+            for (int S = 0; S < D; S++)
+                p->map_off[S * P + q] = pb + mpos[q][S];
+            if (total[q] > 0)
+                DDH_HIP(hipMemcpyAsync(p->d_maps + pb, mapp[q], sizeof(int) * total[q],
+                                       hipMemcpyDeviceToDevice, s));
+            pb += total[q];
+        }
+    }
+
+    // global id per slot, home slot per home atom
+    DDH_HIP(owned_alloc(p, &p->d_slot_gid, (size_t)p->n_slots));
+    DDH_HIP(owned_alloc(p, &p->d_home_slot, (size_t)n_atoms));
+    {
+        std::vector<int> base32(D);
+        for (int Dm = 0; Dm < D; Dm++)
+            base32[Dm] = (int)p->base[Dm];
+        int* d_base;
+        DDH_HIP(sc.alloc(&d_base, (size_t)D));
+        DDH_HIP(upload(d_base, base32, s));
+        if (n_atoms > 0)
+            hipLaunchKernelGGL(fill_home_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s,
+                               p->d_home_gid, d_hs, D, d_base, n_atoms, p->d_slot_gid,
+                               p->d_home_slot);
+        std::vector<int*> d_rs((size_t)P), d_dst((size_t)P);
+        std::vector<std::vector<int>> dsts((size_t)P);  // alive until the sync below
+        for (int q = 0; q < P; q++) {
+            std::vector<int>& dst = dsts[q];
+            dst.resize(D);
+            for (int R = 0; R < D; R++)
+                dst[R] = base32[R] + roff_at[R * P + q];
+            DDH_HIP(sc.alloc(&d_rs[q], (size_t)D + 1));
+            DDH_HIP(sc.alloc(&d_dst[q], (size_t)D));
+            DDH_HIP(upload(d_rs[q], rsprefix[q], s));
+            DDH_HIP(upload(d_dst[q], dst, s));
+            if (total[q] > 0)
+                hipLaunchKernelGGL(fill_region_kernel, dim3(blocks(total[q])), dim3(256), 0, s,
+                                   rgid[q], total[q], d_rs[q], D, d_dst[q], p->d_slot_gid);
+        }
+        DDH_HIP(hipGetLastError());
+        DDH_HIP(hipStreamSynchronize(s));
+    }
+
+    // ---- 5: work items and chunk tables
+    p->chunk = p->chunk_req > 0 ? p->chunk_req : auto_chunk(nh);
+    p->items.assign(DP, DItem{});
+    for (int S = 0; S < D; S++)
+        for (int q = 0; q < P; q++) {
+            const int it = S * P + q;
+            DItem& m = p->items[it];
+            const int R = p->recv[it];
+            m.src_base = (int32_t)p->base[S];
+            m.dst_base = (int32_t)(p->base[R] + p->roff[it]);
+            m.map_off = (int32_t)p->map_off[it];
+            m.send = p->send[it];
+            m.comp = g.pdim[q];
+            m.do_shift = p->shift[it];
+            m.shift = g.L[g.pdim[q]];
+            m.S = S;
+            m.R = R;
+            m.p = q;
+        }
+    std::vector<int32_t> hmaps((size_t)nh);
+    if (nh > 0)
+        DDH_HIP(hipMemcpyAsync(hmaps.data(), p->d_maps, sizeof(int32_t) * nh,
+                               hipMemcpyDeviceToHost, s));
+    DDH_HIP(hipStreamSynchronize(s));
+    make_work_tables(p, hmaps);
+
+    DDH_HIP(owned_alloc(p, &p->d_items, p->items.size()));
+    DDH_HIP(owned_alloc(p, &p->d_xch_fused, p->xch_fused.size()));
+    DDH_HIP(owned_alloc(p, &p->d_xch_pulse, p->xch_pulse.size()));
+    DDH_HIP(owned_alloc(p, &p->d_fch, p->fch.size()));
+    DDH_HIP(upload(p->d_items, p->items, s));
+    DDH_HIP(upload(p->d_xch_fused, p->xch_fused, s));
+    DDH_HIP(upload(p->d_xch_pulse, p->xch_pulse, s));
+    DDH_HIP(upload(p->d_fch, p->fch, s));
+    const size_t words = (size_t)kCtrlWords + 4 * DP;
+    DDH_HIP(owned_alloc(p, &p->d_ctrl, words));
+    DDH_HIP(hipMemsetAsync(p->d_ctrl, 0, sizeof(uint32_t) * words, s));
+    p->d_xflag = p->d_ctrl + kCtrlWords;
+    p->d_fflag = p->d_xflag + DP;
+    p->d_xcnt = p->d_fflag + DP;
+    p->d_fcnt = p->d_xcnt + DP;
+    DDH_HIP(hipStreamSynchronize(s));
+    p->built = true;
+    return DDH_OK;
+}
+
+}  // namespace ddh

@@ -1,0 +1,232 @@
+/*
+ * ddh.h - staged halo exchange of a domain-decomposed MD step on one MI355X.
+ *
+ * Every domain of a spatial decomposition is a virtual rank whose atoms live
+ * in one flat device array of float3 records. The library builds the per-pulse
+ * index maps and then runs, as hand-written gfx950 kernels,
+ *   - the coordinate pass: pulse by pulse Z -> Y -> X, each pulse gathering
+ *     boundary records through its index map (with the periodic shift) and
+ *     writing them straight into the receiving domain's slots, later pulses
+ *     relaying records received in earlier ones;
+ *   - the force pass: the same pulses in reverse order X -> Y -> Z, each
+ *     scatter-adding the receiver's halo forces back through the map.
+ *
+ * Source ("the guide"): NVIDIA technical blog "A Practical Guide to
+ * GPU-Initiated Communication for Molecular Dynamics at Scale". The sections
+ * that define each call are named in its comment.
+ *
+ * Conventions for every call:
+ *   - Return value: DDH_OK (0) or a negative DDH_E* code; no exception or
+ *     abort ever crosses this boundary. ddh_last_error() gives a text for the
+ *     last failure on the calling thread.
+ *   - Pointers marked _dev are device pointers on the plan's device; _host
+ *     pointers are host memory. The caller owns every buffer it passes and
+ *     keeps it alive until the enqueued work has finished.
+ *   - stream is a hipStream_t (NULL = the default stream), passed as void*.
+ *     Exchange calls only enqueue work and return at once; they never wait
+ *     for the device. Map building waits (it must learn the sizes).
+ *   - Arrays of coordinates and forces are float32 AoS: slot s occupies
+ *     floats [3s, 3s+3). "capacity_slots" is the number of slots the caller's
+ *     buffer holds; a call rejects a buffer smaller than the plan's layout
+ *     with DDH_ECAPACITY before enqueuing anything.
+ *   - A plan is not thread-safe: use one plan per host thread and stream.
+ *
+ * Layout of the flat slot array (the guide, "From MPI baseline to optimized
+ * GPU-native halo exchange": received coordinates land at the receiver's
+ * offset and are used in place). Domain D = ix + nx * (iy + ny * iz) owns
+ * slots [base_D, base_D + n_total_D): first its n_home_D home atoms, ordered
+ * by sort cell and then by global id, then one contiguous received region per
+ * pulse in global pulse order.
+ */
+#ifndef DDH_H
+#define DDH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ error codes */
+#define DDH_OK 0
+#define DDH_EINVAL (-1)    /* bad argument: null pointer, ndom < 1, rc <= 0,
+                              box <= 0, a position outside [0, L) or NaN */
+#define DDH_ERANGE (-2)    /* rc > L_d - max width on a decomposed dimension
+                              (the halo would wrap onto itself), or more
+                              pulses than DDH_MAX_PULSES */
+#define DDH_ECAPACITY (-3) /* caller buffer smaller than the layout needs, or
+                              a layout beyond 2^31 - 1 slots */
+#define DDH_EHIP (-4)      /* a HIP runtime call failed; see ddh_last_error */
+#define DDH_ETIMEOUT (-5)  /* a device-side wait exceeded its spin limit */
+#define DDH_ENOTIMPL (-6)  /* not implemented */
+#define DDH_ESTATE (-7)    /* call out of order (e.g. exchange before build) */
+
+#define DDH_MAX_PULSES 16
+
+/* ---------------------------------------------------------------- types */
+typedef struct ddh_params {
+    int32_t ndom[3]; /* virtual domains along x, y, z (each >= 1) */
+    float box[3];    /* periodic box edges L_x, L_y, L_z (nm) */
+    float rc;        /* halo cutoff (nm), > 0 */
+    float cell;      /* edge of the cells home atoms are sorted by (nm);
+                        <= 0 orders home atoms by global id only */
+    int32_t flags;   /* reserved, pass 0 */
+} ddh_params;
+
+typedef struct ddh_layout {
+    int32_t n_domains;
+    int32_t n_pulses;                  /* total pulses, global order */
+    int64_t n_slots;                   /* slots of the flat array */
+    int64_t n_halo;                    /* sum of every map's size per pass */
+    int32_t n_atoms;                   /* atoms given to ddh_build_maps */
+    int32_t pulse_dim[DDH_MAX_PULSES]; /* dimension of pulse p: 0=x 1=y 2=z */
+    int32_t pulse_k[DDH_MAX_PULSES];   /* index of pulse p in its dimension */
+} ddh_layout;
+
+typedef struct ddh_plan ddh_plan;
+
+/* Execution modes for the exchange calls (ddh_set_mode). */
+#define DDH_MODE_FUSED 0   /* one persistent launch per pass: all pulses
+                              chained on per-pulse device flags */
+#define DDH_MODE_PULSE 1   /* one launch per pulse, ordered by the stream */
+#define DDH_MODE_GRAPH 16  /* OR-able: replay the call's launches from a
+                              captured hipGraph */
+
+/* ------------------------------------------------------------- lifecycle */
+
+/*
+ * Create a plan for one decomposition. Validates the parameters, computes the
+ * domain boundaries b_d[i] = fl32(L_d * i / n_d) and the pulse schedule:
+ * dimensions Z, then Y, then X ("Accelerating GROMACS using Device-initiated
+ * Remote Memory Access"), ceil-style pulse count per dimension (the smallest
+ * k with k * min width >= rc), none for a dimension with one domain.
+ * Uses the current HIP device. Errors: DDH_EINVAL, DDH_ERANGE, DDH_EHIP.
+ */
+int ddh_plan_create(const ddh_params *params, ddh_plan **out);
+
+/* Release every device and host resource of the plan (NULL is a no-op). */
+void ddh_plan_destroy(ddh_plan *plan);
+
+/* Text for the last failure on the calling thread ("" if none). */
+const char *ddh_last_error(void);
+
+/* ------------------------------------------------------------- map build */
+
+/*
+ * Build the halo maps from global positions x_global_dev[n_atoms][3]
+ * (device, float32, every coordinate in [0, L)). Runs on `stream` and waits
+ * for it. Steps: assign each atom to the domain whose half-open interval
+ * holds it in every dimension; order each domain's home atoms by sort cell
+ * and global id; then for every pulse p (dimension d) and sender S choose the
+ * candidate slots (k == 0: home plus all slots received in earlier pulses;
+ * k >= 1: the slots received in the previous pulse of d), keep those with
+ * fl(x_d - lo_d(S)) < rc in increasing slot order, and deliver them to the
+ * -d neighbour. Cell-sorted home atoms, slab selection and multi-pulse relay
+ * follow "Accelerating GROMACS using Device-initiated Remote Memory Access"
+ * and "Enabling parallelism across pulses through kernel fusion" (the
+ * dependency offset of each map is the sender's home count).
+ * Replaces any previous maps of the plan. Errors: DDH_EINVAL (bad pointer or
+ * position), DDH_ECAPACITY (layout too large), DDH_EHIP.
+ */
+int ddh_build_maps(ddh_plan *plan, const float *x_global_dev, int32_t n_atoms, void *stream);
+
+/* Layout summary. Before ddh_build_maps only the domain count and the pulse
+   schedule are set (slot, halo and atom counts are 0). Errors: DDH_EINVAL. */
+int ddh_query(const ddh_plan *plan, ddh_layout *out);
+
+/* Slot range of domain dom: base, home count, total count (host outputs). */
+int ddh_domain_info(const ddh_plan *plan, int32_t dom, int64_t *base, int32_t *n_home,
+                    int32_t *n_total);
+
+/*
+ * Map metadata of sender dom in pulse p (host outputs, any may be NULL):
+ * send_size (entries), split (entries below the sender's home count: the
+ * independent head), recv_dom (receiving domain), recv_offset (first slot of
+ * the region inside the receiver, relative to its base), shift (1 if the
+ * pulse's component gets + L at this sender).
+ */
+int ddh_pulse_info(const ddh_plan *plan, int32_t dom, int32_t pulse, int32_t *send_size,
+                   int32_t *split, int32_t *recv_dom, int32_t *recv_offset, int32_t *shift);
+
+/*
+ * Copy every map (sender-local slot indices, int32) to maps_dev, concatenated
+ * with the sender outer and the pulse inner; capacity is in int32 elements
+ * and must be >= n_halo. Asynchronous on stream.
+ */
+int ddh_copy_maps(const ddh_plan *plan, int32_t *maps_dev, int64_t capacity, void *stream);
+
+/* Global atom id of every slot (int32[n_slots], device). Asynchronous. */
+int ddh_local_ids(const ddh_plan *plan, int32_t *ids_dev, int64_t capacity, void *stream);
+
+/*
+ * Fill the home slots of x_local_dev from x_global_dev (the array given to
+ * ddh_build_maps or any array of the same atoms). Halo slots are untouched.
+ * Asynchronous.
+ */
+int ddh_gather_home(ddh_plan *plan, const float *x_global_dev, float *x_local_dev,
+                    int64_t capacity_slots, void *stream);
+
+/* ----------------------------------------------------------- exchanges */
+
+/*
+ * Coordinate pass ("From MPI baseline to optimized GPU-native halo exchange",
+ * "Optimizing for efficient transfers across NVIDIA NVLink-connected GPUs",
+ * "Dependency-aware packing"): for pulses in increasing order, every sender S
+ * copies x[base_S + map[i]] to x[base_R + recv_offset + i], adding L_d to
+ * component d when S sits at index 0 of d. Reads home slots, writes every
+ * halo slot; the result is bit-identical to the sequential pulse order.
+ * Asynchronous on stream.
+ */
+int ddh_exchange_coords(ddh_plan *plan, float *x_local_dev, int64_t capacity_slots,
+                        void *stream);
+
+/*
+ * Force pass ("From MPI baseline to optimized GPU-native halo exchange",
+ * "Force halo exchange: Reversing the dependency chain"): for pulses in
+ * decreasing order, every sender S adds f[base_R + recv_offset + i] into
+ * f[base_S + map[i]] (fp32, in place). Each slot receives its adds in
+ * decreasing pulse order, so the result is bit-identical to the sequential
+ * reverse pass over the whole array, halo slots included. Asynchronous.
+ */
+int ddh_exchange_forces(ddh_plan *plan, float *f_local_dev, int64_t capacity_slots,
+                        void *stream);
+
+/*
+ * One coordinate pass followed by one force pass in a single launch (fused
+ * mode) or one launch sequence (pulse mode); the force pass starts only once
+ * every coordinate region has been delivered. Same results as
+ * ddh_exchange_coords then ddh_exchange_forces. Asynchronous.
+ */
+int ddh_exchange_step(ddh_plan *plan, float *x_local_dev, float *f_local_dev,
+                      int64_t capacity_slots, void *stream);
+
+/* Select DDH_MODE_FUSED or DDH_MODE_PULSE, optionally | DDH_MODE_GRAPH. */
+int ddh_set_mode(ddh_plan *plan, int32_t mode);
+
+/*
+ * Wait for stream, then read and clear the plan's device error word.
+ * Returns DDH_OK, DDH_ETIMEOUT (a device wait hit its spin limit: the
+ * results of that call are not valid) or DDH_EHIP.
+ */
+int ddh_check(ddh_plan *plan, void *stream);
+
+/* -------------------------------------------------------------- tuning */
+#define DDH_TUNE_CHUNK 1        /* map entries per work chunk (64..8192, rounded
+                                   to a multiple of 64); 0 = automatic */
+#define DDH_TUNE_GRID 2         /* workgroups of a fused launch; 0 = automatic */
+#define DDH_TUNE_SPIN_LIMIT 3   /* polls before a device wait gives up */
+#define DDH_TUNE_FORCE_TIMEOUT 4 /* 1: every dependent wait targets a value no
+                                    one writes, so it ends at the spin limit
+                                    (tests of the timeout path) */
+#define DDH_TUNE_REFINED_WAITS 5 /* 1 (default): a chunk waits only on the
+                                    pulses its entries reference; 0: on all
+                                    earlier (coordinates) / later (forces) */
+
+/* Set a tuning knob; takes effect at the next build (CHUNK) or call. */
+int ddh_tune(ddh_plan *plan, int32_t key, int64_t value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDH_H */

@@ -39,7 +39,8 @@
  *    sender sits at index 0 of dimension d;
  *  - the dependency offset of a map is the sender's home-atom count;
  *  - pulses per dimension: the smallest k >= 1 with k * min_i w_d[i] >= rc,
- *    and a configuration with rc > L_d - max_i w_d[i] is rejected;
+ *    and a configuration with rc > L_d - max_i w_d[i], or needing more than
+ *    n_d - 1 pulses, is rejected (the halo would wrap onto itself);
  *  - boundaries b_d[i] = fl32(L_d * i / n_d) evaluated in double, intervals
  *    half-open [b_d[i], b_d[i+1]);
  *  - home atoms are ordered by sort cell, then by global id; the cell index
@@ -232,6 +233,10 @@ static int schedule(oplan *o)
         int np = 1;
         while ((double)np * wmin < (double)o->rc)
             np++;
+        /* a relay chain longer than n_d - 1 would carry atoms back to their
+           own domain (possible only within rounding of rc == L - w) */
+        if (np > o->n[d] - 1)
+            return DDHO_ERANGE;
         for (int k = 0; k < np; k++) {
             if (o->P >= DDHO_MAXP)
                 return DDHO_ERANGE;

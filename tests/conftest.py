@@ -33,3 +33,13 @@ def workload_plan():
         return _plans[k]
 
     return get
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    """Name every test on the real stderr before it runs (GPU runs stay legible
+    even when a box ends mid-test)."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"\n[start] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

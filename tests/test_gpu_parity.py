@@ -1,0 +1,280 @@
+"""GPU parity: the HIP library, through its C ABI, against the CPU oracle.
+
+Bar (coordinates, maps, layout, ids: exact; forces: exact given the fixed
+reverse pulse order): every comparison is bit for bit on the raw float32
+words. Cases: the workloads at full size (maps, layout, coordinates, forces,
+fused step), every execution mode (fused persistent launch, one launch per
+pulse, both replayed from captured graphs) over several consecutive steps,
+ragged and extreme chunk/grid settings (down to a single work-group), exact
+dyadic boxes with multi-pulse relay, empty and one-sided inputs, error paths
+and the bounded-wait timeout path.
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import domain_decomposition_halo_amd as ddh  # noqa: E402
+import oracle  # noqa: E402
+import workloads as W  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+MODES = {
+    "fused": ddh.DDH_MODE_FUSED,
+    "pulse": ddh.DDH_MODE_PULSE,
+    "fused_graph": ddh.DDH_MODE_FUSED | ddh.DDH_MODE_GRAPH,
+    "pulse_graph": ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH,
+}
+
+
+def bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+class GpuPlan:
+    """A device plan built from host positions, with host views of its output."""
+
+    def __init__(self, x, grid, box, rc, cell=0.5, mode=0, chunk=0, wg=0, refined=1):
+        self.plan = ddh.Plan(grid, box, rc, cell)
+        self.plan.tune(ddh.DDH_TUNE_CHUNK, chunk)
+        self.plan.tune(ddh.DDH_TUNE_GRID, wg)
+        self.plan.tune(ddh.DDH_TUNE_REFINED_WAITS, refined)
+        self.plan.set_mode(mode)
+        self.xg = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        self.lay = self.plan.build_maps(self.xg)
+        self.n_slots = self.lay["n_slots"]
+        self.D, self.P = self.lay["n_domains"], self.lay["n_pulses"]
+
+    def tables(self):
+        info = [self.plan.domain_info(D) for D in range(self.D)]
+        base = np.array([i[0] for i in info], np.int64)
+        nhome = np.array([i[1] for i in info], np.int32)
+        ntotal = np.array([i[2] for i in info], np.int32)
+        pul = np.array([[self.plan.pulse_info(S, p) for p in range(self.P)] for S in range(self.D)],
+                       np.int32).reshape(self.D, self.P, 5)
+        return base, nhome, ntotal, pul
+
+    def maps(self):
+        out = torch.empty(max(self.lay["n_halo"], 1), dtype=torch.int32, device="cuda")
+        self.plan.copy_maps(out)
+        return out.cpu().numpy()[:self.lay["n_halo"]]
+
+    def ids(self):
+        out = torch.empty(max(self.n_slots, 1), dtype=torch.int32, device="cuda")
+        self.plan.local_ids(out)
+        return out.cpu().numpy()[:self.n_slots]
+
+    def new_coords(self):
+        xl = torch.zeros((max(self.n_slots, 1), 3), dtype=torch.float32, device="cuda")
+        self.plan.gather_home(self.xg, xl)
+        return xl
+
+    def close(self):
+        self.plan.close()
+
+
+def check_layout(g: GpuPlan, ref: oracle.OraclePlan):
+    assert (g.D, g.P, g.n_slots, g.lay["n_halo"]) == (ref.n_domains, ref.n_pulses, ref.n_slots,
+                                                       ref.halo_atoms)
+    assert g.lay["pulses"] == ref.pulses
+    base, nhome, ntotal, pul = g.tables()
+    assert np.array_equal(base, ref.base)
+    assert np.array_equal(nhome, ref.nhome)
+    assert np.array_equal(ntotal, ref.ntotal)
+    for k, arr in enumerate((ref.send, ref.split, ref.recv, ref.roff, ref.shift)):
+        assert np.array_equal(pul[:, :, k], arr), ("send", "split", "recv", "roff", "shift")[k]
+    want = np.concatenate([ref.maps[(S, p)] for S in range(ref.n_domains)
+                           for p in range(ref.n_pulses)] or [np.zeros(0, np.int32)])
+    assert np.array_equal(g.maps(), want)
+    assert np.array_equal(g.ids(), ref.slot_ids)
+
+
+def check_steps(g: GpuPlan, ref: oracle.OraclePlan, w_key, steps=3, fused_step=False):
+    """Several consecutive steps; every one bit-identical to the oracle."""
+    xl = g.new_coords()
+    fl = torch.empty((max(g.n_slots, 1), 3), dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(w_key)
+    for s in range(steps):
+        f0 = rng.normal(0, 10, size=(g.n_slots, 3)).astype(np.float32)
+        fl[:g.n_slots].copy_(torch.from_numpy(f0))
+        if fused_step:
+            g.plan.exchange_step(xl, fl)
+        else:
+            g.plan.exchange_coords(xl)
+            g.plan.exchange_forces(fl)
+        assert g.plan.check() == ddh.DDH_OK
+        assert np.array_equal(bits(xl.cpu().numpy()[:g.n_slots]), bits(ref.x_local)), f"coords step {s}"
+        fr = f0.copy()
+        ref.exchange_forces(fr)
+        assert np.array_equal(bits(fl.cpu().numpy()[:g.n_slots]), bits(fr)), f"forces step {s}"
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_workload_layout_maps_ids(k, workload_plan):
+    w, x, ref = workload_plan(k)
+    g = GpuPlan(x, **w.params())
+    check_layout(g, ref)
+    g.close()
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_workload_coords_forces(k, mode, workload_plan):
+    w, x, ref = workload_plan(k)
+    g = GpuPlan(x, **w.params(), mode=MODES[mode])
+    check_steps(g, ref, k)
+    g.close()
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("k", [2, 4])
+def test_workload_fused_step(k, mode, workload_plan):
+    w, x, ref = workload_plan(k)
+    g = GpuPlan(x, **w.params(), mode=MODES[mode])
+    check_steps(g, ref, 10 + k, fused_step=True)
+    g.close()
+
+
+@pytest.mark.parametrize("chunk,wg,refined", [(64, 0, 1), (320, 0, 1), (8192, 0, 1), (64, 1, 1),
+                                              (192, 3, 0), (256, 1, 0), (1024, 5, 1)])
+@pytest.mark.parametrize("k", [2, 4])
+def test_chunk_and_grid_variants(k, chunk, wg, refined, workload_plan):
+    # a single work-group must drain every ticket in order without waiting forever
+    w, x, ref = workload_plan(k)
+    for mode in (ddh.DDH_MODE_FUSED, ddh.DDH_MODE_PULSE):
+        g = GpuPlan(x, **w.params(), mode=mode, chunk=chunk, wg=wg, refined=refined)
+        check_steps(g, ref, 20 + k, steps=2)
+        check_steps(g, ref, 30 + k, steps=1, fused_step=True)
+        g.close()
+
+
+DYADIC = [
+    ((1, 1, 1), (4.0, 4.0, 4.0), 0.75, 500),
+    ((2, 1, 1), (8.0, 4.0, 4.0), 1.25, 2000),
+    ((2, 2, 2), (8.0, 8.0, 8.0), 1.25, 4000),
+    ((3, 2, 2), (12.0, 8.0, 8.0), 2.5, 4000),
+    ((4, 2, 1), (8.0, 6.0, 4.0), 1.5, 3000),
+    ((8, 2, 2), (8.0, 8.0, 8.0), 2.5, 4000),
+    ((4, 1, 1), (8.0, 4.0, 4.0), 2.0, 1500),
+    ((2, 2, 2), (8.0, 8.0, 8.0), 4.0, 1500),
+    ((4, 4, 2), (4.0, 4.0, 4.0), 1.0, 3000),
+    ((1, 8, 1), (4.0, 16.0, 4.0), 4.5, 3000),
+]
+
+
+@pytest.mark.parametrize("grid,box,rc,n", DYADIC)
+def test_dyadic_boxes(grid, box, rc, n):
+    x = W.lattice_positions(n, box, seed=40 + n)
+    x[:5] = 0.0                                   # atoms exactly on the origin
+    ref = oracle.OraclePlan(x, grid, box, rc)
+    for mode in MODES.values():
+        g = GpuPlan(x, grid, box, rc, mode=mode, chunk=64)
+        check_layout(g, ref)
+        check_steps(g, ref, n, steps=2)
+        check_steps(g, ref, n + 1, steps=1, fused_step=True)
+        g.close()
+
+
+def test_empty_and_one_sided_inputs():
+    box = (8.0, 8.0, 8.0)
+    # no atoms
+    ref = oracle.OraclePlan(np.zeros((0, 3), np.float32), (2, 2, 2), box, 1.0)
+    g = GpuPlan(np.zeros((0, 3), np.float32), (2, 2, 2), box, 1.0)
+    assert g.n_slots == 0 and g.lay["n_halo"] == 0 and g.P == 3
+    xl = torch.zeros((1, 3), dtype=torch.float32, device="cuda")
+    g.plan.exchange_coords(xl)
+    g.plan.exchange_forces(xl)
+    assert g.plan.check() == ddh.DDH_OK
+    g.close()
+    # all atoms in one domain: seven domains own nothing but still receive
+    x = W.lattice_positions(700, (4.0, 4.0, 4.0), seed=3)
+    ref = oracle.OraclePlan(x, (2, 2, 2), box, 1.25)
+    g = GpuPlan(x, (2, 2, 2), box, 1.25)
+    check_layout(g, ref)
+    check_steps(g, ref, 5)
+    g.close()
+    # cell <= 0: home atoms ordered by global id only
+    x = W.lattice_positions(900, box, seed=4)
+    ref = oracle.OraclePlan(x, (2, 2, 2), box, 1.25, cell=0.0)
+    g = GpuPlan(x, (2, 2, 2), box, 1.25, cell=0.0)
+    check_layout(g, ref)
+    g.close()
+
+
+def test_error_paths():
+    box = (8.0, 8.0, 8.0)
+    plan = ddh.Plan((2, 2, 2), box, 1.0)
+    for bad in (8.0, -0.5, float("nan")):
+        x = W.lattice_positions(200, box, seed=1)
+        x[7, 2] = bad
+        with pytest.raises(ddh.DDHError) as e:
+            plan.build_maps(torch.from_numpy(x).cuda())
+        assert e.value.code == ddh.DDH_EINVAL
+    x = W.lattice_positions(2000, box, seed=2)
+    lay = plan.build_maps(torch.from_numpy(x).cuda())
+    small = torch.zeros((lay["n_slots"] - 1, 3), dtype=torch.float32, device="cuda")
+    with pytest.raises(ddh.DDHError) as e:
+        plan.exchange_coords(small)
+    assert e.value.code == ddh.DDH_ECAPACITY
+    full = torch.zeros((lay["n_slots"], 3), dtype=torch.float32, device="cuda")
+    with pytest.raises(ddh.DDHError) as e:
+        plan.exchange_step(full, full)
+    assert e.value.code == ddh.DDH_EINVAL
+    plan.close()
+
+
+def test_timeout_path_is_reported_and_recovers(workload_plan):
+    w, x, ref = workload_plan(2)
+    for mode in (ddh.DDH_MODE_FUSED, ddh.DDH_MODE_PULSE):
+        g = GpuPlan(x, **w.params(), mode=mode)
+        g.plan.tune(ddh.DDH_TUNE_SPIN_LIMIT, 64)
+        g.plan.tune(ddh.DDH_TUNE_FORCE_TIMEOUT, 1)
+        xl = g.new_coords()
+        g.plan.exchange_coords(xl)
+        assert g.plan.check() == ddh.DDH_ETIMEOUT
+        fl = torch.zeros_like(xl)
+        g.plan.exchange_step(xl, fl)
+        assert g.plan.check() == ddh.DDH_ETIMEOUT
+        g.plan.tune(ddh.DDH_TUNE_FORCE_TIMEOUT, 0)
+        g.plan.tune(ddh.DDH_TUNE_SPIN_LIMIT, 1 << 20)
+        check_steps(g, ref, 77, steps=2)
+        g.close()
+
+
+def test_repeated_force_passes_are_deterministic(workload_plan):
+    w, x, ref = workload_plan(3)
+    g = GpuPlan(x, **w.params())
+    f0 = W.forces(w, g.n_slots)
+    fr = f0.copy()
+    ref.exchange_forces(fr)
+    fl = torch.empty((g.n_slots, 3), dtype=torch.float32, device="cuda")
+    src = torch.from_numpy(f0).cuda()
+    for _ in range(20):
+        fl.copy_(src)
+        g.plan.exchange_forces(fl)
+        assert np.array_equal(bits(fl.cpu().numpy()), bits(fr))
+    assert g.plan.check() == ddh.DDH_OK
+    g.close()
+
+
+def test_workload5_full_size():
+    # 12M atoms, 8x8x8 domains: the bench's largest workload, default launch
+    w = W.WORKLOADS[5]
+    x = W.positions(w)
+    ref = oracle.OraclePlan(x, **w.params())
+    for mode in (ddh.DDH_MODE_FUSED, ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH):
+        g = GpuPlan(x, **w.params(), mode=mode)
+        if mode == ddh.DDH_MODE_FUSED:
+            check_layout(g, ref)
+        xl = g.new_coords()
+        f0 = W.forces(w, g.n_slots)
+        fl = torch.from_numpy(f0).cuda()
+        g.plan.exchange_step(xl, fl)
+        assert g.plan.check() == ddh.DDH_OK
+        assert np.array_equal(bits(xl.cpu().numpy()), bits(ref.x_local))
+        fr = f0.copy()
+        ref.exchange_forces(fr)
+        assert np.array_equal(bits(fl.cpu().numpy()), bits(fr))
+        g.close()
