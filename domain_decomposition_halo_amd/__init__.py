@@ -58,6 +58,14 @@ class DDHError(RuntimeError):
 
 
 def _load():
+    # torch brings its own HIP runtime (SONAME libamdhip64.so.7). Loading it
+    # first makes libddh.so bind to that same runtime, so device pointers and
+    # streams from torch are valid in the library; loading libddh.so first
+    # would pull a second runtime into the process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
                           "(python -m domain_decomposition_halo_amd._build)")

@@ -150,3 +150,15 @@ def test_build_without_device_fails_cleanly():
     code = ddh.ddh_build_maps(plan._h, ctypes.c_void_p(0), 0, None)
     assert code == ddh.DDH_EHIP
     plan.close()
+
+
+def test_single_hip_runtime_in_process():
+    # the binding must bind libddh.so to torch's HIP runtime, whatever the
+    # import order of the caller
+    code = ("import domain_decomposition_halo_amd, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "libs = {l.split()[-1] for l in maps if 'libamdhip64' in l}\n"
+            "print(len(libs))\n")
+    res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip() == "1"
