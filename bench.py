@@ -1,0 +1,388 @@
+#!/usr/bin/env python3
+"""Bench: staged halo exchange on one MI355X (coordinates Z->Y->X with relay,
+forces X->Y->Z with scatter-add), all domains virtual ranks in one GPU's HBM.
+
+A step is one coordinate pass plus one force pass over the workload's
+synthetic atoms (the whole hot path; the map build runs once before the
+timed region and is reported separately, as a neighbour-search step would
+be). Inputs are resident in HBM when timing starts. Default workload: 96,000
+atoms, 2x2x2 domains, rc 1.0 nm. Variant "auto" (default) runs what the
+library's automatic mode picks: "step" (both passes in one launch, all pulses
+chained on device counters) for a small pass, "pulse" (one launch per pulse)
+for a large one.
+
+Prints one JSON line. `value` is halo atoms moved per second (sum of every
+(domain, pulse) map size, counted once per pass). The timed region replays a
+graph of --graph-steps captured steps, so the host never starves the GPU;
+HIP events on the launch stream bracket every replay. `roofline` compares the
+step's algorithmic bytes (28 B per halo atom for the coordinate pass, 40 B
+for the force pass) with the 8 TB/s HBM peak over the measured GPU time per
+launch; `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+       [--variant auto|step|split|pulse] [--cold]
+Counter traffic: profiles/traffic_<variant>_<workload>.md, written by
+`python bench.py --summarize-pmc FETCH_CSV WRITE_CSV ...` from two rocprofv3
+--pmc runs of this script with --copy-probe; it is reported only while the
+exchange kernel source is unchanged since those runs.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "halo exchange µs/step + halo atoms/s & HBM GB/s fraction (1 MI355X)"
+HBM_PEAK_GBS = 8000.0
+BYTES_X, BYTES_F = 28, 40
+KERNEL_SRC = os.path.join(ROOT, "domain_decomposition_halo_amd", "csrc", "ddh_exchange.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+VARIANTS = ("auto", "step", "split", "pulse")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def traffic_file(variant: str, wname: str) -> str:
+    return os.path.join(PROFILES, f"traffic_{variant}_{wname}.md")
+
+
+def read_traffic(variant: str, wname: str):
+    """Counter bytes per launch from a stored summary, if still current."""
+    path = traffic_file(variant, wname)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ GPU run
+
+def run_gpu(args, w):
+    import numpy as np
+    import torch
+
+    import domain_decomposition_halo_amd as ddh
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    x = W.positions(w)
+    xg = torch.from_numpy(x).to(dev)
+    plan = ddh.Plan(**w.params())
+    # the timed region replays captured graphs itself, so the library's own
+    # graph mode stays off here
+    mode = {"auto": ddh.DDH_MODE_AUTO, "step": ddh.DDH_MODE_FUSED, "split": ddh.DDH_MODE_FUSED,
+            "pulse": ddh.DDH_MODE_PULSE}[args.variant]
+    plan.set_mode(mode)
+    if args.chunk:
+        plan.tune(ddh.DDH_TUNE_CHUNK, args.chunk)
+    if args.grid:
+        plan.tune(ddh.DDH_TUNE_GRID, args.grid)
+    if args.block:
+        plan.tune(ddh.DDH_TUNE_BLOCK, args.block)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    lay = plan.build_maps(xg)
+    torch.cuda.synchronize()
+    build_ms = (time.perf_counter() - t0) * 1e3
+    # a second build, now warm, is the one reported
+    t0 = time.perf_counter()
+    lay = plan.build_maps(xg)
+    torch.cuda.synchronize()
+    build_ms = min(build_ms, (time.perf_counter() - t0) * 1e3)
+
+    n_slots, n_halo = lay["n_slots"], lay["n_halo"]
+    # "auto" runs what the library's automatic mode picks for this layout
+    variant = args.variant
+    if variant == "auto":
+        variant = "step" if n_halo <= ddh.DDH_AUTO_FUSED_MAX else "pulse"
+    xl = torch.zeros((n_slots, 3), dtype=torch.float32, device=dev)
+    plan.gather_home(xg, xl)
+    fl = torch.from_numpy(W.forces(w, n_slots)).to(dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
+
+    if variant == "split":
+        calls = [("coords", lambda: plan.exchange_coords(xl), BYTES_X * n_halo),
+                 ("forces", lambda: plan.exchange_forces(fl), BYTES_F * n_halo)]
+    else:
+        calls = [("step", lambda: plan.exchange_step(xl, fl), (BYTES_X + BYTES_F) * n_halo)]
+
+    launches_per_step = {"step": 1, "split": 2}.get(variant, 2 * lay["n_pulses"] + 1)
+    for _ in range(args.warmup):
+        for _, fn, _ in calls:
+            fn()
+    assert plan.check() == ddh.DDH_OK
+
+    torch.cuda.synchronize()
+    if args.cold:
+        # eager, one step at a time: caches evicted before every step; the
+        # eviction keeps the GPU busy while the host enqueues the step
+        durs = []
+        for _ in range(args.steps):
+            flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _, fn, _ in calls:
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            durs.append(e0.elapsed_time(e1) * 1e-3)
+        wall = sum(durs)
+        steps_done = args.steps
+    else:
+        # G steps captured in one graph and replayed: the host enqueues one
+        # graph per G steps, so the GPU never waits for the host
+        G = max(1, min(args.graph_steps, args.steps))
+        n_rep = max(1, args.steps // G)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(G):
+                for _, fn, _ in calls:
+                    fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert plan.check() == ddh.DDH_OK
+        evs = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_rep):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        steps_done = n_rep * G
+        durs = [a.elapsed_time(b) * 1e-3 / G for a, b in evs]
+        del graph
+    assert plan.check() == ddh.DDH_OK
+
+    durs = sorted(durs)
+    avg_step_gpu = sum(durs) / len(durs)
+    step_bytes = sum(nb for _, _, nb in calls)
+    avg_launch = avg_step_gpu / launches_per_step
+    achieved = step_bytes / avg_step_gpu / 1e9
+    traffic = read_traffic(variant, w.name)
+    kernel = {"step": "exchange_kernel (fused step, one launch)",
+              "split": "exchange_kernel (coordinate launch + force launch)"}.get(
+                  variant, "pulse_kernel (one launch per pulse) + signal_kernel")
+
+    if args.copy_probe:
+        # a plain copy of known size, for scaling the HBM byte counters
+        nb = args.copy_probe << 20
+        a = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    step_s = wall / steps_done
+    res = dict(
+        n_slots=n_slots, n_halo=n_halo, n_pulses=lay["n_pulses"], build_ms=build_ms,
+        variant=variant,
+        step_s=step_s, steps=steps_done, gpu_step_us=round(avg_step_gpu * 1e6, 3),
+        roofline=dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel,
+                      launches_per_step=launches_per_step,
+                      algorithmic_bytes_per_step=step_bytes,
+                      avg_launch_us=round(avg_launch * 1e6, 3),
+                      p10_step_us=round(durs[len(durs) // 10] * 1e6, 3),
+                      p90_step_us=round(durs[(9 * len(durs)) // 10] * 1e6, 3)),
+    )
+    plan.close()
+    return res
+
+
+# ------------------------------------------------------------- CPU baseline
+
+def run_cpu_baseline(w, seconds: float):
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    x = W.positions(w)
+    ref = oracle.OraclePlan(x, **w.params())
+    threads = max(1, min(ref.n_domains, os.cpu_count() or 1, 16,
+                         int(os.environ.get("OMP_NUM_THREADS", "16") or 16)))
+    xl = ref.x_local.copy()
+    f = W.forces(w, ref.n_slots)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        ref.exchange_coords(xl, nthreads=threads)
+        ref.exchange_forces(f, nthreads=threads)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or steps >= 100000:
+            break
+    per_step = el / steps
+    return dict(value=round(ref.halo_atoms / per_step, 1), unit="halo atoms/s", cores=threads,
+                kind="oracle",
+                sample=(f"{steps} steps (coordinate + force pass) of workload {w.name} "
+                        f"in {el:.1f} s, OpenMP over domains, maps prebuilt "
+                        f"(oracle map build {ref.build_seconds * 1e3:.0f} ms)"),
+                us_per_step=round(per_step * 1e6, 2))
+
+
+# --------------------------------------------------------- counter summary
+
+def summarize_pmc(fetch_csv, write_csv, variant, wname, copy_mb, command):
+    """Turn two rocprofv3 --pmc runs into profiles/traffic_<variant>_<wname>.md."""
+    def rows(path):
+        with open(path) as fh:
+            return list(csv.DictReader(fh))
+
+    def per_kernel(rows_, counter):
+        out = {}
+        for r in rows_:
+            name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+            if r.get("Counter_Name", counter) != counter:
+                continue
+            v = float(r.get("Counter_Value") or r.get(counter) or 0.0)
+            out.setdefault(name, []).append(v)
+        return out
+
+    fk = per_kernel(rows(fetch_csv), "FETCH_SIZE")
+    wk = per_kernel(rows(write_csv), "WRITE_SIZE")
+    ex = [k for k in fk if "exchange_kernel" in k]
+    cp = [k for k in fk if "copy" in k.lower() or "elementwise" in k.lower()]
+    if not ex or not cp:
+        raise SystemExit(f"kernels not found: exchange={ex} copy={cp}")
+    import statistics
+    f_ex = statistics.median(fk[ex[0]])
+    w_ex = statistics.median(wk[ex[0]])
+    # the copy probe: the largest copy-like dispatch
+    cbest = max(cp, key=lambda k: max(fk[k]))
+    f_cp = max(fk[cbest])
+    w_cp = max(wk.get(cbest, [0.0]))
+    expect_kib = copy_mb * 1024.0
+    sf = expect_kib / f_cp if f_cp else 1.0
+    sw = expect_kib / w_cp if w_cp else 1.0
+    traffic = (f_ex * sf + w_ex * sw) * 1024.0
+    path = traffic_file(variant, wname)
+    with open(path, "w") as fh:
+        fh.write(f"# HBM traffic of exchange_kernel, variant {variant}, workload {wname}\n\n")
+        fh.write("Two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),\n"
+                 "scaled by what the same counters read for a plain copy of known size.\n\n")
+        fh.write(f"Command (each counter in its own run):\n\n```\n{command}\n```\n\n")
+        fh.write(f"- kernel_source_sha256: `{kernel_hash()}`\n")
+        fh.write(f"- kernel: `{ex[0][:90]}`\n")
+        fh.write(f"- dispatches: {len(fk[ex[0]])}\n")
+        fh.write(f"- FETCH_SIZE_KiB_per_dispatch (median): {f_ex:.1f}\n")
+        fh.write(f"- WRITE_SIZE_KiB_per_dispatch (median): {w_ex:.1f}\n")
+        fh.write(f"- copy_probe_kernel: `{cbest[:90]}`\n")
+        fh.write(f"- copy_probe_MiB: {copy_mb}\n")
+        fh.write(f"- copy_probe_FETCH_KiB: {f_cp:.1f}\n")
+        fh.write(f"- copy_probe_WRITE_KiB: {w_cp:.1f}\n")
+        fh.write(f"- scale_fetch: {sf:.4f}\n")
+        fh.write(f"- scale_write: {sw:.4f}\n")
+        fh.write(f"- traffic_bytes_per_launch: {traffic:.0f}\n")
+    print(path)
+
+
+# ------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--variant", default="auto", choices=VARIANTS)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--block", type=int, default=0, choices=[0, 256, 1024])
+    ap.add_argument("--cold", action="store_true", help="evict caches before every step")
+    ap.add_argument("--graph-steps", type=int, default=50,
+                    help="steps captured per graph replay in the timed region")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
+                    help="after timing, copy a buffer of this size (counter scaling)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--pmc-command", default="")
+    args = ap.parse_args()
+
+    import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    if args.summarize_pmc:
+        if args.variant == "auto":
+            sys.exit("--summarize-pmc names the variant the counters were taken on: "
+                     "pass --variant step|split|pulse")
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.variant, w.name,
+                      args.copy_probe, args.pmc_command)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: every domain is a virtual rank inside one "
+              f"GPU's HBM (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    if args.steps is None:
+        args.steps = 1000 if w.n_atoms <= 100_000 else 200
+
+    gpu = run_gpu(args, w)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = run_cpu_baseline(w, args.cpu_seconds)
+    step_s = gpu["step_s"]
+    value = gpu["n_halo"] / step_s
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "halo atoms/s",
+        "n_gpus": 1,
+        "steps": gpu["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 6),
+        "gpu_us_per_step": gpu["gpu_step_us"],
+        "us_per_step": round(step_s * 1e6, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "atoms": w.n_atoms, "box_nm": w.box32[0], "grid": list(w.grid),
+            "rc_nm": w.rc, "cell_nm": w.cell, "pulses": gpu["n_pulses"],
+            "halo_atoms_per_pass": gpu["n_halo"], "slots": gpu["n_slots"],
+            "variant": gpu["variant"], "cache": "cold" if args.cold else "warm",
+            "step": "coordinate pass + force pass",
+        },
+        "step_hbm_frac": round((BYTES_X + BYTES_F) * gpu["n_halo"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "map_build_ms": round(gpu["build_ms"], 3),
+        "roofline": gpu["roofline"],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -27,9 +27,14 @@ ERROR_NAMES = {DDH_EINVAL: "DDH_EINVAL", DDH_ERANGE: "DDH_ERANGE", DDH_ECAPACITY
                DDH_EHIP: "DDH_EHIP", DDH_ETIMEOUT: "DDH_ETIMEOUT", DDH_ENOTIMPL: "DDH_ENOTIMPL",
                DDH_ESTATE: "DDH_ESTATE"}
 DDH_MAX_PULSES = 16
-DDH_MODE_FUSED, DDH_MODE_PULSE, DDH_MODE_GRAPH = 0, 1, 16
+DDH_MODE_FUSED, DDH_MODE_PULSE, DDH_MODE_AUTO, DDH_MODE_GRAPH = 0, 1, 2, 16
+DDH_AUTO_FUSED_MAX = 200000
 DDH_TUNE_CHUNK, DDH_TUNE_GRID, DDH_TUNE_SPIN_LIMIT, DDH_TUNE_FORCE_TIMEOUT, DDH_TUNE_REFINED_WAITS = (
     1, 2, 3, 4, 5)
+DDH_TUNE_TRACE = 6
+DDH_TUNE_BLOCK = 7
+TRACE_RECORDS = 64
+TRACE_EVENTS = {1: "start", 2: "claim", 3: "head", 4: "waited", 5: "chunk", 6: "publish", 7: "exit"}
 
 # every symbol declared in include/ddh.h
 EXPORTS = ("ddh_plan_create", "ddh_plan_destroy", "ddh_last_error", "ddh_build_maps", "ddh_query",

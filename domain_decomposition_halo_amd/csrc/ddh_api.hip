@@ -313,8 +313,9 @@ int ddh_set_mode(ddh_plan* p, int32_t mode)
 {
     if (!p)
         return fail(DDH_EINVAL, "ddh_set_mode: null plan");
-    if (mode & ~(DDH_MODE_PULSE | DDH_MODE_GRAPH))
-        return fail(DDH_EINVAL, "ddh_set_mode: unknown mode bits");
+    const int32_t base = mode & ~DDH_MODE_GRAPH;
+    if (base != DDH_MODE_FUSED && base != DDH_MODE_PULSE && base != DDH_MODE_AUTO)
+        return fail(DDH_EINVAL, "ddh_set_mode: unknown mode");
     p->mode = mode;
     return DDH_OK;
 }
@@ -364,6 +365,14 @@ int ddh_tune(ddh_plan* p, int32_t key, int64_t value)
         return DDH_OK;
     case DDH_TUNE_REFINED_WAITS:
         p->refined_waits = value != 0;
+        return DDH_OK;
+    case DDH_TUNE_BLOCK:
+        if (value != 0 && value != 256 && value != 1024)
+            return fail(DDH_EINVAL, "ddh_tune: block must be 0, 256 or 1024");
+        p->block_req = (int)value;
+        return DDH_OK;
+    case DDH_TUNE_TRACE:
+        p->trace = (uint64_t*)(uintptr_t)value;
         return DDH_OK;
     default:
         return fail(DDH_EINVAL, "ddh_tune: unknown key");

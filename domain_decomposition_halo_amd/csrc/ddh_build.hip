@@ -439,15 +439,13 @@ void free_built(Plan* p)
         (void)hipFree(q);
     p->owned.clear();
     p->d_maps = p->d_slot_gid = p->d_home_gid = p->d_home_slot = nullptr;
-    p->d_items = nullptr;
-    p->d_xch_fused = p->d_xch_pulse = p->d_fch = nullptr;
-    p->d_ctrl = p->d_xflag = p->d_fflag = p->d_xcnt = p->d_fcnt = nullptr;
+    p->d_xch = p->d_fch = nullptr;
+    p->d_ctrl = p->d_xcnt = p->d_fcnt = p->d_xneed = p->d_fneed = p->d_pflag = nullptr;
     p->built = false;
     p->n_slots = p->n_halo = 0;
     p->n_atoms = 0;
-    p->items.clear();
-    p->xch_fused.clear();
-    p->xch_pulse.clear();
+    p->nchunks.clear();
+    p->xch.clear();
     p->fch.clear();
 }
 
@@ -472,109 +470,120 @@ static void make_work_tables(Plan* p, const std::vector<int32_t>& maps)
                 inmap[(size_t)(p->base[S] + m[i])] |= 1u << q;
         }
 
-    struct Cut { int item, begin, end; bool tail; };
-    std::vector<std::vector<Cut>> cuts((size_t)D * P);
-    for (int S = 0; S < D; S++)
-        for (int q = 0; q < P; q++) {
-            const int it = S * P + q;
-            auto& v = cuts[it];
-            const int split = p->split[it], send = p->send[it];
-            for (int b = 0; b < split; b += CH)
-                v.push_back({it, b, std::min(b + CH, split), false});
-            for (int b = split; b < send; b += CH)
-                v.push_back({it, b, std::min(b + CH, send), true});
-            if (v.empty())
-                v.push_back({it, 0, 0, false});
-            p->items[it].nchunks = (int)v.size();
-        }
+    p->nchunks.assign((size_t)D * P, 1);
+    for (int it = 0; it < D * P; it++)
+        p->nchunks[it] = std::max(1, (p->send[it] + CH - 1) / CH);
 
-    auto xwait = [&](const Cut& c) -> uint32_t {
-        if (!c.tail)
-            return 0u;
-        const int S = c.item / P, q = c.item % P;
-        if (!p->refined_waits)
-            return (1u << q) - 1u;
-        uint32_t w = 0;
-        const int32_t* m = maps.data() + p->map_off[c.item];
-        for (int i = c.begin; i < c.end; i++)
-            w |= 1u << rid[(size_t)(p->base[S] + m[i])];
-        return w;
-    };
-    auto fwait = [&](const Cut& c, uint32_t& wa, uint32_t& wb) {
-        const int S = c.item / P, q = c.item % P;
-        const uint32_t later = ~((2u << q) - 1u) & ((1u << P) - 1u);
-        if (!p->refined_waits) {
-            wa = wb = later;
-            return;
-        }
-        wa = wb = 0;
-        const int32_t* m = maps.data() + p->map_off[c.item];
-        for (int i = c.begin; i < c.end; i++)
-            wa |= inmap[(size_t)(p->base[S] + m[i])];
-        const int R = p->recv[c.item];
-        const int64_t b = p->base[R] + p->roff[c.item];
-        for (int i = c.begin; i < c.end; i++)
-            wb |= inmap[(size_t)(b + i)];
-        wa &= later;
-        wb &= later;
-    };
-    auto xchunk = [&](const Cut& c) {
+    auto base_chunk = [&](int it) {
+        const int S = it / P, q = it % P;
         DChunk d{};
-        d.item = c.item;
-        d.begin = c.begin;
-        d.end = c.end;
-        d.wait_a = xwait(c);
+        d.src_base = (int32_t)p->base[S];
+        d.R = p->recv[it];
+        d.dst_base = (int32_t)(p->base[d.R] + p->roff[it]);
+        d.map_off = (int32_t)p->map_off[it];
+        d.flags = g.pdim[q] | (p->shift[it] ? kChunkShift : 0);
+        d.shift = g.L[g.pdim[q]];
+        d.S = S;
+        d.p = q;
+        return d;
+    };
+    // coordinates: the k-th slice of the independent head and of the
+    // dependent tail; the chunk advances the counter of the region it fills
+    auto xchunk = [&](int it, int k) {
+        const int c = p->nchunks[it], h = p->split[it], tl = p->send[it] - h;
+        DChunk d = base_chunk(it);
+        d.hb = (int32_t)((int64_t)h * k / c);
+        d.he = (int32_t)((int64_t)h * (k + 1) / c);
+        d.tb = h + (int32_t)((int64_t)tl * k / c);
+        d.te = h + (int32_t)((int64_t)tl * (k + 1) / c);
+        d.ctr = d.R * P + d.p;
+        uint32_t w = 0;
+        if (d.te > d.tb) {
+            if (!p->refined_waits) {
+                w = (1u << d.p) - 1u;
+            } else {
+                const int32_t* m = maps.data() + p->map_off[it];
+                for (int i = d.tb; i < d.te; i++)
+                    w |= 1u << rid[(size_t)(p->base[d.S] + m[i])];
+            }
+        }
+        d.wait_a = w;
+        return d;
+    };
+    // forces: the k-th slice of the map; waits on the later pulses that add
+    // into the same slots of S or into the slots of R's region that it reads
+    auto fchunk = [&](int it, int k) {
+        const int c = p->nchunks[it], n = p->send[it];
+        DChunk d = base_chunk(it);
+        d.hb = (int32_t)((int64_t)n * k / c);
+        d.he = (int32_t)((int64_t)n * (k + 1) / c);
+        d.tb = d.te = d.he;
+        d.ctr = d.S * P + d.p;
+        const uint32_t later = ~((2u << d.p) - 1u) & ((1u << P) - 1u);
+        if (!p->refined_waits) {
+            d.wait_a = d.wait_b = later;
+        } else {
+            uint32_t wa = 0, wb = 0;
+            const int32_t* m = maps.data() + p->map_off[it];
+            const int64_t rb = p->base[d.R] + p->roff[it];
+            for (int i = d.hb; i < d.he; i++) {
+                wa |= inmap[(size_t)(p->base[d.S] + m[i])];
+                wb |= inmap[(size_t)(rb + i)];
+            }
+            d.wait_a = wa & later;
+            d.wait_b = wb & later;
+        }
         return d;
     };
 
-    p->xch_fused.clear();
-    p->xch_pulse.clear();
+    p->xch.clear();
     p->fch.clear();
     p->xpulse_begin.assign((size_t)P + 1, 0);
     p->fpulse_begin.assign((size_t)P + 1, 0);
-    // fused: every independent head first, then the dependent tails, each in
-    // pulse order
-    for (int pass = 0; pass < 2; pass++)
-        for (int q = 0; q < P; q++)
-            for (int S = 0; S < D; S++)
-                for (const Cut& c : cuts[S * P + q])
-                    if (c.tail == (pass == 1))
-                        p->xch_fused.push_back(xchunk(c));
-    // pulse mode: one ticket range per pulse
+    // coordinates in pulse order (a chunk waits only on earlier pulses)
     for (int q = 0; q < P; q++) {
-        p->xpulse_begin[q] = (int)p->xch_pulse.size();
-        for (int pass = 0; pass < 2; pass++)
-            for (int S = 0; S < D; S++)
-                for (const Cut& c : cuts[S * P + q])
-                    if (c.tail == (pass == 1))
-                        p->xch_pulse.push_back(xchunk(c));
+        p->xpulse_begin[q] = (int)p->xch.size();
+        for (int S = 0; S < D; S++)
+            for (int k = 0; k < p->nchunks[S * P + q]; k++)
+                p->xch.push_back(xchunk(S * P + q, k));
     }
-    p->xpulse_begin[P] = (int)p->xch_pulse.size();
-    // forces: decreasing pulse order
+    p->xpulse_begin[P] = (int)p->xch.size();
+    // forces in decreasing pulse order (a chunk waits only on later pulses)
     for (int r = 0; r < P; r++) {
         const int q = P - 1 - r;
         p->fpulse_begin[r] = (int)p->fch.size();
         for (int S = 0; S < D; S++)
-            for (const Cut& c : cuts[S * P + q]) {
-                DChunk d{};
-                d.item = c.item;
-                d.begin = c.begin;
-                d.end = c.end;
-                fwait(c, d.wait_a, d.wait_b);
-                p->fch.push_back(d);
-            }
+            for (int k = 0; k < p->nchunks[S * P + q]; k++)
+                p->fch.push_back(fchunk(S * P + q, k));
     }
     p->fpulse_begin[P] = (int)p->fch.size();
+
+    // a chunk publishes with a release fence only if a later chunk of the
+    // same launch waits on its counter (and so reads what it wrote)
+    std::vector<char> xread((size_t)D * P, 0), fread((size_t)D * P, 0);
+    for (const DChunk& c : p->xch)
+        for (uint32_t m = c.wait_a; m; m &= m - 1)
+            xread[(size_t)c.S * P + __builtin_ctz(m)] = 1;
+    for (const DChunk& c : p->fch) {
+        for (uint32_t m = c.wait_a; m; m &= m - 1)
+            fread[(size_t)c.S * P + __builtin_ctz(m)] = 1;
+        for (uint32_t m = c.wait_b; m; m &= m - 1)
+            fread[(size_t)c.R * P + __builtin_ctz(m)] = 1;
+    }
+    for (DChunk& c : p->xch)
+        if (xread[c.ctr])
+            c.flags |= kChunkRelease;
+    for (DChunk& c : p->fch)
+        if (fread[c.ctr])
+            c.flags |= kChunkRelease;
 }
 
-static int auto_chunk(int64_t n_halo)
-{
-    if (n_halo >= 2048ll * 1024)
-        return 1024;
-    if (n_halo >= 256ll * 512)
-        return 512;
-    return 256;
-}
+// Entries per work chunk: 4096. A small (latency-bound) pass then gives one
+// chunk per map, run by one 1024-wide work-group of the fused launch, which
+// keeps the number of device-wide serialized operations (ticket claims,
+// releases, acquires) per dependency stage small; a large pass run with
+// per-pulse launches gives blocks of two rounds of 8 entries per thread.
+static int auto_chunk(int64_t) { return 4096; }
 
 int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
 {
@@ -871,25 +880,8 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         DDH_HIP(hipStreamSynchronize(s));
     }
 
-    // ---- 5: work items and chunk tables
+    // ---- 5: chunk tables, counters
     p->chunk = p->chunk_req > 0 ? p->chunk_req : auto_chunk(nh);
-    p->items.assign(DP, DItem{});
-    for (int S = 0; S < D; S++)
-        for (int q = 0; q < P; q++) {
-            const int it = S * P + q;
-            DItem& m = p->items[it];
-            const int R = p->recv[it];
-            m.src_base = (int32_t)p->base[S];
-            m.dst_base = (int32_t)(p->base[R] + p->roff[it]);
-            m.map_off = (int32_t)p->map_off[it];
-            m.send = p->send[it];
-            m.comp = g.pdim[q];
-            m.do_shift = p->shift[it];
-            m.shift = g.L[g.pdim[q]];
-            m.S = S;
-            m.R = R;
-            m.p = q;
-        }
     std::vector<int32_t> hmaps((size_t)nh);
     if (nh > 0)
         DDH_HIP(hipMemcpyAsync(hmaps.data(), p->d_maps, sizeof(int32_t) * nh,
@@ -897,21 +889,27 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     DDH_HIP(hipStreamSynchronize(s));
     make_work_tables(p, hmaps);
 
-    DDH_HIP(owned_alloc(p, &p->d_items, p->items.size()));
-    DDH_HIP(owned_alloc(p, &p->d_xch_fused, p->xch_fused.size()));
-    DDH_HIP(owned_alloc(p, &p->d_xch_pulse, p->xch_pulse.size()));
+    std::vector<uint32_t> xneed(DP, 0u), fneed(DP, 0u);
+    for (int S = 0; S < D; S++)
+        for (int q = 0; q < P; q++) {
+            const int it = S * P + q;
+            xneed[(size_t)p->recv[it] * P + q] = (uint32_t)p->nchunks[it];
+            fneed[it] = (uint32_t)p->nchunks[it];
+        }
+    DDH_HIP(owned_alloc(p, &p->d_xch, p->xch.size()));
     DDH_HIP(owned_alloc(p, &p->d_fch, p->fch.size()));
-    DDH_HIP(upload(p->d_items, p->items, s));
-    DDH_HIP(upload(p->d_xch_fused, p->xch_fused, s));
-    DDH_HIP(upload(p->d_xch_pulse, p->xch_pulse, s));
+    DDH_HIP(upload(p->d_xch, p->xch, s));
     DDH_HIP(upload(p->d_fch, p->fch, s));
-    const size_t words = (size_t)kCtrlWords + 4 * DP;
+    const size_t words = (size_t)kCtrlWords + 4 * DP + 2 * (size_t)DDH_MAX_PULSES;
     DDH_HIP(owned_alloc(p, &p->d_ctrl, words));
     DDH_HIP(hipMemsetAsync(p->d_ctrl, 0, sizeof(uint32_t) * words, s));
-    p->d_xflag = p->d_ctrl + kCtrlWords;
-    p->d_fflag = p->d_xflag + DP;
-    p->d_xcnt = p->d_fflag + DP;
+    p->d_xcnt = p->d_ctrl + kCtrlWords;
     p->d_fcnt = p->d_xcnt + DP;
+    p->d_xneed = p->d_fcnt + DP;
+    p->d_fneed = p->d_xneed + DP;
+    p->d_pflag = p->d_fneed + DP;
+    DDH_HIP(upload(p->d_xneed, xneed, s));
+    DDH_HIP(upload(p->d_fneed, fneed, s));
     DDH_HIP(hipStreamSynchronize(s));
     p->built = true;
     return DDH_OK;

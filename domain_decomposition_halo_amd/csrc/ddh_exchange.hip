@@ -4,39 +4,44 @@
 // Source ("the guide"): NVIDIA technical blog "A Practical Guide to
 // GPU-Initiated Communication for Molecular Dynamics at Scale".
 //
-// Design on one MI355X. Every domain is a slice of one device array, so the
-// guide's direct-store path ("Optimizing for efficient transfers across
-// NVIDIA NVLink-connected GPUs") is the only path: a sender gathers its map
-// entries and stores them straight into the receiver's slots; nothing is
-// staged and nothing is "put". The work of a pass is cut into chunks (an
-// entry range of one (sender, pulse) map) listed in a ticket table; a launch
-// claims tickets in table order with one atomic per chunk, so a chunk only
-// ever waits on chunks claimed before it and the launch cannot deadlock,
-// whatever the grid size.
+// Every domain is a slice of one device array, so the guide's direct-store
+// path ("Optimizing for efficient transfers across NVIDIA NVLink-connected
+// GPUs") is the only path: a sender gathers its map entries and stores them
+// straight into the receiver's slots; nothing is staged and nothing is "put".
+// The work of a pass is cut into chunks (DChunk: a slice of one (sender,
+// pulse) map). Two ways to run them:
 //
-//  - Coordinates ("Enabling parallelism across pulses through kernel fusion",
-//    "Dependency-aware packing"): the ticket table lists the independent
-//    heads of every map first (entries below the sender's home count), in
-//    pulse order, then the dependent tails in pulse order. A tail chunk waits
-//    until the regions its entries read have been delivered.
-//  - Forces ("Force halo exchange: Reversing the dependency chain"): chunks
-//    in decreasing pulse order. A chunk of (S, p) adds into slots of S and
-//    reads region p of R; it waits until the later pulses that add into the
-//    same slots of S, and those that add into R's region p, are done, so each
-//    slot receives its adds in decreasing pulse order and the result matches
-//    the sequential reverse pass bit for bit.
-//  - Completion ("Dependency-aware packing", hierarchical release): each
-//    work-group ends a chunk with one agent-scope acq_rel increment of the
-//    item's counter; the work-group that completes the item resets the
-//    counter and release-stores the pass number into the item's flag. All
-//    eight XCDs form one agent, so agent scope plays the role the guide gives
-//    to system scope.
-//  - Pass numbers: flags hold the number of the pass that set them; the
-//    number lives in device memory and the launch that ends a pass publishes
-//    it, so flags never need clearing and a captured graph replays as is.
-//  - Every wait is bounded by a spin limit; on expiry the wait records
-//    DDH_ETIMEOUT in the control block and the work-group carries on, so the
-//    launch always drains.
+//  - Per-pulse launches (DDH_MODE_PULSE; the guide's stream-ordered design of
+//    "Replacing host-side communication with NVSHMEM"): one launch per pulse,
+//    block b runs chunk b of the pulse; the stream orders the pulses, so no
+//    kernel waits, counts or fences. A one-thread launch afterwards publishes
+//    per-pulse flags. Best where bandwidth matters.
+//
+//  - One fused launch per call (DDH_MODE_FUSED; "Enabling parallelism across
+//    pulses through kernel fusion", "Dependency-aware packing", "Force halo
+//    exchange: Reversing the dependency chain"): work-groups claim chunks in
+//    ticket order (a chunk only ever waits on chunks claimed before it, so
+//    the launch cannot deadlock whatever the grid size). A coordinate chunk
+//    packs its independent slice, waits until the regions its dependent
+//    slice reads are complete, then packs that slice; a force chunk waits
+//    until the later pulses that add into the same slots of S, or into the
+//    slots of R's region it reads, are done, so each slot receives its adds
+//    in decreasing pulse order and matches the sequential reverse pass bit
+//    for bit. Best where latency matters.
+//
+// Completion in the fused launch ("Dependency-aware packing", hierarchical
+// release): a chunk ends with one agent-scope release fence and relaxed
+// increments of its map's counter (and of the coordinate-chunk total). The
+// counters only grow, one step per chunk and pass, so a waiter polls until a
+// counter reaches pass * chunks-per-pass and then acquires: every increment
+// continues the release sequence of the earlier ones, and no counter or flag
+// is ever reset. All eight XCDs form one agent, so agent scope plays the role
+// the guide gives to system scope. On MI355X each agent-scope fence and each
+// same-address atomic is serialized device-wide (tens of ns), which is why
+// chunks are large and a chunk issues one fence, not one per entry.
+//
+// Every wait is bounded by a spin limit; on expiry it records DDH_ETIMEOUT in
+// the control block and the work-group carries on, so every launch drains.
 #pragma clang fp contract(off)
 
 #include "ddh_internal.h"
@@ -55,132 +60,198 @@ __device__ __forceinline__ void st_relaxed(uint32_t* p, uint32_t v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Spin until *p == v or the spin limit expires (then record the timeout).
-__device__ void wait_eq(const uint32_t* p, uint32_t v, const XArgs& a)
+__device__ __forceinline__ void add_relaxed(uint32_t* p, uint32_t v)
 {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Event log of thread 0 (see kTraceRecords); a no-op without a buffer.
+__device__ __forceinline__ void trace_rec(const XArgs& a, int& n, uint32_t code, uint32_t info)
+{
+    if (a.trace && n < kTraceRecords) {
+        uint64_t* r = a.trace + 2ull * ((uint64_t)blockIdx.x * kTraceRecords + n);
+        r[0] = ((uint64_t)code << 32) | info;
+        r[1] = wall_clock64();
+        n++;
+    }
+}
+
+// Index of the n-th set bit of m (n < popcount(m)).
+__device__ __forceinline__ int nth_bit(uint32_t m, int n)
+{
+    for (; n > 0; n--)
+        m &= m - 1;
+    return __builtin_ctz(m);
+}
+
+// Wave 0 waits for every counter a chunk needs at once: lane l polls the
+// l-th of (the coordinate-chunk total, if need_x; the counters of the pulses
+// in mask_a at row_a; those in mask_b at row_b), so one round trip checks
+// them all. The loop exit is a wave-wide vote. Ends with an acquire fence.
+__device__ void wave_wait(const XArgs& a, const uint32_t* cnt, const uint32_t* need, uint32_t pass,
+                          bool need_x, uint32_t px, uint32_t mask_a, int row_a, uint32_t mask_b,
+                          int row_b, uint32_t bump)
+{
+    const int lane = (int)(threadIdx.x & 63);
+    const uint32_t* ptr = nullptr;
+    uint32_t target = 0;
+    int l = lane;
+    if (need_x) {
+        if (l == 0) {
+            ptr = a.ctrl + kCtrlXDone;
+            target = px * (uint32_t)a.n_xchunks + bump;
+        }
+        l--;
+    }
+    const int na = __builtin_popcount(mask_a);
+    if (!ptr && l >= 0 && l < na) {
+        const int r = row_a + nth_bit(mask_a, l);
+        ptr = cnt + r;
+        target = pass * need[r] + bump;
+    } else if (!ptr && l >= na && l - na < __builtin_popcount(mask_b)) {
+        const int r = row_b + nth_bit(mask_b, l - na);
+        ptr = cnt + r;
+        target = pass * need[r] + bump;
+    }
     uint32_t n = 0;
-    while (ld_relaxed(p) != v) {
+    for (;;) {
+        const bool ok = !ptr || (int32_t)(ld_relaxed(ptr) - target) >= 0;
+        if (__all(ok))
+            break;
         if (++n >= a.spin_limit) {
-            uint32_t zero = 0;
-            __hip_atomic_compare_exchange_strong(a.ctrl + kCtrlError, &zero,
-                                                 (uint32_t)DDH_ETIMEOUT, __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return;
+            if (lane == 0) {
+                uint32_t zero = 0;
+                __hip_atomic_compare_exchange_strong(a.ctrl + kCtrlError, &zero,
+                                                     (uint32_t)DDH_ETIMEOUT, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            break;
         }
         __builtin_amdgcn_s_sleep(1);
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-// One work-group finished a chunk of an item: count it; the work-group that
-// completes the item resets the counter and publishes the item's flag.
-__device__ void finish_chunk(uint32_t* cnt, uint32_t nchunks, uint32_t* flag, uint32_t pass,
-                             uint32_t* xdone)
+// Map entries of one round: entry i0 + e * B + tid for e < E (B threads).
+template <int E, int B>
+__device__ __forceinline__ void load_map(const int32_t* map, int i0, int end, int (&j)[E])
 {
-    uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == nchunks - 1u) {
-        st_relaxed(cnt, 0u);
-        __hip_atomic_store(flag, pass, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        if (xdone)
-            __hip_atomic_fetch_add(xdone, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        const int i = i0 + e * B + (int)threadIdx.x;
+        j[e] = i < end ? map[i] : -1;
     }
 }
 
-// Coordinates: x[dst + i] = x[src + map[i]] (+ L on the pulse's component).
-// Each thread holds E records: all map loads, then all gathers, then all
-// stores, so a wavefront keeps 3E independent memory requests in flight.
-template <int E>
-__device__ void coords_chunk(const XArgs& a, const DItem& it, int begin, int end)
+// Coordinates, one round: x[dst + i] = x[src + map[i]] (+ L on the pulse's
+// component). All E gathers are issued before any store, so a wavefront
+// keeps 3E independent requests in flight. Stores are non-temporal: a region
+// is written once per pass and not re-read by the writing work-group.
+template <int E, int B>
+__device__ __forceinline__ void coords_round(const float* src, float* dst, const DChunk& c, int i0,
+                                             int end, const int (&j)[E])
 {
-    const int32_t* map = a.maps + it.map_off;
-    const float* src = a.x + 3ll * it.src_base;
-    float* dst = a.x + 3ll * it.dst_base;
-    for (int i0 = begin; i0 < end; i0 += kBlock * E) {
+    float v[E][3];
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        if (j[e] >= 0) {
+            const float* s = src + 3ll * j[e];
+            v[e][0] = s[0];
+            v[e][1] = s[1];
+            v[e][2] = s[2];
+        }
+    }
+    // uniform per-component branches keep v[][] in registers
+    if (c.flags & kChunkShift) {
+#pragma unroll
+        for (int k = 0; k < 3; k++)
+            if ((c.flags & 0xff) == k) {
+#pragma unroll
+                for (int e = 0; e < E; e++)
+                    v[e][k] = v[e][k] + c.shift;
+            }
+    }
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        const int i = i0 + e * B + (int)threadIdx.x;
+        if (i < end) {
+            float* d = dst + 3ll * i;
+            __builtin_nontemporal_store(v[e][0], d);
+            __builtin_nontemporal_store(v[e][1], d + 1);
+            __builtin_nontemporal_store(v[e][2], d + 2);
+        }
+    }
+}
+
+// Forces, one round: f[src + map[i]] += f[dst + i] (the receiver's region
+// back into the sender's slots).
+template <int E, int B>
+__device__ __forceinline__ void forces_round(const float* from, float* tgt, int i0, int end,
+                                             const int (&j)[E])
+{
+    float s[E][3], t[E][3];
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        const int i = i0 + e * B + (int)threadIdx.x;
+        if (j[e] >= 0) {
+            const float* r = from + 3ll * i;
+            s[e][0] = r[0];
+            s[e][1] = r[1];
+            s[e][2] = r[2];
+            const float* q = tgt + 3ll * j[e];
+            t[e][0] = q[0];
+            t[e][1] = q[1];
+            t[e][2] = q[2];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        if (j[e] >= 0) {
+            float* q = tgt + 3ll * j[e];
+            __builtin_nontemporal_store(t[e][0] + s[e][0], q);
+            __builtin_nontemporal_store(t[e][1] + s[e][1], q + 1);
+            __builtin_nontemporal_store(t[e][2] + s[e][2], q + 2);
+        }
+    }
+}
+
+// Entries [begin, end) of a chunk's map; j0 holds the first round's map
+// entries (loaded by the caller, possibly before a wait).
+template <int E, int B>
+__device__ void coords_range(float* x, const int32_t* maps, const DChunk& c, int begin, int end,
+                             const int (&j0)[E])
+{
+    const int32_t* map = maps + c.map_off;
+    const float* src = x + 3ll * c.src_base;
+    float* dst = x + 3ll * c.dst_base;
+    coords_round<E, B>(src, dst, c, begin, end, j0);
+    for (int i0 = begin + B * E; i0 < end; i0 += B * E) {
         int j[E];
-        float v[E][3];
-#pragma unroll
-        for (int e = 0; e < E; e++) {
-            const int i = i0 + e * kBlock + (int)threadIdx.x;
-            j[e] = i < end ? map[i] : -1;
-        }
-#pragma unroll
-        for (int e = 0; e < E; e++) {
-            if (j[e] >= 0) {
-                const float* s = src + 3ll * j[e];
-                v[e][0] = s[0];
-                v[e][1] = s[1];
-                v[e][2] = s[2];
-            }
-        }
-        // uniform per-component branches keep v[][] in registers
-        if (it.do_shift) {
-#pragma unroll
-            for (int c = 0; c < 3; c++)
-                if (it.comp == c) {
-#pragma unroll
-                    for (int e = 0; e < E; e++)
-                        v[e][c] = v[e][c] + it.shift;
-                }
-        }
-#pragma unroll
-        for (int e = 0; e < E; e++) {
-            const int i = i0 + e * kBlock + (int)threadIdx.x;
-            if (i < end) {
-                float* d = dst + 3ll * i;
-                d[0] = v[e][0];
-                d[1] = v[e][1];
-                d[2] = v[e][2];
-            }
-        }
+        load_map<E, B>(map, i0, end, j);
+        coords_round<E, B>(src, dst, c, i0, end, j);
     }
 }
 
-// Forces: f[src + map[i]] += f[dst + i] (the receiver's region back into the
-// sender's slots).
-template <int E>
-__device__ void forces_chunk(const XArgs& a, const DItem& it, int begin, int end)
+template <int E, int B>
+__device__ void forces_range(float* f, const int32_t* maps, const DChunk& c, int begin, int end,
+                             const int (&j0)[E])
 {
-    const int32_t* map = a.maps + it.map_off;
-    float* tgt = a.f + 3ll * it.src_base;
-    const float* from = a.f + 3ll * it.dst_base;
-    for (int i0 = begin; i0 < end; i0 += kBlock * E) {
+    const int32_t* map = maps + c.map_off;
+    float* tgt = f + 3ll * c.src_base;
+    const float* from = f + 3ll * c.dst_base;
+    forces_round<E, B>(from, tgt, begin, end, j0);
+    for (int i0 = begin + B * E; i0 < end; i0 += B * E) {
         int j[E];
-        float s[E][3], t[E][3];
-#pragma unroll
-        for (int e = 0; e < E; e++) {
-            const int i = i0 + e * kBlock + (int)threadIdx.x;
-            j[e] = i < end ? map[i] : -1;
-            if (j[e] >= 0) {
-                const float* r = from + 3ll * i;
-                s[e][0] = r[0];
-                s[e][1] = r[1];
-                s[e][2] = r[2];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < E; e++) {
-            if (j[e] >= 0) {
-                const float* q = tgt + 3ll * j[e];
-                t[e][0] = q[0];
-                t[e][1] = q[1];
-                t[e][2] = q[2];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < E; e++) {
-            if (j[e] >= 0) {
-                float* q = tgt + 3ll * j[e];
-                q[0] = t[e][0] + s[e][0];
-                q[1] = t[e][1] + s[e][1];
-                q[2] = t[e][2] + s[e][2];
-            }
-        }
+        load_map<E, B>(map, i0, end, j);
+        forces_round<E, B>(from, tgt, i0, end, j);
     }
 }
 
-__device__ __forceinline__ int grab_ticket(const XArgs& a)
+__device__ __forceinline__ int claim_ticket(const XArgs& a)
 {
-    return (int)__hip_atomic_fetch_add(a.ctrl + kCtrlTicket, 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+    const int t = (int)__hip_atomic_fetch_add(a.ctrl + kCtrlTicket, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    return a.static_first ? t + (int)gridDim.x : t;
 }
 
 // Thread 0 does every cross-work-group step (ticket claims, waits, chunk
@@ -190,82 +261,151 @@ __device__ __forceinline__ int grab_ticket(const XArgs& a)
 // back edge: a region that did (finish at the end of one iteration, claim at
 // the start of the next) lets the compiler park lane 0 outside the loop while
 // the other lanes pass the barrier and re-read a stale ticket forever.
-template <int E>
-__global__ __launch_bounds__(kBlock) void exchange_kernel(XArgs a)
+template <int E, int B>
+__global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
 {
     __shared__ int s_ticket;
-    const uint32_t pass = ld_relaxed(a.ctrl + kCtrlEpoch) + 1u;
-    const uint32_t want = a.force_timeout ? pass + 0x40000000u : pass;
-    const int nx = a.x_end - a.x_begin;
-    const int nt = nx + (a.f_end - a.f_begin);
     const int P = a.P;
+    const int nt = a.nx + a.nf;
+    const uint32_t bump = a.force_timeout ? 0x40000000u : 0u;  // a value nobody reaches
+    const uint32_t px = ld_relaxed(a.ctrl + kCtrlPassX) + (a.nx > 0 ? 1u : 0u);
+    const uint32_t pf = ld_relaxed(a.ctrl + kCtrlPassF) + 1u;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> 6;  // uniform: 0 in wave 0
 
-    if (threadIdx.x == 0)
-        s_ticket = grab_ticket(a);
+    int ntr = 0;  // trace records written by thread 0
+    if (threadIdx.x == 0) {
+        trace_rec(a, ntr, kTrStart, gridDim.x);
+        s_ticket = a.static_first ? (int)blockIdx.x : claim_ticket(a);
+    }
     __syncthreads();
     for (;;) {
         const int t = __builtin_amdgcn_readfirstlane(s_ticket);
         if (t >= nt)
             break;
-        if (t < nx) {
-            const DChunk c = a.xchunks[a.x_begin + t];
-            const DItem it = a.items[c.item];
+        if (threadIdx.x == 0)
+            trace_rec(a, ntr, kTrClaim, (uint32_t)t);
+        if (t < a.nx) {
+            const DChunk c = a.xchunks[t];
+            // the guide's two-pass pack at work-group level: the independent
+            // slice goes out first; the map entries of the dependent slice
+            // are loaded before the wait, its records packed after it
+            int jh[E], jt[E];
+            load_map<E, B>(a.maps + c.map_off, c.hb, c.he, jh);
+            load_map<E, B>(a.maps + c.map_off, c.tb, c.te, jt);
+            coords_range<E, B>(a.x, a.maps, c, c.hb, c.he, jh);
             if (c.wait_a) {
-                if (threadIdx.x == 0) {
-                    for (uint32_t m = c.wait_a; m; m &= m - 1)
-                        wait_eq(a.xflag + it.S * P + __builtin_ctz(m), want, a);
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                if (wave == 0) {
+                    if (threadIdx.x == 0)
+                        trace_rec(a, ntr, kTrHead, (uint32_t)(c.he - c.hb));
+                    wave_wait(a, a.xcnt, a.xneed, px, false, px, c.wait_a, c.S * P, 0u, 0, bump);
+                    if (threadIdx.x == 0)
+                        trace_rec(a, ntr, kTrWaited, c.wait_a);
                 }
                 __syncthreads();
             }
-            coords_chunk<E>(a, it, c.begin, c.end);
+            coords_range<E, B>(a.x, a.maps, c, c.tb, c.te, jt);
             __syncthreads();
             if (threadIdx.x == 0) {
-                finish_chunk(a.xcnt + c.item, (uint32_t)it.nchunks, a.xflag + it.R * P + it.p, pass,
-                             a.f_end > a.f_begin ? a.ctrl + kCtrlXDone : nullptr);
-                s_ticket = grab_ticket(a);
+                trace_rec(a, ntr, kTrChunk, (uint32_t)(c.he - c.hb + c.te - c.tb));
+                // forces never read coordinates, so the step's count of
+                // finished coordinate chunks needs no fence of its own
+                if (c.flags & kChunkRelease)
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                add_relaxed(a.xcnt + c.ctr, 1u);
+                add_relaxed(a.ctrl + kCtrlXDone, 1u);
+                trace_rec(a, ntr, kTrPublish, (uint32_t)c.ctr);
+                s_ticket = claim_ticket(a);
             }
             __syncthreads();
         } else {
-            const DChunk c = a.fchunks[a.f_begin + (t - nx)];
-            const DItem it = a.items[c.item];
-            if (threadIdx.x == 0) {
-                if (nx > 0)
-                    wait_eq(a.ctrl + kCtrlXDone,
-                            a.force_timeout ? (uint32_t)a.n_items + 0x40000000u : (uint32_t)a.n_items,
-                            a);
-                for (uint32_t m = c.wait_a; m; m &= m - 1)
-                    wait_eq(a.fflag + it.S * P + __builtin_ctz(m), want, a);
-                for (uint32_t m = c.wait_b; m; m &= m - 1)
-                    wait_eq(a.fflag + it.R * P + __builtin_ctz(m), want, a);
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            const DChunk c = a.fchunks[t - a.nx];
+            int j0[E];
+            load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);  // static: before any wait
+            if (a.nx > 0 || c.wait_a || c.wait_b) {
+                if (wave == 0) {
+                    // forces of a step start once every region is filled
+                    wave_wait(a, a.fcnt, a.fneed, pf, a.nx > 0, px, c.wait_a, c.S * P, c.wait_b,
+                              c.R * P, bump);
+                    if (threadIdx.x == 0)
+                        trace_rec(a, ntr, kTrWaited, c.wait_a | (c.wait_b << 16));
+                }
+                __syncthreads();
             }
-            __syncthreads();
-            forces_chunk<E>(a, it, c.begin, c.end);
+            forces_range<E, B>(a.f, a.maps, c, c.hb, c.he, j0);
             __syncthreads();
             if (threadIdx.x == 0) {
-                finish_chunk(a.fcnt + c.item, (uint32_t)it.nchunks, a.fflag + it.S * P + it.p, pass,
-                             nullptr);
-                s_ticket = grab_ticket(a);
+                trace_rec(a, ntr, kTrChunk, (uint32_t)(c.he - c.hb));
+                if (c.flags & kChunkRelease)
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                add_relaxed(a.fcnt + c.ctr, 1u);
+                trace_rec(a, ntr, kTrPublish, (uint32_t)(0x10000 | c.ctr));
+                s_ticket = claim_ticket(a);
             }
             __syncthreads();
         }
     }
 
-    // Leave: the last work-group re-arms the ticket counters for the next
-    // launch and, if this launch ends a pass, publishes the pass number.
+    // Leave: the last work-group re-arms the ticket counter for the next
+    // launch and publishes the numbers of the passes this launch completed.
     if (threadIdx.x == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(a.ctrl + kCtrlDone, 1u, __ATOMIC_ACQ_REL,
+        trace_rec(a, ntr, kTrExit, 0);
+        const uint32_t old = __hip_atomic_fetch_add(a.ctrl + kCtrlDone, 1u, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
         if (old == gridDim.x - 1u) {
             st_relaxed(a.ctrl + kCtrlTicket, 0u);
             st_relaxed(a.ctrl + kCtrlDone, 0u);
-            st_relaxed(a.ctrl + kCtrlXDone, 0u);
-            if (a.bump_epoch)
-                __hip_atomic_store(a.ctrl + kCtrlEpoch, pass, __ATOMIC_RELEASE,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            if (a.nx > 0)
+                st_relaxed(a.ctrl + kCtrlPassX, px);
+            if (a.nf > 0)
+                st_relaxed(a.ctrl + kCtrlPassF, pf);
         }
     }
+}
+
+// One pulse of one pass, ordered against the other pulses by the stream
+// alone: block b runs chunk begin + b of the pulse. No tickets, counters,
+// waits or fences: the kernel boundary publishes the writes.
+struct PArgs {
+    float* x;
+    float* f;
+    const int32_t* maps;
+    const DChunk* chunks;
+    int32_t begin;
+};
+
+template <int E, int OP>
+__global__ __launch_bounds__(kBlock) void pulse_kernel(PArgs a)
+{
+    const DChunk c = a.chunks[a.begin + (int)blockIdx.x];
+    int j0[E];
+    load_map<E, kBlock>(a.maps + c.map_off, c.hb, c.he, j0);
+    if (OP == kOpCoords) {
+        coords_range<E, kBlock>(a.x, a.maps, c, c.hb, c.he, j0);
+        if (c.te > c.tb) {
+            int jt[E];
+            load_map<E, kBlock>(a.maps + c.map_off, c.tb, c.te, jt);
+            coords_range<E, kBlock>(a.x, a.maps, c, c.tb, c.te, jt);
+        }
+    } else {
+        forces_range<E, kBlock>(a.f, a.maps, c, c.hb, c.he, j0);
+    }
+}
+
+// After the pulse launches of a call (stream-ordered, so complete): one
+// release, then the per-pulse flags of the finished passes and their number.
+__global__ void signal_kernel(uint32_t* ctrl, uint32_t* pflag, int P, int op)
+{
+    const uint32_t pass = ld_relaxed(ctrl + kCtrlPassP) + 1u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int q = threadIdx.x;
+    if (q < P) {
+        if (op & kOpCoords)
+            st_relaxed(pflag + q, pass);
+        if (op & kOpForces)
+            st_relaxed(pflag + P + q, pass);
+    }
+    if (q == 0)
+        st_relaxed(ctrl + kCtrlPassP, pass);
 }
 
 // x_local[home_slot[r]] = x_global[home_gid[r]] for every home atom r.
@@ -285,91 +425,101 @@ __global__ __launch_bounds__(kBlock) void gather_home_kernel(const float* __rest
     d[2] = s[2];
 }
 
-int entries_per_thread(int chunk)
+int launch_fused(const Plan* p, XArgs a, hipStream_t s)
 {
-    return chunk >= 4 * kBlock ? 4 : (chunk >= 2 * kBlock ? 2 : 1);
-}
-
-int launch(const Plan* p, const XArgs& a, int n_tickets, hipStream_t s)
-{
-    if (n_tickets <= 0)
+    const int nt = a.nx + a.nf;
+    if (nt <= 0)
         return DDH_OK;
-    int grid = p->grid_req > 0 ? p->grid_req : p->n_cu * 8;
-    if (grid > n_tickets)
-        grid = n_tickets;
-    const int E = entries_per_thread(p->chunk);
-    if (E == 4)
-        hipLaunchKernelGGL(exchange_kernel<4>, dim3(grid), dim3(kBlock), 0, s, a);
-    else if (E == 2)
-        hipLaunchKernelGGL(exchange_kernel<2>, dim3(grid), dim3(kBlock), 0, s, a);
-    else
-        hipLaunchKernelGGL(exchange_kernel<1>, dim3(grid), dim3(kBlock), 0, s, a);
+    int grid = p->grid_req > 0 ? p->grid_req : p->n_cu * 4;
+    if (grid > nt)
+        grid = nt;
+    // a grid of at most one work-group per compute unit can all be resident,
+    // so each work-group may take its first ticket without claiming it
+    a.static_first = grid <= p->n_cu ? 1 : 0;
+    // work-group width: 1024 lanes when the grid leaves compute units idle
+    // (few, latency-bound chunks), else 256; entries per lane and round from
+    // the chunk size
+    const bool wide = p->block_req ? p->block_req == 1024 : grid <= p->n_cu / 2;
+    const int lanes = wide ? 1024 : 256;
+    const int per = (p->chunk + lanes - 1) / lanes;
+    if (wide) {
+        if (per > 2)
+            hipLaunchKernelGGL((exchange_kernel<4, 1024>), dim3(grid), dim3(1024), 0, s, a);
+        else if (per > 1)
+            hipLaunchKernelGGL((exchange_kernel<2, 1024>), dim3(grid), dim3(1024), 0, s, a);
+        else
+            hipLaunchKernelGGL((exchange_kernel<1, 1024>), dim3(grid), dim3(1024), 0, s, a);
+    } else {
+        if (per > 8)
+            hipLaunchKernelGGL((exchange_kernel<16, 256>), dim3(grid), dim3(256), 0, s, a);
+        else if (per > 4)
+            hipLaunchKernelGGL((exchange_kernel<8, 256>), dim3(grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((exchange_kernel<4, 256>), dim3(grid), dim3(256), 0, s, a);
+    }
     DDH_HIP(hipGetLastError());
     return DDH_OK;
 }
 
-XArgs base_args(const Plan* p, float* x, float* f)
+int launch_pulse(const Plan* p, int op, float* x, float* f, const DChunk* table, int begin, int end,
+                 hipStream_t s)
 {
-    XArgs a{};
+    if (end <= begin)
+        return DDH_OK;
+    PArgs a{};
     a.x = x;
     a.f = f;
     a.maps = p->d_maps;
-    a.items = p->d_items;
-    a.xchunks = (p->mode & DDH_MODE_PULSE) ? p->d_xch_pulse : p->d_xch_fused;
-    a.fchunks = p->d_fch;
-    a.ctrl = p->d_ctrl;
-    a.xflag = p->d_xflag;
-    a.fflag = p->d_fflag;
-    a.xcnt = p->d_xcnt;
-    a.fcnt = p->d_fcnt;
-    a.P = p->g.P;
-    a.n_items = (int32_t)p->items.size();
-    a.force_timeout = p->force_timeout;
-    a.spin_limit = p->spin_limit;
-    return a;
+    a.chunks = table;
+    a.begin = begin;
+    const dim3 grid(end - begin), block(kBlock);
+    if (op == kOpCoords)
+        hipLaunchKernelGGL((pulse_kernel<8, kOpCoords>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((pulse_kernel<8, kOpForces>), grid, block, 0, s, a);
+    DDH_HIP(hipGetLastError());
+    return DDH_OK;
 }
 
 // The launches of one call, enqueued on s.
 int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s)
 {
     const int P = p->g.P;
-    const int nx = (int)p->xch_fused.size();
-    const int nf = (int)p->fch.size();
-    if (!(p->mode & DDH_MODE_PULSE)) {
-        XArgs a = base_args(p, x, f);
-        a.bump_epoch = 1;
-        if (op & kOpCoords) {
-            a.x_begin = 0;
-            a.x_end = nx;
-        }
-        if (op & kOpForces) {
-            a.f_begin = 0;
-            a.f_end = nf;
-        }
-        return launch(p, a, (a.x_end - a.x_begin) + (a.f_end - a.f_begin), s);
+    if (!(p->effective_mode() & DDH_MODE_PULSE)) {
+        XArgs a{};
+        a.x = x;
+        a.f = f;
+        a.maps = p->d_maps;
+        a.xchunks = p->d_xch;
+        a.fchunks = p->d_fch;
+        a.nx = (op & kOpCoords) ? (int)p->xch.size() : 0;
+        a.nf = (op & kOpForces) ? (int)p->fch.size() : 0;
+        a.ctrl = p->d_ctrl;
+        a.xcnt = p->d_xcnt;
+        a.fcnt = p->d_fcnt;
+        a.xneed = p->d_xneed;
+        a.fneed = p->d_fneed;
+        a.P = P;
+        a.n_xchunks = (int)p->xch.size();
+        a.force_timeout = p->force_timeout;
+        a.spin_limit = p->spin_limit;
+        a.trace = p->trace;
+        return launch_fused(p, a, s);
     }
-    // one launch per pulse; the stream orders them, the flags are still set
-    std::vector<XArgs> seq;
+    // one launch per pulse: coordinates in increasing, forces in decreasing
+    // pulse order; then the per-pulse flags
+    int rc = DDH_OK;
     if (op & kOpCoords)
-        for (int q = 0; q < P; q++) {
-            XArgs a = base_args(p, x, f);
-            a.x_begin = p->xpulse_begin[q];
-            a.x_end = p->xpulse_begin[q + 1];
-            seq.push_back(a);
-        }
+        for (int q = 0; q < P && !rc; q++)
+            rc = launch_pulse(p, kOpCoords, x, f, p->d_xch, p->xpulse_begin[q],
+                              p->xpulse_begin[q + 1], s);
     if (op & kOpForces)
-        for (int q = P - 1; q >= 0; q--) {
-            XArgs a = base_args(p, x, f);
-            a.f_begin = p->fpulse_begin[P - 1 - q];
-            a.f_end = p->fpulse_begin[P - q];
-            seq.push_back(a);
-        }
-    for (size_t i = 0; i < seq.size(); i++) {
-        seq[i].bump_epoch = (i + 1 == seq.size());
-        int rc = launch(p, seq[i], (seq[i].x_end - seq[i].x_begin) + (seq[i].f_end - seq[i].f_begin), s);
-        if (rc)
-            return rc;
-    }
+        for (int r = 0; r < P && !rc; r++)
+            rc = launch_pulse(p, kOpForces, x, f, p->d_fch, p->fpulse_begin[r], p->fpulse_begin[r + 1], s);
+    if (rc)
+        return rc;
+    hipLaunchKernelGGL(signal_kernel, dim3(1), dim3(64), 0, s, p->d_ctrl, p->d_pflag, P, op);
+    DDH_HIP(hipGetLastError());
     return DDH_OK;
 }
 
@@ -377,12 +527,12 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s)
 
 int enqueue_exchange(Plan* p, int op, float* x, float* f, hipStream_t s)
 {
-    if (p->g.P == 0 || p->items.empty())
+    if (p->g.P == 0 || p->nchunks.empty())
         return DDH_OK;
     if (!(p->mode & DDH_MODE_GRAPH))
         return enqueue_raw(p, op, x, f, s);
 
-    const auto key = std::make_tuple(op, (void*)x, (void*)f, p->mode);
+    const auto key = std::make_tuple(op, (void*)x, (void*)f, p->effective_mode());
     auto found = p->graphs.find(key);
     if (found == p->graphs.end()) {
         if (!p->capture_stream)

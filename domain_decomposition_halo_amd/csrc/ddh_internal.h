@@ -14,65 +14,83 @@
 
 namespace ddh {
 
-// Work-group size of every exchange kernel: four 64-wide wavefronts.
+// Work-group size of the per-pulse and helper kernels (four 64-wide
+// wavefronts); the fused launch picks 256 or 1024.
 constexpr int kBlock = 256;
 
-// Control words, each on its own 256-byte line (index in uint32 units).
+// Control words, each on its own 128-byte line (index in uint32 units).
 enum CtrlWord : int {
-    kCtrlEpoch = 0,    // last completed pass number
-    kCtrlTicket = 64,  // next work ticket of the running launch
-    kCtrlDone = 128,   // work-groups that left the running launch
-    kCtrlXDone = 192,  // coordinate items completed in a fused step launch
-    kCtrlError = 256,  // first device-side error code (0 = none)
-    kCtrlWords = 320
+    kCtrlPassX = 0,    // fused coordinate passes completed
+    kCtrlPassF = 32,   // fused force passes completed
+    kCtrlPassP = 64,   // passes of the per-pulse mode completed
+    kCtrlTicket = 96,  // next dynamic work ticket of the running fused launch
+    kCtrlDone = 128,   // work-groups that left the running fused launch
+    kCtrlXDone = 160,  // coordinate chunks completed over all fused passes
+    kCtrlError = 192,  // first device-side error code (0 = none)
+    kCtrlWords = 224
 };
 
-// One (sender S, pulse p) map: 64 bytes, read with scalar loads.
-struct DItem {
-    int32_t src_base;  // first slot of sender S
-    int32_t dst_base;  // first slot of the region at receiver R
-    int32_t map_off;   // first entry of the map in the map array
-    int32_t send;      // map entries
-    int32_t comp;      // pulse dimension d
-    int32_t do_shift;  // 1: component d gets + shift
-    float shift;       // L_d
-    int32_t S, R, p;
-    int32_t nchunks;   // chunks of this item (same in every chunk table)
-    int32_t pad[5];
-};
-static_assert(sizeof(DItem) == 64, "DItem layout");
-
-// One work chunk: a contiguous entry range of one item's map. 32 bytes.
+// One work chunk of one (sender S, pulse p) map: 64 bytes, read with one
+// scalar load. A map with c chunks gives chunk k the k-th of c slices of its
+// independent head (entries below the sender's home count) and, for the
+// coordinate pass, the k-th slice of its dependent tail (forwarded records),
+// so the dependent work of a map is spread over c work-groups.
 struct DChunk {
-    int32_t item;
-    int32_t begin, end;  // entry range [begin, end) of the item's map
-    uint32_t wait_a;     // coords: pulses q whose region at S must be complete
-                         // forces: later pulses q whose (S, q) item must be done
-    uint32_t wait_b;     // forces: later pulses q whose (R, q) item must be done
-    int32_t pad[3];
+    int32_t hb, he;      // independent entries [hb, he) of the map
+    int32_t tb, te;      // coordinates: dependent entries [tb, te); forces: empty
+    uint32_t wait_a;     // coords: pulses q whose region at S the tail reads
+                         // forces: later pulses q whose (S, q) map must be done
+    uint32_t wait_b;     // forces: later pulses q whose (R, q) map must be done
+    int32_t src_base;    // first slot of sender S
+    int32_t dst_base;    // first slot of the region at receiver R
+    int32_t map_off;     // first entry of the (S, p) map in the map array
+    int32_t flags;       // bits 0-7: pulse dimension d; kChunkShift: component d
+                         // gets + shift; kChunkRelease: later chunks of the same
+                         // launch read what this chunk writes (publish with a
+                         // release fence)
+    int32_t unused;
+    float shift;         // L_d
+    int32_t S, R;
+    int32_t ctr;         // counter this chunk advances: coords R*P+p, forces S*P+p
+    int32_t p;
 };
-static_assert(sizeof(DChunk) == 32, "DChunk layout");
+constexpr int32_t kChunkShift = 1 << 8;
+constexpr int32_t kChunkRelease = 1 << 9;
+static_assert(sizeof(DChunk) == 64, "DChunk layout");
 
-// Kernel arguments of one exchange launch (passed by value).
+// Kernel arguments of one fused launch (passed by value). Tickets
+// [0, nx) are coordinate chunks, [nx, nx + nf) force chunks.
 struct XArgs {
     float* x;
     float* f;
     const int32_t* maps;
-    const DItem* items;
     const DChunk* xchunks;
     const DChunk* fchunks;
-    int32_t x_begin, x_end;  // ticket range of coordinate chunks
-    int32_t f_begin, f_end;  // ticket range of force chunks
+    int32_t nx, nf;
     uint32_t* ctrl;
-    uint32_t* xflag;  // [R * P + p] = pass number once region p of R is filled
-    uint32_t* fflag;  // [S * P + p] = pass number once item (S, p) has added
-    uint32_t* xcnt;   // per-item chunk completion counters (self-resetting)
-    uint32_t* fcnt;
+    uint32_t* xcnt;          // [R*P+p] chunks that filled region p of R, all passes
+    uint32_t* fcnt;          // [S*P+p] chunks of item (S, p) that added, all passes
+    const uint32_t* xneed;   // [R*P+p] chunks per pass behind xcnt
+    const uint32_t* fneed;   // [S*P+p] chunks per pass behind fcnt
     int32_t P;
-    int32_t n_items;
-    int32_t bump_epoch;     // this launch ends the pass: publish its number
-    int32_t force_timeout;  // waits target a value nobody writes
+    int32_t n_xchunks;       // coordinate chunks per pass
+    int32_t static_first;    // 1: work-group b starts with ticket b
+    int32_t force_timeout;   // waits target a value nobody writes
     uint32_t spin_limit;
+    uint64_t* trace;         // optional event log (null: off)
+};
+
+// Event log: work-group b writes record k at trace[2 * (b * kTraceRecords + k)]
+// as (code << 32 | info, wall-clock ticks of the 100 MHz constant counter).
+constexpr int kTraceRecords = 64;
+enum TraceCode : uint32_t {
+    kTrStart = 1,    // info: grid size
+    kTrClaim = 2,    // info: ticket
+    kTrHead = 3,     // info: entries of the independent part done
+    kTrWaited = 4,   // info: wait masks
+    kTrChunk = 5,    // info: entries of the chunk done
+    kTrPublish = 6,  // info: counter advanced
+    kTrExit = 7
 };
 
 struct Geometry {
@@ -93,12 +111,6 @@ struct Geometry {
     int index(const int c[3]) const { return c[0] + n[0] * (c[1] + n[1] * c[2]); }
 };
 
-// A device allocation owned by the plan.
-struct DevBuf {
-    void* p = nullptr;
-    size_t bytes = 0;
-};
-
 struct Plan {
     int device = 0;
     int n_cu = 256;
@@ -107,23 +119,35 @@ struct Plan {
     int32_t n_atoms = 0;
     int64_t n_slots = 0;
     int64_t n_halo = 0;
-    int32_t mode = DDH_MODE_FUSED;
+    int32_t mode = DDH_MODE_AUTO;   // as requested (ddh_set_mode)
+    // FUSED or PULSE (plus the GRAPH bit): AUTO resolved against the layout
+    int32_t effective_mode() const
+    {
+        const int32_t base = mode & ~DDH_MODE_GRAPH;
+        const int32_t m = base == DDH_MODE_AUTO
+                              ? (n_halo <= DDH_AUTO_FUSED_MAX ? DDH_MODE_FUSED : DDH_MODE_PULSE)
+                              : base;
+        return m | (mode & DDH_MODE_GRAPH);
+    }
 
     // tuning
     int chunk_req = 0;
     int grid_req = 0;
+    int block_req = 0;          // fused work-group width: 0 automatic, 256 or 1024
     uint32_t spin_limit = 1u << 20;
     int force_timeout = 0;
     int refined_waits = 1;
-    int chunk = 256;  // entries per chunk in use
+    uint64_t* trace = nullptr;  // caller-owned device buffer (DDH_TUNE_TRACE)
+    int chunk = 4096;           // entries per chunk in use
 
     // host copies of the layout
     std::vector<int64_t> base;     // per domain
     std::vector<int32_t> nhome, ntotal;
     std::vector<int32_t> send, split, recv, roff, shift;  // [S * P + p]
     std::vector<int64_t> map_off;  // [S * P + p]
-    std::vector<DItem> items;      // [S * P + p]
-    std::vector<DChunk> xch_fused, xch_pulse, fch;
+    std::vector<int32_t> nchunks;  // [S * P + p] chunks of the map
+    std::vector<DChunk> xch, fch;  // coordinate chunks in pulse order, force
+                                   // chunks in decreasing pulse order
     std::vector<int32_t> xpulse_begin, fpulse_begin;  // per pulse ranges (+1)
 
     // device state
@@ -131,15 +155,14 @@ struct Plan {
     int32_t* d_slot_gid = nullptr; // global id per slot
     int32_t* d_home_gid = nullptr; // home atoms in slot order, all domains
     int32_t* d_home_slot = nullptr;
-    DItem* d_items = nullptr;
-    DChunk* d_xch_fused = nullptr;
-    DChunk* d_xch_pulse = nullptr;
+    DChunk* d_xch = nullptr;
     DChunk* d_fch = nullptr;
-    uint32_t* d_ctrl = nullptr;    // control words + flags + counters
-    uint32_t* d_xflag = nullptr;
-    uint32_t* d_fflag = nullptr;
+    uint32_t* d_ctrl = nullptr;    // control words, then the arrays below
     uint32_t* d_xcnt = nullptr;
     uint32_t* d_fcnt = nullptr;
+    uint32_t* d_xneed = nullptr;
+    uint32_t* d_fneed = nullptr;
+    uint32_t* d_pflag = nullptr;   // [p] / [P + p]: per-pulse flags of pulse mode
     std::vector<void*> owned;      // every hipMalloc of the built state
 
     // graph replay cache: (op, x, f, mode) -> executable graph
@@ -151,9 +174,9 @@ struct Plan {
 int fail(int code, const std::string& msg);
 int hip_fail(hipError_t e, const char* what);
 
-#define DDH_HIP(call)                                     \
-    do {                                                  \
-        hipError_t _e = (call);                           \
+#define DDH_HIP(call)                                          \
+    do {                                                       \
+        hipError_t _e = (call);                                \
         if (_e != hipSuccess) return ddh::hip_fail(_e, #call); \
     } while (0)
 

@@ -86,11 +86,16 @@ typedef struct ddh_layout {
 typedef struct ddh_plan ddh_plan;
 
 /* Execution modes for the exchange calls (ddh_set_mode). */
-#define DDH_MODE_FUSED 0   /* one persistent launch per pass: all pulses
-                              chained on per-pulse device flags */
-#define DDH_MODE_PULSE 1   /* one launch per pulse, ordered by the stream */
+#define DDH_MODE_FUSED 0   /* one launch per call: all pulses chained on
+                              per-map device counters */
+#define DDH_MODE_PULSE 1   /* one launch per pulse, ordered by the stream,
+                              then one launch that publishes per-pulse flags */
+#define DDH_MODE_AUTO 2    /* default: FUSED when a pass moves at most
+                              DDH_AUTO_FUSED_MAX halo atoms (latency-bound),
+                              else PULSE (bandwidth-bound) */
 #define DDH_MODE_GRAPH 16  /* OR-able: replay the call's launches from a
                               captured hipGraph */
+#define DDH_AUTO_FUSED_MAX 200000
 
 /* ------------------------------------------------------------- lifecycle */
 
@@ -200,7 +205,8 @@ int ddh_exchange_forces(ddh_plan *plan, float *f_local_dev, int64_t capacity_slo
 int ddh_exchange_step(ddh_plan *plan, float *x_local_dev, float *f_local_dev,
                       int64_t capacity_slots, void *stream);
 
-/* Select DDH_MODE_FUSED or DDH_MODE_PULSE, optionally | DDH_MODE_GRAPH. */
+/* Select DDH_MODE_FUSED, DDH_MODE_PULSE or DDH_MODE_AUTO, optionally
+   | DDH_MODE_GRAPH. */
 int ddh_set_mode(ddh_plan *plan, int32_t mode);
 
 /*
@@ -215,12 +221,27 @@ int ddh_check(ddh_plan *plan, void *stream);
                                    to a multiple of 64); 0 = automatic */
 #define DDH_TUNE_GRID 2         /* workgroups of a fused launch; 0 = automatic */
 #define DDH_TUNE_SPIN_LIMIT 3   /* polls before a device wait gives up */
-#define DDH_TUNE_FORCE_TIMEOUT 4 /* 1: every dependent wait targets a value no
-                                    one writes, so it ends at the spin limit
-                                    (tests of the timeout path) */
+#define DDH_TUNE_FORCE_TIMEOUT 4 /* 1: every dependent wait of the fused mode
+                                    targets a value no one writes, so it ends
+                                    at the spin limit (tests of the timeout
+                                    path); pulse mode has no device waits */
 #define DDH_TUNE_REFINED_WAITS 5 /* 1 (default): a chunk waits only on the
                                     pulses its entries reference; 0: on all
                                     earlier (coordinates) / later (forces) */
+
+#define DDH_TUNE_TRACE 6          /* value: device address of a uint64 buffer of
+                                    2 * 64 * (work-groups of a fused launch)
+                                    words, or 0 (off). Thread 0 of every
+                                    work-group of a fused launch logs its events
+                                    (claim, head done, wait done, chunk done,
+                                    flag published, exit) as pairs
+                                    (code << 32 | info, 100 MHz wall-clock
+                                    ticks), up to 64 per work-group. The caller
+                                    owns the buffer and sizes it for the grid
+                                    (DDH_TUNE_GRID); the buffer is not cleared. */
+
+#define DDH_TUNE_BLOCK 7           /* work-group width of the fused launch: 0
+                                    (automatic), 256 or 1024 */
 
 /* Set a tuning knob; takes effect at the next build (CHUNK) or call. */
 int ddh_tune(ddh_plan *plan, int32_t key, int64_t value);

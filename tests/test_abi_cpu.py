@@ -127,8 +127,10 @@ def test_mode_and_tune_validation():
     plan = ddh.Plan((2, 2, 2), (8.0, 8.0, 8.0), 1.0)
     plan.set_mode(ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH)
     plan.set_mode(ddh.DDH_MODE_FUSED)
-    with pytest.raises(ddh.DDHError):
-        plan.set_mode(4)
+    plan.set_mode(ddh.DDH_MODE_AUTO | ddh.DDH_MODE_GRAPH)
+    for bad in (3, 4, 8, 32):
+        with pytest.raises(ddh.DDHError):
+            plan.set_mode(bad)
     plan.tune(ddh.DDH_TUNE_CHUNK, 100)
     plan.tune(ddh.DDH_TUNE_CHUNK, 0)
     for key, val in [(ddh.DDH_TUNE_CHUNK, 10), (ddh.DDH_TUNE_CHUNK, 10000),

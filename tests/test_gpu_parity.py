@@ -26,6 +26,7 @@ MODES = {
     "pulse": ddh.DDH_MODE_PULSE,
     "fused_graph": ddh.DDH_MODE_FUSED | ddh.DDH_MODE_GRAPH,
     "pulse_graph": ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH,
+    "auto": ddh.DDH_MODE_AUTO,
 }
 
 
@@ -36,10 +37,11 @@ def bits(a):
 class GpuPlan:
     """A device plan built from host positions, with host views of its output."""
 
-    def __init__(self, x, grid, box, rc, cell=0.5, mode=0, chunk=0, wg=0, refined=1):
+    def __init__(self, x, grid, box, rc, cell=0.5, mode=0, chunk=0, wg=0, refined=1, block=0):
         self.plan = ddh.Plan(grid, box, rc, cell)
         self.plan.tune(ddh.DDH_TUNE_CHUNK, chunk)
         self.plan.tune(ddh.DDH_TUNE_GRID, wg)
+        self.plan.tune(ddh.DDH_TUNE_BLOCK, block)
         self.plan.tune(ddh.DDH_TUNE_REFINED_WAITS, refined)
         self.plan.set_mode(mode)
         self.xg = torch.from_numpy(np.ascontiguousarray(x)).cuda()
@@ -137,14 +139,16 @@ def test_workload_fused_step(k, mode, workload_plan):
     g.close()
 
 
-@pytest.mark.parametrize("chunk,wg,refined", [(64, 0, 1), (320, 0, 1), (8192, 0, 1), (64, 1, 1),
-                                              (192, 3, 0), (256, 1, 0), (1024, 5, 1)])
+@pytest.mark.parametrize("chunk,wg,refined,block", [
+    (64, 0, 1, 0), (320, 0, 1, 0), (8192, 0, 1, 0), (64, 1, 1, 0), (192, 3, 0, 0),
+    (256, 1, 0, 0), (1024, 5, 1, 0), (2048, 0, 1, 1024), (4096, 0, 0, 1024), (1024, 0, 1, 256),
+    (3000, 7, 1, 1024), (8192, 1, 1, 1024), (640, 300, 1, 256)])
 @pytest.mark.parametrize("k", [2, 4])
-def test_chunk_and_grid_variants(k, chunk, wg, refined, workload_plan):
+def test_chunk_and_grid_variants(k, chunk, wg, refined, block, workload_plan):
     # a single work-group must drain every ticket in order without waiting forever
     w, x, ref = workload_plan(k)
     for mode in (ddh.DDH_MODE_FUSED, ddh.DDH_MODE_PULSE):
-        g = GpuPlan(x, **w.params(), mode=mode, chunk=chunk, wg=wg, refined=refined)
+        g = GpuPlan(x, **w.params(), mode=mode, chunk=chunk, wg=wg, refined=refined, block=block)
         check_steps(g, ref, 20 + k, steps=2)
         check_steps(g, ref, 30 + k, steps=1, fused_step=True)
         g.close()
@@ -232,11 +236,14 @@ def test_timeout_path_is_reported_and_recovers(workload_plan):
         g.plan.tune(ddh.DDH_TUNE_SPIN_LIMIT, 64)
         g.plan.tune(ddh.DDH_TUNE_FORCE_TIMEOUT, 1)
         xl = g.new_coords()
-        g.plan.exchange_coords(xl)
-        assert g.plan.check() == ddh.DDH_ETIMEOUT
         fl = torch.zeros_like(xl)
+        # only the fused launch waits on the device; pulse mode is ordered
+        # by the stream and has nothing that can time out
+        want = ddh.DDH_ETIMEOUT if mode == ddh.DDH_MODE_FUSED else ddh.DDH_OK
+        g.plan.exchange_coords(xl)
+        assert g.plan.check() == want
         g.plan.exchange_step(xl, fl)
-        assert g.plan.check() == ddh.DDH_ETIMEOUT
+        assert g.plan.check() == want
         g.plan.tune(ddh.DDH_TUNE_FORCE_TIMEOUT, 0)
         g.plan.tune(ddh.DDH_TUNE_SPIN_LIMIT, 1 << 20)
         check_steps(g, ref, 77, steps=2)
