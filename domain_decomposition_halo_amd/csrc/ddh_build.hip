@@ -439,40 +439,46 @@ void free_built(Plan* p)
         (void)hipFree(q);
     p->owned.clear();
     p->d_maps = p->d_slot_gid = p->d_home_gid = p->d_home_slot = nullptr;
-    p->d_xch = p->d_fch = nullptr;
+    p->fused = WorkTable{};
+    p->pulse = WorkTable{};
     p->d_ctrl = p->d_xcnt = p->d_fcnt = p->d_xneed = p->d_fneed = p->d_pflag = nullptr;
     p->built = false;
     p->n_slots = p->n_halo = 0;
     p->n_atoms = 0;
-    p->nchunks.clear();
-    p->xch.clear();
-    p->fch.clear();
 }
 
-// Chunk tables and per-chunk waits, from the maps (host copies).
-static void make_work_tables(Plan* p, const std::vector<int32_t>& maps)
+// Chunk table of chunk size t.chunk, from the maps (host copies). With
+// waits: the per-chunk wait masks and release flags of the fused launch;
+// without: the masks stay empty (per-pulse launches are ordered by the
+// stream).
+static void make_work_table(const Plan* p, const std::vector<int32_t>& maps, bool waits,
+                            WorkTable& t)
 {
     const Geometry& g = p->g;
-    const int D = g.ndom, P = g.P, CH = p->chunk;
+    const int D = g.ndom, P = g.P, CH = t.chunk;
     // per slot: pulse the slot was received in (-1 home), and the set of
     // pulses whose map holds the slot (as a bit mask)
-    std::vector<int8_t> rid((size_t)p->n_slots, -1);
-    std::vector<uint32_t> inmap((size_t)p->n_slots, 0u);
-    for (int S = 0; S < D; S++)
-        for (int q = 0; q < P; q++) {
-            const int it = S * P + q;
-            const int R = p->recv[it];
-            const int64_t b = p->base[R] + p->roff[it];
-            for (int i = 0; i < p->send[it]; i++)
-                rid[(size_t)(b + i)] = (int8_t)q;
-            const int32_t* m = maps.data() + p->map_off[it];
-            for (int i = 0; i < p->send[it]; i++)
-                inmap[(size_t)(p->base[S] + m[i])] |= 1u << q;
-        }
+    std::vector<int8_t> rid;
+    std::vector<uint32_t> inmap;
+    if (waits) {
+        rid.assign((size_t)p->n_slots, -1);
+        inmap.assign((size_t)p->n_slots, 0u);
+        for (int S = 0; S < D; S++)
+            for (int q = 0; q < P; q++) {
+                const int it = S * P + q;
+                const int R = p->recv[it];
+                const int64_t b = p->base[R] + p->roff[it];
+                for (int i = 0; i < p->send[it]; i++)
+                    rid[(size_t)(b + i)] = (int8_t)q;
+                const int32_t* m = maps.data() + p->map_off[it];
+                for (int i = 0; i < p->send[it]; i++)
+                    inmap[(size_t)(p->base[S] + m[i])] |= 1u << q;
+            }
+    }
 
-    p->nchunks.assign((size_t)D * P, 1);
+    t.nchunks.assign((size_t)D * P, 1);
     for (int it = 0; it < D * P; it++)
-        p->nchunks[it] = std::max(1, (p->send[it] + CH - 1) / CH);
+        t.nchunks[it] = std::max(1, (p->send[it] + CH - 1) / CH);
 
     auto base_chunk = [&](int it) {
         const int S = it / P, q = it % P;
@@ -490,7 +496,7 @@ static void make_work_tables(Plan* p, const std::vector<int32_t>& maps)
     // coordinates: the k-th slice of the independent head and of the
     // dependent tail; the chunk advances the counter of the region it fills
     auto xchunk = [&](int it, int k) {
-        const int c = p->nchunks[it], h = p->split[it], tl = p->send[it] - h;
+        const int c = t.nchunks[it], h = p->split[it], tl = p->send[it] - h;
         DChunk d = base_chunk(it);
         d.hb = (int32_t)((int64_t)h * k / c);
         d.he = (int32_t)((int64_t)h * (k + 1) / c);
@@ -498,7 +504,7 @@ static void make_work_tables(Plan* p, const std::vector<int32_t>& maps)
         d.te = h + (int32_t)((int64_t)tl * (k + 1) / c);
         d.ctr = d.R * P + d.p;
         uint32_t w = 0;
-        if (d.te > d.tb) {
+        if (waits && d.te > d.tb) {
             if (!p->refined_waits) {
                 w = (1u << d.p) - 1u;
             } else {
@@ -513,14 +519,16 @@ static void make_work_tables(Plan* p, const std::vector<int32_t>& maps)
     // forces: the k-th slice of the map; waits on the later pulses that add
     // into the same slots of S or into the slots of R's region that it reads
     auto fchunk = [&](int it, int k) {
-        const int c = p->nchunks[it], n = p->send[it];
+        const int c = t.nchunks[it], n = p->send[it];
         DChunk d = base_chunk(it);
         d.hb = (int32_t)((int64_t)n * k / c);
         d.he = (int32_t)((int64_t)n * (k + 1) / c);
         d.tb = d.te = d.he;
         d.ctr = d.S * P + d.p;
         const uint32_t later = ~((2u << d.p) - 1u) & ((1u << P) - 1u);
-        if (!p->refined_waits) {
+        if (!waits) {
+            d.wait_a = d.wait_b = 0;
+        } else if (!p->refined_waits) {
             d.wait_a = d.wait_b = later;
         } else {
             uint32_t wa = 0, wb = 0;
@@ -536,54 +544,74 @@ static void make_work_tables(Plan* p, const std::vector<int32_t>& maps)
         return d;
     };
 
-    p->xch.clear();
-    p->fch.clear();
-    p->xpulse_begin.assign((size_t)P + 1, 0);
-    p->fpulse_begin.assign((size_t)P + 1, 0);
+    t.xch.clear();
+    t.fch.clear();
+    t.xpulse_begin.assign((size_t)P + 1, 0);
+    t.fpulse_begin.assign((size_t)P + 1, 0);
     // coordinates in pulse order (a chunk waits only on earlier pulses)
     for (int q = 0; q < P; q++) {
-        p->xpulse_begin[q] = (int)p->xch.size();
+        t.xpulse_begin[q] = (int)t.xch.size();
         for (int S = 0; S < D; S++)
-            for (int k = 0; k < p->nchunks[S * P + q]; k++)
-                p->xch.push_back(xchunk(S * P + q, k));
+            for (int k = 0; k < t.nchunks[S * P + q]; k++)
+                t.xch.push_back(xchunk(S * P + q, k));
     }
-    p->xpulse_begin[P] = (int)p->xch.size();
+    t.xpulse_begin[P] = (int)t.xch.size();
     // forces in decreasing pulse order (a chunk waits only on later pulses)
     for (int r = 0; r < P; r++) {
         const int q = P - 1 - r;
-        p->fpulse_begin[r] = (int)p->fch.size();
+        t.fpulse_begin[r] = (int)t.fch.size();
         for (int S = 0; S < D; S++)
-            for (int k = 0; k < p->nchunks[S * P + q]; k++)
-                p->fch.push_back(fchunk(S * P + q, k));
+            for (int k = 0; k < t.nchunks[S * P + q]; k++)
+                t.fch.push_back(fchunk(S * P + q, k));
     }
-    p->fpulse_begin[P] = (int)p->fch.size();
+    t.fpulse_begin[P] = (int)t.fch.size();
+    if (!waits)
+        return;
 
     // a chunk publishes with a release fence only if a later chunk of the
     // same launch waits on its counter (and so reads what it wrote)
     std::vector<char> xread((size_t)D * P, 0), fread((size_t)D * P, 0);
-    for (const DChunk& c : p->xch)
+    for (const DChunk& c : t.xch)
         for (uint32_t m = c.wait_a; m; m &= m - 1)
             xread[(size_t)c.S * P + __builtin_ctz(m)] = 1;
-    for (const DChunk& c : p->fch) {
+    for (const DChunk& c : t.fch) {
         for (uint32_t m = c.wait_a; m; m &= m - 1)
             fread[(size_t)c.S * P + __builtin_ctz(m)] = 1;
         for (uint32_t m = c.wait_b; m; m &= m - 1)
             fread[(size_t)c.R * P + __builtin_ctz(m)] = 1;
     }
-    for (DChunk& c : p->xch)
+    for (DChunk& c : t.xch)
         if (xread[c.ctr])
             c.flags |= kChunkRelease;
-    for (DChunk& c : p->fch)
+    for (DChunk& c : t.fch)
         if (fread[c.ctr])
             c.flags |= kChunkRelease;
 }
 
-// Entries per work chunk: 4096. A small (latency-bound) pass then gives one
-// chunk per map, run by one 1024-wide work-group of the fused launch, which
-// keeps the number of device-wide serialized operations (ticket claims,
-// releases, acquires) per dependency stage small; a large pass run with
-// per-pulse launches gives blocks of two rounds of 8 entries per thread.
-static int auto_chunk(int64_t) { return 4096; }
+// Entries per chunk of the fused launch: 4096. A small (latency-bound) pass
+// then gives one chunk per map, run by one 1024-wide work-group, which keeps
+// the device-wide serialized operations (ticket claims, releases, acquires)
+// per dependency stage few.
+static int fused_chunk() { return 4096; }
+
+// Entries per block of the per-pulse launches: the largest of 2048, 1024 and
+// 512 that still gives every pulse's launch at least two blocks per compute
+// unit (a launch with fewer blocks than compute units leaves bandwidth idle).
+static int pulse_chunk(const Plan* p)
+{
+    const int D = p->g.ndom, P = p->g.P;
+    int64_t smallest = INT64_MAX;
+    for (int q = 0; q < P; q++) {
+        int64_t n = 0;
+        for (int S = 0; S < D; S++)
+            n += p->send[S * P + q];
+        smallest = std::min(smallest, n);
+    }
+    for (int ch = 2048; ch > 512; ch /= 2)
+        if (smallest / ch >= 2ll * p->n_cu)
+            return ch;
+    return 512;
+}
 
 int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
 {
@@ -881,25 +909,29 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     }
 
     // ---- 5: chunk tables, counters
-    p->chunk = p->chunk_req > 0 ? p->chunk_req : auto_chunk(nh);
+    p->fused.chunk = p->chunk_req > 0 ? p->chunk_req : fused_chunk();
+    p->pulse.chunk = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p);
     std::vector<int32_t> hmaps((size_t)nh);
     if (nh > 0)
         DDH_HIP(hipMemcpyAsync(hmaps.data(), p->d_maps, sizeof(int32_t) * nh,
                                hipMemcpyDeviceToHost, s));
     DDH_HIP(hipStreamSynchronize(s));
-    make_work_tables(p, hmaps);
+    make_work_table(p, hmaps, true, p->fused);
+    make_work_table(p, hmaps, false, p->pulse);
 
     std::vector<uint32_t> xneed(DP, 0u), fneed(DP, 0u);
     for (int S = 0; S < D; S++)
         for (int q = 0; q < P; q++) {
             const int it = S * P + q;
-            xneed[(size_t)p->recv[it] * P + q] = (uint32_t)p->nchunks[it];
-            fneed[it] = (uint32_t)p->nchunks[it];
+            xneed[(size_t)p->recv[it] * P + q] = (uint32_t)p->fused.nchunks[it];
+            fneed[it] = (uint32_t)p->fused.nchunks[it];
         }
-    DDH_HIP(owned_alloc(p, &p->d_xch, p->xch.size()));
-    DDH_HIP(owned_alloc(p, &p->d_fch, p->fch.size()));
-    DDH_HIP(upload(p->d_xch, p->xch, s));
-    DDH_HIP(upload(p->d_fch, p->fch, s));
+    for (WorkTable* t : {&p->fused, &p->pulse}) {
+        DDH_HIP(owned_alloc(p, &t->d_xch, t->xch.size()));
+        DDH_HIP(owned_alloc(p, &t->d_fch, t->fch.size()));
+        DDH_HIP(upload(t->d_xch, t->xch, s));
+        DDH_HIP(upload(t->d_fch, t->fch, s));
+    }
     const size_t words = (size_t)kCtrlWords + 4 * DP + 2 * (size_t)DDH_MAX_PULSES;
     DDH_HIP(owned_alloc(p, &p->d_ctrl, words));
     DDH_HIP(hipMemsetAsync(p->d_ctrl, 0, sizeof(uint32_t) * words, s));

@@ -441,7 +441,7 @@ int launch_fused(const Plan* p, XArgs a, hipStream_t s)
     // the chunk size
     const bool wide = p->block_req ? p->block_req == 1024 : grid <= p->n_cu / 2;
     const int lanes = wide ? 1024 : 256;
-    const int per = (p->chunk + lanes - 1) / lanes;
+    const int per = (p->fused.chunk + lanes - 1) / lanes;
     if (wide) {
         if (per > 2)
             hipLaunchKernelGGL((exchange_kernel<4, 1024>), dim3(grid), dim3(1024), 0, s, a);
@@ -461,8 +461,19 @@ int launch_fused(const Plan* p, XArgs a, hipStream_t s)
     return DDH_OK;
 }
 
-int launch_pulse(const Plan* p, int op, float* x, float* f, const DChunk* table, int begin, int end,
-                 hipStream_t s)
+template <int E>
+void launch_pulse_e(int op, dim3 grid, hipStream_t s, const PArgs& a)
+{
+    if (op == kOpCoords)
+        hipLaunchKernelGGL((pulse_kernel<E, kOpCoords>), grid, dim3(kBlock), 0, s, a);
+    else
+        hipLaunchKernelGGL((pulse_kernel<E, kOpForces>), grid, dim3(kBlock), 0, s, a);
+}
+
+// Chunks [begin, end) of table t, one block each; entries per lane and
+// round from the table's chunk size (larger chunks take several rounds).
+int launch_pulse(const Plan* p, int op, float* x, float* f, const WorkTable& t,
+                 const DChunk* table, int begin, int end, hipStream_t s)
 {
     if (end <= begin)
         return DDH_OK;
@@ -472,11 +483,14 @@ int launch_pulse(const Plan* p, int op, float* x, float* f, const DChunk* table,
     a.maps = p->d_maps;
     a.chunks = table;
     a.begin = begin;
-    const dim3 grid(end - begin), block(kBlock);
-    if (op == kOpCoords)
-        hipLaunchKernelGGL((pulse_kernel<8, kOpCoords>), grid, block, 0, s, a);
+    const dim3 grid(end - begin);
+    const int per = (t.chunk + kBlock - 1) / kBlock;
+    if (per > 4)
+        launch_pulse_e<8>(op, grid, s, a);
+    else if (per > 2)
+        launch_pulse_e<4>(op, grid, s, a);
     else
-        hipLaunchKernelGGL((pulse_kernel<8, kOpForces>), grid, block, 0, s, a);
+        launch_pulse_e<2>(op, grid, s, a);
     DDH_HIP(hipGetLastError());
     return DDH_OK;
 }
@@ -490,17 +504,18 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s)
         a.x = x;
         a.f = f;
         a.maps = p->d_maps;
-        a.xchunks = p->d_xch;
-        a.fchunks = p->d_fch;
-        a.nx = (op & kOpCoords) ? (int)p->xch.size() : 0;
-        a.nf = (op & kOpForces) ? (int)p->fch.size() : 0;
+        const WorkTable& t = p->fused;
+        a.xchunks = t.d_xch;
+        a.fchunks = t.d_fch;
+        a.nx = (op & kOpCoords) ? (int)t.xch.size() : 0;
+        a.nf = (op & kOpForces) ? (int)t.fch.size() : 0;
         a.ctrl = p->d_ctrl;
         a.xcnt = p->d_xcnt;
         a.fcnt = p->d_fcnt;
         a.xneed = p->d_xneed;
         a.fneed = p->d_fneed;
         a.P = P;
-        a.n_xchunks = (int)p->xch.size();
+        a.n_xchunks = (int)t.xch.size();
         a.force_timeout = p->force_timeout;
         a.spin_limit = p->spin_limit;
         a.trace = p->trace;
@@ -508,14 +523,16 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s)
     }
     // one launch per pulse: coordinates in increasing, forces in decreasing
     // pulse order; then the per-pulse flags
+    const WorkTable& t = p->pulse;
     int rc = DDH_OK;
     if (op & kOpCoords)
         for (int q = 0; q < P && !rc; q++)
-            rc = launch_pulse(p, kOpCoords, x, f, p->d_xch, p->xpulse_begin[q],
-                              p->xpulse_begin[q + 1], s);
+            rc = launch_pulse(p, kOpCoords, x, f, t, t.d_xch, t.xpulse_begin[q],
+                              t.xpulse_begin[q + 1], s);
     if (op & kOpForces)
         for (int r = 0; r < P && !rc; r++)
-            rc = launch_pulse(p, kOpForces, x, f, p->d_fch, p->fpulse_begin[r], p->fpulse_begin[r + 1], s);
+            rc = launch_pulse(p, kOpForces, x, f, t, t.d_fch, t.fpulse_begin[r],
+                              t.fpulse_begin[r + 1], s);
     if (rc)
         return rc;
     hipLaunchKernelGGL(signal_kernel, dim3(1), dim3(64), 0, s, p->d_ctrl, p->d_pflag, P, op);
@@ -527,7 +544,7 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s)
 
 int enqueue_exchange(Plan* p, int op, float* x, float* f, hipStream_t s)
 {
-    if (p->g.P == 0 || p->nchunks.empty())
+    if (p->g.P == 0 || p->fused.nchunks.empty())
         return DDH_OK;
     if (!(p->mode & DDH_MODE_GRAPH))
         return enqueue_raw(p, op, x, f, s);

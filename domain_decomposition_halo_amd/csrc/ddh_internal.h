@@ -111,6 +111,17 @@ struct Geometry {
     int index(const int c[3]) const { return c[0] + n[0] * (c[1] + n[1] * c[2]); }
 };
 
+// The chunks of one execution mode: coordinate chunks in pulse order, force
+// chunks in decreasing pulse order, each pulse's chunks contiguous.
+struct WorkTable {
+    int chunk = 0;                  // entries per chunk
+    std::vector<int32_t> nchunks;   // [S * P + p] chunks of the map
+    std::vector<DChunk> xch, fch;
+    std::vector<int32_t> xpulse_begin, fpulse_begin;  // per pulse ranges (+1)
+    DChunk* d_xch = nullptr;        // device copies
+    DChunk* d_fch = nullptr;
+};
+
 struct Plan {
     int device = 0;
     int n_cu = 256;
@@ -138,25 +149,20 @@ struct Plan {
     int force_timeout = 0;
     int refined_waits = 1;
     uint64_t* trace = nullptr;  // caller-owned device buffer (DDH_TUNE_TRACE)
-    int chunk = 4096;           // entries per chunk in use
 
     // host copies of the layout
     std::vector<int64_t> base;     // per domain
     std::vector<int32_t> nhome, ntotal;
     std::vector<int32_t> send, split, recv, roff, shift;  // [S * P + p]
     std::vector<int64_t> map_off;  // [S * P + p]
-    std::vector<int32_t> nchunks;  // [S * P + p] chunks of the map
-    std::vector<DChunk> xch, fch;  // coordinate chunks in pulse order, force
-                                   // chunks in decreasing pulse order
-    std::vector<int32_t> xpulse_begin, fpulse_begin;  // per pulse ranges (+1)
+    WorkTable fused;               // fused launch: waits and release flags set
+    WorkTable pulse;               // per-pulse launches: no waits
 
     // device state
     int32_t* d_maps = nullptr;     // all maps, pulse-major
     int32_t* d_slot_gid = nullptr; // global id per slot
     int32_t* d_home_gid = nullptr; // home atoms in slot order, all domains
     int32_t* d_home_slot = nullptr;
-    DChunk* d_xch = nullptr;
-    DChunk* d_fch = nullptr;
     uint32_t* d_ctrl = nullptr;    // control words, then the arrays below
     uint32_t* d_xcnt = nullptr;
     uint32_t* d_fcnt = nullptr;
