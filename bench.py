@@ -45,14 +45,19 @@ if ROOT not in sys.path:
 METRIC = "halo exchange µs/step + halo atoms/s & HBM GB/s fraction (1 MI355X)"
 HBM_PEAK_GBS = 8000.0
 BYTES_X, BYTES_F = 28, 40
-KERNEL_SRC = os.path.join(ROOT, "domain_decomposition_halo_amd", "csrc", "ddh_exchange.hip")
+# the sources that decide what the exchange launches read and write
+KERNEL_SRCS = [os.path.join(ROOT, "domain_decomposition_halo_amd", "csrc", f)
+               for f in ("ddh_exchange.hip", "ddh_build.hip", "ddh_internal.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 VARIANTS = ("auto", "step", "split", "pulse")
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_file(variant: str, wname: str) -> str:
@@ -211,6 +216,8 @@ def run_gpu(args, w):
         roofline=dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel,
                       launches_per_step=launches_per_step,
+                      per="launch" if launches_per_step == 1 else
+                          f"step ({launches_per_step} launches; achieved and traffic are per step)",
                       algorithmic_bytes_per_step=step_bytes,
                       avg_launch_us=round(avg_launch * 1e6, 3),
                       p10_step_us=round(durs[len(durs) // 10] * 1e6, 3),
@@ -272,13 +279,28 @@ def summarize_pmc(fetch_csv, write_csv, variant, wname, copy_mb, command):
 
     fk = per_kernel(rows(fetch_csv), "FETCH_SIZE")
     wk = per_kernel(rows(write_csv), "WRITE_SIZE")
-    ex = [k for k in fk if "exchange_kernel" in k]
     cp = [k for k in fk if "copy" in k.lower() or "elementwise" in k.lower()]
-    if not ex or not cp:
-        raise SystemExit(f"kernels not found: exchange={ex} copy={cp}")
-    import statistics
-    f_ex = statistics.median(fk[ex[0]])
-    w_ex = statistics.median(wk[ex[0]])
+    if variant == "pulse":
+        # per step: every per-pulse launch of the step; each step ends with
+        # exactly one signal_kernel launch
+        ex = sorted(k for k in fk if "pulse_kernel" in k)
+        sig = [k for k in fk if "signal_kernel" in k]
+        if not ex or not sig or not cp:
+            raise SystemExit(f"kernels not found: pulse={ex} signal={sig} copy={cp}")
+        n_steps = len(fk[sig[0]])
+        f_ex = sum(sum(fk[k]) for k in ex) / n_steps
+        w_ex = sum(sum(wk.get(k, [])) for k in ex) / n_steps
+        n_disp = sum(len(fk[k]) for k in ex)
+        unit = "step (all per-pulse launches of one step)"
+    else:
+        ex = [k for k in fk if "exchange_kernel" in k]
+        if not ex or not cp:
+            raise SystemExit(f"kernels not found: exchange={ex} copy={cp}")
+        import statistics
+        f_ex = statistics.median(fk[ex[0]])
+        w_ex = statistics.median(wk[ex[0]])
+        n_disp = len(fk[ex[0]])
+        unit = "dispatch"
     # the copy probe: the largest copy-like dispatch
     cbest = max(cp, key=lambda k: max(fk[k]))
     f_cp = max(fk[cbest])
@@ -289,15 +311,16 @@ def summarize_pmc(fetch_csv, write_csv, variant, wname, copy_mb, command):
     traffic = (f_ex * sf + w_ex * sw) * 1024.0
     path = traffic_file(variant, wname)
     with open(path, "w") as fh:
-        fh.write(f"# HBM traffic of exchange_kernel, variant {variant}, workload {wname}\n\n")
+        fh.write(f"# HBM traffic of the exchange, variant {variant}, workload {wname}\n\n")
         fh.write("Two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),\n"
                  "scaled by what the same counters read for a plain copy of known size.\n\n")
         fh.write(f"Command (each counter in its own run):\n\n```\n{command}\n```\n\n")
         fh.write(f"- kernel_source_sha256: `{kernel_hash()}`\n")
-        fh.write(f"- kernel: `{ex[0][:90]}`\n")
-        fh.write(f"- dispatches: {len(fk[ex[0]])}\n")
-        fh.write(f"- FETCH_SIZE_KiB_per_dispatch (median): {f_ex:.1f}\n")
-        fh.write(f"- WRITE_SIZE_KiB_per_dispatch (median): {w_ex:.1f}\n")
+        fh.write(f"- kernels: {', '.join('`' + k[:90] + '`' for k in ex)}\n")
+        fh.write(f"- dispatches: {n_disp}\n")
+        fh.write(f"- unit: {unit}\n")
+        fh.write(f"- FETCH_SIZE_KiB_per_unit: {f_ex:.1f}\n")
+        fh.write(f"- WRITE_SIZE_KiB_per_unit: {w_ex:.1f}\n")
         fh.write(f"- copy_probe_kernel: `{cbest[:90]}`\n")
         fh.write(f"- copy_probe_MiB: {copy_mb}\n")
         fh.write(f"- copy_probe_FETCH_KiB: {f_cp:.1f}\n")
