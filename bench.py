@@ -136,7 +136,9 @@ def run_gpu(args, w):
     else:
         calls = [("step", lambda: plan.exchange_step(xl, fl), (BYTES_X + BYTES_F) * n_halo)]
 
-    launches_per_step = {"step": 1, "split": 2}.get(variant, 2 * lay["n_pulses"] + 1)
+    # pulse mode: a step pairs coordinate pulse q with force pulse P-1-q in
+    # one launch, then one flag launch
+    launches_per_step = {"step": 1, "split": 2}.get(variant, lay["n_pulses"] + 1)
     for _ in range(args.warmup):
         for _, fn, _ in calls:
             fn()
@@ -189,6 +191,34 @@ def run_gpu(args, w):
         del graph
     assert plan.check() == ddh.DDH_OK
 
+    # each pass alone (pack = coordinate pass, unpack = force pass), the same
+    # way: graphs of G calls, replayed
+    passes = None
+    if not args.cold:
+        passes = {}
+        G = max(1, min(args.graph_steps, args.steps))
+        n_rep = max(1, min(args.steps // G, 10))
+        for name, fn, nb in (("coords", lambda: plan.exchange_coords(xl), BYTES_X * n_halo),
+                             ("forces", lambda: plan.exchange_forces(fl), BYTES_F * n_halo)):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(G):
+                    fn()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n_rep):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (n_rep * G)
+            passes[name + "_us"] = round(us, 3)
+            passes[name + "_frac"] = round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            del graph
+        assert plan.check() == ddh.DDH_OK
+
     durs = sorted(durs)
     avg_step_gpu = sum(durs) / len(durs)
     step_bytes = sum(nb for _, _, nb in calls)
@@ -197,7 +227,7 @@ def run_gpu(args, w):
     traffic = read_traffic(variant, w.name)
     kernel = {"step": "exchange_kernel (fused step, one launch)",
               "split": "exchange_kernel (coordinate launch + force launch)"}.get(
-                  variant, "pulse_kernel (one launch per pulse) + signal_kernel")
+                  variant, "pulse_kernel (coordinate pulse q + force pulse P-1-q per launch) + signal_kernel")
 
     if args.copy_probe:
         # a plain copy of known size, for scaling the HBM byte counters
@@ -211,7 +241,7 @@ def run_gpu(args, w):
     step_s = wall / steps_done
     res = dict(
         n_slots=n_slots, n_halo=n_halo, n_pulses=lay["n_pulses"], build_ms=build_ms,
-        variant=variant,
+        variant=variant, passes=passes,
         step_s=step_s, steps=steps_done, gpu_step_us=round(avg_step_gpu * 1e6, 3),
         roofline=dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel,
@@ -401,6 +431,7 @@ def main():
         },
         "step_hbm_frac": round((BYTES_X + BYTES_F) * gpu["n_halo"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "map_build_ms": round(gpu["build_ms"], 3),
+        "passes": gpu["passes"],
         "roofline": gpu["roofline"],
         "cpu_baseline": cpu,
     }

@@ -498,11 +498,19 @@ static void make_work_table(const Plan* p, const std::vector<int32_t>& maps, boo
     auto xchunk = [&](int it, int k) {
         const int c = t.nchunks[it], h = p->split[it], tl = p->send[it] - h;
         DChunk d = base_chunk(it);
+        d.ctr = d.R * P + d.p;
+        if (!waits) {
+            // no waits: one contiguous slice of the map
+            const int n = p->send[it];
+            d.hb = (int32_t)((int64_t)n * k / c);
+            d.he = (int32_t)((int64_t)n * (k + 1) / c);
+            d.tb = d.te = d.he;
+            return d;
+        }
         d.hb = (int32_t)((int64_t)h * k / c);
         d.he = (int32_t)((int64_t)h * (k + 1) / c);
         d.tb = h + (int32_t)((int64_t)tl * k / c);
         d.te = h + (int32_t)((int64_t)tl * (k + 1) / c);
-        d.ctr = d.R * P + d.p;
         uint32_t w = 0;
         if (waits && d.te > d.tb) {
             if (!p->refined_waits) {

@@ -14,8 +14,9 @@
 //  - Per-pulse launches (DDH_MODE_PULSE; the guide's stream-ordered design of
 //    "Replacing host-side communication with NVSHMEM"): one launch per pulse,
 //    block b runs chunk b of the pulse; the stream orders the pulses, so no
-//    kernel waits, counts or fences. A one-thread launch afterwards publishes
-//    per-pulse flags. Best where bandwidth matters.
+//    kernel waits, counts or fences. A step call runs coordinate pulse q and
+//    force pulse P-1-q in the same launch. A one-wave launch afterwards
+//    publishes per-pulse flags. Best where bandwidth matters.
 //
 //  - One fused launch per call (DDH_MODE_FUSED; "Enabling parallelism across
 //    pulses through kernel fusion", "Dependency-aware packing", "Force halo
@@ -363,31 +364,39 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
 }
 
 // One pulse of one pass, ordered against the other pulses by the stream
-// alone: block b runs chunk begin + b of the pulse. No tickets, counters,
-// waits or fences: the kernel boundary publishes the writes.
+// alone: block b runs coordinate chunk xbegin + b for b < nxb, else force
+// chunk fbegin + b - nxb. A step call pairs coordinate pulse q with force
+// pulse P-1-q in one launch (the two passes touch different arrays, and each
+// pair's predecessors are complete at the launch boundary). No tickets,
+// counters, waits or fences: the kernel boundary publishes the writes.
 struct PArgs {
     float* x;
     float* f;
     const int32_t* maps;
-    const DChunk* chunks;
-    int32_t begin;
+    const DChunk* xchunks;
+    const DChunk* fchunks;
+    int32_t xbegin, nxb, fbegin;
 };
 
-template <int E, int OP>
-__global__ __launch_bounds__(kBlock) void pulse_kernel(PArgs a)
+template <int E, int B>
+__global__ __launch_bounds__(B) void pulse_kernel(PArgs a)
 {
-    const DChunk c = a.chunks[a.begin + (int)blockIdx.x];
-    int j0[E];
-    load_map<E, kBlock>(a.maps + c.map_off, c.hb, c.he, j0);
-    if (OP == kOpCoords) {
-        coords_range<E, kBlock>(a.x, a.maps, c, c.hb, c.he, j0);
+    const int b = (int)blockIdx.x;
+    if (b < a.nxb) {
+        const DChunk c = a.xchunks[a.xbegin + b];
+        int j0[E];
+        load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);
+        coords_range<E, B>(a.x, a.maps, c, c.hb, c.he, j0);
         if (c.te > c.tb) {
             int jt[E];
-            load_map<E, kBlock>(a.maps + c.map_off, c.tb, c.te, jt);
-            coords_range<E, kBlock>(a.x, a.maps, c, c.tb, c.te, jt);
+            load_map<E, B>(a.maps + c.map_off, c.tb, c.te, jt);
+            coords_range<E, B>(a.x, a.maps, c, c.tb, c.te, jt);
         }
     } else {
-        forces_range<E, kBlock>(a.f, a.maps, c, c.hb, c.he, j0);
+        const DChunk c = a.fchunks[a.fbegin + b - a.nxb];
+        int j0[E];
+        load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);
+        forces_range<E, B>(a.f, a.maps, c, c.hb, c.he, j0);
     }
 }
 
@@ -461,36 +470,45 @@ int launch_fused(const Plan* p, XArgs a, hipStream_t s)
     return DDH_OK;
 }
 
-template <int E>
-void launch_pulse_e(int op, dim3 grid, hipStream_t s, const PArgs& a)
+// Coordinate chunks [xb, xe) and force chunks [fb, fe) of table t in one
+// launch, one block per chunk; entries per lane and round from the table's
+// chunk size (larger chunks take several rounds).
+int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, int xe, int fb,
+                 int fe, hipStream_t s)
 {
-    if (op == kOpCoords)
-        hipLaunchKernelGGL((pulse_kernel<E, kOpCoords>), grid, dim3(kBlock), 0, s, a);
-    else
-        hipLaunchKernelGGL((pulse_kernel<E, kOpForces>), grid, dim3(kBlock), 0, s, a);
-}
-
-// Chunks [begin, end) of table t, one block each; entries per lane and
-// round from the table's chunk size (larger chunks take several rounds).
-int launch_pulse(const Plan* p, int op, float* x, float* f, const WorkTable& t,
-                 const DChunk* table, int begin, int end, hipStream_t s)
-{
-    if (end <= begin)
+    const int nb = (xe - xb) + (fe - fb);
+    if (nb <= 0)
         return DDH_OK;
     PArgs a{};
     a.x = x;
     a.f = f;
     a.maps = p->d_maps;
-    a.chunks = table;
-    a.begin = begin;
-    const dim3 grid(end - begin);
-    const int per = (t.chunk + kBlock - 1) / kBlock;
-    if (per > 4)
-        launch_pulse_e<8>(op, grid, s, a);
-    else if (per > 2)
-        launch_pulse_e<4>(op, grid, s, a);
-    else
-        launch_pulse_e<2>(op, grid, s, a);
+    a.xchunks = t.d_xch;
+    a.fchunks = t.d_fch;
+    a.xbegin = xb;
+    a.nxb = xe - xb;
+    a.fbegin = fb;
+    // 1024-wide blocks with few entries per lane by default: on the 12M-atom
+    // maps they move about 8% more than 256-wide blocks with 8 per lane;
+    // chunks below 1024 entries take 256-wide blocks (no idle lanes)
+    const int lanes = p->block_req ? p->block_req : (t.chunk >= 1024 ? 1024 : 256);
+    const int per = (t.chunk + lanes - 1) / lanes;
+    const dim3 grid(nb), block(lanes);
+    if (lanes == 1024) {
+        if (per > 2)
+            hipLaunchKernelGGL((pulse_kernel<4, 1024>), grid, block, 0, s, a);
+        else if (per > 1)
+            hipLaunchKernelGGL((pulse_kernel<2, 1024>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((pulse_kernel<1, 1024>), grid, block, 0, s, a);
+    } else {
+        if (per > 4)
+            hipLaunchKernelGGL((pulse_kernel<8, 256>), grid, block, 0, s, a);
+        else if (per > 2)
+            hipLaunchKernelGGL((pulse_kernel<4, 256>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((pulse_kernel<2, 256>), grid, block, 0, s, a);
+    }
     DDH_HIP(hipGetLastError());
     return DDH_OK;
 }
@@ -522,17 +540,22 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s)
         return launch_fused(p, a, s);
     }
     // one launch per pulse: coordinates in increasing, forces in decreasing
-    // pulse order; then the per-pulse flags
+    // pulse order (fpulse_begin is already in that order); a step pairs the
+    // q-th launch of each pass; then the per-pulse flags
     const WorkTable& t = p->pulse;
+    const auto& xb = t.xpulse_begin;
+    const auto& fb = t.fpulse_begin;
     int rc = DDH_OK;
-    if (op & kOpCoords)
+    if (op == kOpStep) {
         for (int q = 0; q < P && !rc; q++)
-            rc = launch_pulse(p, kOpCoords, x, f, t, t.d_xch, t.xpulse_begin[q],
-                              t.xpulse_begin[q + 1], s);
-    if (op & kOpForces)
+            rc = launch_pulse(p, x, f, t, xb[q], xb[q + 1], fb[q], fb[q + 1], s);
+    } else if (op == kOpCoords) {
+        for (int q = 0; q < P && !rc; q++)
+            rc = launch_pulse(p, x, f, t, xb[q], xb[q + 1], 0, 0, s);
+    } else {
         for (int r = 0; r < P && !rc; r++)
-            rc = launch_pulse(p, kOpForces, x, f, t, t.d_fch, t.fpulse_begin[r],
-                              t.fpulse_begin[r + 1], s);
+            rc = launch_pulse(p, x, f, t, 0, 0, fb[r], fb[r + 1], s);
+    }
     if (rc)
         return rc;
     hipLaunchKernelGGL(signal_kernel, dim3(1), dim3(64), 0, s, p->d_ctrl, p->d_pflag, P, op);

@@ -240,8 +240,10 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     owns the buffer and sizes it for the grid
                                     (DDH_TUNE_GRID); the buffer is not cleared. */
 
-#define DDH_TUNE_BLOCK 7           /* work-group width of the fused launch: 0
-                                    (automatic), 256 or 1024 */
+#define DDH_TUNE_BLOCK 7           /* work-group width of the exchange launches:
+                                    0 (automatic: fused 1024 when its grid
+                                    leaves compute units idle, else 256;
+                                    per-pulse 1024), 256 or 1024 */
 
 /* Set a tuning knob; takes effect at the next build (CHUNK) or call. */
 int ddh_tune(ddh_plan *plan, int32_t key, int64_t value);
