@@ -101,6 +101,10 @@ def run_gpu(args, w):
     # graph mode stays off here
     mode = {"auto": ddh.DDH_MODE_AUTO, "step": ddh.DDH_MODE_FUSED, "split": ddh.DDH_MODE_FUSED,
             "pulse": ddh.DDH_MODE_PULSE}[args.variant]
+    if args.lib_graph:
+        if not args.eager:
+            sys.exit("--lib-graph replays the library's own graphs: use it with --eager")
+        mode |= ddh.DDH_MODE_GRAPH
     plan.set_mode(mode)
     if args.chunk:
         plan.tune(ddh.DDH_TUNE_CHUNK, args.chunk)
@@ -121,10 +125,13 @@ def run_gpu(args, w):
     build_ms = min(build_ms, (time.perf_counter() - t0) * 1e3)
 
     n_slots, n_halo = lay["n_slots"], lay["n_halo"]
-    # "auto" runs what the library's automatic mode picks for this layout
+    # "auto" runs what the library's automatic mode picks: per-pulse launches
+    # when the calls are replayed from a graph, and for eager calls unless the
+    # pass is tiny
     variant = args.variant
     if variant == "auto":
-        variant = "step" if n_halo <= ddh.DDH_AUTO_FUSED_MAX else "pulse"
+        eager = (args.eager or args.cold) and not args.lib_graph
+        variant = "step" if (eager and n_halo <= ddh.DDH_AUTO_FUSED_MAX) else "pulse"
     xl = torch.zeros((n_slots, 3), dtype=torch.float32, device=dev)
     plan.gather_home(xg, xl)
     fl = torch.from_numpy(W.forces(w, n_slots)).to(dev)
@@ -161,6 +168,21 @@ def run_gpu(args, w):
             durs.append(e0.elapsed_time(e1) * 1e-3)
         wall = sum(durs)
         steps_done = args.steps
+    elif args.eager:
+        # eager: the host enqueues every call of every step itself (no graph),
+        # as an MD code without graph capture would
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            for _, fn, _ in calls:
+                fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        steps_done = args.steps
+        durs = [e0.elapsed_time(e1) * 1e-3 / args.steps]
     else:
         # G steps captured in one graph and replayed: the host enqueues one
         # graph per G steps, so the GPU never waits for the host
@@ -194,7 +216,7 @@ def run_gpu(args, w):
     # each pass alone (pack = coordinate pass, unpack = force pass), the same
     # way: graphs of G calls, replayed
     passes = None
-    if not args.cold:
+    if not args.cold and not args.eager:
         passes = {}
         G = max(1, min(args.graph_steps, args.steps))
         n_rep = max(1, min(args.steps // G, 10))
@@ -219,6 +241,34 @@ def run_gpu(args, w):
             del graph
         assert plan.check() == ddh.DDH_OK
 
+    # the single persistent launch (both passes, all pulses, one kernel), the
+    # same way, when it is not already the variant timed above
+    single = None
+    if not args.cold and not args.eager and variant != "step":
+        plan.set_mode(ddh.DDH_MODE_FUSED)
+        G = max(1, min(args.graph_steps, args.steps))
+        n_rep = max(1, min(args.steps // G, 4))
+        fn = lambda: plan.exchange_step(xl, fl)
+        fn()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(G):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_rep):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (n_rep * G)
+        single = {"kernel": "exchange_kernel", "us_per_step": round(us, 3),
+                  "frac": round((BYTES_X + BYTES_F) * n_halo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del graph
+        assert plan.check() == ddh.DDH_OK
+
     durs = sorted(durs)
     avg_step_gpu = sum(durs) / len(durs)
     step_bytes = sum(nb for _, _, nb in calls)
@@ -241,7 +291,7 @@ def run_gpu(args, w):
     step_s = wall / steps_done
     res = dict(
         n_slots=n_slots, n_halo=n_halo, n_pulses=lay["n_pulses"], build_ms=build_ms,
-        variant=variant, passes=passes,
+        variant=variant, passes=passes, single=single,
         step_s=step_s, steps=steps_done, gpu_step_us=round(avg_step_gpu * 1e6, 3),
         roofline=dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel,
@@ -374,6 +424,10 @@ def main():
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--block", type=int, default=0, choices=[0, 256, 1024])
     ap.add_argument("--cold", action="store_true", help="evict caches before every step")
+    ap.add_argument("--eager", action="store_true",
+                    help="enqueue every step from the host (no graph replay)")
+    ap.add_argument("--lib-graph", action="store_true",
+                    help="with --eager: each call replays the library's cached hipGraph")
     ap.add_argument("--graph-steps", type=int, default=50,
                     help="steps captured per graph replay in the timed region")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -427,11 +481,13 @@ def main():
             "rc_nm": w.rc, "cell_nm": w.cell, "pulses": gpu["n_pulses"],
             "halo_atoms_per_pass": gpu["n_halo"], "slots": gpu["n_slots"],
             "variant": gpu["variant"], "cache": "cold" if args.cold else "warm",
+            "launch": "eager" if (args.eager or args.cold) else "graph replay",
             "step": "coordinate pass + force pass",
         },
         "step_hbm_frac": round((BYTES_X + BYTES_F) * gpu["n_halo"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "map_build_ms": round(gpu["build_ms"], 3),
         "passes": gpu["passes"],
+        "single_launch": gpu["single"],
         "roofline": gpu["roofline"],
         "cpu_baseline": cpu,
     }

@@ -85,6 +85,17 @@ __device__ __forceinline__ int nth_bit(uint32_t m, int n)
     return __builtin_ctz(m);
 }
 
+// Wait until every vector memory operation this wave issued has completed
+// (s_waitcnt vmcnt 0; expcnt and lgkmcnt left at their maxima, so no wait on
+// them). Needed wherever one wave's fence or barrier stands for the whole
+// work-group: an agent-scope fence waits only for the wave that executes it,
+// and __syncthreads() emits no vmcnt wait on gfx950 (a workgroup-scope
+// release needs none, since the waves share the CU).
+__device__ __forceinline__ void wait_vm_idle()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // Wave 0 waits for every counter a chunk needs at once: lane l polls the
 // l-th of (the coordinate-chunk total, if need_x; the counters of the pulses
 // in mask_a at row_a; those in mask_b at row_b), so one round trip checks
@@ -131,6 +142,9 @@ __device__ void wave_wait(const XArgs& a, const uint32_t* cnt, const uint32_t* n
         __builtin_amdgcn_s_sleep(1);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // the invalidation has completed before the barrier that lets the
+    // work-group's other waves read
+    wait_vm_idle();
 }
 
 // Map entries of one round: entry i0 + e * B + tid for e < E (B threads).
@@ -305,6 +319,9 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
                 __syncthreads();
             }
             coords_range<E, B>(a.x, a.maps, c, c.tb, c.te, jt);
+            // every wave's records are in L2 before thread 0 releases them
+            if (c.flags & kChunkRelease)
+                wait_vm_idle();
             __syncthreads();
             if (threadIdx.x == 0) {
                 trace_rec(a, ntr, kTrChunk, (uint32_t)(c.he - c.hb + c.te - c.tb));
@@ -333,6 +350,9 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
                 __syncthreads();
             }
             forces_range<E, B>(a.f, a.maps, c, c.hb, c.he, j0);
+            // every wave's sums are in L2 before thread 0 releases them
+            if (c.flags & kChunkRelease)
+                wait_vm_idle();
             __syncthreads();
             if (threadIdx.x == 0) {
                 trace_rec(a, ntr, kTrChunk, (uint32_t)(c.he - c.hb));
@@ -513,11 +533,11 @@ int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, 
     return DDH_OK;
 }
 
-// The launches of one call, enqueued on s.
-int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s)
+// The launches of one call in mode (FUSED or PULSE), enqueued on s.
+int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s, int mode)
 {
     const int P = p->g.P;
-    if (!(p->effective_mode() & DDH_MODE_PULSE)) {
+    if (!(mode & DDH_MODE_PULSE)) {
         XArgs a{};
         a.x = x;
         a.f = f;
@@ -569,16 +589,25 @@ int enqueue_exchange(Plan* p, int op, float* x, float* f, hipStream_t s)
 {
     if (p->g.P == 0 || p->fused.nchunks.empty())
         return DDH_OK;
-    if (!(p->mode & DDH_MODE_GRAPH))
-        return enqueue_raw(p, op, x, f, s);
+    if (!(p->mode & DDH_MODE_GRAPH)) {
+        // a capturing stream means the launches will be replayed from the
+        // caller's graph (the legacy null stream is never captured)
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (s && hipStreamIsCapturing(s, &cs) != hipSuccess) {
+            (void)hipGetLastError();
+            cs = hipStreamCaptureStatusNone;
+        }
+        return enqueue_raw(p, op, x, f, s, p->effective_mode(cs == hipStreamCaptureStatusActive));
+    }
 
-    const auto key = std::make_tuple(op, (void*)x, (void*)f, p->effective_mode());
+    const int mode = p->effective_mode(true);
+    const auto key = std::make_tuple(op, (void*)x, (void*)f, mode);
     auto found = p->graphs.find(key);
     if (found == p->graphs.end()) {
         if (!p->capture_stream)
             DDH_HIP(hipStreamCreateWithFlags(&p->capture_stream, hipStreamNonBlocking));
         DDH_HIP(hipStreamBeginCapture(p->capture_stream, hipStreamCaptureModeThreadLocal));
-        int rc = enqueue_raw(p, op, x, f, p->capture_stream);
+        int rc = enqueue_raw(p, op, x, f, p->capture_stream, mode);
         hipGraph_t graph = nullptr;
         hipError_t e = hipStreamEndCapture(p->capture_stream, &graph);
         if (rc)

@@ -132,12 +132,15 @@ struct Plan {
     int64_t n_halo = 0;
     int32_t mode = DDH_MODE_AUTO;   // as requested (ddh_set_mode)
     // FUSED or PULSE (plus the GRAPH bit): AUTO resolved against the layout
-    int32_t effective_mode() const
+    // and against how the call's launches will run (replayed from a graph:
+    // captured by the caller or DDH_MODE_GRAPH; else enqueued eagerly)
+    int32_t effective_mode(bool captured) const
     {
         const int32_t base = mode & ~DDH_MODE_GRAPH;
-        const int32_t m = base == DDH_MODE_AUTO
-                              ? (n_halo <= DDH_AUTO_FUSED_MAX ? DDH_MODE_FUSED : DDH_MODE_PULSE)
-                              : base;
+        const bool replayed = captured || (mode & DDH_MODE_GRAPH);
+        const int32_t m = base != DDH_MODE_AUTO ? base
+                          : (!replayed && n_halo <= DDH_AUTO_FUSED_MAX) ? DDH_MODE_FUSED
+                                                                        : DDH_MODE_PULSE;
         return m | (mode & DDH_MODE_GRAPH);
     }
 

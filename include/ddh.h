@@ -90,12 +90,14 @@ typedef struct ddh_plan ddh_plan;
                               per-map device counters */
 #define DDH_MODE_PULSE 1   /* one launch per pulse, ordered by the stream,
                               then one launch that publishes per-pulse flags */
-#define DDH_MODE_AUTO 2    /* default: FUSED when a pass moves at most
-                              DDH_AUTO_FUSED_MAX halo atoms (latency-bound),
-                              else PULSE (bandwidth-bound) */
+#define DDH_MODE_AUTO 2    /* default: PULSE, except for a call that is
+                              enqueued eagerly (the stream is not capturing
+                              and DDH_MODE_GRAPH is off) on a pass of at most
+                              DDH_AUTO_FUSED_MAX halo atoms, which runs FUSED:
+                              there the host's cost per launch dominates */
 #define DDH_MODE_GRAPH 16  /* OR-able: replay the call's launches from a
                               captured hipGraph */
-#define DDH_AUTO_FUSED_MAX 200000
+#define DDH_AUTO_FUSED_MAX 16384
 
 /* ------------------------------------------------------------- lifecycle */
 

@@ -164,3 +164,15 @@ def test_single_hip_runtime_in_process():
     res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
     assert res.stdout.strip() == "1"
+
+
+def test_binding_constants_match_the_header():
+    # every integer #define of the header that the binding mirrors has the
+    # header's value
+    hdr = open(os.path.join(ROOT, "include", "ddh.h")).read()
+    defs = dict(re.findall(r"^#define\s+(DDH_[A-Z0-9_]+)\s+\(?(-?\d+)\)?", hdr, re.M))
+    assert len(defs) >= 20
+    mirrored = [k for k in defs if hasattr(ddh, k)]
+    assert len(mirrored) >= 15, mirrored
+    for k in mirrored:
+        assert getattr(ddh, k) == int(defs[k]), k

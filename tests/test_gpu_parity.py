@@ -139,6 +139,51 @@ def test_workload_fused_step(k, mode, workload_plan):
     g.close()
 
 
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("mode", ["auto", "pulse", "fused"])
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_captured_in_a_caller_graph(k, mode, split, workload_plan):
+    """Calls captured in a torch CUDA graph and replayed several times, with
+    eager work (new forces, a check) between replays: every replay matches
+    the oracle bit for bit."""
+    w, x, ref = workload_plan(k)
+    g = GpuPlan(x, **w.params(), mode=MODES[mode])
+    xl = g.new_coords()
+    fl = torch.zeros((max(g.n_slots, 1), 3), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        if split:
+            g.plan.exchange_coords(xl)
+            g.plan.exchange_forces(fl)
+        else:
+            g.plan.exchange_step(xl, fl)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        if split:
+            g.plan.exchange_coords(xl)
+            g.plan.exchange_forces(fl)
+        else:
+            g.plan.exchange_step(xl, fl)
+    rng = np.random.default_rng(300 + k)
+    for r in range(4):
+        xl.copy_(g.new_coords())
+        f0 = rng.normal(0, 10, size=(g.n_slots, 3)).astype(np.float32)
+        fl[:g.n_slots].copy_(torch.from_numpy(f0))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert g.plan.check() == ddh.DDH_OK
+        assert np.array_equal(bits(xl.cpu().numpy()[:g.n_slots]), bits(ref.x_local)), f"replay {r}"
+        fr = f0.copy()
+        ref.exchange_forces(fr)
+        assert np.array_equal(bits(fl.cpu().numpy()[:g.n_slots]), bits(fr)), f"replay {r}"
+    del graph
+    g.close()
+
+
 @pytest.mark.parametrize("chunk,wg,refined,block", [
     (64, 0, 1, 0), (320, 0, 1, 0), (8192, 0, 1, 0), (64, 1, 1, 0), (192, 3, 0, 0),
     (256, 1, 0, 0), (1024, 5, 1, 0), (2048, 0, 1, 1024), (4096, 0, 0, 1024), (1024, 0, 1, 256),

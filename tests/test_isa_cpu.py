@@ -108,3 +108,36 @@ def test_builder_barriers_never_share_a_loop_with_divergent_exits(tmp_path):
     assert any("select_write_kernel" in k for k in kernels)
     for name, lines in kernels.items():
         assert loops_with_barrier_and_divergent_exit(lines) == [], name
+
+
+def release_barriers_without_store_wait(lines, window=8):
+    """Indexes of buffer_wbl2 (agent-scope release) whose preceding s_barrier
+    is not preceded, within `window` lines, by s_waitcnt vmcnt(0): the other
+    waves' stores would then not be covered by the one wave's release."""
+    bad = []
+    for i, ln in enumerate(lines):
+        if "buffer_wbl2" not in ln:
+            continue
+        j = max((k for k in range(i) if "s_barrier" in lines[k]), default=None)
+        if j is None:
+            continue
+        if not any("s_waitcnt vmcnt(0)" in lines[k] for k in range(max(0, j - window), j)):
+            bad.append(i)
+    return bad
+
+
+def test_exchange_kernel_releases_cover_every_wave(tmp_path):
+    kernels = _isa(os.path.join(CSRC, "ddh_exchange.hip"), tmp_path)
+    ex = {k: v for k, v in kernels.items() if "exchange_kernel" in k}
+    assert len(ex) >= 3
+    for name, lines in ex.items():
+        assert sum("buffer_wbl2" in ln for ln in lines) >= 2, name
+        assert release_barriers_without_store_wait(lines) == [], name
+
+
+def test_release_checker_flags_a_bare_barrier():
+    lines = ["\tglobal_store_dwordx3 v[8:9], v[4:6], off nt", "\ts_or_b64 exec, exec, s[16:17]",
+             "\ts_barrier", "\tbuffer_wbl2 sc1", "\ts_waitcnt vmcnt(0)", "\tglobal_atomic_add v[4:5], v3, off"]
+    assert release_barriers_without_store_wait(lines) == [3]
+    fixed = lines[:2] + ["\ts_waitcnt vmcnt(0)"] + lines[2:]
+    assert release_barriers_without_store_wait(fixed) == []
