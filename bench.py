@@ -216,7 +216,7 @@ def run_gpu(args, w):
     # each pass alone (pack = coordinate pass, unpack = force pass), the same
     # way: graphs of G calls, replayed
     passes = None
-    if not args.cold and not args.eager:
+    if not args.cold and not args.eager and not args.only_step:
         passes = {}
         G = max(1, min(args.graph_steps, args.steps))
         n_rep = max(1, min(args.steps // G, 10))
@@ -244,7 +244,7 @@ def run_gpu(args, w):
     # the single persistent launch (both passes, all pulses, one kernel), the
     # same way, when it is not already the variant timed above
     single = None
-    if not args.cold and not args.eager and variant != "step":
+    if not args.cold and not args.eager and not args.only_step and variant != "step":
         plan.set_mode(ddh.DDH_MODE_FUSED)
         G = max(1, min(args.graph_steps, args.steps))
         n_rep = max(1, min(args.steps // G, 4))
@@ -390,6 +390,7 @@ def summarize_pmc(fetch_csv, write_csv, variant, wname, copy_mb, command):
     sw = expect_kib / w_cp if w_cp else 1.0
     traffic = (f_ex * sf + w_ex * sw) * 1024.0
     path = traffic_file(variant, wname)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as fh:
         fh.write(f"# HBM traffic of the exchange, variant {variant}, workload {wname}\n\n")
         fh.write("Two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),\n"
@@ -426,6 +427,9 @@ def main():
     ap.add_argument("--cold", action="store_true", help="evict caches before every step")
     ap.add_argument("--eager", action="store_true",
                     help="enqueue every step from the host (no graph replay)")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the step only (no per-pass or single-launch lines); "
+                         "for profiler runs")
     ap.add_argument("--lib-graph", action="store_true",
                     help="with --eager: each call replays the library's cached hipGraph")
     ap.add_argument("--graph-steps", type=int, default=50,
