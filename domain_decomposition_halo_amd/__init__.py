@@ -28,7 +28,7 @@ ERROR_NAMES = {DDH_EINVAL: "DDH_EINVAL", DDH_ERANGE: "DDH_ERANGE", DDH_ECAPACITY
                DDH_ESTATE: "DDH_ESTATE"}
 DDH_MAX_PULSES = 16
 DDH_MODE_FUSED, DDH_MODE_PULSE, DDH_MODE_AUTO, DDH_MODE_GRAPH = 0, 1, 2, 16
-DDH_AUTO_FUSED_MAX = 16384
+DDH_AUTO_FUSED_MAX = 200000
 DDH_TUNE_CHUNK, DDH_TUNE_GRID, DDH_TUNE_SPIN_LIMIT, DDH_TUNE_FORCE_TIMEOUT, DDH_TUNE_REFINED_WAITS = (
     1, 2, 3, 4, 5)
 DDH_TUNE_TRACE = 6

@@ -304,8 +304,11 @@ int ddh_exchange_step(ddh_plan* p, float* x, float* f, int64_t cap, void* stream
     rc = check_buffer(p, f, cap, "ddh_exchange_step (forces)");
     if (rc)
         return rc;
-    if (x == f && p->n_slots > 0)
-        return fail(DDH_EINVAL, "ddh_exchange_step: coordinates and forces share a buffer");
+    // the passes may overlap in time, so the arrays must not overlap in memory
+    const uintptr_t xb = (uintptr_t)x, fb = (uintptr_t)f;
+    const uintptr_t nb = (uintptr_t)p->n_slots * 3u * sizeof(float);
+    if (nb > 0 && xb < fb + nb && fb < xb + nb)
+        return fail(DDH_EINVAL, "ddh_exchange_step: coordinate and force arrays overlap");
     return enqueue_exchange(p, kOpStep, x, f, (hipStream_t)stream);
 }
 

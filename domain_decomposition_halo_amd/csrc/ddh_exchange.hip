@@ -97,30 +97,21 @@ __device__ __forceinline__ void wait_vm_idle()
 }
 
 // Wave 0 waits for every counter a chunk needs at once: lane l polls the
-// l-th of (the coordinate-chunk total, if need_x; the counters of the pulses
-// in mask_a at row_a; those in mask_b at row_b), so one round trip checks
-// them all. The loop exit is a wave-wide vote. Ends with an acquire fence.
+// l-th of (the counters of the pulses in mask_a at row_a; those in mask_b at
+// row_b), so one round trip checks them all. The loop exit is a wave-wide
+// vote. Ends with an acquire fence.
 __device__ void wave_wait(const XArgs& a, const uint32_t* cnt, const uint32_t* need, uint32_t pass,
-                          bool need_x, uint32_t px, uint32_t mask_a, int row_a, uint32_t mask_b,
-                          int row_b, uint32_t bump)
+                          uint32_t mask_a, int row_a, uint32_t mask_b, int row_b, uint32_t bump)
 {
-    const int lane = (int)(threadIdx.x & 63);
+    const int l = (int)(threadIdx.x & 63);
     const uint32_t* ptr = nullptr;
     uint32_t target = 0;
-    int l = lane;
-    if (need_x) {
-        if (l == 0) {
-            ptr = a.ctrl + kCtrlXDone;
-            target = px * (uint32_t)a.n_xchunks + bump;
-        }
-        l--;
-    }
     const int na = __builtin_popcount(mask_a);
-    if (!ptr && l >= 0 && l < na) {
+    if (l < na) {
         const int r = row_a + nth_bit(mask_a, l);
         ptr = cnt + r;
         target = pass * need[r] + bump;
-    } else if (!ptr && l >= na && l - na < __builtin_popcount(mask_b)) {
+    } else if (l - na < __builtin_popcount(mask_b)) {
         const int r = row_b + nth_bit(mask_b, l - na);
         ptr = cnt + r;
         target = pass * need[r] + bump;
@@ -131,7 +122,7 @@ __device__ void wave_wait(const XArgs& a, const uint32_t* cnt, const uint32_t* n
         if (__all(ok))
             break;
         if (++n >= a.spin_limit) {
-            if (lane == 0) {
+            if (l == 0) {
                 uint32_t zero = 0;
                 __hip_atomic_compare_exchange_strong(a.ctrl + kCtrlError, &zero,
                                                      (uint32_t)DDH_ETIMEOUT, __ATOMIC_RELAXED,
@@ -312,7 +303,7 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
                 if (wave == 0) {
                     if (threadIdx.x == 0)
                         trace_rec(a, ntr, kTrHead, (uint32_t)(c.he - c.hb));
-                    wave_wait(a, a.xcnt, a.xneed, px, false, px, c.wait_a, c.S * P, 0u, 0, bump);
+                    wave_wait(a, a.xcnt, a.xneed, px, c.wait_a, c.S * P, 0u, 0, bump);
                     if (threadIdx.x == 0)
                         trace_rec(a, ntr, kTrWaited, c.wait_a);
                 }
@@ -325,12 +316,9 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
             __syncthreads();
             if (threadIdx.x == 0) {
                 trace_rec(a, ntr, kTrChunk, (uint32_t)(c.he - c.hb + c.te - c.tb));
-                // forces never read coordinates, so the step's count of
-                // finished coordinate chunks needs no fence of its own
                 if (c.flags & kChunkRelease)
                     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
                 add_relaxed(a.xcnt + c.ctr, 1u);
-                add_relaxed(a.ctrl + kCtrlXDone, 1u);
                 trace_rec(a, ntr, kTrPublish, (uint32_t)c.ctr);
                 s_ticket = claim_ticket(a);
             }
@@ -339,11 +327,11 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
             const DChunk c = a.fchunks[t - a.nx];
             int j0[E];
             load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);  // static: before any wait
-            if (a.nx > 0 || c.wait_a || c.wait_b) {
+            // a step's force chunks do not wait for its coordinate chunks:
+            // the passes touch different arrays
+            if (c.wait_a || c.wait_b) {
                 if (wave == 0) {
-                    // forces of a step start once every region is filled
-                    wave_wait(a, a.fcnt, a.fneed, pf, a.nx > 0, px, c.wait_a, c.S * P, c.wait_b,
-                              c.R * P, bump);
+                    wave_wait(a, a.fcnt, a.fneed, pf, c.wait_a, c.S * P, c.wait_b, c.R * P, bump);
                     if (threadIdx.x == 0)
                         trace_rec(a, ntr, kTrWaited, c.wait_a | (c.wait_b << 16));
                 }
@@ -553,7 +541,6 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s, int mode)
         a.xneed = p->d_xneed;
         a.fneed = p->d_fneed;
         a.P = P;
-        a.n_xchunks = (int)t.xch.size();
         a.force_timeout = p->force_timeout;
         a.spin_limit = p->spin_limit;
         a.trace = p->trace;

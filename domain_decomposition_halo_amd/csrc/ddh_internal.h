@@ -25,7 +25,6 @@ enum CtrlWord : int {
     kCtrlPassP = 64,   // passes of the per-pulse mode completed
     kCtrlTicket = 96,  // next dynamic work ticket of the running fused launch
     kCtrlDone = 128,   // work-groups that left the running fused launch
-    kCtrlXDone = 160,  // coordinate chunks completed over all fused passes
     kCtrlError = 192,  // first device-side error code (0 = none)
     kCtrlWords = 224
 };
@@ -73,7 +72,6 @@ struct XArgs {
     const uint32_t* xneed;   // [R*P+p] chunks per pass behind xcnt
     const uint32_t* fneed;   // [S*P+p] chunks per pass behind fcnt
     int32_t P;
-    int32_t n_xchunks;       // coordinate chunks per pass
     int32_t static_first;    // 1: work-group b starts with ticket b
     int32_t force_timeout;   // waits target a value nobody writes
     uint32_t spin_limit;

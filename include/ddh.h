@@ -97,7 +97,7 @@ typedef struct ddh_plan ddh_plan;
                               there the host's cost per launch dominates */
 #define DDH_MODE_GRAPH 16  /* OR-able: replay the call's launches from a
                               captured hipGraph */
-#define DDH_AUTO_FUSED_MAX 16384
+#define DDH_AUTO_FUSED_MAX 200000
 
 /* ------------------------------------------------------------- lifecycle */
 
@@ -199,10 +199,12 @@ int ddh_exchange_forces(ddh_plan *plan, float *f_local_dev, int64_t capacity_slo
                         void *stream);
 
 /*
- * One coordinate pass followed by one force pass in a single launch (fused
- * mode) or one launch sequence (pulse mode); the force pass starts only once
- * every coordinate region has been delivered. Same results as
- * ddh_exchange_coords then ddh_exchange_forces. Asynchronous.
+ * One coordinate pass and one force pass in a single launch (fused mode) or
+ * one launch sequence (pulse mode: coordinate pulse q and force pulse P-1-q
+ * share a launch). The passes touch different arrays and may overlap in
+ * time; the results are those of ddh_exchange_coords then
+ * ddh_exchange_forces. The two arrays must not overlap (DDH_EINVAL).
+ * Asynchronous.
  */
 int ddh_exchange_step(ddh_plan *plan, float *x_local_dev, float *f_local_dev,
                       int64_t capacity_slots, void *stream);
