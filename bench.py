@@ -21,7 +21,7 @@ launch; `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
-       [--variant auto|step|split|pulse] [--cold]
+       [--variant auto|step|split|pulse|staged] [--cold] [--eager]
 Counter traffic: profiles/traffic_<variant>_<workload>.md, written by
 `python bench.py --summarize-pmc FETCH_CSV WRITE_CSV ...` from two rocprofv3
 --pmc runs of this script with --copy-probe; it is reported only while the
@@ -49,7 +49,7 @@ BYTES_X, BYTES_F = 28, 40
 KERNEL_SRCS = [os.path.join(ROOT, "domain_decomposition_halo_amd", "csrc", f)
                for f in ("ddh_exchange.hip", "ddh_build.hip", "ddh_internal.h")]
 PROFILES = os.path.join(ROOT, "profiles")
-VARIANTS = ("auto", "step", "split", "pulse")
+VARIANTS = ("auto", "step", "split", "pulse", "staged")
 
 
 def kernel_hash() -> str:
@@ -100,7 +100,7 @@ def run_gpu(args, w):
     # the timed region replays captured graphs itself, so the library's own
     # graph mode stays off here
     mode = {"auto": ddh.DDH_MODE_AUTO, "step": ddh.DDH_MODE_FUSED, "split": ddh.DDH_MODE_FUSED,
-            "pulse": ddh.DDH_MODE_PULSE}[args.variant]
+            "pulse": ddh.DDH_MODE_PULSE, "staged": ddh.DDH_MODE_STAGED}[args.variant]
     if args.lib_graph:
         if not args.eager:
             sys.exit("--lib-graph replays the library's own graphs: use it with --eager")
@@ -145,7 +145,8 @@ def run_gpu(args, w):
 
     # pulse mode: a step pairs coordinate pulse q with force pulse P-1-q in
     # one launch, then one flag launch
-    launches_per_step = {"step": 1, "split": 2}.get(variant, lay["n_pulses"] + 1)
+    launches_per_step = {"step": 1, "split": 2,
+                         "staged": 2 * lay["n_pulses"] + 1}.get(variant, lay["n_pulses"] + 1)
     for _ in range(args.warmup):
         for _, fn, _ in calls:
             fn()
@@ -276,7 +277,9 @@ def run_gpu(args, w):
     achieved = step_bytes / avg_step_gpu / 1e9
     traffic = read_traffic(variant, w.name)
     kernel = {"step": "exchange_kernel (fused step, one launch)",
-              "split": "exchange_kernel (coordinate launch + force launch)"}.get(
+              "split": "exchange_kernel (coordinate launch + force launch)",
+              "staged": "pulse_kernel pack/unpack + one hipMemcpyAsync per sender and pulse, "
+                        "two host waits per pulse"}.get(
                   variant, "pulse_kernel (coordinate pulse q + force pulse P-1-q per launch) + signal_kernel")
 
     if args.copy_probe:
@@ -441,6 +444,10 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--pmc-command", default="")
     args = ap.parse_args()
+    if args.variant == "staged":
+        # the host-orchestrated baseline waits on the host inside every call:
+        # it cannot be captured, so it is timed eagerly
+        args.eager = True
 
     import workloads as W
 

@@ -27,7 +27,7 @@ ERROR_NAMES = {DDH_EINVAL: "DDH_EINVAL", DDH_ERANGE: "DDH_ERANGE", DDH_ECAPACITY
                DDH_EHIP: "DDH_EHIP", DDH_ETIMEOUT: "DDH_ETIMEOUT", DDH_ENOTIMPL: "DDH_ENOTIMPL",
                DDH_ESTATE: "DDH_ESTATE"}
 DDH_MAX_PULSES = 16
-DDH_MODE_FUSED, DDH_MODE_PULSE, DDH_MODE_AUTO, DDH_MODE_GRAPH = 0, 1, 2, 16
+DDH_MODE_FUSED, DDH_MODE_PULSE, DDH_MODE_AUTO, DDH_MODE_STAGED, DDH_MODE_GRAPH = 0, 1, 2, 3, 16
 DDH_AUTO_FUSED_MAX = 200000
 DDH_TUNE_CHUNK, DDH_TUNE_GRID, DDH_TUNE_SPIN_LIMIT, DDH_TUNE_FORCE_TIMEOUT, DDH_TUNE_REFINED_WAITS = (
     1, 2, 3, 4, 5)

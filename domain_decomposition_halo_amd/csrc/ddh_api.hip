@@ -317,8 +317,12 @@ int ddh_set_mode(ddh_plan* p, int32_t mode)
     if (!p)
         return fail(DDH_EINVAL, "ddh_set_mode: null plan");
     const int32_t base = mode & ~DDH_MODE_GRAPH;
-    if (base != DDH_MODE_FUSED && base != DDH_MODE_PULSE && base != DDH_MODE_AUTO)
+    if (base != DDH_MODE_FUSED && base != DDH_MODE_PULSE && base != DDH_MODE_AUTO &&
+        base != DDH_MODE_STAGED)
         return fail(DDH_EINVAL, "ddh_set_mode: unknown mode");
+    if (base == DDH_MODE_STAGED && (mode & DDH_MODE_GRAPH))
+        return fail(DDH_EINVAL, "ddh_set_mode: DDH_MODE_STAGED waits on the host and cannot "
+                                "be replayed from a graph");
     p->mode = mode;
     return DDH_OK;
 }

@@ -442,6 +442,7 @@ void free_built(Plan* p)
     p->fused = WorkTable{};
     p->pulse = WorkTable{};
     p->d_ctrl = p->d_xcnt = p->d_fcnt = p->d_xneed = p->d_fneed = p->d_pflag = nullptr;
+    p->d_stage = nullptr;
     p->built = false;
     p->n_slots = p->n_halo = 0;
     p->n_atoms = 0;

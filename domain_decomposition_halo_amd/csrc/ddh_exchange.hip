@@ -223,13 +223,15 @@ __device__ __forceinline__ void forces_round(const float* from, float* tgt, int 
 
 // Entries [begin, end) of a chunk's map; j0 holds the first round's map
 // entries (loaded by the caller, possibly before a wait).
+// With a staging buffer (the host-orchestrated baseline), entry i of a map
+// goes to / comes from stage[map_off + i] instead of the receiver's region.
 template <int E, int B>
 __device__ void coords_range(float* x, const int32_t* maps, const DChunk& c, int begin, int end,
-                             const int (&j0)[E])
+                             const int (&j0)[E], float* stage = nullptr)
 {
     const int32_t* map = maps + c.map_off;
     const float* src = x + 3ll * c.src_base;
-    float* dst = x + 3ll * c.dst_base;
+    float* dst = stage ? stage + 3ll * c.map_off : x + 3ll * c.dst_base;
     coords_round<E, B>(src, dst, c, begin, end, j0);
     for (int i0 = begin + B * E; i0 < end; i0 += B * E) {
         int j[E];
@@ -240,11 +242,11 @@ __device__ void coords_range(float* x, const int32_t* maps, const DChunk& c, int
 
 template <int E, int B>
 __device__ void forces_range(float* f, const int32_t* maps, const DChunk& c, int begin, int end,
-                             const int (&j0)[E])
+                             const int (&j0)[E], const float* stage = nullptr)
 {
     const int32_t* map = maps + c.map_off;
     float* tgt = f + 3ll * c.src_base;
-    const float* from = f + 3ll * c.dst_base;
+    const float* from = stage ? stage + 3ll * c.map_off : f + 3ll * c.dst_base;
     forces_round<E, B>(from, tgt, begin, end, j0);
     for (int i0 = begin + B * E; i0 < end; i0 += B * E) {
         int j[E];
@@ -384,6 +386,7 @@ struct PArgs {
     const DChunk* xchunks;
     const DChunk* fchunks;
     int32_t xbegin, nxb, fbegin;
+    float* stage;  // null, or the staging buffer of the host-orchestrated mode
 };
 
 template <int E, int B>
@@ -394,17 +397,17 @@ __global__ __launch_bounds__(B) void pulse_kernel(PArgs a)
         const DChunk c = a.xchunks[a.xbegin + b];
         int j0[E];
         load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);
-        coords_range<E, B>(a.x, a.maps, c, c.hb, c.he, j0);
+        coords_range<E, B>(a.x, a.maps, c, c.hb, c.he, j0, a.stage);
         if (c.te > c.tb) {
             int jt[E];
             load_map<E, B>(a.maps + c.map_off, c.tb, c.te, jt);
-            coords_range<E, B>(a.x, a.maps, c, c.tb, c.te, jt);
+            coords_range<E, B>(a.x, a.maps, c, c.tb, c.te, jt, a.stage);
         }
     } else {
         const DChunk c = a.fchunks[a.fbegin + b - a.nxb];
         int j0[E];
         load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);
-        forces_range<E, B>(a.f, a.maps, c, c.hb, c.he, j0);
+        forces_range<E, B>(a.f, a.maps, c, c.hb, c.he, j0, a.stage);
     }
 }
 
@@ -482,7 +485,7 @@ int launch_fused(const Plan* p, XArgs a, hipStream_t s)
 // launch, one block per chunk; entries per lane and round from the table's
 // chunk size (larger chunks take several rounds).
 int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, int xe, int fb,
-                 int fe, hipStream_t s)
+                 int fe, hipStream_t s, float* stage = nullptr)
 {
     const int nb = (xe - xb) + (fe - fb);
     if (nb <= 0)
@@ -496,6 +499,7 @@ int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, 
     a.xbegin = xb;
     a.nxb = xe - xb;
     a.fbegin = fb;
+    a.stage = stage;
     // 1024-wide blocks with few entries per lane by default: on the 12M-atom
     // maps they move about 8% more than 256-wide blocks with 8 per lane;
     // chunks below 1024 entries take 256-wide blocks (no idle lanes)
@@ -570,6 +574,61 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s, int mode)
     return DDH_OK;
 }
 
+// The host-orchestrated baseline ("From MPI baseline to optimized GPU-native
+// halo exchange": pack, hand the buffer to the host, send and receive, then
+// unpack; two blocking waits per pulse). Per coordinate pulse: one pack
+// launch into the staging buffer, a host wait, one device-to-device copy per
+// sender into the receiver's region, a host wait. Per force pulse (reverse
+// order): one copy per sender of the receiver's region into the staging
+// buffer, a host wait, one unpack launch that adds, a host wait. The staging
+// buffer holds every map entry once (entry i of map (S, p) at map_off + i).
+int enqueue_staged(Plan* p, int op, float* x, float* f, hipStream_t s)
+{
+    const int P = p->g.P, D = p->g.ndom;
+    if (!p->d_stage && p->n_halo > 0) {
+        DDH_HIP(hipMalloc((void**)&p->d_stage, sizeof(float) * 3 * (size_t)p->n_halo));
+        p->owned.push_back(p->d_stage);
+    }
+    const WorkTable& t = p->pulse;
+    const auto& xb = t.xpulse_begin;
+    const auto& fb = t.fpulse_begin;
+    auto copies = [&](int q, float* arr, bool to_region) -> int {
+        for (int S = 0; S < D; S++) {
+            const int it = S * P + q;
+            const size_t n = (size_t)p->send[it];
+            if (n == 0)
+                continue;
+            float* region = arr + 3 * (p->base[p->recv[it]] + p->roff[it]);
+            float* staged = p->d_stage + 3 * p->map_off[it];
+            DDH_HIP(hipMemcpyAsync(to_region ? region : staged, to_region ? staged : region,
+                                   sizeof(float) * 3 * n, hipMemcpyDeviceToDevice, s));
+        }
+        return DDH_OK;
+    };
+    int rc = DDH_OK;
+    if (op & kOpCoords)
+        for (int q = 0; q < P; q++) {
+            if ((rc = launch_pulse(p, x, f, t, xb[q], xb[q + 1], 0, 0, s, p->d_stage)))
+                return rc;
+            DDH_HIP(hipStreamSynchronize(s));
+            if ((rc = copies(q, x, true)))
+                return rc;
+            DDH_HIP(hipStreamSynchronize(s));
+        }
+    if (op & kOpForces)
+        for (int r = 0; r < P; r++) {
+            if ((rc = copies(P - 1 - r, f, false)))
+                return rc;
+            DDH_HIP(hipStreamSynchronize(s));
+            if ((rc = launch_pulse(p, x, f, t, 0, 0, fb[r], fb[r + 1], s, p->d_stage)))
+                return rc;
+            DDH_HIP(hipStreamSynchronize(s));
+        }
+    hipLaunchKernelGGL(signal_kernel, dim3(1), dim3(64), 0, s, p->d_ctrl, p->d_pflag, P, op);
+    DDH_HIP(hipGetLastError());
+    return DDH_OK;
+}
+
 }  // namespace
 
 int enqueue_exchange(Plan* p, int op, float* x, float* f, hipStream_t s)
@@ -584,7 +643,13 @@ int enqueue_exchange(Plan* p, int op, float* x, float* f, hipStream_t s)
             (void)hipGetLastError();
             cs = hipStreamCaptureStatusNone;
         }
-        return enqueue_raw(p, op, x, f, s, p->effective_mode(cs == hipStreamCaptureStatusActive));
+        const bool captured = cs == hipStreamCaptureStatusActive;
+        if (p->mode == DDH_MODE_STAGED) {
+            if (captured)
+                return fail(DDH_EINVAL, "DDH_MODE_STAGED waits on the host: it cannot be captured");
+            return enqueue_staged(p, op, x, f, s);
+        }
+        return enqueue_raw(p, op, x, f, s, p->effective_mode(captured));
     }
 
     const int mode = p->effective_mode(true);

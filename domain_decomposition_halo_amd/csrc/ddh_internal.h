@@ -170,6 +170,7 @@ struct Plan {
     uint32_t* d_xneed = nullptr;
     uint32_t* d_fneed = nullptr;
     uint32_t* d_pflag = nullptr;   // [p] / [P + p]: per-pulse flags of pulse mode
+    float* d_stage = nullptr;      // staging buffer of DDH_MODE_STAGED (first use)
     std::vector<void*> owned;      // every hipMalloc of the built state
 
     // graph replay cache: (op, x, f, mode) -> executable graph

@@ -95,6 +95,15 @@ typedef struct ddh_plan ddh_plan;
                               and DDH_MODE_GRAPH is off) on a pass of at most
                               DDH_AUTO_FUSED_MAX halo atoms, which runs FUSED:
                               there the host's cost per launch dominates */
+#define DDH_MODE_STAGED 3  /* host-orchestrated baseline ("From MPI baseline
+                              to optimized GPU-native halo exchange"): per
+                              pulse a pack launch into a staging buffer, a
+                              host wait, one device-to-device copy per sender,
+                              a host wait (forces: the reverse, with an unpack
+                              launch that adds). The call returns when the
+                              pass is complete; it cannot be captured
+                              (DDH_EINVAL with DDH_MODE_GRAPH or on a
+                              capturing stream). Same results as the others. */
 #define DDH_MODE_GRAPH 16  /* OR-able: replay the call's launches from a
                               captured hipGraph */
 #define DDH_AUTO_FUSED_MAX 200000
@@ -210,7 +219,7 @@ int ddh_exchange_step(ddh_plan *plan, float *x_local_dev, float *f_local_dev,
                       int64_t capacity_slots, void *stream);
 
 /* Select DDH_MODE_FUSED, DDH_MODE_PULSE or DDH_MODE_AUTO, optionally
-   | DDH_MODE_GRAPH. */
+   | DDH_MODE_GRAPH, or DDH_MODE_STAGED alone. */
 int ddh_set_mode(ddh_plan *plan, int32_t mode);
 
 /*

@@ -128,7 +128,10 @@ def test_mode_and_tune_validation():
     plan.set_mode(ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH)
     plan.set_mode(ddh.DDH_MODE_FUSED)
     plan.set_mode(ddh.DDH_MODE_AUTO | ddh.DDH_MODE_GRAPH)
-    for bad in (3, 4, 8, 32):
+    plan.set_mode(ddh.DDH_MODE_STAGED)
+    with pytest.raises(ddh.DDHError):
+        plan.set_mode(ddh.DDH_MODE_STAGED | ddh.DDH_MODE_GRAPH)
+    for bad in (4, 8, 32):
         with pytest.raises(ddh.DDHError):
             plan.set_mode(bad)
     plan.tune(ddh.DDH_TUNE_CHUNK, 100)

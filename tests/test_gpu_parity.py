@@ -27,6 +27,7 @@ MODES = {
     "fused_graph": ddh.DDH_MODE_FUSED | ddh.DDH_MODE_GRAPH,
     "pulse_graph": ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH,
     "auto": ddh.DDH_MODE_AUTO,
+    "staged": ddh.DDH_MODE_STAGED,
 }
 
 
@@ -181,6 +182,26 @@ def test_captured_in_a_caller_graph(k, mode, split, workload_plan):
         ref.exchange_forces(fr)
         assert np.array_equal(bits(fl.cpu().numpy()[:g.n_slots]), bits(fr)), f"replay {r}"
     del graph
+    g.close()
+
+
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
+def test_staged_mode_refuses_capture(workload_plan):
+    w, x, ref = workload_plan(1)
+    g = GpuPlan(x, **w.params(), mode=ddh.DDH_MODE_STAGED)
+    xl = g.new_coords()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(ddh.DDHError) as e:
+        with torch.cuda.graph(graph):
+            g.plan.exchange_coords(xl)
+    assert e.value.code == ddh.DDH_EINVAL
+    del graph
+    torch.cuda.synchronize()
+    # the plan still works eagerly afterwards
+    g.plan.exchange_coords(xl)
+    assert g.plan.check() == ddh.DDH_OK
+    assert np.array_equal(bits(xl.cpu().numpy()[:g.n_slots]), bits(ref.x_local))
     g.close()
 
 
