@@ -310,6 +310,91 @@ def run_gpu(args, w):
     return res
 
 
+# ------------------------------------------------------ overlap with compute
+
+def run_overlap(args, w):
+    """Exchange step beside a CU-filling compute load on a second stream.
+
+    The load stands in for the local non-bonded work that runs while the
+    halo exchange is in flight: a chain of bf16 matrix products, sized by
+    --overlap-dim and --overlap-reps. Every stream keeps the default
+    priority. Each of (load alone, exchange alone, both) is captured as G
+    iterations in one graph (the two streams forked and joined inside it)
+    and replayed; exposed = both - load alone."""
+    import torch
+
+    import domain_decomposition_halo_amd as ddh
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    main_s = torch.cuda.current_stream()
+    x = W.positions(w)
+    xg = torch.from_numpy(x).to(dev)
+    plan = ddh.Plan(**w.params())
+    mode = {"auto": ddh.DDH_MODE_AUTO, "step": ddh.DDH_MODE_FUSED,
+            "pulse": ddh.DDH_MODE_PULSE}.get(args.variant, ddh.DDH_MODE_AUTO)
+    plan.set_mode(mode)
+    lay = plan.build_maps(xg)
+    n_slots, n_halo = lay["n_slots"], lay["n_halo"]
+    xl = torch.zeros((n_slots, 3), dtype=torch.float32, device=dev)
+    plan.gather_home(xg, xl)
+    fl = torch.from_numpy(W.forces(w, n_slots)).to(dev)
+    n = args.overlap_dim
+    g = torch.Generator(device="cpu").manual_seed(7)
+    a = torch.randn((n, n), generator=g).to(dev, torch.bfloat16)
+    b = torch.randn((n, n), generator=g).to(dev, torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream()
+
+    def load():
+        for _ in range(args.overlap_reps):
+            torch.mm(a, b, out=c)
+
+    def exchange():
+        plan.exchange_step(xl, fl)
+
+    def both():
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            load()
+        exchange()
+        torch.cuda.current_stream().wait_stream(side)
+
+    G = 20
+    out = {}
+    for name, fn in (("load", load), ("exchange", exchange), ("both", both)):
+        fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(G):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(main_s)
+            graph.replay()
+            e1.record(main_s)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / G
+            best = us if best is None else min(best, us)
+        out[name + "_us"] = round(best, 3)
+        del graph
+    assert plan.check() == ddh.DDH_OK
+    plan.close()
+    exposed = out["both_us"] - out["load_us"]
+    out["exposed_exchange_us"] = round(exposed, 3)
+    out["hidden_frac"] = round(1.0 - exposed / out["exchange_us"], 4) if out["exchange_us"] else None
+    out["load"] = f"{args.overlap_reps} x bf16 mm {n}x{n}x{n} on a second stream (default priority)"
+    out["workload"] = w.name
+    out["mode"] = args.variant
+    return out
+
+
 # ------------------------------------------------------------- CPU baseline
 
 def run_cpu_baseline(w, seconds: float):
@@ -430,11 +515,19 @@ def main():
     ap.add_argument("--cold", action="store_true", help="evict caches before every step")
     ap.add_argument("--eager", action="store_true",
                     help="enqueue every step from the host (no graph replay)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="time the step beside a compute load on a second stream "
+                         "(prints one JSON object of its own)")
+    ap.add_argument("--overlap-dim", type=int, default=2048)
+    ap.add_argument("--overlap-reps", type=int, default=4)
     ap.add_argument("--only-step", action="store_true",
                     help="time the step only (no per-pass or single-launch lines); "
                          "for profiler runs")
     ap.add_argument("--lib-graph", action="store_true",
                     help="with --eager: each call replays the library's cached hipGraph")
+    ap.add_argument("--also", default="5",
+                    help="comma-separated workload keys timed after the main one and "
+                         "summarized under 'also' (empty: none; skipped with --only-step)")
     ap.add_argument("--graph-steps", type=int, default=50,
                     help="steps captured per graph replay in the timed region")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -466,7 +559,26 @@ def main():
     if args.steps is None:
         args.steps = 1000 if w.n_atoms <= 100_000 else 200
 
+    if args.overlap:
+        print(json.dumps({"overlap": run_overlap(args, w)}), flush=True)
+        return
     gpu = run_gpu(args, w)
+    also = {}
+    keys = [int(k) for k in args.also.split(",") if k.strip()] if args.also else []
+    if not args.only_step and not args.copy_probe:
+        for k in keys:
+            if k == args.workload:
+                continue
+            wk = W.WORKLOADS[k]
+            sub = argparse.Namespace(**vars(args))
+            sub.steps = 1000 if wk.n_atoms <= 100_000 else 200
+            g2 = run_gpu(sub, wk)
+            also[wk.name] = {
+                "variant": g2["variant"], "halo_atoms_per_pass": g2["n_halo"],
+                "gpu_us_per_step": g2["gpu_step_us"],
+                "halo_atoms_per_s": round(g2["n_halo"] / g2["step_s"], 1),
+                "roofline_frac": g2["roofline"]["frac"], "achieved_GBps": g2["roofline"]["achieved"],
+                "passes": g2["passes"], "single_launch": g2["single"]}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(w, args.cpu_seconds)
@@ -501,6 +613,7 @@ def main():
         "single_launch": gpu["single"],
         "roofline": gpu["roofline"],
         "cpu_baseline": cpu,
+        "also": also or None,
     }
     print(json.dumps(out), flush=True)
 
