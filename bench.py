@@ -419,12 +419,26 @@ def run_cpu_baseline(w, seconds: float):
         if el >= seconds or steps >= 100000:
             break
     per_step = el / steps
+    # the same loops on one thread, for a quarter of the time
+    steps1 = 0
+    t0 = time.perf_counter()
+    while True:
+        ref.exchange_coords(xl, nthreads=1)
+        ref.exchange_forces(f, nthreads=1)
+        steps1 += 1
+        el1 = time.perf_counter() - t0
+        if el1 >= seconds / 4 or steps1 >= 100000:
+            break
+    per_step1 = el1 / steps1
     return dict(value=round(ref.halo_atoms / per_step, 1), unit="halo atoms/s", cores=threads,
                 kind="oracle",
                 sample=(f"{steps} steps (coordinate + force pass) of workload {w.name} "
                         f"in {el:.1f} s, OpenMP over domains, maps prebuilt "
                         f"(oracle map build {ref.build_seconds * 1e3:.0f} ms)"),
-                us_per_step=round(per_step * 1e6, 2))
+                us_per_step=round(per_step * 1e6, 2),
+                single_thread={"value": round(ref.halo_atoms / per_step1, 1),
+                               "us_per_step": round(per_step1 * 1e6, 2),
+                               "sample": f"{steps1} steps in {el1:.1f} s"})
 
 
 # --------------------------------------------------------- counter summary

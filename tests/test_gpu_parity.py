@@ -231,6 +231,8 @@ DYADIC = [
     ((2, 2, 2), (8.0, 8.0, 8.0), 4.0, 1500),
     ((4, 4, 2), (4.0, 4.0, 4.0), 1.0, 3000),
     ((1, 8, 1), (4.0, 16.0, 4.0), 4.5, 3000),
+    ((16, 1, 1), (16.0, 4.0, 4.0), 15.0, 2000),   # rc = L - w: 15 pulses, the most 16 domains allow
+    ((8, 8, 1), (8.0, 8.0, 4.0), 7.0, 3000),      # 7 + 7 = 14 pulses over two dimensions
 ]
 
 

@@ -31,6 +31,8 @@ DYADIC = [
     ((4, 1, 1), (8.0, 4.0, 4.0), 2.0, 1500),      # rc == width: one pulse
     ((2, 2, 2), (8.0, 8.0, 8.0), 4.0, 1500),      # rc == L - w: largest allowed
     ((4, 4, 2), (4.0, 4.0, 4.0), 1.0, 3000),      # rc == w in X/Y, 1 pulse
+    ((16, 1, 1), (16.0, 4.0, 4.0), 15.0, 2000),   # rc == L - w: 15 pulses, the most 16 allow
+    ((8, 8, 1), (8.0, 8.0, 4.0), 7.0, 3000),      # 7 + 7 = 14 pulses over two dimensions
 ]
 
 
