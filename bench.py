@@ -112,6 +112,8 @@ def run_gpu(args, w):
         plan.tune(ddh.DDH_TUNE_GRID, args.grid)
     if args.block:
         plan.tune(ddh.DDH_TUNE_BLOCK, args.block)
+    if args.static_first:
+        plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 1)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -335,6 +337,8 @@ def run_overlap(args, w):
     mode = {"auto": ddh.DDH_MODE_AUTO, "step": ddh.DDH_MODE_FUSED,
             "pulse": ddh.DDH_MODE_PULSE}.get(args.variant, ddh.DDH_MODE_AUTO)
     plan.set_mode(mode)
+    if args.static_first:
+        plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 1)
     lay = plan.build_maps(xg)
     n_slots, n_halo = lay["n_slots"], lay["n_halo"]
     xl = torch.zeros((n_slots, 3), dtype=torch.float32, device=dev)
@@ -526,6 +530,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--block", type=int, default=0, choices=[0, 256, 1024])
+    ap.add_argument("--static-first", action="store_true",
+                    help="fused launch: first tickets unclaimed (DDH_TUNE_STATIC_FIRST)")
     ap.add_argument("--cold", action="store_true", help="evict caches before every step")
     ap.add_argument("--eager", action="store_true",
                     help="enqueue every step from the host (no graph replay)")

@@ -33,6 +33,7 @@ DDH_TUNE_CHUNK, DDH_TUNE_GRID, DDH_TUNE_SPIN_LIMIT, DDH_TUNE_FORCE_TIMEOUT, DDH_
     1, 2, 3, 4, 5)
 DDH_TUNE_TRACE = 6
 DDH_TUNE_BLOCK = 7
+DDH_TUNE_STATIC_FIRST = 8
 TRACE_RECORDS = 64
 TRACE_EVENTS = {1: "start", 2: "claim", 3: "head", 4: "waited", 5: "chunk", 6: "publish", 7: "exit"}
 

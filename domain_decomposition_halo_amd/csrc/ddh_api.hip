@@ -381,6 +381,11 @@ int ddh_tune(ddh_plan* p, int32_t key, int64_t value)
     case DDH_TUNE_TRACE:
         p->trace = (uint64_t*)(uintptr_t)value;
         return DDH_OK;
+    case DDH_TUNE_STATIC_FIRST:
+        if (value != 0 && value != 1)
+            return fail(DDH_EINVAL, "ddh_tune: static-first must be 0 or 1");
+        p->static_first = (int)value;
+        return DDH_OK;
     default:
         return fail(DDH_EINVAL, "ddh_tune: unknown key");
     }

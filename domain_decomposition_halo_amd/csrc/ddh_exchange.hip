@@ -453,9 +453,14 @@ int launch_fused(const Plan* p, XArgs a, hipStream_t s)
     int grid = p->grid_req > 0 ? p->grid_req : p->n_cu * 4;
     if (grid > nt)
         grid = nt;
-    // a grid of at most one work-group per compute unit can all be resident,
-    // so each work-group may take its first ticket without claiming it
-    a.static_first = grid <= p->n_cu ? 1 : 0;
+    // Tickets are claimed in the order work-groups start, so a chunk only
+    // waits on chunks whose work-groups are already running, whatever else
+    // shares the GPU. On request (the caller guarantees the launch has the
+    // GPU to itself) a grid of at most one work-group per compute unit lets
+    // work-group b start with ticket b unclaimed; a concurrent kernel that
+    // holds compute units could then leave a producer undispatched behind
+    // its consumers.
+    a.static_first = (p->static_first && grid <= p->n_cu) ? 1 : 0;
     // work-group width: 1024 lanes when the grid leaves compute units idle
     // (few, latency-bound chunks), else 256; entries per lane and round from
     // the chunk size

@@ -258,6 +258,15 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     leaves compute units idle, else 256;
                                     per-pulse 1024), 256 or 1024 */
 
+#define DDH_TUNE_STATIC_FIRST 8    /* fused mode: 0 (default) every work-group
+                                    claims its tickets in start order, so no
+                                    chunk waits on one that has not started,
+                                    whatever else runs on the GPU; 1 work-group
+                                    b of a grid of at most one per compute
+                                    unit starts with ticket b unclaimed (saves
+                                    one atomic per work-group, but only safe
+                                    while the launch has the GPU to itself) */
+
 /* Set a tuning knob; takes effect at the next build (CHUNK) or call. */
 int ddh_tune(ddh_plan *plan, int32_t key, int64_t value);
 

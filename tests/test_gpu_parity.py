@@ -38,8 +38,10 @@ def bits(a):
 class GpuPlan:
     """A device plan built from host positions, with host views of its output."""
 
-    def __init__(self, x, grid, box, rc, cell=0.5, mode=0, chunk=0, wg=0, refined=1, block=0):
+    def __init__(self, x, grid, box, rc, cell=0.5, mode=0, chunk=0, wg=0, refined=1, block=0,
+                 static_first=0):
         self.plan = ddh.Plan(grid, box, rc, cell)
+        self.plan.tune(ddh.DDH_TUNE_STATIC_FIRST, static_first)
         self.plan.tune(ddh.DDH_TUNE_CHUNK, chunk)
         self.plan.tune(ddh.DDH_TUNE_GRID, wg)
         self.plan.tune(ddh.DDH_TUNE_BLOCK, block)
@@ -213,8 +215,9 @@ def test_staged_mode_refuses_capture(workload_plan):
 def test_chunk_and_grid_variants(k, chunk, wg, refined, block, workload_plan):
     # a single work-group must drain every ticket in order without waiting forever
     w, x, ref = workload_plan(k)
-    for mode in (ddh.DDH_MODE_FUSED, ddh.DDH_MODE_PULSE):
-        g = GpuPlan(x, **w.params(), mode=mode, chunk=chunk, wg=wg, refined=refined, block=block)
+    for mode, sf in ((ddh.DDH_MODE_FUSED, 0), (ddh.DDH_MODE_FUSED, 1), (ddh.DDH_MODE_PULSE, 0)):
+        g = GpuPlan(x, **w.params(), mode=mode, chunk=chunk, wg=wg, refined=refined, block=block,
+                    static_first=sf)
         check_steps(g, ref, 20 + k, steps=2)
         check_steps(g, ref, 30 + k, steps=1, fused_step=True)
         g.close()
