@@ -6,40 +6,49 @@
 //
 // Every domain is a slice of one device array, so the guide's direct-store
 // path ("Optimizing for efficient transfers across NVIDIA NVLink-connected
-// GPUs") is the only path: a sender gathers its map entries and stores them
+// GPUs") is the main path: a sender gathers its map entries and stores them
 // straight into the receiver's slots; nothing is staged and nothing is "put".
 // The work of a pass is cut into chunks (DChunk: a slice of one (sender,
-// pulse) map). Two ways to run them:
+// pulse) map). Three ways to run them:
 //
 //  - Per-pulse launches (DDH_MODE_PULSE; the guide's stream-ordered design of
 //    "Replacing host-side communication with NVSHMEM"): one launch per pulse,
 //    block b runs chunk b of the pulse; the stream orders the pulses, so no
 //    kernel waits, counts or fences. A step call runs coordinate pulse q and
 //    force pulse P-1-q in the same launch. A one-wave launch afterwards
-//    publishes per-pulse flags. Best where bandwidth matters.
+//    publishes per-pulse flags. The default whenever the calls are replayed
+//    from a graph: on MI355X a kernel boundary inside a graph costs less than
+//    a dependency carried across XCDs inside a kernel.
 //
 //  - One fused launch per call (DDH_MODE_FUSED; "Enabling parallelism across
 //    pulses through kernel fusion", "Dependency-aware packing", "Force halo
 //    exchange: Reversing the dependency chain"): work-groups claim chunks in
 //    ticket order (a chunk only ever waits on chunks claimed before it, so
-//    the launch cannot deadlock whatever the grid size). A coordinate chunk
-//    packs its independent slice, waits until the regions its dependent
-//    slice reads are complete, then packs that slice; a force chunk waits
-//    until the later pulses that add into the same slots of S, or into the
-//    slots of R's region it reads, are done, so each slot receives its adds
-//    in decreasing pulse order and matches the sequential reverse pass bit
-//    for bit. Best where latency matters.
+//    the launch cannot deadlock whatever the grid size or whatever else runs
+//    on the GPU). A coordinate chunk packs its independent slice, waits until
+//    the regions its dependent slice reads are complete, then packs that
+//    slice; a force chunk waits until the later pulses that add into the same
+//    slots of S, or into the slots of R's region it reads, are done, so each
+//    slot receives its adds in decreasing pulse order and matches the
+//    sequential reverse pass bit for bit. The single-launch form, and the
+//    default for eager calls on small passes, where the host's cost per
+//    launch dominates.
+//
+//  - The host-orchestrated baseline (DDH_MODE_STAGED; "From MPI baseline to
+//    optimized GPU-native halo exchange"): pack into a staging buffer, host
+//    wait, one copy per sender, host wait; forces the reverse.
 //
 // Completion in the fused launch ("Dependency-aware packing", hierarchical
-// release): a chunk ends with one agent-scope release fence and relaxed
-// increments of its map's counter (and of the coordinate-chunk total). The
-// counters only grow, one step per chunk and pass, so a waiter polls until a
-// counter reaches pass * chunks-per-pass and then acquires: every increment
-// continues the release sequence of the earlier ones, and no counter or flag
-// is ever reset. All eight XCDs form one agent, so agent scope plays the role
-// the guide gives to system scope. On MI355X each agent-scope fence and each
-// same-address atomic is serialized device-wide (tens of ns), which is why
-// chunks are large and a chunk issues one fence, not one per entry.
+// release): every wave of a chunk's work-group waits for its own stores, then
+// thread 0 issues one agent-scope release fence and a relaxed increment of
+// the map's counter. The counters only grow, one step per chunk and pass, so
+// a waiter polls until a counter reaches pass * chunks-per-pass and then
+// acquires: every increment continues the release sequence of the earlier
+// ones, and no counter or flag is ever reset. All eight XCDs form one agent,
+// so agent scope plays the role the guide gives to system scope. On MI355X
+// each agent-scope fence and each same-address atomic is serialized
+// device-wide (tens of ns), which is why chunks are large and a chunk issues
+// one fence, not one per entry.
 //
 // Every wait is bounded by a spin limit; on expiry it records DDH_ETIMEOUT in
 // the control block and the work-group carries on, so every launch drains.
