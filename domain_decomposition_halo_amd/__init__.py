@@ -40,6 +40,7 @@ TRACE_EVENTS = {1: "start", 2: "claim", 3: "head", 4: "waited", 5: "chunk", 6: "
 # every symbol declared in include/ddh.h
 EXPORTS = ("ddh_plan_create", "ddh_plan_destroy", "ddh_last_error", "ddh_build_maps", "ddh_query",
            "ddh_domain_info", "ddh_pulse_info", "ddh_copy_maps", "ddh_local_ids",
+           "ddh_flags", "ddh_copy_flags",
            "ddh_gather_home", "ddh_exchange_coords", "ddh_exchange_forces",
            "ddh_exchange_step", "ddh_set_mode", "ddh_check", "ddh_tune")
 
@@ -88,6 +89,8 @@ def _load():
         "ddh_pulse_info": ([V, I32, I32] + [ctypes.POINTER(I32)] * 5, ctypes.c_int),
         "ddh_copy_maps": ([V, P, I64, V], ctypes.c_int),
         "ddh_local_ids": ([V, P, I64, V], ctypes.c_int),
+        "ddh_flags": ([V, ctypes.POINTER(ctypes.c_void_p)], ctypes.c_int),
+        "ddh_copy_flags": ([V, P, V], ctypes.c_int),
         "ddh_gather_home": ([V, P, P, I64, V], ctypes.c_int),
         "ddh_exchange_coords": ([V, P, I64, V], ctypes.c_int),
         "ddh_exchange_forces": ([V, P, I64, V], ctypes.c_int),
@@ -182,6 +185,19 @@ class Plan:
         _check(_lib.ddh_copy_maps(self._h, _dev_ptr(out, "int32", "maps"), out.numel(),
                                   _stream(stream)), "ddh_copy_maps")
         return out
+
+    def flags_address(self) -> int:
+        """Device address of the per-pulse completion flags (uint32[2 * 16])."""
+        ptr = ctypes.c_void_p()
+        _check(_lib.ddh_flags(self._h, ctypes.byref(ptr)), "ddh_flags")
+        return ptr.value or 0
+
+    def copy_flags(self, out, stream=None):
+        """Snapshot of the flags into a device int32/uint32 tensor of >= 32 words."""
+        if out.numel() < 2 * DDH_MAX_PULSES:
+            raise ValueError("copy_flags: the tensor needs 2 * DDH_MAX_PULSES words")
+        _check(_lib.ddh_copy_flags(self._h, _dev_ptr(out, "int32", "flags"), _stream(stream)),
+               "ddh_copy_flags")
 
     def local_ids(self, out, stream=None):
         _check(_lib.ddh_local_ids(self._h, _dev_ptr(out, "int32", "ids"), out.numel(),

@@ -244,6 +244,29 @@ int ddh_copy_maps(const ddh_plan* p, int32_t* maps_dev, int64_t capacity, void* 
     return DDH_OK;
 }
 
+int ddh_flags(const ddh_plan* p, uint32_t** flags_dev)
+{
+    int rc = check_built(p);
+    if (rc)
+        return rc;
+    if (!flags_dev)
+        return fail(DDH_EINVAL, "ddh_flags: null output");
+    *flags_dev = p->d_pflag;
+    return DDH_OK;
+}
+
+int ddh_copy_flags(const ddh_plan* p, uint32_t* flags_dev, void* stream)
+{
+    int rc = check_built(p);
+    if (rc)
+        return rc;
+    if (!flags_dev)
+        return fail(DDH_EINVAL, "ddh_copy_flags: null buffer");
+    DDH_HIP(hipMemcpyAsync(flags_dev, p->d_pflag, sizeof(uint32_t) * 2 * DDH_MAX_PULSES,
+                           hipMemcpyDeviceToDevice, (hipStream_t)stream));
+    return DDH_OK;
+}
+
 int ddh_local_ids(const ddh_plan* p, int32_t* ids_dev, int64_t capacity, void* stream)
 {
     int rc = check_built(p);

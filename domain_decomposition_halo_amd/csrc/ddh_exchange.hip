@@ -289,7 +289,9 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
     const uint32_t pf = ld_relaxed(a.ctrl + kCtrlPassF) + 1u;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> 6;  // uniform: 0 in wave 0
 
-    int ntr = 0;  // trace records written by thread 0
+    int ntr = 0;         // trace records written by thread 0
+    bool held = false;   // this work-group wrote records it has not released
+                         // (uniform: every thread tracks the same chunks)
     if (threadIdx.x == 0) {
         trace_rec(a, ntr, kTrStart, gridDim.x);
         s_ticket = a.static_first ? (int)blockIdx.x : claim_ticket(a);
@@ -324,6 +326,7 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
             // every wave's records are in L2 before thread 0 releases them
             if (c.flags & kChunkRelease)
                 wait_vm_idle();
+            held = !(c.flags & kChunkRelease);
             __syncthreads();
             if (threadIdx.x == 0) {
                 trace_rec(a, ntr, kTrChunk, (uint32_t)(c.he - c.hb + c.te - c.tb));
@@ -352,6 +355,7 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
             // every wave's sums are in L2 before thread 0 releases them
             if (c.flags & kChunkRelease)
                 wait_vm_idle();
+            held = !(c.flags & kChunkRelease);
             __syncthreads();
             if (threadIdx.x == 0) {
                 trace_rec(a, ntr, kTrChunk, (uint32_t)(c.he - c.hb));
@@ -365,19 +369,40 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
         }
     }
 
-    // Leave: the last work-group re-arms the ticket counter for the next
-    // launch and publishes the numbers of the passes this launch completed.
+    // Leave: a work-group that still holds unreleased records (chunks no
+    // later chunk of the launch reads) releases them; the last work-group to
+    // leave then sees every work-group's records, re-arms the ticket counter
+    // for the next launch, and publishes the passes this launch completed:
+    // the fused pass counters and, after a release, every pulse's completion
+    // flag ("Dependency-aware packing": the last arrival stores the flag).
+    if (held) {
+        wait_vm_idle();
+        __syncthreads();
+    }
     if (threadIdx.x == 0) {
         trace_rec(a, ntr, kTrExit, 0);
+        if (held)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const uint32_t old = __hip_atomic_fetch_add(a.ctrl + kCtrlDone, 1u, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
         if (old == gridDim.x - 1u) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
             st_relaxed(a.ctrl + kCtrlTicket, 0u);
             st_relaxed(a.ctrl + kCtrlDone, 0u);
-            if (a.nx > 0)
+            if (a.nx > 0) {
+                const uint32_t e = ld_relaxed(a.ctrl + kCtrlEpochX) + 1u;
                 st_relaxed(a.ctrl + kCtrlPassX, px);
-            if (a.nf > 0)
+                for (int q = 0; q < P; q++)
+                    st_relaxed(a.flags + q, e);
+                st_relaxed(a.ctrl + kCtrlEpochX, e);
+            }
+            if (a.nf > 0) {
+                const uint32_t e = ld_relaxed(a.ctrl + kCtrlEpochF) + 1u;
                 st_relaxed(a.ctrl + kCtrlPassF, pf);
+                for (int q = 0; q < P; q++)
+                    st_relaxed(a.flags + DDH_MAX_PULSES + q, e);
+                st_relaxed(a.ctrl + kCtrlEpochF, e);
+            }
         }
     }
 }
@@ -395,12 +420,31 @@ struct PArgs {
     const DChunk* xchunks;
     const DChunk* fchunks;
     int32_t xbegin, nxb, fbegin;
-    float* stage;  // null, or the staging buffer of the host-orchestrated mode
+    float* stage;     // null, or the staging buffer of the host-orchestrated mode
+    uint32_t* ctrl;
+    uint32_t* flags;
+    uint32_t xdone;   // coordinate / force pulses that earlier launches of the
+    uint32_t fdone;   // call completed, whose flags this launch publishes
 };
+
+// Completion flags of pulses that earlier launches of the same call finished:
+// the launch boundary has made their records visible, so relaxed stores of
+// the epoch the call is completing suffice.
+__device__ __forceinline__ void publish_done(const PArgs& a)
+{
+    const int q = (int)threadIdx.x;
+    if (blockIdx.x == 0 && q < DDH_MAX_PULSES && ((a.xdone | a.fdone) >> q & 1u)) {
+        if (a.xdone >> q & 1u)
+            st_relaxed(a.flags + q, ld_relaxed(a.ctrl + kCtrlEpochX) + 1u);
+        if (a.fdone >> q & 1u)
+            st_relaxed(a.flags + DDH_MAX_PULSES + q, ld_relaxed(a.ctrl + kCtrlEpochF) + 1u);
+    }
+}
 
 template <int E, int B>
 __global__ __launch_bounds__(B) void pulse_kernel(PArgs a)
 {
+    publish_done(a);
     const int b = (int)blockIdx.x;
     if (b < a.nxb) {
         const DChunk c = a.xchunks[a.xbegin + b];
@@ -420,21 +464,28 @@ __global__ __launch_bounds__(B) void pulse_kernel(PArgs a)
     }
 }
 
-// After the pulse launches of a call (stream-ordered, so complete): one
-// release, then the per-pulse flags of the finished passes and their number.
-__global__ void signal_kernel(uint32_t* ctrl, uint32_t* pflag, int P, int op)
+// After the launches of a call (stream-ordered, so complete): the completion
+// flags of the pulses in xmask / fmask not published yet, then the epochs of
+// the passes the call completed (op: kOpCoords / kOpForces bits).
+__global__ void signal_kernel(uint32_t* ctrl, uint32_t* flags, uint32_t xmask, uint32_t fmask,
+                              int op)
 {
-    const uint32_t pass = ld_relaxed(ctrl + kCtrlPassP) + 1u;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const int q = threadIdx.x;
-    if (q < P) {
-        if (op & kOpCoords)
-            st_relaxed(pflag + q, pass);
-        if (op & kOpForces)
-            st_relaxed(pflag + P + q, pass);
+    const uint32_t ex = ld_relaxed(ctrl + kCtrlEpochX) + 1u;
+    const uint32_t ef = ld_relaxed(ctrl + kCtrlEpochF) + 1u;
+    if (q < DDH_MAX_PULSES) {
+        if (xmask >> q & 1u)
+            st_relaxed(flags + q, ex);
+        if (fmask >> q & 1u)
+            st_relaxed(flags + DDH_MAX_PULSES + q, ef);
     }
-    if (q == 0)
-        st_relaxed(ctrl + kCtrlPassP, pass);
+    __syncthreads();
+    if (q == 0) {
+        if (op & kOpCoords)
+            st_relaxed(ctrl + kCtrlEpochX, ex);
+        if (op & kOpForces)
+            st_relaxed(ctrl + kCtrlEpochF, ef);
+    }
 }
 
 // x_local[home_slot[r]] = x_global[home_gid[r]] for every home atom r.
@@ -498,8 +549,10 @@ int launch_fused(const Plan* p, XArgs a, hipStream_t s)
 // Coordinate chunks [xb, xe) and force chunks [fb, fe) of table t in one
 // launch, one block per chunk; entries per lane and round from the table's
 // chunk size (larger chunks take several rounds).
+// xdone / fdone: pulses completed by earlier launches of the call whose flags
+// this launch publishes; cleared when the launch takes them over.
 int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, int xe, int fb,
-                 int fe, hipStream_t s, float* stage = nullptr)
+                 int fe, hipStream_t s, uint32_t& xdone, uint32_t& fdone, float* stage = nullptr)
 {
     const int nb = (xe - xb) + (fe - fb);
     if (nb <= 0)
@@ -514,6 +567,11 @@ int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, 
     a.nxb = xe - xb;
     a.fbegin = fb;
     a.stage = stage;
+    a.ctrl = p->d_ctrl;
+    a.flags = p->d_pflag;
+    a.xdone = xdone;
+    a.fdone = fdone;
+    xdone = fdone = 0u;
     // 1024-wide blocks with few entries per lane by default: on the 12M-atom
     // maps they move about 8% more than 256-wide blocks with 8 per lane;
     // chunks below 1024 entries take 256-wide blocks (no idle lanes)
@@ -562,28 +620,31 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s, int mode)
         a.force_timeout = p->force_timeout;
         a.spin_limit = p->spin_limit;
         a.trace = p->trace;
+        a.flags = p->d_pflag;
         return launch_fused(p, a, s);
     }
     // one launch per pulse: coordinates in increasing, forces in decreasing
     // pulse order (fpulse_begin is already in that order); a step pairs the
-    // q-th launch of each pass; then the per-pulse flags
+    // q-th launch of each pass. Launch q publishes the flags of launch q-1's
+    // pulses; a last one-wave launch those of the final launch.
     const WorkTable& t = p->pulse;
     const auto& xb = t.xpulse_begin;
     const auto& fb = t.fpulse_begin;
+    const bool xs = op & kOpCoords, fs = op & kOpForces;
     int rc = DDH_OK;
-    if (op == kOpStep) {
-        for (int q = 0; q < P && !rc; q++)
-            rc = launch_pulse(p, x, f, t, xb[q], xb[q + 1], fb[q], fb[q + 1], s);
-    } else if (op == kOpCoords) {
-        for (int q = 0; q < P && !rc; q++)
-            rc = launch_pulse(p, x, f, t, xb[q], xb[q + 1], 0, 0, s);
-    } else {
-        for (int r = 0; r < P && !rc; r++)
-            rc = launch_pulse(p, x, f, t, 0, 0, fb[r], fb[r + 1], s);
+    uint32_t xdone = 0u, fdone = 0u;  // completed pulses whose flags are pending
+    for (int q = 0; q < P && !rc; q++) {
+        rc = launch_pulse(p, x, f, t, xs ? xb[q] : 0, xs ? xb[q + 1] : 0, fs ? fb[q] : 0,
+                          fs ? fb[q + 1] : 0, s, xdone, fdone);
+        if (xs)
+            xdone |= 1u << q;
+        if (fs)
+            fdone |= 1u << (P - 1 - q);
     }
     if (rc)
         return rc;
-    hipLaunchKernelGGL(signal_kernel, dim3(1), dim3(64), 0, s, p->d_ctrl, p->d_pflag, P, op);
+    hipLaunchKernelGGL(signal_kernel, dim3(1), dim3(64), 0, s, p->d_ctrl, p->d_pflag, xdone, fdone,
+                       op);
     DDH_HIP(hipGetLastError());
     return DDH_OK;
 }
@@ -606,6 +667,7 @@ int enqueue_staged(Plan* p, int op, float* x, float* f, hipStream_t s)
     const WorkTable& t = p->pulse;
     const auto& xb = t.xpulse_begin;
     const auto& fb = t.fpulse_begin;
+    uint32_t none = 0u;  // the flags are published once, at the end of the call
     auto copies = [&](int q, float* arr, bool to_region) -> int {
         for (int S = 0; S < D; S++) {
             const int it = S * P + q;
@@ -622,7 +684,7 @@ int enqueue_staged(Plan* p, int op, float* x, float* f, hipStream_t s)
     int rc = DDH_OK;
     if (op & kOpCoords)
         for (int q = 0; q < P; q++) {
-            if ((rc = launch_pulse(p, x, f, t, xb[q], xb[q + 1], 0, 0, s, p->d_stage)))
+            if ((rc = launch_pulse(p, x, f, t, xb[q], xb[q + 1], 0, 0, s, none, none, p->d_stage)))
                 return rc;
             DDH_HIP(hipStreamSynchronize(s));
             if ((rc = copies(q, x, true)))
@@ -634,11 +696,13 @@ int enqueue_staged(Plan* p, int op, float* x, float* f, hipStream_t s)
             if ((rc = copies(P - 1 - r, f, false)))
                 return rc;
             DDH_HIP(hipStreamSynchronize(s));
-            if ((rc = launch_pulse(p, x, f, t, 0, 0, fb[r], fb[r + 1], s, p->d_stage)))
+            if ((rc = launch_pulse(p, x, f, t, 0, 0, fb[r], fb[r + 1], s, none, none, p->d_stage)))
                 return rc;
             DDH_HIP(hipStreamSynchronize(s));
         }
-    hipLaunchKernelGGL(signal_kernel, dim3(1), dim3(64), 0, s, p->d_ctrl, p->d_pflag, P, op);
+    const uint32_t all = (P >= 32 ? 0u : (1u << P)) - 1u;
+    hipLaunchKernelGGL(signal_kernel, dim3(1), dim3(64), 0, s, p->d_ctrl, p->d_pflag,
+                       (op & kOpCoords) ? all : 0u, (op & kOpForces) ? all : 0u, op);
     DDH_HIP(hipGetLastError());
     return DDH_OK;
 }

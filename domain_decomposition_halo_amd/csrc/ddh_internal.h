@@ -20,9 +20,10 @@ constexpr int kBlock = 256;
 
 // Control words, each on its own 128-byte line (index in uint32 units).
 enum CtrlWord : int {
-    kCtrlPassX = 0,    // fused coordinate passes completed
+    kCtrlPassX = 0,    // fused coordinate passes completed (counter targets)
     kCtrlPassF = 32,   // fused force passes completed
-    kCtrlPassP = 64,   // passes of the per-pulse mode completed
+    kCtrlEpochX = 64,  // coordinate passes completed in any mode (flag values)
+    kCtrlEpochF = 80,  // force passes completed in any mode
     kCtrlTicket = 96,  // next dynamic work ticket of the running fused launch
     kCtrlDone = 128,   // work-groups that left the running fused launch
     kCtrlError = 192,  // first device-side error code (0 = none)
@@ -76,6 +77,7 @@ struct XArgs {
     int32_t force_timeout;   // waits target a value nobody writes
     uint32_t spin_limit;
     uint64_t* trace;         // optional event log (null: off)
+    uint32_t* flags;         // per-pulse completion flags, published at exit
 };
 
 // Event log: work-group b writes record k at trace[2 * (b * kTraceRecords + k)]
@@ -170,7 +172,8 @@ struct Plan {
     uint32_t* d_fcnt = nullptr;
     uint32_t* d_xneed = nullptr;
     uint32_t* d_fneed = nullptr;
-    uint32_t* d_pflag = nullptr;   // [p] / [P + p]: per-pulse flags of pulse mode
+    uint32_t* d_pflag = nullptr;   // per-pulse completion flags: [p] coordinates,
+                                   // [DDH_MAX_PULSES + p] forces (epoch values)
     float* d_stage = nullptr;      // staging buffer of DDH_MODE_STAGED (first use)
     std::vector<void*> owned;      // every hipMalloc of the built state
 

@@ -171,6 +171,32 @@ int ddh_pulse_info(const ddh_plan *plan, int32_t dom, int32_t pulse, int32_t *se
  */
 int ddh_copy_maps(const ddh_plan *plan, int32_t *maps_dev, int64_t capacity, void *stream);
 
+/*
+ * Per-pulse completion flags ("From MPI baseline to optimized GPU-native halo
+ * exchange": a signal counter per pulse; "Dependency-aware packing": the
+ * last arrival stores the flag). *flags_dev receives the device address of
+ * the plan's uint32[2 * DDH_MAX_PULSES]: word p counts the coordinate passes
+ * whose pulse p has been delivered to every receiver, word DDH_MAX_PULSES + p
+ * the force passes whose pulse-p adds are all done, since the last
+ * ddh_build_maps (which zeroes them). The words only grow (modulo 2^32). A
+ * kernel on another stream may poll word p (agent-scope atomic load) until it
+ * reaches the pass it needs, then acquire (agent-scope fence) and read the
+ * pulse's region. When each word is published:
+ *   - DDH_MODE_PULSE: pulse q's words when the call's next launch starts
+ *     (in a step, pulse q of the coordinates and P-1-q of the forces share a
+ *     launch), the last launch's words by the call's final one-wave launch;
+ *   - DDH_MODE_FUSED: every pulse's words when the launch's last work-group
+ *     leaves;
+ *   - DDH_MODE_STAGED: every pulse's words at the end of the call.
+ * The array belongs to the plan and lives until ddh_plan_destroy or the next
+ * ddh_build_maps.
+ */
+int ddh_flags(const ddh_plan *plan, uint32_t **flags_dev);
+
+/* Copy the 2 * DDH_MAX_PULSES flag words into flags_dev (device, uint32),
+   ordered on stream after the work enqueued before it. Asynchronous. */
+int ddh_copy_flags(const ddh_plan *plan, uint32_t *flags_dev, void *stream);
+
 /* Global atom id of every slot (int32[n_slots], device). Asynchronous. */
 int ddh_local_ids(const ddh_plan *plan, int32_t *ids_dev, int64_t capacity, void *stream);
 

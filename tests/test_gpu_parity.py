@@ -187,6 +187,45 @@ def test_captured_in_a_caller_graph(k, mode, split, workload_plan):
     g.close()
 
 
+def test_completion_flags_count_passes(workload_plan):
+    """Every mode publishes every pulse's completion flag with the number of
+    passes completed so far; words past the plan's pulses stay zero."""
+    w, x, ref = workload_plan(4)
+    g = GpuPlan(x, **w.params())
+    P = g.P
+    xl = g.new_coords()
+    fl = torch.zeros((max(g.n_slots, 1), 3), dtype=torch.float32, device="cuda")
+    buf = torch.zeros(2 * ddh.DDH_MAX_PULSES, dtype=torch.int32, device="cuda")
+    assert g.plan.flags_address() != 0
+
+    def check(nx, nf):
+        g.plan.copy_flags(buf)
+        v = buf.cpu().numpy().view(np.uint32)
+        m = ddh.DDH_MAX_PULSES
+        assert (v[:P] == nx).all() and (v[P:m] == 0).all(), (nx, v[:m])
+        assert (v[m:m + P] == nf).all() and (v[m + P:] == 0).all(), (nf, v[m:])
+
+    check(0, 0)
+    nx = nf = 0
+    for mode in (ddh.DDH_MODE_PULSE, ddh.DDH_MODE_FUSED, ddh.DDH_MODE_STAGED, ddh.DDH_MODE_AUTO,
+                 ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, ddh.DDH_MODE_FUSED | ddh.DDH_MODE_GRAPH):
+        g.plan.set_mode(mode)
+        g.plan.exchange_coords(xl)
+        nx += 1
+        check(nx, nf)
+        g.plan.exchange_forces(fl)
+        nf += 1
+        check(nx, nf)
+        g.plan.exchange_step(xl, fl)
+        nx += 1
+        nf += 1
+        check(nx, nf)
+    assert g.plan.check() == ddh.DDH_OK
+    # the coordinates are still the oracle's after all these passes
+    assert np.array_equal(bits(xl.cpu().numpy()[:g.n_slots]), bits(ref.x_local))
+    g.close()
+
+
 @pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
 def test_staged_mode_refuses_capture(workload_plan):
     w, x, ref = workload_plan(1)
