@@ -27,6 +27,7 @@ ERROR_NAMES = {DDH_EINVAL: "DDH_EINVAL", DDH_ERANGE: "DDH_ERANGE", DDH_ECAPACITY
                DDH_EHIP: "DDH_EHIP", DDH_ETIMEOUT: "DDH_ETIMEOUT", DDH_ENOTIMPL: "DDH_ENOTIMPL",
                DDH_ESTATE: "DDH_ESTATE"}
 DDH_MAX_PULSES = 16
+DDH_PASS_COORDS, DDH_PASS_FORCES = 0, 1
 DDH_MODE_FUSED, DDH_MODE_PULSE, DDH_MODE_AUTO, DDH_MODE_STAGED, DDH_MODE_GRAPH = 0, 1, 2, 3, 16
 DDH_AUTO_FUSED_MAX = 200000
 DDH_TUNE_CHUNK, DDH_TUNE_GRID, DDH_TUNE_SPIN_LIMIT, DDH_TUNE_FORCE_TIMEOUT, DDH_TUNE_REFINED_WAITS = (
@@ -40,7 +41,7 @@ TRACE_EVENTS = {1: "start", 2: "claim", 3: "head", 4: "waited", 5: "chunk", 6: "
 # every symbol declared in include/ddh.h
 EXPORTS = ("ddh_plan_create", "ddh_plan_destroy", "ddh_last_error", "ddh_build_maps", "ddh_query",
            "ddh_domain_info", "ddh_pulse_info", "ddh_copy_maps", "ddh_local_ids",
-           "ddh_flags", "ddh_copy_flags",
+           "ddh_flags", "ddh_copy_flags", "ddh_wait_flag",
            "ddh_gather_home", "ddh_exchange_coords", "ddh_exchange_forces",
            "ddh_exchange_step", "ddh_set_mode", "ddh_check", "ddh_tune")
 
@@ -91,6 +92,7 @@ def _load():
         "ddh_local_ids": ([V, P, I64, V], ctypes.c_int),
         "ddh_flags": ([V, ctypes.POINTER(ctypes.c_void_p)], ctypes.c_int),
         "ddh_copy_flags": ([V, P, V], ctypes.c_int),
+        "ddh_wait_flag": ([V, I32, I32, ctypes.c_uint32, V], ctypes.c_int),
         "ddh_gather_home": ([V, P, P, I64, V], ctypes.c_int),
         "ddh_exchange_coords": ([V, P, I64, V], ctypes.c_int),
         "ddh_exchange_forces": ([V, P, I64, V], ctypes.c_int),
@@ -198,6 +200,11 @@ class Plan:
             raise ValueError("copy_flags: the tensor needs 2 * DDH_MAX_PULSES words")
         _check(_lib.ddh_copy_flags(self._h, _dev_ptr(out, "int32", "flags"), _stream(stream)),
                "ddh_copy_flags")
+
+    def wait_flag(self, pass_kind: int, pulse: int, epoch: int, stream=None):
+        """Enqueue on stream a device wait for pulse `pulse` of a pass to reach `epoch`."""
+        _check(_lib.ddh_wait_flag(self._h, pass_kind, pulse, epoch & 0xFFFFFFFF, _stream(stream)),
+               "ddh_wait_flag")
 
     def local_ids(self, out, stream=None):
         _check(_lib.ddh_local_ids(self._h, _dev_ptr(out, "int32", "ids"), out.numel(),

@@ -267,6 +267,20 @@ int ddh_copy_flags(const ddh_plan* p, uint32_t* flags_dev, void* stream)
     return DDH_OK;
 }
 
+int ddh_wait_flag(ddh_plan* p, int32_t pass_kind, int32_t pulse, uint32_t epoch, void* stream)
+{
+    int rc = check_built(p);
+    if (rc)
+        return rc;
+    if (pass_kind != DDH_PASS_COORDS && pass_kind != DDH_PASS_FORCES)
+        return fail(DDH_EINVAL, "ddh_wait_flag: pass_kind must be DDH_PASS_COORDS or "
+                                "DDH_PASS_FORCES");
+    if (pulse < 0 || pulse >= p->g.P)
+        return fail(DDH_EINVAL, "ddh_wait_flag: pulse out of range");
+    const int idx = (pass_kind == DDH_PASS_FORCES ? DDH_MAX_PULSES : 0) + pulse;
+    return enqueue_wait_flag(p, idx, epoch, (hipStream_t)stream);
+}
+
 int ddh_local_ids(const ddh_plan* p, int32_t* ids_dev, int64_t capacity, void* stream)
 {
     int rc = check_built(p);

@@ -488,6 +488,31 @@ __global__ void signal_kernel(uint32_t* ctrl, uint32_t* flags, uint32_t xmask, u
     }
 }
 
+// One wave waits until flags[idx] reaches epoch (modulo 2^32), then
+// acquires, so the work enqueued after it on the same stream sees every
+// record the flag covers. Bounded by the spin limit (DDH_ETIMEOUT).
+__global__ void wait_flag_kernel(const uint32_t* flags, int idx, uint32_t epoch, uint32_t* ctrl,
+                                 uint32_t spin_limit)
+{
+    uint32_t n = 0;
+    for (;;) {
+        const bool ok = (int32_t)(ld_relaxed(flags + idx) - epoch) >= 0;
+        if (__all(ok))
+            break;
+        if (++n >= spin_limit) {
+            if (threadIdx.x == 0) {
+                uint32_t zero = 0;
+                __hip_atomic_compare_exchange_strong(ctrl + kCtrlError, &zero,
+                                                     (uint32_t)DDH_ETIMEOUT, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
 // x_local[home_slot[r]] = x_global[home_gid[r]] for every home atom r.
 __global__ __launch_bounds__(kBlock) void gather_home_kernel(const float* __restrict__ xg,
                                                              float* __restrict__ x,
@@ -757,6 +782,14 @@ int enqueue_exchange(Plan* p, int op, float* x, float* f, hipStream_t s)
         found = p->graphs.emplace(key, exec).first;
     }
     DDH_HIP(hipGraphLaunch(found->second, s));
+    return DDH_OK;
+}
+
+int enqueue_wait_flag(Plan* p, int idx, uint32_t epoch, hipStream_t s)
+{
+    hipLaunchKernelGGL(wait_flag_kernel, dim3(1), dim3(64), 0, s, p->d_pflag, idx, epoch,
+                       p->d_ctrl, p->spin_limit);
+    DDH_HIP(hipGetLastError());
     return DDH_OK;
 }
 

@@ -200,5 +200,6 @@ void free_built(Plan* plan);
 enum Op : int { kOpCoords = 1, kOpForces = 2, kOpStep = 3 };
 int enqueue_exchange(Plan* plan, int op, float* x, float* f, hipStream_t stream);
 int enqueue_gather_home(Plan* plan, const float* xg, float* x, hipStream_t stream);
+int enqueue_wait_flag(Plan* plan, int idx, uint32_t epoch, hipStream_t stream);
 
 }  // namespace ddh

@@ -197,6 +197,23 @@ int ddh_flags(const ddh_plan *plan, uint32_t **flags_dev);
    ordered on stream after the work enqueued before it. Asynchronous. */
 int ddh_copy_flags(const ddh_plan *plan, uint32_t *flags_dev, void *stream);
 
+#define DDH_PASS_COORDS 0
+#define DDH_PASS_FORCES 1
+
+/*
+ * Make the work enqueued on stream after this call wait until pulse `pulse`
+ * of the coordinate (DDH_PASS_COORDS) or force (DDH_PASS_FORCES) pass has
+ * completed `epoch` times (its flag word reaches epoch, modulo 2^32), and
+ * see the records it delivered: a one-wave wait on the device, ending with
+ * an agent-scope acquire ("From MPI baseline to optimized GPU-native halo
+ * exchange": the receiver's wait on the pulse's signal). It lets work that
+ * needs only pulse p's halo, on another stream, start before the rest of the
+ * exchange. The wait is bounded by DDH_TUNE_SPIN_LIMIT polls; on expiry
+ * ddh_check reports DDH_ETIMEOUT and the stream goes on. Asynchronous;
+ * DDH_EINVAL for a bad pass kind or pulse.
+ */
+int ddh_wait_flag(ddh_plan *plan, int32_t pass_kind, int32_t pulse, uint32_t epoch, void *stream);
+
 /* Global atom id of every slot (int32[n_slots], device). Asynchronous. */
 int ddh_local_ids(const ddh_plan *plan, int32_t *ids_dev, int64_t capacity, void *stream);
 

@@ -226,6 +226,57 @@ def test_completion_flags_count_passes(workload_plan):
     g.close()
 
 
+@pytest.mark.parametrize("mode", ["pulse", "fused"])
+def test_wait_flag_orders_a_consumer_stream(mode, workload_plan):
+    """A consumer stream that waits on a pulse's flag reads that pulse's
+    delivered records: the exchange on one stream, then on a second stream
+    a flag wait followed by a gather of every receiver's region of the pulse,
+    for each pulse and two passes."""
+    w, x, ref = workload_plan(2)
+    g = GpuPlan(x, **w.params(), mode=MODES[mode])
+    base, nhome, ntotal, pul = g.tables()
+    xl = g.new_coords()
+    prod = torch.cuda.Stream()
+    cons = torch.cuda.Stream()
+    for p in range(g.P):
+        idx = np.concatenate([base[pul[S, p, 2]] + pul[S, p, 3] + np.arange(pul[S, p, 0])
+                              for S in range(g.D)]).astype(np.int64)
+        idx_d = torch.from_numpy(idx).cuda()
+        for epoch in (2 * p + 1, 2 * p + 2):
+            torch.cuda.synchronize()
+            xl.copy_(g.new_coords())  # halo slots cleared
+            torch.cuda.synchronize()
+            with torch.cuda.stream(prod):
+                g.plan.exchange_coords(xl)
+            with torch.cuda.stream(cons):
+                g.plan.wait_flag(ddh.DDH_PASS_COORDS, p, epoch)
+                got = xl.index_select(0, idx_d)
+            torch.cuda.synchronize()
+            assert g.plan.check() == ddh.DDH_OK
+            assert np.array_equal(bits(got.cpu().numpy()), bits(ref.x_local[idx])), (p, epoch)
+    g.close()
+
+
+def test_wait_flag_errors_and_timeout(workload_plan):
+    w, x, ref = workload_plan(1)
+    g = GpuPlan(x, **w.params())
+    for kind, pulse in ((2, 0), (ddh.DDH_PASS_COORDS, g.P), (ddh.DDH_PASS_FORCES, -1)):
+        with pytest.raises(ddh.DDHError) as e:
+            g.plan.wait_flag(kind, pulse, 1)
+        assert e.value.code == ddh.DDH_EINVAL
+    # a pass that never comes: the wait gives up after the spin limit
+    g.plan.tune(ddh.DDH_TUNE_SPIN_LIMIT, 2000)
+    g.plan.wait_flag(ddh.DDH_PASS_FORCES, 0, 5)
+    assert g.plan.check() == ddh.DDH_ETIMEOUT
+    assert g.plan.check() == ddh.DDH_OK
+    xl = g.new_coords()
+    g.plan.exchange_coords(xl)
+    g.plan.wait_flag(ddh.DDH_PASS_COORDS, 0, 1)
+    assert g.plan.check() == ddh.DDH_OK
+    assert np.array_equal(bits(xl.cpu().numpy()[:g.n_slots]), bits(ref.x_local))
+    g.close()
+
+
 @pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
 def test_staged_mode_refuses_capture(workload_plan):
     w, x, ref = workload_plan(1)
