@@ -352,23 +352,104 @@ __global__ __launch_bounds__(256) void fill_home_kernel(const int* __restrict__ 
 }
 
 // slot_gid for the region records of one pulse (stored receiver-major).
-__global__ __launch_bounds__(256) void fill_region_kernel(const int* __restrict__ rgid, int total,
-                                                          const int* __restrict__ rs, int ndom,
-                                                          const int* __restrict__ dst,
-                                                          int* __restrict__ slot_gid)
+// Index of the segment of prefix[0..n] (non-decreasing, prefix[0] = 0) that
+// holds e: the largest k < n with prefix[k] <= e.
+__device__ __forceinline__ int segment_of(const int* prefix, int n, int e)
 {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= total)
-        return;
-    int lo = 0, hi = ndom;  // find R with rs[R] <= idx < rs[R+1]
+    int lo = 0, hi = n;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (rs[mid] <= idx)
+        if (prefix[mid] <= e)
             lo = mid;
         else
             hi = mid;
     }
-    slot_gid[dst[lo] + (idx - rs[lo])] = rgid[idx];
+    return lo;
+}
+
+// Region q of every receiver: global id of each received slot, and the pulse
+// it was received in (rid).
+__global__ __launch_bounds__(256) void fill_region_kernel(const int* __restrict__ rgid, int total,
+                                                          const int* __restrict__ rs, int ndom,
+                                                          const int* __restrict__ dst,
+                                                          int* __restrict__ slot_gid,
+                                                          uint8_t* __restrict__ rid, int q)
+{
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total)
+        return;
+    const int R = segment_of(rs, ndom, idx);  // rs[R] <= idx < rs[R+1]
+    const int slot = dst[R] + (idx - rs[R]);
+    slot_gid[slot] = rgid[idx];
+    rid[slot] = (uint8_t)q;
+}
+
+// inmap[slot] |= bit for every entry of pulse q's maps (maps_q: the pulse's
+// maps of all senders, sender S's at mpos[S]..mpos[S+1]). Within one pulse
+// every slot appears at most once (a map holds distinct slots of its own
+// sender), so plain read-modify-writes suffice; pulses run one after the
+// other on the stream.
+__global__ __launch_bounds__(256) void inmap_kernel(const int32_t* __restrict__ maps_q, int total,
+                                                    const int* __restrict__ mpos, int ndom,
+                                                    const int* __restrict__ base,
+                                                    uint32_t* __restrict__ inmap, uint32_t bit)
+{
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total)
+        return;
+    const int S = segment_of(mpos, ndom, idx);
+    const int slot = base[S] + maps_q[idx];
+    inmap[slot] |= bit;
+}
+
+// Wait masks of the fused launch's chunks, one block per chunk. Coordinate
+// chunk: the pulses whose regions at S its dependent slice reads (bit
+// rid[slot] of every entry of [tb, te)). Force chunk: the later pulses whose
+// maps hold a slot it adds into (at S) or a slot of R's region it reads.
+__global__ __launch_bounds__(256) void chunk_masks_kernel(DChunk* __restrict__ xch, int nx,
+                                                          DChunk* __restrict__ fch, int nf,
+                                                          const int32_t* __restrict__ maps,
+                                                          const uint8_t* __restrict__ rid,
+                                                          const uint32_t* __restrict__ inmap,
+                                                          int P)
+{
+    __shared__ uint32_t s_a, s_b;
+    if (threadIdx.x == 0) {
+        s_a = 0u;
+        s_b = 0u;
+    }
+    __syncthreads();
+    const int b = (int)blockIdx.x;
+    uint32_t wa = 0u, wb = 0u;
+    if (b < nx) {
+        const DChunk c = xch[b];
+        for (int i = c.tb + (int)threadIdx.x; i < c.te; i += 256) {
+            const uint8_t r = rid[c.src_base + maps[c.map_off + i]];
+            if (r < 32)
+                wa |= 1u << r;
+        }
+    } else {
+        const DChunk c = fch[b - nx];
+        for (int i = c.hb + (int)threadIdx.x; i < c.he; i += 256) {
+            wa |= inmap[c.src_base + maps[c.map_off + i]];
+            wb |= inmap[c.dst_base + i];
+        }
+    }
+    if (wa)
+        atomicOr(&s_a, wa);
+    if (wb)
+        atomicOr(&s_b, wb);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        if (b < nx) {
+            xch[b].wait_a = s_a;
+        } else {
+            DChunk& c = fch[b - nx];
+            const uint32_t later = ~((2u << c.p) - 1u) & ((1u << P) - 1u);
+            c.wait_a = s_a & later;
+            c.wait_b = s_b & later;
+        }
+    }
 }
 
 // ---------------------------------------------------------------- host side
@@ -448,35 +529,17 @@ void free_built(Plan* p)
     p->n_atoms = 0;
 }
 
-// Chunk table of chunk size t.chunk, from the maps (host copies). With
-// waits: the per-chunk wait masks and release flags of the fused launch;
-// without: the masks stay empty (per-pulse launches are ordered by the
-// stream).
-static void make_work_table(const Plan* p, const std::vector<int32_t>& maps, bool waits,
-                            WorkTable& t)
+// Chunk table of chunk size t.chunk. With waits (the fused launch) a
+// coordinate chunk takes the k-th slice of its map's independent head and of
+// its dependent tail, and a force chunk the k-th slice of the map; the wait
+// masks are the conservative ones (every earlier / later pulse) unless
+// refined waits are on, in which case chunk_masks_kernel fills them in from
+// the maps. Without waits (per-pulse launches, ordered by the stream) every
+// chunk is one contiguous slice and the masks stay empty.
+static void make_work_table(const Plan* p, bool waits, WorkTable& t)
 {
     const Geometry& g = p->g;
     const int D = g.ndom, P = g.P, CH = t.chunk;
-    // per slot: pulse the slot was received in (-1 home), and the set of
-    // pulses whose map holds the slot (as a bit mask)
-    std::vector<int8_t> rid;
-    std::vector<uint32_t> inmap;
-    if (waits) {
-        rid.assign((size_t)p->n_slots, -1);
-        inmap.assign((size_t)p->n_slots, 0u);
-        for (int S = 0; S < D; S++)
-            for (int q = 0; q < P; q++) {
-                const int it = S * P + q;
-                const int R = p->recv[it];
-                const int64_t b = p->base[R] + p->roff[it];
-                for (int i = 0; i < p->send[it]; i++)
-                    rid[(size_t)(b + i)] = (int8_t)q;
-                const int32_t* m = maps.data() + p->map_off[it];
-                for (int i = 0; i < p->send[it]; i++)
-                    inmap[(size_t)(p->base[S] + m[i])] |= 1u << q;
-            }
-    }
-
     t.nchunks.assign((size_t)D * P, 1);
     for (int it = 0; it < D * P; it++)
         t.nchunks[it] = std::max(1, (p->send[it] + CH - 1) / CH);
@@ -494,6 +557,7 @@ static void make_work_table(const Plan* p, const std::vector<int32_t>& maps, boo
         d.p = q;
         return d;
     };
+    const bool conservative = waits && !p->refined_waits;
     // coordinates: the k-th slice of the independent head and of the
     // dependent tail; the chunk advances the counter of the region it fills
     auto xchunk = [&](int it, int k) {
@@ -501,7 +565,6 @@ static void make_work_table(const Plan* p, const std::vector<int32_t>& maps, boo
         DChunk d = base_chunk(it);
         d.ctr = d.R * P + d.p;
         if (!waits) {
-            // no waits: one contiguous slice of the map
             const int n = p->send[it];
             d.hb = (int32_t)((int64_t)n * k / c);
             d.he = (int32_t)((int64_t)n * (k + 1) / c);
@@ -512,21 +575,11 @@ static void make_work_table(const Plan* p, const std::vector<int32_t>& maps, boo
         d.he = (int32_t)((int64_t)h * (k + 1) / c);
         d.tb = h + (int32_t)((int64_t)tl * k / c);
         d.te = h + (int32_t)((int64_t)tl * (k + 1) / c);
-        uint32_t w = 0;
-        if (waits && d.te > d.tb) {
-            if (!p->refined_waits) {
-                w = (1u << d.p) - 1u;
-            } else {
-                const int32_t* m = maps.data() + p->map_off[it];
-                for (int i = d.tb; i < d.te; i++)
-                    w |= 1u << rid[(size_t)(p->base[d.S] + m[i])];
-            }
-        }
-        d.wait_a = w;
+        d.wait_a = (conservative && d.te > d.tb) ? (1u << d.p) - 1u : 0u;
         return d;
     };
-    // forces: the k-th slice of the map; waits on the later pulses that add
-    // into the same slots of S or into the slots of R's region that it reads
+    // forces: the k-th slice of the map; the chunk advances its own item's
+    // counter
     auto fchunk = [&](int it, int k) {
         const int c = t.nchunks[it], n = p->send[it];
         DChunk d = base_chunk(it);
@@ -535,21 +588,7 @@ static void make_work_table(const Plan* p, const std::vector<int32_t>& maps, boo
         d.tb = d.te = d.he;
         d.ctr = d.S * P + d.p;
         const uint32_t later = ~((2u << d.p) - 1u) & ((1u << P) - 1u);
-        if (!waits) {
-            d.wait_a = d.wait_b = 0;
-        } else if (!p->refined_waits) {
-            d.wait_a = d.wait_b = later;
-        } else {
-            uint32_t wa = 0, wb = 0;
-            const int32_t* m = maps.data() + p->map_off[it];
-            const int64_t rb = p->base[d.R] + p->roff[it];
-            for (int i = d.hb; i < d.he; i++) {
-                wa |= inmap[(size_t)(p->base[d.S] + m[i])];
-                wb |= inmap[(size_t)(rb + i)];
-            }
-            d.wait_a = wa & later;
-            d.wait_b = wb & later;
-        }
+        d.wait_a = d.wait_b = conservative ? later : 0u;
         return d;
     };
 
@@ -574,11 +613,14 @@ static void make_work_table(const Plan* p, const std::vector<int32_t>& maps, boo
                 t.fch.push_back(fchunk(S * P + q, k));
     }
     t.fpulse_begin[P] = (int)t.fch.size();
-    if (!waits)
-        return;
+}
 
-    // a chunk publishes with a release fence only if a later chunk of the
-    // same launch waits on its counter (and so reads what it wrote)
+// A chunk of the fused launch publishes with a release fence only if a
+// later chunk of the same launch waits on its counter (and so reads what it
+// wrote). Needs the final wait masks.
+static void set_release_flags(const Plan* p, WorkTable& t)
+{
+    const int D = p->g.ndom, P = p->g.P;
     std::vector<char> xread((size_t)D * P, 0), fread((size_t)D * P, 0);
     for (const DChunk& c : t.xch)
         for (uint32_t m = c.wait_a; m; m &= m - 1)
@@ -884,14 +926,18 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         }
     }
 
-    // global id per slot, home slot per home atom
+    // global id per slot, home slot per home atom; pulse of every received
+    // slot (rid, 0xff for home slots) for the wait masks
     DDH_HIP(owned_alloc(p, &p->d_slot_gid, (size_t)p->n_slots));
     DDH_HIP(owned_alloc(p, &p->d_home_slot, (size_t)n_atoms));
+    uint8_t* d_rid;
+    DDH_HIP(sc.alloc(&d_rid, (size_t)p->n_slots));
+    DDH_HIP(hipMemsetAsync(d_rid, 0xff, (size_t)p->n_slots, s));
+    std::vector<int> base32(D);
+    int* d_base;
     {
-        std::vector<int> base32(D);
         for (int Dm = 0; Dm < D; Dm++)
             base32[Dm] = (int)p->base[Dm];
-        int* d_base;
         DDH_HIP(sc.alloc(&d_base, (size_t)D));
         DDH_HIP(upload(d_base, base32, s));
         if (n_atoms > 0)
@@ -911,22 +957,60 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
             DDH_HIP(upload(d_dst[q], dst, s));
             if (total[q] > 0)
                 hipLaunchKernelGGL(fill_region_kernel, dim3(blocks(total[q])), dim3(256), 0, s,
-                                   rgid[q], total[q], d_rs[q], D, d_dst[q], p->d_slot_gid);
+                                   rgid[q], total[q], d_rs[q], D, d_dst[q], p->d_slot_gid, d_rid,
+                                   q);
         }
         DDH_HIP(hipGetLastError());
         DDH_HIP(hipStreamSynchronize(s));
     }
 
-    // ---- 5: chunk tables, counters
+    // ---- 5: chunk tables (wait masks computed on the device), counters
     p->fused.chunk = p->chunk_req > 0 ? p->chunk_req : fused_chunk();
     p->pulse.chunk = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p);
-    std::vector<int32_t> hmaps((size_t)nh);
-    if (nh > 0)
-        DDH_HIP(hipMemcpyAsync(hmaps.data(), p->d_maps, sizeof(int32_t) * nh,
-                               hipMemcpyDeviceToHost, s));
-    DDH_HIP(hipStreamSynchronize(s));
-    make_work_table(p, hmaps, true, p->fused);
-    make_work_table(p, hmaps, false, p->pulse);
+    make_work_table(p, true, p->fused);
+    make_work_table(p, false, p->pulse);
+    for (WorkTable* t : {&p->fused, &p->pulse}) {
+        DDH_HIP(owned_alloc(p, &t->d_xch, t->xch.size()));
+        DDH_HIP(owned_alloc(p, &t->d_fch, t->fch.size()));
+        DDH_HIP(upload(t->d_xch, t->xch, s));
+        DDH_HIP(upload(t->d_fch, t->fch, s));
+    }
+    if (p->refined_waits && P > 0) {
+        WorkTable& t = p->fused;
+        uint32_t* d_inmap;
+        int* d_mpos;
+        DDH_HIP(sc.alloc(&d_inmap, (size_t)p->n_slots));
+        DDH_HIP(sc.alloc(&d_mpos, ((size_t)D + 1) * P));
+        DDH_HIP(hipMemsetAsync(d_inmap, 0, sizeof(uint32_t) * (size_t)p->n_slots, s));
+        std::vector<int> mposall(((size_t)D + 1) * P);
+        for (int q = 0; q < P; q++) {
+            for (int S = 0; S < D; S++)
+                mposall[(size_t)q * (D + 1) + S] = mpos[q][S];
+            mposall[(size_t)q * (D + 1) + D] = total[q];
+        }
+        DDH_HIP(upload(d_mpos, mposall, s));
+        int64_t pb = 0;
+        for (int q = 0; q < P; q++) {
+            if (total[q] > 0)
+                hipLaunchKernelGGL(inmap_kernel, dim3(blocks(total[q])), dim3(256), 0, s,
+                                   p->d_maps + pb, total[q], d_mpos + (size_t)q * (D + 1), D,
+                                   d_base, d_inmap, 1u << q);
+            pb += total[q];
+        }
+        const int nx = (int)t.xch.size(), nf = (int)t.fch.size();
+        if (nx + nf > 0)
+            hipLaunchKernelGGL(chunk_masks_kernel, dim3(nx + nf), dim3(256), 0, s, t.d_xch, nx,
+                               t.d_fch, nf, p->d_maps, d_rid, d_inmap, P);
+        DDH_HIP(hipGetLastError());
+        DDH_HIP(hipMemcpyAsync(t.xch.data(), t.d_xch, sizeof(DChunk) * nx, hipMemcpyDeviceToHost,
+                               s));
+        DDH_HIP(hipMemcpyAsync(t.fch.data(), t.d_fch, sizeof(DChunk) * nf, hipMemcpyDeviceToHost,
+                               s));
+        DDH_HIP(hipStreamSynchronize(s));
+    }
+    set_release_flags(p, p->fused);
+    DDH_HIP(upload(p->fused.d_xch, p->fused.xch, s));
+    DDH_HIP(upload(p->fused.d_fch, p->fused.fch, s));
 
     std::vector<uint32_t> xneed(DP, 0u), fneed(DP, 0u);
     for (int S = 0; S < D; S++)
@@ -935,12 +1019,6 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
             xneed[(size_t)p->recv[it] * P + q] = (uint32_t)p->fused.nchunks[it];
             fneed[it] = (uint32_t)p->fused.nchunks[it];
         }
-    for (WorkTable* t : {&p->fused, &p->pulse}) {
-        DDH_HIP(owned_alloc(p, &t->d_xch, t->xch.size()));
-        DDH_HIP(owned_alloc(p, &t->d_fch, t->fch.size()));
-        DDH_HIP(upload(t->d_xch, t->xch, s));
-        DDH_HIP(upload(t->d_fch, t->fch, s));
-    }
     const size_t words = (size_t)kCtrlWords + 4 * DP + 2 * (size_t)DDH_MAX_PULSES;
     DDH_HIP(owned_alloc(p, &p->d_ctrl, words));
     DDH_HIP(hipMemsetAsync(p->d_ctrl, 0, sizeof(uint32_t) * words, s));
