@@ -305,6 +305,8 @@ def run_gpu(args, w):
                           f"step ({launches_per_step} launches; achieved and traffic are per step)",
                       algorithmic_bytes_per_step=step_bytes,
                       avg_launch_us=round(avg_launch * 1e6, 3),
+                      traffic_GBps=(round(traffic / avg_step_gpu / 1e9, 2) if traffic else None),
+                      median_step_us=round(durs[len(durs) // 2] * 1e6, 3),
                       p10_step_us=round(durs[len(durs) // 10] * 1e6, 3),
                       p90_step_us=round(durs[(9 * len(durs)) // 10] * 1e6, 3)),
     )
