@@ -578,6 +578,7 @@ def main():
         print(f"bench.py runs on one GPU only: every domain is a virtual rank inside one "
               f"GPU's HBM (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    steps_given = args.steps
     if args.steps is None:
         args.steps = 1000 if w.n_atoms <= 100_000 else 200
 
@@ -593,7 +594,7 @@ def main():
                 continue
             wk = W.WORKLOADS[k]
             sub = argparse.Namespace(**vars(args))
-            sub.steps = 1000 if wk.n_atoms <= 100_000 else 200
+            sub.steps = steps_given or (1000 if wk.n_atoms <= 100_000 else 200)
             g2 = run_gpu(sub, wk)
             also[wk.name] = {
                 "variant": g2["variant"], "halo_atoms_per_pass": g2["n_halo"],
