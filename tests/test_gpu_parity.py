@@ -187,6 +187,44 @@ def test_captured_in_a_caller_graph(k, mode, split, workload_plan):
     g.close()
 
 
+def random_configs(n, seed):
+    """Seeded random decompositions the schedule accepts: 1-6 domains per
+    dimension, boxes of 2-9 nm per edge, cutoffs up to the largest the
+    widths allow (so several pulses per dimension occur), 200-6000 uniform
+    atoms."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        grid = tuple(int(g) for g in rng.integers(1, 7, size=3))
+        box = tuple(float(np.float32(b)) for b in rng.uniform(2.0, 9.0, size=3))
+        wmin = min(box[d] / grid[d] for d in range(3) if grid[d] > 1) if max(grid) > 1 else 1.0
+        rc = float(np.float32(rng.uniform(0.2, 2.5) * wmin))
+        try:
+            P = len(oracle.schedule(grid, box, rc))
+        except oracle.OracleError:
+            continue
+        if P > ddh.DDH_MAX_PULSES:
+            continue
+        out.append((grid, box, rc, int(rng.integers(200, 6000))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", random_configs(12, 2024))
+def test_random_decompositions(cfg):
+    """Random grids, boxes, cutoffs (one to several pulses per dimension) and
+    atom counts: layout, maps, ids, coordinates and forces bit-identical to
+    the oracle in every mode, over two steps."""
+    grid, box, rc, n = cfg
+    x = W.uniform_positions(n, box, seed=n)
+    ref = oracle.OraclePlan(x, grid, box, rc)
+    for mode in MODES.values():
+        g = GpuPlan(x, grid, box, rc, mode=mode)
+        check_layout(g, ref)
+        check_steps(g, ref, n, steps=2)
+        check_steps(g, ref, n + 1, steps=1, fused_step=True)
+        g.close()
+
+
 def test_completion_flags_count_passes(workload_plan):
     """Every mode publishes every pulse's completion flag with the number of
     passes completed so far; words past the plan's pulses stay zero."""

@@ -113,3 +113,41 @@ def test_workload5_schedule_and_counts():
     assert counts.max() <= 8
     # density x slab volume: about 8.46M halo atoms per pass
     assert abs(plan.halo_atoms - 8_463_804) < 0.01 * 8_463_804
+
+
+def _random_configs(n, seed):
+    """Seeded random decompositions the schedule accepts (1-6 domains per
+    dimension, 2-9 nm edges, cutoffs up to the largest the widths allow)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        grid = tuple(int(g) for g in rng.integers(1, 7, size=3))
+        box = tuple(float(np.float32(b)) for b in rng.uniform(2.0, 9.0, size=3))
+        wmin = min(box[d] / grid[d] for d in range(3) if grid[d] > 1) if max(grid) > 1 else 1.0
+        rc = float(np.float32(rng.uniform(0.2, 2.5) * wmin))
+        try:
+            oracle.schedule(grid, box, rc)
+        except oracle.OracleError:
+            continue
+        out.append((grid, box, rc, int(rng.integers(200, 3000))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(10, 77))
+def test_random_decompositions_vs_bruteforce(cfg):
+    """Random boxes and cutoffs (several pulses per dimension included): the
+    received sets against brute force (tie band as above), and forces
+    against the order-free integer expectation."""
+    grid, box, rc, n = cfg
+    x = W.uniform_positions(n, box, seed=n + 1)
+    plan = oracle.OraclePlan(x, grid, box, rc)
+    band = 4.0 * float(np.spacing(np.float32(max(box))))
+    n_band = bf.check_halo_against(plan, x, grid, box, rc, plan.bounds, band=band)
+    assert n_band <= 1e-3 * plan.halo_atoms + 5
+    home_rows = np.concatenate([np.arange(plan.base[D], plan.base[D] + plan.nhome[D])
+                                for D in range(plan.n_domains)])
+    fi = W.integer_forces(plan.n_slots, seed=n)
+    f = fi.copy()
+    plan.exchange_forces(f)
+    expect = bf.integer_force_expectation(plan, fi)
+    assert np.array_equal(f[home_rows].astype(np.float64), expect[home_rows])
