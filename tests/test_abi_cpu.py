@@ -183,3 +183,27 @@ def test_binding_constants_match_the_header():
     assert len(mirrored) >= 15, mirrored
     for k in mirrored:
         assert getattr(ddh, k) == int(defs[k]), k
+
+
+def test_header_is_c99_and_links(tmp_path):
+    """A C99 program that includes the header and takes the address of every
+    declared call compiles with gcc and links against the library."""
+    import shutil
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    hdr = open(HEADER).read()
+    names = sorted(set(re.findall(r"\b(ddh_[a-z_]+)\s*\(", hdr)))
+    src = tmp_path / "uses_ddh.c"
+    body = "\n".join(f"    (void)&{n};" for n in names)
+    src.write_text('#include "ddh.h"\n#include <stdio.h>\n'
+                   "int main(void)\n{\n" + body + "\n"
+                   "    ddh_params prm = {{2, 2, 2}, {8.0f, 8.0f, 8.0f}, 1.0f, 0.5f, 0};\n"
+                   "    (void)prm;\n    return 0;\n}\n")
+    exe = tmp_path / "uses_ddh"
+    libdir = os.path.dirname(ddh.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic",
+                        "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                        "-L", libdir, "-lddh", "-Wl,--unresolved-symbols=ignore-in-shared-libs"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert len(names) >= 19
