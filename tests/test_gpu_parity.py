@@ -225,6 +225,70 @@ def test_random_decompositions(cfg):
         g.close()
 
 
+def test_two_plans_on_two_streams(workload_plan):
+    """Two plans (different decompositions) exchanging at the same time on
+    two streams, fused and per-pulse: each keeps its own tickets, counters
+    and flags, and both match the oracle."""
+    cases = [workload_plan(2), workload_plan(4)]
+    for modes in ((ddh.DDH_MODE_FUSED, ddh.DDH_MODE_FUSED), (ddh.DDH_MODE_PULSE, ddh.DDH_MODE_FUSED)):
+        gs, xs, fs, f0s = [], [], [], []
+        for (w, x, ref), mode in zip(cases, modes):
+            g = GpuPlan(x, **w.params(), mode=mode)
+            gs.append(g)
+            xs.append(g.new_coords())
+            f0 = np.random.default_rng(g.n_slots).normal(0, 10, size=(g.n_slots, 3)).astype(np.float32)
+            f0s.append(f0)
+            fs.append(torch.from_numpy(f0).cuda())
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        torch.cuda.synchronize()
+        for _ in range(3):
+            for g, xl, fl, st in zip(gs, xs, fs, streams):
+                with torch.cuda.stream(st):
+                    g.plan.exchange_coords(xl)
+        for g, xl, fl, st in zip(gs, xs, fs, streams):
+            with torch.cuda.stream(st):
+                g.plan.exchange_forces(fl)
+        torch.cuda.synchronize()
+        for g, xl, fl, f0, (w, x, ref) in zip(gs, xs, fs, f0s, cases):
+            assert g.plan.check() == ddh.DDH_OK
+            assert np.array_equal(bits(xl.cpu().numpy()[:g.n_slots]), bits(ref.x_local))
+            fr = f0.copy()
+            ref.exchange_forces(fr)
+            assert np.array_equal(bits(fl.cpu().numpy()[:g.n_slots]), bits(fr))
+            g.close()
+
+
+def test_plans_release_their_device_memory(workload_plan):
+    """Build, exchange and destroy a plan many times (and rebuild one plan
+    repeatedly): the free device memory returns to where it was."""
+    w, x, ref = workload_plan(3)
+    xg = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    torch.cuda.synchronize()
+
+    def cycle():
+        plan = ddh.Plan(**w.params())
+        lay = plan.build_maps(xg)
+        plan.build_maps(xg)
+        xl = torch.zeros((lay["n_slots"], 3), dtype=torch.float32, device="cuda")
+        plan.gather_home(xg, xl)
+        for mode in (ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, ddh.DDH_MODE_STAGED):
+            plan.set_mode(mode)
+            plan.exchange_coords(xl)
+        assert plan.check() == ddh.DDH_OK
+        plan.close()
+        del xl
+        torch.cuda.synchronize()
+
+    cycle()
+    torch.cuda.empty_cache()
+    free0 = torch.cuda.mem_get_info()[0]
+    for _ in range(8):
+        cycle()
+    torch.cuda.empty_cache()
+    free1 = torch.cuda.mem_get_info()[0]
+    assert free0 - free1 < 16 << 20, (free0, free1)
+
+
 def test_completion_flags_count_passes(workload_plan):
     """Every mode publishes every pulse's completion flag with the number of
     passes completed so far; words past the plan's pulses stay zero."""
