@@ -153,6 +153,7 @@ void ddh_plan_destroy(ddh_plan* p)
     if (!p)
         return;
     free_built(p);
+    free_scratch(p);
     if (p->capture_stream)
         (void)hipStreamDestroy(p->capture_stream);
     delete p;

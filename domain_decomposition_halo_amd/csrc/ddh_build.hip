@@ -454,23 +454,40 @@ __global__ __launch_bounds__(256) void chunk_masks_kernel(DChunk* __restrict__ x
 
 // ---------------------------------------------------------------- host side
 
-// Device allocations that live only during one build.
+// Device buffers used only during a build. They stay with the plan between
+// builds (maps are rebuilt every neighbour-search step): the k-th request of
+// a build reuses the k-th buffer of the previous one when it is large
+// enough, and grows it otherwise. A build waits for its stream before it
+// returns, so no work of an earlier build still uses them; after a failed
+// build the next one first waits for the device.
 struct Scratch {
-    std::vector<void*> ptrs;
-    ~Scratch()
-    {
-        for (void* p : ptrs)
-            (void)hipFree(p);
-    }
+    Plan* plan;
+    size_t next = 0;
+    explicit Scratch(Plan* p) : plan(p) {}
     template <class T>
     hipError_t alloc(T** out, size_t n)
     {
-        void* p = nullptr;
-        hipError_t e = hipMalloc(&p, std::max<size_t>(n, 1) * sizeof(T));
-        if (e == hipSuccess)
-            ptrs.push_back(p);
-        *out = (T*)p;
-        return e;
+        const size_t bytes = (std::max<size_t>(n, 1) * sizeof(T) + 255) & ~size_t(255);
+        auto& cache = plan->scratch;
+        if (next < cache.size() && cache[next].second >= bytes) {
+            *out = (T*)cache[next++].first;
+            return hipSuccess;
+        }
+        void* q = nullptr;
+        hipError_t e = hipMalloc(&q, bytes);
+        if (e != hipSuccess) {
+            *out = nullptr;
+            return e;
+        }
+        if (next < cache.size()) {
+            (void)hipFree(cache[next].first);
+            cache[next] = {q, bytes};
+        } else {
+            cache.emplace_back(q, bytes);
+        }
+        next++;
+        *out = (T*)q;
+        return hipSuccess;
     }
 };
 
@@ -510,6 +527,13 @@ int scan_exclusive(Scratch& sc, const uint32_t* in, int64_t n, uint32_t* out, hi
 int blocks(int64_t n) { return (int)((n + 255) / 256); }
 
 }  // namespace
+
+void free_scratch(Plan* p)
+{
+    for (auto& kv : p->scratch)
+        (void)hipFree(kv.first);
+    p->scratch.clear();
+}
 
 void free_built(Plan* p)
 {
@@ -671,7 +695,10 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     const int D = g.ndom, P = g.P;
     if (n_atoms < 0 || (n_atoms > 0 && !xg))
         return fail(DDH_EINVAL, "ddh_build_maps: bad positions pointer or count");
-    Scratch sc;
+    if (p->build_failed)
+        DDH_HIP(hipDeviceSynchronize());  // kernels of the failed build may still run
+    p->build_failed = true;
+    Scratch sc(p);
 
     // ---- geometry tables
     std::vector<float> bcat;
@@ -1031,6 +1058,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     DDH_HIP(upload(p->d_fneed, fneed, s));
     DDH_HIP(hipStreamSynchronize(s));
     p->built = true;
+    p->build_failed = false;
     return DDH_OK;
 }
 

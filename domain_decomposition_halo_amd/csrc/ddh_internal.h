@@ -8,6 +8,7 @@
 #include <map>
 #include <string>
 #include <tuple>
+#include <utility>
 #include <vector>
 
 #include "../../include/ddh.h"
@@ -176,6 +177,8 @@ struct Plan {
                                    // [DDH_MAX_PULSES + p] forces (epoch values)
     float* d_stage = nullptr;      // staging buffer of DDH_MODE_STAGED (first use)
     std::vector<void*> owned;      // every hipMalloc of the built state
+    std::vector<std::pair<void*, size_t>> scratch;  // build scratch, kept between builds
+    bool build_failed = false;     // the last build returned an error midway
 
     // graph replay cache: (op, x, f, mode) -> executable graph
     hipStream_t capture_stream = nullptr;
@@ -195,6 +198,7 @@ int hip_fail(hipError_t e, const char* what);
 // map builder (ddh_build.hip)
 int build_maps(Plan* plan, const float* xg, int32_t n_atoms, hipStream_t stream);
 void free_built(Plan* plan);
+void free_scratch(Plan* plan);
 
 // exchange launches (ddh_exchange.hip)
 enum Op : int { kOpCoords = 1, kOpForces = 2, kOpStep = 3 };

@@ -225,6 +225,42 @@ def test_random_decompositions(cfg):
         g.close()
 
 
+def test_rebuild_after_atoms_move():
+    """One plan rebuilt for moving atoms (as at every neighbour-search step,
+    sizes changing between builds): every build and exchange bit-identical
+    to a fresh oracle plan of the same positions, in both main modes."""
+    w = W.WORKLOADS[2]
+    p = w.params()
+    L = np.float32(p["box"][0])
+    x = W.positions(w)
+    rng = np.random.default_rng(41)
+    for mode in (ddh.DDH_MODE_PULSE, ddh.DDH_MODE_FUSED):
+        plan = ddh.Plan(**p)
+        plan.set_mode(mode)
+        xs = x.copy()
+        for it in range(4):
+            if it:
+                step = rng.normal(0.0, 0.05 * it, size=xs.shape).astype(np.float32)
+                xs = np.mod(xs + step, L).astype(np.float32)
+                xs[xs >= L] = 0.0
+            ref = oracle.OraclePlan(xs, **p)
+            xg = torch.from_numpy(np.ascontiguousarray(xs)).cuda()
+            lay = plan.build_maps(xg)
+            assert (lay["n_slots"], lay["n_halo"]) == (ref.n_slots, ref.halo_atoms)
+            xl = torch.zeros((lay["n_slots"], 3), dtype=torch.float32, device="cuda")
+            plan.gather_home(xg, xl)
+            plan.exchange_coords(xl)
+            f0 = rng.normal(0, 10, size=(ref.n_slots, 3)).astype(np.float32)
+            fl = torch.from_numpy(f0).cuda()
+            plan.exchange_forces(fl)
+            assert plan.check() == ddh.DDH_OK
+            assert np.array_equal(bits(xl.cpu().numpy()), bits(ref.x_local)), it
+            fr = f0.copy()
+            ref.exchange_forces(fr)
+            assert np.array_equal(bits(fl.cpu().numpy()), bits(fr)), it
+        plan.close()
+
+
 def test_two_plans_on_two_streams(workload_plan):
     """Two plans (different decompositions) exchanging at the same time on
     two streams, fused and per-pulse: each keeps its own tickets, counters
