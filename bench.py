@@ -114,6 +114,8 @@ def run_gpu(args, w):
         plan.tune(ddh.DDH_TUNE_BLOCK, args.block)
     if args.static_first:
         plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 1)
+    if args.no_flags:
+        plan.tune(ddh.DDH_TUNE_FLAGS, 0)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -244,6 +246,39 @@ def run_gpu(args, w):
             del graph
         assert plan.check() == ddh.DDH_OK
 
+    def time_steps(fn, reps):
+        """GPU us per call of fn, from graphs of G calls replayed reps times."""
+        G = max(1, min(args.graph_steps, args.steps))
+        fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(G):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del graph
+        return e0.elapsed_time(e1) * 1e3 / (reps * G)
+
+    # the same step with the completion flags off (callers that rely on
+    # stream order alone): one launch fewer per call in per-pulse mode
+    without_flags = None
+    if not args.cold and not args.eager and not args.only_step and not args.no_flags:
+        plan.tune(ddh.DDH_TUNE_FLAGS, 0)
+        us = time_steps(calls[0][1] if len(calls) == 1 else
+                        (lambda: [fn() for _, fn, _ in calls]), max(1, min(args.steps // 50, 10)))
+        plan.tune(ddh.DDH_TUNE_FLAGS, 1)
+        without_flags = {"us_per_step": round(us, 3),
+                         "frac": round((BYTES_X + BYTES_F) * n_halo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        assert plan.check() == ddh.DDH_OK
+
     # the single persistent launch (both passes, all pulses, one kernel), the
     # same way, when it is not already the variant timed above
     single = None
@@ -296,7 +331,7 @@ def run_gpu(args, w):
     step_s = wall / steps_done
     res = dict(
         n_slots=n_slots, n_halo=n_halo, n_pulses=lay["n_pulses"], build_ms=build_ms,
-        variant=variant, passes=passes, single=single,
+        variant=variant, passes=passes, single=single, without_flags=without_flags,
         step_s=step_s, steps=steps_done, gpu_step_us=round(avg_step_gpu * 1e6, 3),
         roofline=dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel,
@@ -341,6 +376,8 @@ def run_overlap(args, w):
     plan.set_mode(mode)
     if args.static_first:
         plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 1)
+    if args.no_flags:
+        plan.tune(ddh.DDH_TUNE_FLAGS, 0)
     lay = plan.build_maps(xg)
     n_slots, n_halo = lay["n_slots"], lay["n_halo"]
     xl = torch.zeros((n_slots, 3), dtype=torch.float32, device=dev)
@@ -534,6 +571,8 @@ def main():
     ap.add_argument("--block", type=int, default=0, choices=[0, 256, 1024])
     ap.add_argument("--static-first", action="store_true",
                     help="fused launch: first tickets unclaimed (DDH_TUNE_STATIC_FIRST)")
+    ap.add_argument("--no-flags", action="store_true",
+                    help="calls skip the per-pulse completion flags (DDH_TUNE_FLAGS = 0)")
     ap.add_argument("--cold", action="store_true", help="evict caches before every step")
     ap.add_argument("--eager", action="store_true",
                     help="enqueue every step from the host (no graph replay)")
@@ -601,7 +640,8 @@ def main():
                 "gpu_us_per_step": g2["gpu_step_us"],
                 "halo_atoms_per_s": round(g2["n_halo"] / g2["step_s"], 1),
                 "roofline_frac": g2["roofline"]["frac"], "achieved_GBps": g2["roofline"]["achieved"],
-                "passes": g2["passes"], "single_launch": g2["single"]}
+                "passes": g2["passes"], "single_launch": g2["single"],
+                "without_flags": g2["without_flags"]}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(w, args.cpu_seconds)
@@ -628,12 +668,14 @@ def main():
             "halo_atoms_per_pass": gpu["n_halo"], "slots": gpu["n_slots"],
             "variant": gpu["variant"], "cache": "cold" if args.cold else "warm",
             "launch": "eager" if (args.eager or args.cold) else "graph replay",
+            "completion_flags": not args.no_flags,
             "step": "coordinate pass + force pass",
         },
         "step_hbm_frac": round((BYTES_X + BYTES_F) * gpu["n_halo"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "map_build_ms": round(gpu["build_ms"], 3),
         "passes": gpu["passes"],
         "single_launch": gpu["single"],
+        "without_flags": gpu["without_flags"],
         "roofline": gpu["roofline"],
         "cpu_baseline": cpu,
         "also": also or None,

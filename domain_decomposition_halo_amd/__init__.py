@@ -35,6 +35,7 @@ DDH_TUNE_CHUNK, DDH_TUNE_GRID, DDH_TUNE_SPIN_LIMIT, DDH_TUNE_FORCE_TIMEOUT, DDH_
 DDH_TUNE_TRACE = 6
 DDH_TUNE_BLOCK = 7
 DDH_TUNE_STATIC_FIRST = 8
+DDH_TUNE_FLAGS = 9
 TRACE_RECORDS = 64
 TRACE_EVENTS = {1: "start", 2: "claim", 3: "head", 4: "waited", 5: "chunk", 6: "publish", 7: "exit"}
 

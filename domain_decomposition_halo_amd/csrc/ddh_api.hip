@@ -245,9 +245,18 @@ int ddh_copy_maps(const ddh_plan* p, int32_t* maps_dev, int64_t capacity, void* 
     return DDH_OK;
 }
 
+static int check_flags_on(const Plan* p, const char* what)
+{
+    if (!p->flags)
+        return fail(DDH_ESTATE, std::string(what) + ": completion flags are off (DDH_TUNE_FLAGS)");
+    return DDH_OK;
+}
+
 int ddh_flags(const ddh_plan* p, uint32_t** flags_dev)
 {
     int rc = check_built(p);
+    if (!rc)
+        rc = check_flags_on(p, "ddh_flags");
     if (rc)
         return rc;
     if (!flags_dev)
@@ -259,6 +268,8 @@ int ddh_flags(const ddh_plan* p, uint32_t** flags_dev)
 int ddh_copy_flags(const ddh_plan* p, uint32_t* flags_dev, void* stream)
 {
     int rc = check_built(p);
+    if (!rc)
+        rc = check_flags_on(p, "ddh_copy_flags");
     if (rc)
         return rc;
     if (!flags_dev)
@@ -271,6 +282,8 @@ int ddh_copy_flags(const ddh_plan* p, uint32_t* flags_dev, void* stream)
 int ddh_wait_flag(ddh_plan* p, int32_t pass_kind, int32_t pulse, uint32_t epoch, void* stream)
 {
     int rc = check_built(p);
+    if (!rc)
+        rc = check_flags_on(p, "ddh_wait_flag");
     if (rc)
         return rc;
     if (pass_kind != DDH_PASS_COORDS && pass_kind != DDH_PASS_FORCES)
@@ -418,6 +431,11 @@ int ddh_tune(ddh_plan* p, int32_t key, int64_t value)
         return DDH_OK;
     case DDH_TUNE_TRACE:
         p->trace = (uint64_t*)(uintptr_t)value;
+        return DDH_OK;
+    case DDH_TUNE_FLAGS:
+        if (value != 0 && value != 1)
+            return fail(DDH_EINVAL, "ddh_tune: flags must be 0 or 1");
+        p->flags = (int)value;
         return DDH_OK;
     case DDH_TUNE_STATIC_FIRST:
         if (value != 0 && value != 1)

@@ -375,33 +375,40 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
     // for the next launch, and publishes the passes this launch completed:
     // the fused pass counters and, after a release, every pulse's completion
     // flag ("Dependency-aware packing": the last arrival stores the flag).
-    if (held) {
+    // (Without completion flags, a.flags is null: nothing to release here.)
+    const bool publish = a.flags != nullptr;
+    if (held && publish) {
         wait_vm_idle();
         __syncthreads();
     }
     if (threadIdx.x == 0) {
         trace_rec(a, ntr, kTrExit, 0);
-        if (held)
+        if (held && publish)
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const uint32_t old = __hip_atomic_fetch_add(a.ctrl + kCtrlDone, 1u, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
         if (old == gridDim.x - 1u) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+            if (publish)
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
             st_relaxed(a.ctrl + kCtrlTicket, 0u);
             st_relaxed(a.ctrl + kCtrlDone, 0u);
             if (a.nx > 0) {
-                const uint32_t e = ld_relaxed(a.ctrl + kCtrlEpochX) + 1u;
                 st_relaxed(a.ctrl + kCtrlPassX, px);
-                for (int q = 0; q < P; q++)
-                    st_relaxed(a.flags + q, e);
-                st_relaxed(a.ctrl + kCtrlEpochX, e);
+                if (publish) {
+                    const uint32_t e = ld_relaxed(a.ctrl + kCtrlEpochX) + 1u;
+                    for (int q = 0; q < P; q++)
+                        st_relaxed(a.flags + q, e);
+                    st_relaxed(a.ctrl + kCtrlEpochX, e);
+                }
             }
             if (a.nf > 0) {
-                const uint32_t e = ld_relaxed(a.ctrl + kCtrlEpochF) + 1u;
                 st_relaxed(a.ctrl + kCtrlPassF, pf);
-                for (int q = 0; q < P; q++)
-                    st_relaxed(a.flags + DDH_MAX_PULSES + q, e);
-                st_relaxed(a.ctrl + kCtrlEpochF, e);
+                if (publish) {
+                    const uint32_t e = ld_relaxed(a.ctrl + kCtrlEpochF) + 1u;
+                    for (int q = 0; q < P; q++)
+                        st_relaxed(a.flags + DDH_MAX_PULSES + q, e);
+                    st_relaxed(a.ctrl + kCtrlEpochF, e);
+                }
             }
         }
     }
@@ -594,8 +601,8 @@ int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, 
     a.stage = stage;
     a.ctrl = p->d_ctrl;
     a.flags = p->d_pflag;
-    a.xdone = xdone;
-    a.fdone = fdone;
+    a.xdone = p->flags ? xdone : 0u;
+    a.fdone = p->flags ? fdone : 0u;
     xdone = fdone = 0u;
     // 1024-wide blocks with few entries per lane by default: on the 12M-atom
     // maps they move about 8% more than 256-wide blocks with 8 per lane;
@@ -645,7 +652,7 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s, int mode)
         a.force_timeout = p->force_timeout;
         a.spin_limit = p->spin_limit;
         a.trace = p->trace;
-        a.flags = p->d_pflag;
+        a.flags = p->flags ? p->d_pflag : nullptr;
         return launch_fused(p, a, s);
     }
     // one launch per pulse: coordinates in increasing, forces in decreasing
@@ -666,7 +673,7 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s, int mode)
         if (fs)
             fdone |= 1u << (P - 1 - q);
     }
-    if (rc)
+    if (rc || !p->flags)
         return rc;
     hipLaunchKernelGGL(signal_kernel, dim3(1), dim3(64), 0, s, p->d_ctrl, p->d_pflag, xdone, fdone,
                        op);
@@ -725,6 +732,8 @@ int enqueue_staged(Plan* p, int op, float* x, float* f, hipStream_t s)
                 return rc;
             DDH_HIP(hipStreamSynchronize(s));
         }
+    if (!p->flags)
+        return DDH_OK;
     const uint32_t all = (P >= 32 ? 0u : (1u << P)) - 1u;
     hipLaunchKernelGGL(signal_kernel, dim3(1), dim3(64), 0, s, p->d_ctrl, p->d_pflag,
                        (op & kOpCoords) ? all : 0u, (op & kOpForces) ? all : 0u, op);

@@ -150,6 +150,7 @@ struct Plan {
     int grid_req = 0;
     int block_req = 0;          // fused work-group width: 0 automatic, 256 or 1024
     int static_first = 0;       // fused: first tickets unclaimed (exclusive GPU)
+    int flags = 1;              // publish the per-pulse completion flags
     uint32_t spin_limit = 1u << 20;
     int force_timeout = 0;
     int refined_waits = 1;

@@ -310,6 +310,15 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     one atomic per work-group, but only safe
                                     while the launch has the GPU to itself) */
 
+#define DDH_TUNE_FLAGS 9           /* 1 (default): every call publishes the
+                                    per-pulse completion flags (ddh_flags);
+                                    0: calls skip it (per-pulse mode: no final
+                                    one-wave launch; fused mode: no exit
+                                    publication) and ddh_flags, ddh_copy_flags
+                                    and ddh_wait_flag return DDH_ESTATE. The
+                                    flag words count the passes run with flags
+                                    on. */
+
 /* Set a tuning knob; takes effect at the next build (CHUNK) or call. */
 int ddh_tune(ddh_plan *plan, int32_t key, int64_t value);
 

@@ -325,6 +325,33 @@ def test_plans_release_their_device_memory(workload_plan):
     assert free0 - free1 < 16 << 20, (free0, free1)
 
 
+@pytest.mark.parametrize("k", [2, 4])
+def test_without_completion_flags(k, workload_plan):
+    """With DDH_TUNE_FLAGS = 0 every mode still matches the oracle, the flag
+    calls report DDH_ESTATE, and turning the flags back on resumes them."""
+    w, x, ref = workload_plan(k)
+    for mode in MODES.values():
+        g = GpuPlan(x, **w.params(), mode=mode)
+        g.plan.tune(ddh.DDH_TUNE_FLAGS, 0)
+        check_steps(g, ref, 50 + k, steps=2)
+        check_steps(g, ref, 60 + k, steps=1, fused_step=True)
+        with pytest.raises(ddh.DDHError) as e:
+            g.plan.flags_address()
+        assert e.value.code == ddh.DDH_ESTATE
+        with pytest.raises(ddh.DDHError) as e:
+            g.plan.wait_flag(ddh.DDH_PASS_COORDS, 0, 1)
+        assert e.value.code == ddh.DDH_ESTATE
+        g.plan.tune(ddh.DDH_TUNE_FLAGS, 1)
+        buf = torch.zeros(2 * ddh.DDH_MAX_PULSES, dtype=torch.int32, device="cuda")
+        g.plan.copy_flags(buf)
+        assert int(buf.cpu().numpy()[0]) == 0  # no pass counted while off
+        check_steps(g, ref, 70 + k, steps=1)
+        g.plan.copy_flags(buf)
+        v = buf.cpu().numpy().view(np.uint32)
+        assert (v[:g.P] == 1).all() and (v[ddh.DDH_MAX_PULSES:ddh.DDH_MAX_PULSES + g.P] == 1).all()
+        g.close()
+
+
 def test_completion_flags_count_passes(workload_plan):
     """Every mode publishes every pulse's completion flag with the number of
     passes completed so far; words past the plan's pulses stay zero."""
