@@ -3,11 +3,17 @@
 Bar (coordinates, maps, layout, ids: exact; forces: exact given the fixed
 reverse pulse order): every comparison is bit for bit on the raw float32
 words. Cases: the workloads at full size (maps, layout, coordinates, forces,
-fused step), every execution mode (fused persistent launch, one launch per
-pulse, both replayed from captured graphs) over several consecutive steps,
-ragged and extreme chunk/grid settings (down to a single work-group), exact
-dyadic boxes with multi-pulse relay, empty and one-sided inputs, error paths
-and the bounded-wait timeout path.
+both passes in one call); every execution mode (fused persistent launch, one
+launch per pulse, both replayed from the library's graphs, automatic, the
+host-orchestrated baseline) over several consecutive steps; calls captured
+in a caller's graph with the halo cleared before each replay; ragged and
+extreme chunk/grid/width settings (down to a single work-group, with and
+without static first tickets); exact dyadic boxes with multi-pulse relay up
+to the most pulses a grid allows; seeded random decompositions; rebuilds for
+moving atoms; two plans on two streams; completion flags (counts, consumer
+streams waiting on them, turned off); device memory released by destroyed
+plans; empty and one-sided inputs, error paths and the bounded-wait timeout
+paths.
 """
 
 import numpy as np
