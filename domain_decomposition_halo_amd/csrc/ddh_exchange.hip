@@ -427,6 +427,7 @@ struct PArgs {
     const DChunk* xchunks;
     const DChunk* fchunks;
     int32_t xbegin, nxb, fbegin;
+    int32_t nb;       // chunks of the launch (blocks loop over them)
     float* stage;     // null, or the staging buffer of the host-orchestrated mode
     uint32_t* ctrl;
     uint32_t* flags;
@@ -452,22 +453,23 @@ template <int E, int B>
 __global__ __launch_bounds__(B) void pulse_kernel(PArgs a)
 {
     publish_done(a);
-    const int b = (int)blockIdx.x;
-    if (b < a.nxb) {
-        const DChunk c = a.xchunks[a.xbegin + b];
-        int j0[E];
-        load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);
-        coords_range<E, B>(a.x, a.maps, c, c.hb, c.he, j0, a.stage);
-        if (c.te > c.tb) {
-            int jt[E];
-            load_map<E, B>(a.maps + c.map_off, c.tb, c.te, jt);
-            coords_range<E, B>(a.x, a.maps, c, c.tb, c.te, jt, a.stage);
+    for (int b = (int)blockIdx.x; b < a.nb; b += (int)gridDim.x) {
+        if (b < a.nxb) {
+            const DChunk c = a.xchunks[a.xbegin + b];
+            int j0[E];
+            load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);
+            coords_range<E, B>(a.x, a.maps, c, c.hb, c.he, j0, a.stage);
+            if (c.te > c.tb) {
+                int jt[E];
+                load_map<E, B>(a.maps + c.map_off, c.tb, c.te, jt);
+                coords_range<E, B>(a.x, a.maps, c, c.tb, c.te, jt, a.stage);
+            }
+        } else {
+            const DChunk c = a.fchunks[a.fbegin + b - a.nxb];
+            int j0[E];
+            load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);
+            forces_range<E, B>(a.f, a.maps, c, c.hb, c.he, j0, a.stage);
         }
-    } else {
-        const DChunk c = a.fchunks[a.fbegin + b - a.nxb];
-        int j0[E];
-        load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);
-        forces_range<E, B>(a.f, a.maps, c, c.hb, c.he, j0, a.stage);
     }
 }
 
@@ -609,7 +611,11 @@ int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, 
     // chunks below 1024 entries take 256-wide blocks (no idle lanes)
     const int lanes = p->block_req ? p->block_req : (t.chunk >= 1024 ? 1024 : 256);
     const int per = (t.chunk + lanes - 1) / lanes;
-    const dim3 grid(nb), block(lanes);
+    // at most the blocks the compute units hold at once; each loops over the
+    // launch's chunks (A/B on MI355X: 96k 9.46 -> 9.22 us, 12M 119.5 -> 118.7)
+    a.nb = nb;
+    const int resident = p->n_cu * (lanes == 1024 ? 2 : 8);
+    const dim3 grid(std::min(nb, resident)), block(lanes);
     if (lanes == 1024) {
         if (per > 2)
             hipLaunchKernelGGL((pulse_kernel<4, 1024>), grid, block, 0, s, a);
