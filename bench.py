@@ -116,6 +116,8 @@ def run_gpu(args, w):
         plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 1)
     if args.no_flags:
         plan.tune(ddh.DDH_TUNE_FLAGS, 0)
+    if args.wide_maps:
+        plan.tune(ddh.DDH_TUNE_NARROW_MAPS, 0)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -328,6 +330,13 @@ def run_gpu(args, w):
         b.copy_(a)
         torch.cuda.synchronize()
 
+    # the kernels read 16-bit map entries when every domain has at most
+    # 65536 slots: the bytes a step must move are then 2 B per entry and
+    # pass below the 28 + 40 B of the index-map accounting
+    max_total = max(plan.domain_info(d)[2] for d in range(lay["n_domains"]))
+    map_bytes = 2 if (max_total <= 65536 and not args.wide_maps) else 4
+    min_bytes = step_bytes - 2 * (4 - map_bytes) * n_halo
+
     step_s = wall / steps_done
     res = dict(
         n_slots=n_slots, n_halo=n_halo, n_pulses=lay["n_pulses"], build_ms=build_ms,
@@ -339,6 +348,9 @@ def run_gpu(args, w):
                       per="launch" if launches_per_step == 1 else
                           f"step ({launches_per_step} launches; achieved and traffic are per step)",
                       algorithmic_bytes_per_step=step_bytes,
+                      map_entry_bytes=map_bytes,
+                      min_bytes_per_step=min_bytes,
+                      frac_at_min_bytes=round(min_bytes / avg_step_gpu / 1e9 / HBM_PEAK_GBS, 4),
                       avg_launch_us=round(avg_launch * 1e6, 3),
                       traffic_GBps=(round(traffic / avg_step_gpu / 1e9, 2) if traffic else None),
                       median_step_us=round(durs[len(durs) // 2] * 1e6, 3),
@@ -378,6 +390,8 @@ def run_overlap(args, w):
         plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 1)
     if args.no_flags:
         plan.tune(ddh.DDH_TUNE_FLAGS, 0)
+    if args.wide_maps:
+        plan.tune(ddh.DDH_TUNE_NARROW_MAPS, 0)
     lay = plan.build_maps(xg)
     n_slots, n_halo = lay["n_slots"], lay["n_halo"]
     xl = torch.zeros((n_slots, 3), dtype=torch.float32, device=dev)
@@ -573,6 +587,8 @@ def main():
                     help="fused launch: first tickets unclaimed (DDH_TUNE_STATIC_FIRST)")
     ap.add_argument("--no-flags", action="store_true",
                     help="calls skip the per-pulse completion flags (DDH_TUNE_FLAGS = 0)")
+    ap.add_argument("--wide-maps", action="store_true",
+                    help="kernels read the 32-bit maps (DDH_TUNE_NARROW_MAPS = 0)")
     ap.add_argument("--cold", action="store_true", help="evict caches before every step")
     ap.add_argument("--eager", action="store_true",
                     help="enqueue every step from the host (no graph replay)")
@@ -640,6 +656,8 @@ def main():
                 "gpu_us_per_step": g2["gpu_step_us"],
                 "halo_atoms_per_s": round(g2["n_halo"] / g2["step_s"], 1),
                 "roofline_frac": g2["roofline"]["frac"], "achieved_GBps": g2["roofline"]["achieved"],
+                "map_entry_bytes": g2["roofline"]["map_entry_bytes"],
+                "frac_at_min_bytes": g2["roofline"]["frac_at_min_bytes"],
                 "passes": g2["passes"], "single_launch": g2["single"],
                 "without_flags": g2["without_flags"]}
     cpu = None

@@ -36,6 +36,7 @@ DDH_TUNE_TRACE = 6
 DDH_TUNE_BLOCK = 7
 DDH_TUNE_STATIC_FIRST = 8
 DDH_TUNE_FLAGS = 9
+DDH_TUNE_NARROW_MAPS = 10
 TRACE_RECORDS = 64
 TRACE_EVENTS = {1: "start", 2: "claim", 3: "head", 4: "waited", 5: "chunk", 6: "publish", 7: "exit"}
 

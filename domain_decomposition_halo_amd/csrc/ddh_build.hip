@@ -384,6 +384,16 @@ __global__ __launch_bounds__(256) void fill_region_kernel(const int* __restrict_
     rid[slot] = (uint8_t)q;
 }
 
+// out[i] = maps[i] as 16 bits; the caller has checked that every domain has
+// at most 65536 slots, so every sender-local index fits.
+__global__ __launch_bounds__(256) void narrow_maps_kernel(const int32_t* __restrict__ maps,
+                                                          int64_t n, uint16_t* __restrict__ out)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        out[i] = (uint16_t)maps[i];
+}
+
 // inmap[slot] |= bit for every entry of pulse q's maps (maps_q: the pulse's
 // maps of all senders, sender S's at mpos[S]..mpos[S+1]). Within one pulse
 // every slot appears at most once (a map holds distinct slots of its own
@@ -544,6 +554,7 @@ void free_built(Plan* p)
         (void)hipFree(q);
     p->owned.clear();
     p->d_maps = p->d_slot_gid = p->d_home_gid = p->d_home_slot = nullptr;
+    p->d_maps16 = nullptr;
     p->fused = WorkTable{};
     p->pulse = WorkTable{};
     p->d_ctrl = p->d_xcnt = p->d_fcnt = p->d_xneed = p->d_fneed = p->d_pflag = nullptr;
@@ -951,6 +962,17 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                                        hipMemcpyDeviceToDevice, s));
             pb += total[q];
         }
+    }
+    // a 16-bit copy when every sender-local slot index fits (halves the
+    // bytes of the map reads in every pass)
+    int32_t max_total = 0;
+    for (int Dm = 0; Dm < D; Dm++)
+        max_total = std::max(max_total, p->ntotal[Dm]);
+    if (nh > 0 && max_total <= 65536) {
+        DDH_HIP(owned_alloc(p, &p->d_maps16, (size_t)nh));
+        hipLaunchKernelGGL(narrow_maps_kernel, dim3(blocks(nh)), dim3(256), 0, s, p->d_maps, nh,
+                           p->d_maps16);
+        DDH_HIP(hipGetLastError());
     }
 
     // global id per slot, home slot per home atom; pulse of every received

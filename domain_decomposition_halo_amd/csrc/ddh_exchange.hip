@@ -13,9 +13,9 @@
 //
 //  - Per-pulse launches (DDH_MODE_PULSE; the guide's stream-ordered design of
 //    "Replacing host-side communication with NVSHMEM"): one launch per pulse,
-//    block b runs chunk b of the pulse; the stream orders the pulses, so no
-//    kernel waits, counts or fences. A step call runs coordinate pulse q and
-//    force pulse P-1-q in the same launch. A one-wave launch afterwards
+//    its blocks loop over the pulse's chunks; the stream orders the pulses,
+//    so no kernel waits, counts or fences. A step call runs coordinate pulse
+//    q and force pulse P-1-q in the same launch. A one-wave launch afterwards
 //    publishes per-pulse flags. The default whenever the calls are replayed
 //    from a graph: on MI355X a kernel boundary inside a graph costs less than
 //    a dependency carried across XCDs inside a kernel.
@@ -148,13 +148,15 @@ __device__ void wave_wait(const XArgs& a, const uint32_t* cnt, const uint32_t* n
 }
 
 // Map entries of one round: entry i0 + e * B + tid for e < E (B threads).
-template <int E, int B>
-__device__ __forceinline__ void load_map(const int32_t* map, int i0, int end, int (&j)[E])
+// I is the stored index type: int32, or uint16 when every domain has at most
+// 65536 slots (half the bytes for the same entries).
+template <int E, int B, typename I>
+__device__ __forceinline__ void load_map(const I* map, int i0, int end, int (&j)[E])
 {
 #pragma unroll
     for (int e = 0; e < E; e++) {
         const int i = i0 + e * B + (int)threadIdx.x;
-        j[e] = i < end ? map[i] : -1;
+        j[e] = i < end ? (int)map[i] : -1;
     }
 }
 
@@ -234,32 +236,32 @@ __device__ __forceinline__ void forces_round(const float* from, float* tgt, int 
 // entries (loaded by the caller, possibly before a wait).
 // With a staging buffer (the host-orchestrated baseline), entry i of a map
 // goes to / comes from stage[map_off + i] instead of the receiver's region.
-template <int E, int B>
-__device__ void coords_range(float* x, const int32_t* maps, const DChunk& c, int begin, int end,
+template <int E, int B, typename I>
+__device__ void coords_range(float* x, const I* maps, const DChunk& c, int begin, int end,
                              const int (&j0)[E], float* stage = nullptr)
 {
-    const int32_t* map = maps + c.map_off;
+    const I* map = maps + c.map_off;
     const float* src = x + 3ll * c.src_base;
     float* dst = stage ? stage + 3ll * c.map_off : x + 3ll * c.dst_base;
     coords_round<E, B>(src, dst, c, begin, end, j0);
     for (int i0 = begin + B * E; i0 < end; i0 += B * E) {
         int j[E];
-        load_map<E, B>(map, i0, end, j);
+        load_map<E, B, I>(map, i0, end, j);
         coords_round<E, B>(src, dst, c, i0, end, j);
     }
 }
 
-template <int E, int B>
-__device__ void forces_range(float* f, const int32_t* maps, const DChunk& c, int begin, int end,
+template <int E, int B, typename I>
+__device__ void forces_range(float* f, const I* maps, const DChunk& c, int begin, int end,
                              const int (&j0)[E], const float* stage = nullptr)
 {
-    const int32_t* map = maps + c.map_off;
+    const I* map = maps + c.map_off;
     float* tgt = f + 3ll * c.src_base;
     const float* from = stage ? stage + 3ll * c.map_off : f + 3ll * c.dst_base;
     forces_round<E, B>(from, tgt, begin, end, j0);
     for (int i0 = begin + B * E; i0 < end; i0 += B * E) {
         int j[E];
-        load_map<E, B>(map, i0, end, j);
+        load_map<E, B, I>(map, i0, end, j);
         forces_round<E, B>(from, tgt, i0, end, j);
     }
 }
@@ -278,10 +280,11 @@ __device__ __forceinline__ int claim_ticket(const XArgs& a)
 // back edge: a region that did (finish at the end of one iteration, claim at
 // the start of the next) lets the compiler park lane 0 outside the loop while
 // the other lanes pass the barrier and re-read a stale ticket forever.
-template <int E, int B>
+template <int E, int B, typename I>
 __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
 {
     __shared__ int s_ticket;
+    const I* maps = static_cast<const I*>(a.maps);
     const int P = a.P;
     const int nt = a.nx + a.nf;
     const uint32_t bump = a.force_timeout ? 0x40000000u : 0u;  // a value nobody reaches
@@ -309,9 +312,9 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
             // slice goes out first; the map entries of the dependent slice
             // are loaded before the wait, its records packed after it
             int jh[E], jt[E];
-            load_map<E, B>(a.maps + c.map_off, c.hb, c.he, jh);
-            load_map<E, B>(a.maps + c.map_off, c.tb, c.te, jt);
-            coords_range<E, B>(a.x, a.maps, c, c.hb, c.he, jh);
+            load_map<E, B, I>(maps + c.map_off, c.hb, c.he, jh);
+            load_map<E, B, I>(maps + c.map_off, c.tb, c.te, jt);
+            coords_range<E, B, I>(a.x, maps, c, c.hb, c.he, jh);
             if (c.wait_a) {
                 if (wave == 0) {
                     if (threadIdx.x == 0)
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
                 }
                 __syncthreads();
             }
-            coords_range<E, B>(a.x, a.maps, c, c.tb, c.te, jt);
+            coords_range<E, B, I>(a.x, maps, c, c.tb, c.te, jt);
             // every wave's records are in L2 before thread 0 releases them
             if (c.flags & kChunkRelease)
                 wait_vm_idle();
@@ -340,7 +343,7 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
         } else {
             const DChunk c = a.fchunks[t - a.nx];
             int j0[E];
-            load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);  // static: before any wait
+            load_map<E, B, I>(maps + c.map_off, c.hb, c.he, j0);  // static: before any wait
             // a step's force chunks do not wait for its coordinate chunks:
             // the passes touch different arrays
             if (c.wait_a || c.wait_b) {
@@ -351,7 +354,7 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
                 }
                 __syncthreads();
             }
-            forces_range<E, B>(a.f, a.maps, c, c.hb, c.he, j0);
+            forces_range<E, B, I>(a.f, maps, c, c.hb, c.he, j0);
             // every wave's sums are in L2 before thread 0 releases them
             if (c.flags & kChunkRelease)
                 wait_vm_idle();
@@ -415,15 +418,15 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
 }
 
 // One pulse of one pass, ordered against the other pulses by the stream
-// alone: block b runs coordinate chunk xbegin + b for b < nxb, else force
-// chunk fbegin + b - nxb. A step call pairs coordinate pulse q with force
+// alone: chunk b of the launch (blocks take b, b + grid, ...) is coordinate
+// chunk xbegin + b for b < nxb, else force chunk fbegin + b - nxb. A step call pairs coordinate pulse q with force
 // pulse P-1-q in one launch (the two passes touch different arrays, and each
 // pair's predecessors are complete at the launch boundary). No tickets,
 // counters, waits or fences: the kernel boundary publishes the writes.
 struct PArgs {
     float* x;
     float* f;
-    const int32_t* maps;
+    const void* maps;  // map entries in the kernel's index type
     const DChunk* xchunks;
     const DChunk* fchunks;
     int32_t xbegin, nxb, fbegin;
@@ -449,26 +452,27 @@ __device__ __forceinline__ void publish_done(const PArgs& a)
     }
 }
 
-template <int E, int B>
+template <int E, int B, typename I>
 __global__ __launch_bounds__(B) void pulse_kernel(PArgs a)
 {
+    const I* maps = static_cast<const I*>(a.maps);
     publish_done(a);
     for (int b = (int)blockIdx.x; b < a.nb; b += (int)gridDim.x) {
         if (b < a.nxb) {
             const DChunk c = a.xchunks[a.xbegin + b];
             int j0[E];
-            load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);
-            coords_range<E, B>(a.x, a.maps, c, c.hb, c.he, j0, a.stage);
+            load_map<E, B, I>(maps + c.map_off, c.hb, c.he, j0);
+            coords_range<E, B, I>(a.x, maps, c, c.hb, c.he, j0, a.stage);
             if (c.te > c.tb) {
                 int jt[E];
-                load_map<E, B>(a.maps + c.map_off, c.tb, c.te, jt);
-                coords_range<E, B>(a.x, a.maps, c, c.tb, c.te, jt, a.stage);
+                load_map<E, B, I>(maps + c.map_off, c.tb, c.te, jt);
+                coords_range<E, B, I>(a.x, maps, c, c.tb, c.te, jt, a.stage);
             }
         } else {
             const DChunk c = a.fchunks[a.fbegin + b - a.nxb];
             int j0[E];
-            load_map<E, B>(a.maps + c.map_off, c.hb, c.he, j0);
-            forces_range<E, B>(a.f, a.maps, c, c.hb, c.he, j0, a.stage);
+            load_map<E, B, I>(maps + c.map_off, c.hb, c.he, j0);
+            forces_range<E, B, I>(a.f, maps, c, c.hb, c.he, j0, a.stage);
         }
     }
 }
@@ -539,6 +543,51 @@ __global__ __launch_bounds__(kBlock) void gather_home_kernel(const float* __rest
     d[2] = s[2];
 }
 
+bool use_narrow_maps(const Plan* p) { return p->narrow_maps && p->d_maps16; }
+
+// The fused kernel instance for the work-group width and entries per lane.
+template <typename I>
+void launch_fused_t(const XArgs& a, int grid, bool wide, int per, hipStream_t s)
+{
+    if (wide) {
+        if (per > 2)
+            hipLaunchKernelGGL((exchange_kernel<4, 1024, I>), dim3(grid), dim3(1024), 0, s, a);
+        else if (per > 1)
+            hipLaunchKernelGGL((exchange_kernel<2, 1024, I>), dim3(grid), dim3(1024), 0, s, a);
+        else
+            hipLaunchKernelGGL((exchange_kernel<1, 1024, I>), dim3(grid), dim3(1024), 0, s, a);
+    } else {
+        if (per > 8)
+            hipLaunchKernelGGL((exchange_kernel<16, 256, I>), dim3(grid), dim3(256), 0, s, a);
+        else if (per > 4)
+            hipLaunchKernelGGL((exchange_kernel<8, 256, I>), dim3(grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((exchange_kernel<4, 256, I>), dim3(grid), dim3(256), 0, s, a);
+    }
+}
+
+// The per-pulse kernel instance for the block width and entries per lane.
+template <typename I>
+void launch_pulse_t(const PArgs& a, dim3 grid, int lanes, int per, hipStream_t s)
+{
+    const dim3 block(lanes);
+    if (lanes == 1024) {
+        if (per > 2)
+            hipLaunchKernelGGL((pulse_kernel<4, 1024, I>), grid, block, 0, s, a);
+        else if (per > 1)
+            hipLaunchKernelGGL((pulse_kernel<2, 1024, I>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((pulse_kernel<1, 1024, I>), grid, block, 0, s, a);
+    } else {
+        if (per > 4)
+            hipLaunchKernelGGL((pulse_kernel<8, 256, I>), grid, block, 0, s, a);
+        else if (per > 2)
+            hipLaunchKernelGGL((pulse_kernel<4, 256, I>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((pulse_kernel<2, 256, I>), grid, block, 0, s, a);
+    }
+}
+
 int launch_fused(const Plan* p, XArgs a, hipStream_t s)
 {
     const int nt = a.nx + a.nf;
@@ -559,30 +608,21 @@ int launch_fused(const Plan* p, XArgs a, hipStream_t s)
     // (few, latency-bound chunks), else 256; entries per lane and round from
     // the chunk size
     const bool wide = p->block_req ? p->block_req == 1024 : grid <= p->n_cu / 2;
-    const int lanes = wide ? 1024 : 256;
-    const int per = (p->fused.chunk + lanes - 1) / lanes;
-    if (wide) {
-        if (per > 2)
-            hipLaunchKernelGGL((exchange_kernel<4, 1024>), dim3(grid), dim3(1024), 0, s, a);
-        else if (per > 1)
-            hipLaunchKernelGGL((exchange_kernel<2, 1024>), dim3(grid), dim3(1024), 0, s, a);
-        else
-            hipLaunchKernelGGL((exchange_kernel<1, 1024>), dim3(grid), dim3(1024), 0, s, a);
+    const int per = (p->fused.chunk + (wide ? 1023 : 255)) / (wide ? 1024 : 256);
+    if (use_narrow_maps(p)) {
+        a.maps = p->d_maps16;
+        launch_fused_t<uint16_t>(a, grid, wide, per, s);
     } else {
-        if (per > 8)
-            hipLaunchKernelGGL((exchange_kernel<16, 256>), dim3(grid), dim3(256), 0, s, a);
-        else if (per > 4)
-            hipLaunchKernelGGL((exchange_kernel<8, 256>), dim3(grid), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((exchange_kernel<4, 256>), dim3(grid), dim3(256), 0, s, a);
+        a.maps = p->d_maps;
+        launch_fused_t<int32_t>(a, grid, wide, per, s);
     }
     DDH_HIP(hipGetLastError());
     return DDH_OK;
 }
 
 // Coordinate chunks [xb, xe) and force chunks [fb, fe) of table t in one
-// launch, one block per chunk; entries per lane and round from the table's
-// chunk size (larger chunks take several rounds).
+// launch; entries per lane and round from the table's chunk size (larger
+// chunks take several rounds).
 // xdone / fdone: pulses completed by earlier launches of the call whose flags
 // this launch publishes; cleared when the launch takes them over.
 int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, int xe, int fb,
@@ -594,7 +634,8 @@ int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, 
     PArgs a{};
     a.x = x;
     a.f = f;
-    a.maps = p->d_maps;
+    const bool narrow = use_narrow_maps(p);
+    a.maps = narrow ? (const void*)p->d_maps16 : (const void*)p->d_maps;
     a.xchunks = t.d_xch;
     a.fchunks = t.d_fch;
     a.xbegin = xb;
@@ -615,22 +656,11 @@ int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, 
     // launch's chunks (A/B on MI355X: 96k 9.46 -> 9.22 us, 12M 119.5 -> 118.7)
     a.nb = nb;
     const int resident = p->n_cu * (lanes == 1024 ? 2 : 8);
-    const dim3 grid(std::min(nb, resident)), block(lanes);
-    if (lanes == 1024) {
-        if (per > 2)
-            hipLaunchKernelGGL((pulse_kernel<4, 1024>), grid, block, 0, s, a);
-        else if (per > 1)
-            hipLaunchKernelGGL((pulse_kernel<2, 1024>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((pulse_kernel<1, 1024>), grid, block, 0, s, a);
-    } else {
-        if (per > 4)
-            hipLaunchKernelGGL((pulse_kernel<8, 256>), grid, block, 0, s, a);
-        else if (per > 2)
-            hipLaunchKernelGGL((pulse_kernel<4, 256>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((pulse_kernel<2, 256>), grid, block, 0, s, a);
-    }
+    const dim3 grid(std::min(nb, resident));
+    if (narrow)
+        launch_pulse_t<uint16_t>(a, grid, lanes, per, s);
+    else
+        launch_pulse_t<int32_t>(a, grid, lanes, per, s);
     DDH_HIP(hipGetLastError());
     return DDH_OK;
 }
@@ -643,7 +673,6 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s, int mode)
         XArgs a{};
         a.x = x;
         a.f = f;
-        a.maps = p->d_maps;
         const WorkTable& t = p->fused;
         a.xchunks = t.d_xch;
         a.fchunks = t.d_fch;

@@ -64,7 +64,8 @@ static_assert(sizeof(DChunk) == 64, "DChunk layout");
 struct XArgs {
     float* x;
     float* f;
-    const int32_t* maps;
+    const void* maps;        // map entries in the kernel's index type (int32
+                             // or uint16)
     const DChunk* xchunks;
     const DChunk* fchunks;
     int32_t nx, nf;
@@ -154,6 +155,7 @@ struct Plan {
     uint32_t spin_limit = 1u << 20;
     int force_timeout = 0;
     int refined_waits = 1;
+    int narrow_maps = 1;        // use the 16-bit copy of the maps when there is one
     uint64_t* trace = nullptr;  // caller-owned device buffer (DDH_TUNE_TRACE)
 
     // host copies of the layout
@@ -166,6 +168,8 @@ struct Plan {
 
     // device state
     int32_t* d_maps = nullptr;     // all maps, pulse-major
+    uint16_t* d_maps16 = nullptr;  // the same entries as 16 bits, when every
+                                   // domain has at most 65536 slots (else null)
     int32_t* d_slot_gid = nullptr; // global id per slot
     int32_t* d_home_gid = nullptr; // home atoms in slot order, all domains
     int32_t* d_home_slot = nullptr;

@@ -319,6 +319,12 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     flag words count the passes run with flags
                                     on. */
 
+#define DDH_TUNE_NARROW_MAPS 10    /* 1 (default): when every domain has at
+                                    most 65536 slots, the exchange kernels read
+                                    a 16-bit copy of the maps (2 bytes per
+                                    entry instead of 4; same entries, same
+                                    results); 0: they read the 32-bit maps */
+
 /* Set a tuning knob; takes effect at the next build (CHUNK) or call. */
 int ddh_tune(ddh_plan *plan, int32_t key, int64_t value);
 

@@ -45,9 +45,10 @@ class GpuPlan:
     """A device plan built from host positions, with host views of its output."""
 
     def __init__(self, x, grid, box, rc, cell=0.5, mode=0, chunk=0, wg=0, refined=1, block=0,
-                 static_first=0):
+                 static_first=0, narrow=1):
         self.plan = ddh.Plan(grid, box, rc, cell)
         self.plan.tune(ddh.DDH_TUNE_STATIC_FIRST, static_first)
+        self.plan.tune(ddh.DDH_TUNE_NARROW_MAPS, narrow)
         self.plan.tune(ddh.DDH_TUNE_CHUNK, chunk)
         self.plan.tune(ddh.DDH_TUNE_GRID, wg)
         self.plan.tune(ddh.DDH_TUNE_BLOCK, block)
@@ -481,6 +482,36 @@ def test_chunk_and_grid_variants(k, chunk, wg, refined, block, workload_plan):
                     static_first=sf)
         check_steps(g, ref, 20 + k, steps=2)
         check_steps(g, ref, 30 + k, steps=1, fused_step=True)
+        g.close()
+
+
+@pytest.mark.parametrize("mode", ["fused", "pulse", "pulse_graph", "staged"])
+@pytest.mark.parametrize("k", [2, 4])
+def test_32bit_maps(k, mode, workload_plan):
+    """DDH_TUNE_NARROW_MAPS = 0: the kernels read the 32-bit maps, the path
+    of every plan with a domain above 65536 slots."""
+    w, x, ref = workload_plan(k)
+    g = GpuPlan(x, **w.params(), mode=MODES[mode], narrow=0)
+    check_steps(g, ref, 40 + k, steps=2)
+    check_steps(g, ref, 50 + k, steps=1, fused_step=True)
+    g.close()
+
+
+@pytest.mark.parametrize("n,wide", [(100_000, False), (140_000, True)])
+def test_map_width_threshold(n, wide):
+    """Two domains of about 50k and 70k home atoms: the first stays within
+    65536 slots per domain, so the 16-bit maps hold indices above 32767; the
+    second exceeds it, so every kernel reads the 32-bit maps."""
+    grid, box, rc = (2, 1, 1), (8.0, 4.0, 4.0), 1.0
+    x = W.uniform_positions(n, box, seed=n)
+    ref = oracle.OraclePlan(x, grid, box, rc)
+    assert (int(ref.ntotal.max()) > 65536) == wide
+    assert int(ref.ntotal.max()) > 32768
+    for mode in (ddh.DDH_MODE_FUSED, ddh.DDH_MODE_PULSE):
+        g = GpuPlan(x, grid, box, rc, mode=mode)
+        check_layout(g, ref)
+        check_steps(g, ref, n, steps=2)
+        check_steps(g, ref, n + 1, steps=1, fused_step=True)
         g.close()
 
 
