@@ -696,7 +696,10 @@ static int pulse_chunk(const Plan* p)
     for (int ch = 2048; ch > 512; ch /= 2)
         if (smallest / ch >= 2ll * p->n_cu)
             return ch;
-    return 512;
+    // small pulses (at 512 entries, chunks for fewer than half the compute
+    // units): 256-entry chunks, one round per block (96k atoms:
+    // 9.04 -> 8.63 us per step; from 1M atoms on, 512 is faster)
+    return smallest / 512 >= p->n_cu / 2 ? 512 : 256;
 }
 
 int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
