@@ -118,6 +118,8 @@ def run_gpu(args, w):
         plan.tune(ddh.DDH_TUNE_FLAGS, 0)
     if args.wide_maps:
         plan.tune(ddh.DDH_TUNE_NARROW_MAPS, 0)
+    if args.wave_chunks:
+        plan.tune(ddh.DDH_TUNE_WAVE_CHUNKS, 1)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -304,7 +306,8 @@ def run_gpu(args, w):
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (n_rep * G)
-        single = {"kernel": "exchange_kernel", "us_per_step": round(us, 3),
+        single = {"kernel": "wave_kernel" if args.wave_chunks else "exchange_kernel",
+                  "us_per_step": round(us, 3),
                   "frac": round((BYTES_X + BYTES_F) * n_halo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del graph
         assert plan.check() == ddh.DDH_OK
@@ -314,9 +317,13 @@ def run_gpu(args, w):
     step_bytes = sum(nb for _, _, nb in calls)
     avg_launch = avg_step_gpu / launches_per_step
     achieved = step_bytes / avg_step_gpu / 1e9
-    traffic = read_traffic(variant, w.name)
-    kernel = {"step": "exchange_kernel (fused step, one launch)",
-              "split": "exchange_kernel (coordinate launch + force launch)",
+    # the stored counters were taken with the default settings
+    tuned = (args.chunk or args.grid or args.block or args.static_first or args.no_flags
+             or args.wide_maps or args.wave_chunks or args.cold)
+    traffic = None if tuned else read_traffic(variant, w.name)
+    fused_name = "wave_kernel" if args.wave_chunks else "exchange_kernel"
+    kernel = {"step": f"{fused_name} (fused step, one launch)",
+              "split": f"{fused_name} (coordinate launch + force launch)",
               "staged": "pulse_kernel pack/unpack + one hipMemcpyAsync per sender and pulse, "
                         "two host waits per pulse"}.get(
                   variant, "pulse_kernel (coordinate pulse q + force pulse P-1-q per launch) + signal_kernel")
@@ -392,6 +399,8 @@ def run_overlap(args, w):
         plan.tune(ddh.DDH_TUNE_FLAGS, 0)
     if args.wide_maps:
         plan.tune(ddh.DDH_TUNE_NARROW_MAPS, 0)
+    if args.wave_chunks:
+        plan.tune(ddh.DDH_TUNE_WAVE_CHUNKS, 1)
     lay = plan.build_maps(xg)
     n_slots, n_halo = lay["n_slots"], lay["n_halo"]
     xl = torch.zeros((n_slots, 3), dtype=torch.float32, device=dev)
@@ -587,6 +596,8 @@ def main():
                     help="fused launch: first tickets unclaimed (DDH_TUNE_STATIC_FIRST)")
     ap.add_argument("--no-flags", action="store_true",
                     help="calls skip the per-pulse completion flags (DDH_TUNE_FLAGS = 0)")
+    ap.add_argument("--wave-chunks", action="store_true",
+                    help="fused launch with wavefront workers (DDH_TUNE_WAVE_CHUNKS = 1)")
     ap.add_argument("--wide-maps", action="store_true",
                     help="kernels read the 32-bit maps (DDH_TUNE_NARROW_MAPS = 0)")
     ap.add_argument("--cold", action="store_true", help="evict caches before every step")

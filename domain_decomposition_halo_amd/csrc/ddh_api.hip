@@ -447,6 +447,11 @@ int ddh_tune(ddh_plan* p, int32_t key, int64_t value)
             return fail(DDH_EINVAL, "ddh_tune: narrow-maps must be 0 or 1");
         p->narrow_maps = (int)value;
         return DDH_OK;
+    case DDH_TUNE_WAVE_CHUNKS:
+        if (value != 0 && value != 1)
+            return fail(DDH_EINVAL, "ddh_tune: wave-chunks must be 0 or 1");
+        p->wave_chunks = (int)value;
+        return DDH_OK;
     default:
         return fail(DDH_EINVAL, "ddh_tune: unknown key");
     }

@@ -566,11 +566,13 @@ void free_built(Plan* p)
 
 // Chunk table of chunk size t.chunk. With waits (the fused launch) a
 // coordinate chunk takes the k-th slice of its map's independent head and of
-// its dependent tail, and a force chunk the k-th slice of the map; the wait
-// masks are the conservative ones (every earlier / later pulse) unless
-// refined waits are on, in which case chunk_masks_kernel fills them in from
-// the maps. Without waits (per-pulse launches, ordered by the stream) every
-// chunk is one contiguous slice and the masks stay empty.
+// its dependent tail (with wavefront workers: the k-th contiguous slice of
+// the map, whose entries at or past the split form its tail), and a force
+// chunk the k-th slice of the map; the wait masks are the conservative ones
+// (every earlier / later pulse) unless refined waits are on, in which case
+// chunk_masks_kernel fills them in from the maps. Without waits (per-pulse
+// launches, ordered by the stream) every chunk is one contiguous slice and
+// the masks stay empty.
 static void make_work_table(const Plan* p, bool waits, WorkTable& t)
 {
     const Geometry& g = p->g;
@@ -606,10 +608,19 @@ static void make_work_table(const Plan* p, bool waits, WorkTable& t)
             d.tb = d.te = d.he;
             return d;
         }
-        d.hb = (int32_t)((int64_t)h * k / c);
-        d.he = (int32_t)((int64_t)h * (k + 1) / c);
-        d.tb = h + (int32_t)((int64_t)tl * k / c);
-        d.te = h + (int32_t)((int64_t)tl * (k + 1) / c);
+        if (p->wave_chunks) {
+            const int n = p->send[it];
+            const int b = (int)((int64_t)n * k / c), e = (int)((int64_t)n * (k + 1) / c);
+            d.hb = b;
+            d.he = std::max(b, std::min(e, h));
+            d.tb = std::min(std::max(b, h), e);
+            d.te = e;
+        } else {
+            d.hb = (int32_t)((int64_t)h * k / c);
+            d.he = (int32_t)((int64_t)h * (k + 1) / c);
+            d.tb = h + (int32_t)((int64_t)tl * k / c);
+            d.te = h + (int32_t)((int64_t)tl * (k + 1) / c);
+        }
         d.wait_a = (conservative && d.te > d.tb) ? (1u << d.p) - 1u : 0u;
         return d;
     };
@@ -677,12 +688,14 @@ static void set_release_flags(const Plan* p, WorkTable& t)
 // Entries per chunk of the fused launch: 4096. A small (latency-bound) pass
 // then gives one chunk per map, run by one 1024-wide work-group, which keeps
 // the device-wide serialized operations (ticket claims, releases, acquires)
-// per dependency stage few.
-static int fused_chunk() { return 4096; }
+// per dependency stage few. With wavefront workers: 1024 (16 entries per
+// lane; smaller slices multiply the serialized ticket claims and releases).
+static int fused_chunk(const Plan* p) { return p->wave_chunks ? 1024 : 4096; }
 
 // Entries per block of the per-pulse launches: the largest of 2048, 1024 and
 // 512 that still gives every pulse's launch at least two blocks per compute
-// unit (a launch with fewer blocks than compute units leaves bandwidth idle).
+// unit (a launch with fewer blocks than compute units leaves bandwidth idle),
+// or 256 for small pulses.
 static int pulse_chunk(const Plan* p)
 {
     const int D = p->g.ndom, P = p->g.P;
@@ -1017,7 +1030,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     }
 
     // ---- 5: chunk tables (wait masks computed on the device), counters
-    p->fused.chunk = p->chunk_req > 0 ? p->chunk_req : fused_chunk();
+    p->fused.chunk = p->chunk_req > 0 ? p->chunk_req : fused_chunk(p);
     p->pulse.chunk = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p);
     make_work_table(p, true, p->fused);
     make_work_table(p, false, p->pulse);

@@ -147,15 +147,17 @@ __device__ void wave_wait(const XArgs& a, const uint32_t* cnt, const uint32_t* n
     wait_vm_idle();
 }
 
-// Map entries of one round: entry i0 + e * B + tid for e < E (B threads).
-// I is the stored index type: int32, or uint16 when every domain has at most
-// 65536 slots (half the bytes for the same entries).
+// Map entries of one round: entry i0 + e * B + tid for e < E. B threads
+// share a round: a whole work-group (B = its width, tid = threadIdx.x) or one
+// wavefront (B = 64, tid = its lane). I is the stored index type: int32, or
+// uint16 when every domain has at most 65536 slots (half the bytes for the
+// same entries).
 template <int E, int B, typename I>
 __device__ __forceinline__ void load_map(const I* map, int i0, int end, int (&j)[E])
 {
 #pragma unroll
     for (int e = 0; e < E; e++) {
-        const int i = i0 + e * B + (int)threadIdx.x;
+        const int i = i0 + e * B + (int)threadIdx.x % B;
         j[e] = i < end ? (int)map[i] : -1;
     }
 }
@@ -190,7 +192,7 @@ __device__ __forceinline__ void coords_round(const float* src, float* dst, const
     }
 #pragma unroll
     for (int e = 0; e < E; e++) {
-        const int i = i0 + e * B + (int)threadIdx.x;
+        const int i = i0 + e * B + (int)threadIdx.x % B;
         if (i < end) {
             float* d = dst + 3ll * i;
             __builtin_nontemporal_store(v[e][0], d);
@@ -209,7 +211,7 @@ __device__ __forceinline__ void forces_round(const float* from, float* tgt, int 
     float s[E][3], t[E][3];
 #pragma unroll
     for (int e = 0; e < E; e++) {
-        const int i = i0 + e * B + (int)threadIdx.x;
+        const int i = i0 + e * B + (int)threadIdx.x % B;
         if (j[e] >= 0) {
             const float* r = from + 3ll * i;
             s[e][0] = r[0];
@@ -263,6 +265,44 @@ __device__ void forces_range(float* f, const I* maps, const DChunk& c, int begin
         int j[E];
         load_map<E, B, I>(map, i0, end, j);
         forces_round<E, B>(from, tgt, i0, end, j);
+    }
+}
+
+// One worker of a fused launch leaves (called by one lane, after the
+// worker's records are released when completion flags are on). The last of
+// the launch's `workers` to leave sees every worker's records, re-arms the
+// ticket and exit counters for the next launch, and publishes the passes the
+// launch completed: the fused pass counters and, with completion flags on,
+// every pulse's flag ("Dependency-aware packing": the last arrival stores the
+// flag).
+__device__ void leave_launch(const XArgs& a, uint32_t workers, uint32_t px, uint32_t pf)
+{
+    const bool publish = a.flags != nullptr;
+    const uint32_t old = __hip_atomic_fetch_add(a.ctrl + kCtrlDone, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (old != workers - 1u)
+        return;
+    if (publish)
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+    st_relaxed(a.ctrl + kCtrlTicket, 0u);
+    st_relaxed(a.ctrl + kCtrlDone, 0u);
+    if (a.nx > 0) {
+        st_relaxed(a.ctrl + kCtrlPassX, px);
+        if (publish) {
+            const uint32_t e = ld_relaxed(a.ctrl + kCtrlEpochX) + 1u;
+            for (int q = 0; q < a.P; q++)
+                st_relaxed(a.flags + q, e);
+            st_relaxed(a.ctrl + kCtrlEpochX, e);
+        }
+    }
+    if (a.nf > 0) {
+        st_relaxed(a.ctrl + kCtrlPassF, pf);
+        if (publish) {
+            const uint32_t e = ld_relaxed(a.ctrl + kCtrlEpochF) + 1u;
+            for (int q = 0; q < a.P; q++)
+                st_relaxed(a.flags + DDH_MAX_PULSES + q, e);
+            st_relaxed(a.ctrl + kCtrlEpochF, e);
+        }
     }
 }
 
@@ -373,11 +413,7 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
     }
 
     // Leave: a work-group that still holds unreleased records (chunks no
-    // later chunk of the launch reads) releases them; the last work-group to
-    // leave then sees every work-group's records, re-arms the ticket counter
-    // for the next launch, and publishes the passes this launch completed:
-    // the fused pass counters and, after a release, every pulse's completion
-    // flag ("Dependency-aware packing": the last arrival stores the flag).
+    // later chunk of the launch reads) releases them, then leave_launch.
     // (Without completion flags, a.flags is null: nothing to release here.)
     const bool publish = a.flags != nullptr;
     if (held && publish) {
@@ -388,33 +424,80 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
         trace_rec(a, ntr, kTrExit, 0);
         if (held && publish)
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const uint32_t old = __hip_atomic_fetch_add(a.ctrl + kCtrlDone, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        if (old == gridDim.x - 1u) {
-            if (publish)
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
-            st_relaxed(a.ctrl + kCtrlTicket, 0u);
-            st_relaxed(a.ctrl + kCtrlDone, 0u);
-            if (a.nx > 0) {
-                st_relaxed(a.ctrl + kCtrlPassX, px);
-                if (publish) {
-                    const uint32_t e = ld_relaxed(a.ctrl + kCtrlEpochX) + 1u;
-                    for (int q = 0; q < P; q++)
-                        st_relaxed(a.flags + q, e);
-                    st_relaxed(a.ctrl + kCtrlEpochX, e);
-                }
-            }
-            if (a.nf > 0) {
-                st_relaxed(a.ctrl + kCtrlPassF, pf);
-                if (publish) {
-                    const uint32_t e = ld_relaxed(a.ctrl + kCtrlEpochF) + 1u;
-                    for (int q = 0; q < P; q++)
-                        st_relaxed(a.flags + DDH_MAX_PULSES + q, e);
-                    st_relaxed(a.ctrl + kCtrlEpochF, e);
-                }
-            }
+        leave_launch(a, gridDim.x, px, pf);
+    }
+}
+
+// Fused mode at wavefront granularity (DDH_TUNE_WAVE_CHUNKS; the per-warp
+// pipelining of the guide's "NVLink path: TMA-based direct stores"): every
+// wavefront of the launch is an independent worker and no work-group barrier
+// is ever taken. A chunk is one contiguous slice of one map. The wavefront
+// claims it, packs the slice's independent entries, waits only if the slice
+// also holds dependent entries (the map's tail), packs those, and publishes
+// by itself: when a later chunk reads its records, a release fence (which
+// waits for the wavefront's own stores and writes them back), then one
+// relaxed add to the map's counter. Same ticket order, counters and targets
+// as exchange_kernel, hence the same freedom from deadlock; in the exit
+// protocol every wavefront counts as one worker.
+template <int E, typename I>
+__global__ __launch_bounds__(256) void wave_kernel(XArgs a)
+{
+    constexpr int W = 64;  // lanes that share a round: one wavefront
+    const I* maps = static_cast<const I*>(a.maps);
+    const int P = a.P;
+    const int nt = a.nx + a.nf;
+    const uint32_t bump = a.force_timeout ? 0x40000000u : 0u;
+    const uint32_t px = ld_relaxed(a.ctrl + kCtrlPassX) + (a.nx > 0 ? 1u : 0u);
+    const uint32_t pf = ld_relaxed(a.ctrl + kCtrlPassF) + 1u;
+    const bool lead = (threadIdx.x & 63) == 0;
+    bool held = false;   // this wavefront wrote records it has not released
+    for (;;) {
+        int t = 0;
+        if (lead)
+            t = (int)__hip_atomic_fetch_add(a.ctrl + kCtrlTicket, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        t = __builtin_amdgcn_readfirstlane(t);  // lane 0's (every lane is active)
+        if (t >= nt)
+            break;
+        if (t < a.nx) {
+            const DChunk c = a.xchunks[t];
+            int jh[E], jt[E];
+            load_map<E, W, I>(maps + c.map_off, c.hb, c.he, jh);
+            load_map<E, W, I>(maps + c.map_off, c.tb, c.te, jt);
+            coords_range<E, W, I>(a.x, maps, c, c.hb, c.he, jh);
+            if (c.wait_a)
+                wave_wait(a, a.xcnt, a.xneed, px, c.wait_a, c.S * P, 0u, 0, bump);
+            coords_range<E, W, I>(a.x, maps, c, c.tb, c.te, jt);
+            if (c.flags & kChunkRelease)
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            held = !(c.flags & kChunkRelease);
+            // the lanes of a wavefront run in lockstep, so every lane's
+            // stores and fence precede lane 0's add; the wave barrier keeps
+            // the compiler from moving anything across it
+            __builtin_amdgcn_wave_barrier();
+            if (lead)
+                add_relaxed(a.xcnt + c.ctr, 1u);
+        } else {
+            const DChunk c = a.fchunks[t - a.nx];
+            int j0[E];
+            load_map<E, W, I>(maps + c.map_off, c.hb, c.he, j0);
+            if (c.wait_a || c.wait_b)
+                wave_wait(a, a.fcnt, a.fneed, pf, c.wait_a, c.S * P, c.wait_b, c.R * P, bump);
+            forces_range<E, W, I>(a.f, maps, c, c.hb, c.he, j0);
+            if (c.flags & kChunkRelease)
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            held = !(c.flags & kChunkRelease);
+            __builtin_amdgcn_wave_barrier();
+            if (lead)
+                add_relaxed(a.fcnt + c.ctr, 1u);
         }
     }
+    const bool publish = a.flags != nullptr;
+    if (held && publish)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_wave_barrier();
+    if (lead)
+        leave_launch(a, gridDim.x * (blockDim.x / 64), px, pf);
 }
 
 // One pulse of one pass, ordered against the other pulses by the stream
@@ -566,6 +649,16 @@ void launch_fused_t(const XArgs& a, int grid, bool wide, int per, hipStream_t s)
     }
 }
 
+// The wavefront-granular fused kernel for the entries per lane.
+template <typename I>
+void launch_wave_t(const XArgs& a, int grid, int per, hipStream_t s)
+{
+    if (per > 4)
+        hipLaunchKernelGGL((wave_kernel<8, I>), dim3(grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((wave_kernel<4, I>), dim3(grid), dim3(256), 0, s, a);
+}
+
 // The per-pulse kernel instance for the block width and entries per lane.
 template <typename I>
 void launch_pulse_t(const PArgs& a, dim3 grid, int lanes, int per, hipStream_t s)
@@ -593,6 +686,23 @@ int launch_fused(const Plan* p, XArgs a, hipStream_t s)
     const int nt = a.nx + a.nf;
     if (nt <= 0)
         return DDH_OK;
+    if (p->wave_chunks) {
+        // work-groups of four independent wavefronts, at most eight per
+        // compute unit and one wavefront per ticket
+        int grid = p->grid_req > 0 ? p->grid_req : p->n_cu * 8;
+        grid = std::min(grid, (nt + 3) / 4);
+        a.static_first = 0;
+        const int per = (p->fused.chunk + 63) / 64;
+        if (use_narrow_maps(p)) {
+            a.maps = p->d_maps16;
+            launch_wave_t<uint16_t>(a, grid, per, s);
+        } else {
+            a.maps = p->d_maps;
+            launch_wave_t<int32_t>(a, grid, per, s);
+        }
+        DDH_HIP(hipGetLastError());
+        return DDH_OK;
+    }
     int grid = p->grid_req > 0 ? p->grid_req : p->n_cu * 4;
     if (grid > nt)
         grid = nt;

@@ -156,6 +156,8 @@ struct Plan {
     int force_timeout = 0;
     int refined_waits = 1;
     int narrow_maps = 1;        // use the 16-bit copy of the maps when there is one
+    int wave_chunks = 0;        // fused: wavefront workers on contiguous slices
+                                // (takes effect at the next build)
     uint64_t* trace = nullptr;  // caller-owned device buffer (DDH_TUNE_TRACE)
 
     // host copies of the layout

@@ -325,7 +325,19 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     entry instead of 4; same entries, same
                                     results); 0: they read the 32-bit maps */
 
-/* Set a tuning knob; takes effect at the next build (CHUNK) or call. */
+#define DDH_TUNE_WAVE_CHUNKS 11    /* fused mode: 0 (default) work-groups
+                                    claim chunks and take barriers around
+                                    their waits; 1 every wavefront is an
+                                    independent worker: chunks are contiguous
+                                    map slices (default 1024 entries), a
+                                    wavefront waits only when its slice holds
+                                    dependent entries and releases its own
+                                    records, with no work-group barrier (the
+                                    guide's per-warp pipelining). Takes effect
+                                    at the next build. */
+
+/* Set a tuning knob; takes effect at the next build (CHUNK, WAVE_CHUNKS) or
+   call. */
 int ddh_tune(ddh_plan *plan, int32_t key, int64_t value);
 
 #ifdef __cplusplus

@@ -6,7 +6,8 @@ words. Cases: the workloads at full size (maps, layout, coordinates, forces,
 both passes in one call); every execution mode (fused persistent launch, one
 launch per pulse, both replayed from the library's graphs, automatic, the
 host-orchestrated baseline) over several consecutive steps; calls captured
-in a caller's graph with the halo cleared before each replay; ragged and
+in a caller's graph with the halo cleared before each replay; the fused
+launch with wavefront workers; 16- and 32-bit map entries; ragged and
 extreme chunk/grid/width settings (down to a single work-group, with and
 without static first tickets); exact dyadic boxes with multi-pulse relay up
 to the most pulses a grid allows; seeded random decompositions; rebuilds for
@@ -45,10 +46,11 @@ class GpuPlan:
     """A device plan built from host positions, with host views of its output."""
 
     def __init__(self, x, grid, box, rc, cell=0.5, mode=0, chunk=0, wg=0, refined=1, block=0,
-                 static_first=0, narrow=1):
+                 static_first=0, narrow=1, wave=0):
         self.plan = ddh.Plan(grid, box, rc, cell)
         self.plan.tune(ddh.DDH_TUNE_STATIC_FIRST, static_first)
         self.plan.tune(ddh.DDH_TUNE_NARROW_MAPS, narrow)
+        self.plan.tune(ddh.DDH_TUNE_WAVE_CHUNKS, wave)
         self.plan.tune(ddh.DDH_TUNE_CHUNK, chunk)
         self.plan.tune(ddh.DDH_TUNE_GRID, wg)
         self.plan.tune(ddh.DDH_TUNE_BLOCK, block)
@@ -150,14 +152,14 @@ def test_workload_fused_step(k, mode, workload_plan):
 
 
 @pytest.mark.parametrize("split", [False, True])
-@pytest.mark.parametrize("mode", ["auto", "pulse", "fused"])
+@pytest.mark.parametrize("mode", ["auto", "pulse", "fused", "wave"])
 @pytest.mark.parametrize("k", [1, 2, 4])
 def test_captured_in_a_caller_graph(k, mode, split, workload_plan):
     """Calls captured in a torch CUDA graph and replayed several times, with
     eager work (new forces, a check) between replays: every replay matches
-    the oracle bit for bit."""
+    the oracle bit for bit. "wave": the fused launch with wavefront workers."""
     w, x, ref = workload_plan(k)
-    g = GpuPlan(x, **w.params(), mode=MODES[mode])
+    g = GpuPlan(x, **w.params(), mode=MODES.get(mode, ddh.DDH_MODE_FUSED), wave=int(mode == "wave"))
     xl = g.new_coords()
     fl = torch.zeros((max(g.n_slots, 1), 3), dtype=torch.float32, device="cuda")
     side = torch.cuda.Stream()
@@ -220,12 +222,12 @@ def random_configs(n, seed):
 def test_random_decompositions(cfg):
     """Random grids, boxes, cutoffs (one to several pulses per dimension) and
     atom counts: layout, maps, ids, coordinates and forces bit-identical to
-    the oracle in every mode, over two steps."""
+    the oracle in every mode (and with wavefront workers), over two steps."""
     grid, box, rc, n = cfg
     x = W.uniform_positions(n, box, seed=n)
     ref = oracle.OraclePlan(x, grid, box, rc)
-    for mode in MODES.values():
-        g = GpuPlan(x, grid, box, rc, mode=mode)
+    for mode, wave in [(m, 0) for m in MODES.values()] + [(ddh.DDH_MODE_FUSED, 1)]:
+        g = GpuPlan(x, grid, box, rc, mode=mode, wave=wave)
         check_layout(g, ref)
         check_steps(g, ref, n, steps=2)
         check_steps(g, ref, n + 1, steps=1, fused_step=True)
@@ -515,6 +517,20 @@ def test_map_width_threshold(n, wide):
         g.close()
 
 
+@pytest.mark.parametrize("chunk,wg", [(0, 0), (64, 0), (1000, 0), (0, 1), (192, 3), (4096, 0)])
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_wave_chunks(k, chunk, wg, workload_plan):
+    """Fused launch with wavefront workers (DDH_TUNE_WAVE_CHUNKS): contiguous
+    map slices, a wavefront waits only when its slice holds dependent
+    entries and releases its own records. Down to one work-group of four
+    wavefronts; ragged and multi-round slices."""
+    w, x, ref = workload_plan(k)
+    g = GpuPlan(x, **w.params(), mode=ddh.DDH_MODE_FUSED, chunk=chunk, wg=wg, wave=1)
+    check_steps(g, ref, 60 + k, steps=2)
+    check_steps(g, ref, 70 + k, steps=1, fused_step=True)
+    g.close()
+
+
 DYADIC = [
     ((1, 1, 1), (4.0, 4.0, 4.0), 0.75, 500),
     ((2, 1, 1), (8.0, 4.0, 4.0), 1.25, 2000),
@@ -541,6 +557,11 @@ def test_dyadic_boxes(grid, box, rc, n):
         check_layout(g, ref)
         check_steps(g, ref, n, steps=2)
         check_steps(g, ref, n + 1, steps=1, fused_step=True)
+        g.close()
+    for chunk in (0, 64):                         # wavefront workers
+        g = GpuPlan(x, grid, box, rc, mode=ddh.DDH_MODE_FUSED, chunk=chunk, wave=1)
+        check_steps(g, ref, n + 2, steps=2)
+        check_steps(g, ref, n + 3, steps=1, fused_step=True)
         g.close()
 
 
@@ -594,8 +615,8 @@ def test_error_paths():
 
 def test_timeout_path_is_reported_and_recovers(workload_plan):
     w, x, ref = workload_plan(2)
-    for mode in (ddh.DDH_MODE_FUSED, ddh.DDH_MODE_PULSE):
-        g = GpuPlan(x, **w.params(), mode=mode)
+    for mode, wave in ((ddh.DDH_MODE_FUSED, 0), (ddh.DDH_MODE_FUSED, 1), (ddh.DDH_MODE_PULSE, 0)):
+        g = GpuPlan(x, **w.params(), mode=mode, wave=wave)
         g.plan.tune(ddh.DDH_TUNE_SPIN_LIMIT, 64)
         g.plan.tune(ddh.DDH_TUNE_FORCE_TIMEOUT, 1)
         xl = g.new_coords()

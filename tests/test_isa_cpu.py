@@ -141,3 +141,15 @@ def test_release_checker_flags_a_bare_barrier():
     assert release_barriers_without_store_wait(lines) == [3]
     fixed = lines[:2] + ["\ts_waitcnt vmcnt(0)"] + lines[2:]
     assert release_barriers_without_store_wait(fixed) == []
+
+
+def test_wave_kernel_takes_no_barrier_and_releases(tmp_path):
+    # wavefront workers are independent: a work-group barrier in their ticket
+    # loop would tie a waiting wavefront to its neighbours; each one releases
+    # its own records with an agent-scope fence (buffer_wbl2)
+    kernels = _isa(os.path.join(CSRC, "ddh_exchange.hip"), tmp_path)
+    wk = {k: v for k, v in kernels.items() if "wave_kernel" in k}
+    assert len(wk) >= 2
+    for name, lines in wk.items():
+        assert not any("s_barrier" in ln for ln in lines), name
+        assert sum("buffer_wbl2" in ln for ln in lines) >= 2, name
