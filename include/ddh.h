@@ -275,7 +275,9 @@ int ddh_check(ddh_plan *plan, void *stream);
 /* -------------------------------------------------------------- tuning */
 #define DDH_TUNE_CHUNK 1        /* map entries per work chunk (64..8192, rounded
                                    to a multiple of 64); 0 = automatic */
-#define DDH_TUNE_GRID 2         /* workgroups of a fused launch; 0 = automatic */
+#define DDH_TUNE_GRID 2         /* workgroups of a fused launch; 0 = automatic
+                                   (one per compute unit, at most one per
+                                   chunk) */
 #define DDH_TUNE_SPIN_LIMIT 3   /* polls before a device wait gives up */
 #define DDH_TUNE_FORCE_TIMEOUT 4 /* 1: every dependent wait of the fused mode
                                     targets a value no one writes, so it ends
@@ -297,9 +299,9 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     (DDH_TUNE_GRID); the buffer is not cleared. */
 
 #define DDH_TUNE_BLOCK 7           /* work-group width of the exchange launches:
-                                    0 (automatic: fused 1024 when its grid
-                                    leaves compute units idle, else 256;
-                                    per-pulse 1024), 256 or 1024 */
+                                    0 (automatic: fused 1024; per-pulse 1024
+                                    for chunks of at least 1024 entries, else
+                                    256), 256 or 1024 */
 
 #define DDH_TUNE_STATIC_FIRST 8    /* fused mode: 0 (default) every work-group
                                     claims its tickets in start order, so no
