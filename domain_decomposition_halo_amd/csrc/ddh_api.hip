@@ -404,8 +404,8 @@ int ddh_tune(ddh_plan* p, int32_t key, int64_t value)
     p->graphs.clear();
     switch (key) {
     case DDH_TUNE_CHUNK:
-        if (value != 0 && (value < 64 || value > 8192))
-            return fail(DDH_EINVAL, "ddh_tune: chunk must be 0 or in [64, 8192]");
+        if (value != 0 && (value < 64 || value > 65536))
+            return fail(DDH_EINVAL, "ddh_tune: chunk must be 0 or in [64, 65536]");
         p->chunk_req = (int)((value + 63) / 64 * 64);
         return DDH_OK;
     case DDH_TUNE_GRID:

@@ -273,7 +273,7 @@ int ddh_set_mode(ddh_plan *plan, int32_t mode);
 int ddh_check(ddh_plan *plan, void *stream);
 
 /* -------------------------------------------------------------- tuning */
-#define DDH_TUNE_CHUNK 1        /* map entries per work chunk (64..8192, rounded
+#define DDH_TUNE_CHUNK 1        /* map entries per work chunk (64..65536, rounded
                                    to a multiple of 64); 0 = automatic */
 #define DDH_TUNE_GRID 2         /* workgroups of a fused launch; 0 = automatic
                                    (one per compute unit, at most one per
