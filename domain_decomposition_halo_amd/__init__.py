@@ -161,7 +161,8 @@ class Plan:
 
     # -- build and layout
     def build_maps(self, x_global, stream=None):
-        assert x_global.dim() == 2 and x_global.shape[1] == 3
+        if x_global.dim() != 2 or x_global.shape[1] != 3:
+            raise DDHError(DDH_EINVAL, "build_maps: x_global must be an (n, 3) tensor")
         _check(_lib.ddh_build_maps(self._h, _dev_ptr(x_global, "float32", "x_global"),
                                    int(x_global.shape[0]), _stream(stream)), "ddh_build_maps")
         return self.layout()
@@ -198,7 +199,8 @@ class Plan:
         return ptr.value or 0
 
     def copy_flags(self, out, stream=None):
-        """Snapshot of the flags into a device int32/uint32 tensor of >= 32 words."""
+        """Snapshot of the flags into a device int32 tensor of >= 32 words (the
+        words are uint32 counts; read them modulo 2**32)."""
         if out.numel() < 2 * DDH_MAX_PULSES:
             raise ValueError("copy_flags: the tensor needs 2 * DDH_MAX_PULSES words")
         _check(_lib.ddh_copy_flags(self._h, _dev_ptr(out, "int32", "flags"), _stream(stream)),

@@ -608,7 +608,7 @@ static void make_work_table(const Plan* p, bool waits, WorkTable& t)
             d.tb = d.te = d.he;
             return d;
         }
-        if (p->wave_chunks) {
+        if (t.wave) {
             const int n = p->send[it];
             const int b = (int)((int64_t)n * k / c), e = (int)((int64_t)n * (k + 1) / c);
             d.hb = b;
@@ -1032,6 +1032,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
 
     // ---- 5: chunk tables (wait masks computed on the device), counters
     p->fused.chunk = p->chunk_req > 0 ? p->chunk_req : fused_chunk(p);
+    p->fused.wave = p->wave_chunks != 0;
     p->pulse.chunk = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p);
     make_work_table(p, true, p->fused);
     make_work_table(p, false, p->pulse);

@@ -686,7 +686,7 @@ int launch_fused(const Plan* p, XArgs a, hipStream_t s)
     const int nt = a.nx + a.nf;
     if (nt <= 0)
         return DDH_OK;
-    if (p->wave_chunks) {
+    if (p->fused.wave) {
         // work-groups of four independent wavefronts, at most eight per
         // compute unit and one wavefront per ticket
         int grid = p->grid_req > 0 ? p->grid_req : p->n_cu * 8;

@@ -117,6 +117,7 @@ struct Geometry {
 // chunks in decreasing pulse order, each pulse's chunks contiguous.
 struct WorkTable {
     int chunk = 0;                  // entries per chunk
+    bool wave = false;              // fused: built for wavefront workers
     std::vector<int32_t> nchunks;   // [S * P + p] chunks of the map
     std::vector<DChunk> xch, fch;
     std::vector<int32_t> xpulse_begin, fpulse_begin;  // per pulse ranges (+1)

@@ -528,6 +528,11 @@ def test_wave_chunks(k, chunk, wg, workload_plan):
     g = GpuPlan(x, **w.params(), mode=ddh.DDH_MODE_FUSED, chunk=chunk, wg=wg, wave=1)
     check_steps(g, ref, 60 + k, steps=2)
     check_steps(g, ref, 70 + k, steps=1, fused_step=True)
+    # the setting belongs to the chunk table: it changes at the next build
+    g.plan.tune(ddh.DDH_TUNE_WAVE_CHUNKS, 0)
+    check_steps(g, ref, 80 + k, steps=1, fused_step=True)
+    g.plan.build_maps(g.xg)
+    check_steps(g, ref, 90 + k, steps=1)
     g.close()
 
 
