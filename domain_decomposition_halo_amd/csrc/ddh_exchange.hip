@@ -32,7 +32,9 @@
 //    slot receives its adds in decreasing pulse order and matches the
 //    sequential reverse pass bit for bit. The single-launch form, and the
 //    default for eager calls on small passes, where the host's cost per
-//    launch dominates.
+//    launch dominates. With DDH_TUNE_WAVE_CHUNKS the same launch runs
+//    wave_kernel, in which every wavefront is an independent worker on
+//    contiguous map slices ("NVLink path: TMA-based direct stores").
 //
 //  - The host-orchestrated baseline (DDH_MODE_STAGED; "From MPI baseline to
 //    optimized GPU-native halo exchange"): pack into a staging buffer, host
