@@ -656,21 +656,44 @@ def test_repeated_force_passes_are_deterministic(workload_plan):
 
 
 def test_workload5_full_size():
-    # 12M atoms, 8x8x8 domains: the bench's largest workload, default launch
+    """12M atoms, 8x8x8 domains, at full size: the fused launch, the
+    library's graph of per-pulse launches, and the bench's own launch (the
+    automatic mode captured in a caller's graph and replayed twice)."""
     w = W.WORKLOADS[5]
     x = W.positions(w)
     ref = oracle.OraclePlan(x, **w.params())
-    for mode in (ddh.DDH_MODE_FUSED, ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH):
+    f0 = W.forces(w, ref.n_slots)
+    fr = f0.copy()
+    ref.exchange_forces(fr)
+    for mode in (ddh.DDH_MODE_FUSED, ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, ddh.DDH_MODE_AUTO):
         g = GpuPlan(x, **w.params(), mode=mode)
         if mode == ddh.DDH_MODE_FUSED:
             check_layout(g, ref)
         xl = g.new_coords()
-        f0 = W.forces(w, g.n_slots)
         fl = torch.from_numpy(f0).cuda()
-        g.plan.exchange_step(xl, fl)
-        assert g.plan.check() == ddh.DDH_OK
-        assert np.array_equal(bits(xl.cpu().numpy()), bits(ref.x_local))
-        fr = f0.copy()
-        ref.exchange_forces(fr)
-        assert np.array_equal(bits(fl.cpu().numpy()), bits(fr))
+        if mode != ddh.DDH_MODE_AUTO:
+            g.plan.exchange_step(xl, fl)
+            replays = 1
+        else:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                g.plan.exchange_step(xl, fl)      # warm-up outside the capture
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                g.plan.exchange_step(xl, fl)
+            replays = 2
+        for r in range(replays):
+            if mode == ddh.DDH_MODE_AUTO:
+                xl.copy_(g.new_coords())
+                fl.copy_(torch.from_numpy(f0))
+                torch.cuda.synchronize()
+                graph.replay()
+            assert g.plan.check() == ddh.DDH_OK
+            assert np.array_equal(bits(xl.cpu().numpy()), bits(ref.x_local)), (mode, r)
+            assert np.array_equal(bits(fl.cpu().numpy()), bits(fr)), (mode, r)
+        if mode == ddh.DDH_MODE_AUTO:
+            del graph
         g.close()
