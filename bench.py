@@ -613,7 +613,7 @@ def main():
                          "for profiler runs")
     ap.add_argument("--lib-graph", action="store_true",
                     help="with --eager: each call replays the library's cached hipGraph")
-    ap.add_argument("--also", default="5",
+    ap.add_argument("--also", default="1,3,4,5",
                     help="comma-separated workload keys timed after the main one and "
                          "summarized under 'also' (empty: none; skipped with --only-step)")
     ap.add_argument("--graph-steps", type=int, default=50,
