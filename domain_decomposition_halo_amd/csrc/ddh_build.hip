@@ -394,6 +394,20 @@ __global__ __launch_bounds__(256) void narrow_maps_kernel(const int32_t* __restr
         out[i] = (uint16_t)maps[i];
 }
 
+// Chunk-aligned copy of the maps for the per-pulse launches: block b writes
+// the entries of chunk b at out[b * CH ...] and zeros up to the next chunk.
+template <typename T>
+__global__ __launch_bounds__(256) void pad_maps_kernel(const T* __restrict__ maps,
+                                                       const DChunk* __restrict__ ch, int CH,
+                                                       T* __restrict__ out)
+{
+    const DChunk c = ch[blockIdx.x];
+    const int n = c.he - c.hb;
+    T* o = out + (int64_t)blockIdx.x * CH;
+    for (int i = threadIdx.x; i < CH; i += 256)
+        o[i] = i < n ? maps[c.map_off + c.hb + i] : (T)0;
+}
+
 // inmap[slot] |= bit for every entry of pulse q's maps (maps_q: the pulse's
 // maps of all senders, sender S's at mpos[S]..mpos[S+1]). Within one pulse
 // every slot appears at most once (a map holds distinct slots of its own
@@ -1041,6 +1055,26 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         DDH_HIP(owned_alloc(p, &t->d_fch, t->fch.size()));
         DDH_HIP(upload(t->d_xch, t->xch, s));
         DDH_HIP(upload(t->d_fch, t->fch, s));
+    }
+    {
+        // chunk-aligned maps of the per-pulse launches (every coordinate
+        // chunk of the table is a contiguous slice [hb, he) of one map)
+        WorkTable& t = p->pulse;
+        const int nch = (int)t.xch.size();
+        const size_t npad = (size_t)nch * t.chunk + kPadTail;
+        DDH_HIP(owned_alloc(p, &t.d_pad, npad));
+        DDH_HIP(hipMemsetAsync(t.d_pad, 0, sizeof(int32_t) * npad, s));
+        if (nch > 0)
+            hipLaunchKernelGGL(pad_maps_kernel<int32_t>, dim3(nch), dim3(256), 0, s, p->d_maps,
+                               t.d_xch, t.chunk, t.d_pad);
+        if (p->d_maps16) {
+            DDH_HIP(owned_alloc(p, &t.d_pad16, npad));
+            DDH_HIP(hipMemsetAsync(t.d_pad16, 0, sizeof(uint16_t) * npad, s));
+            if (nch > 0)
+                hipLaunchKernelGGL(pad_maps_kernel<uint16_t>, dim3(nch), dim3(256), 0, s,
+                                   p->d_maps16, t.d_xch, t.chunk, t.d_pad16);
+        }
+        DDH_HIP(hipGetLastError());
     }
     if (p->refined_waits && P > 0) {
         WorkTable& t = p->fused;

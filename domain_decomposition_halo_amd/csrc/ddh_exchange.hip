@@ -236,15 +236,15 @@ __device__ __forceinline__ void forces_round(const float* from, float* tgt, int 
     }
 }
 
-// Entries [begin, end) of a chunk's map; j0 holds the first round's map
-// entries (loaded by the caller, possibly before a wait).
+// Entries [begin, end) of a chunk's map (map: the chunk's (sender, pulse)
+// map, entry i at map[i]); j0 holds the first round's map entries (loaded by
+// the caller, possibly before a wait).
 // With a staging buffer (the host-orchestrated baseline), entry i of a map
 // goes to / comes from stage[map_off + i] instead of the receiver's region.
 template <int E, int B, typename I>
-__device__ void coords_range(float* x, const I* maps, const DChunk& c, int begin, int end,
+__device__ void coords_range(float* x, const I* map, const DChunk& c, int begin, int end,
                              const int (&j0)[E], float* stage = nullptr)
 {
-    const I* map = maps + c.map_off;
     const float* src = x + 3ll * c.src_base;
     float* dst = stage ? stage + 3ll * c.map_off : x + 3ll * c.dst_base;
     coords_round<E, B>(src, dst, c, begin, end, j0);
@@ -256,10 +256,9 @@ __device__ void coords_range(float* x, const I* maps, const DChunk& c, int begin
 }
 
 template <int E, int B, typename I>
-__device__ void forces_range(float* f, const I* maps, const DChunk& c, int begin, int end,
+__device__ void forces_range(float* f, const I* map, const DChunk& c, int begin, int end,
                              const int (&j0)[E], const float* stage = nullptr)
 {
-    const I* map = maps + c.map_off;
     float* tgt = f + 3ll * c.src_base;
     const float* from = stage ? stage + 3ll * c.map_off : f + 3ll * c.dst_base;
     forces_round<E, B>(from, tgt, begin, end, j0);
@@ -356,7 +355,7 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
             int jh[E], jt[E];
             load_map<E, B, I>(maps + c.map_off, c.hb, c.he, jh);
             load_map<E, B, I>(maps + c.map_off, c.tb, c.te, jt);
-            coords_range<E, B, I>(a.x, maps, c, c.hb, c.he, jh);
+            coords_range<E, B, I>(a.x, maps + c.map_off, c, c.hb, c.he, jh);
             if (c.wait_a) {
                 if (wave == 0) {
                     if (threadIdx.x == 0)
@@ -367,7 +366,7 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
                 }
                 __syncthreads();
             }
-            coords_range<E, B, I>(a.x, maps, c, c.tb, c.te, jt);
+            coords_range<E, B, I>(a.x, maps + c.map_off, c, c.tb, c.te, jt);
             // every wave's records are in L2 before thread 0 releases them
             if (c.flags & kChunkRelease)
                 wait_vm_idle();
@@ -396,7 +395,7 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
                 }
                 __syncthreads();
             }
-            forces_range<E, B, I>(a.f, maps, c, c.hb, c.he, j0);
+            forces_range<E, B, I>(a.f, maps + c.map_off, c, c.hb, c.he, j0);
             // every wave's sums are in L2 before thread 0 releases them
             if (c.flags & kChunkRelease)
                 wait_vm_idle();
@@ -466,10 +465,10 @@ __global__ __launch_bounds__(256) void wave_kernel(XArgs a)
             int jh[E], jt[E];
             load_map<E, W, I>(maps + c.map_off, c.hb, c.he, jh);
             load_map<E, W, I>(maps + c.map_off, c.tb, c.te, jt);
-            coords_range<E, W, I>(a.x, maps, c, c.hb, c.he, jh);
+            coords_range<E, W, I>(a.x, maps + c.map_off, c, c.hb, c.he, jh);
             if (c.wait_a)
                 wave_wait(a, a.xcnt, a.xneed, px, c.wait_a, c.S * P, 0u, 0, bump);
-            coords_range<E, W, I>(a.x, maps, c, c.tb, c.te, jt);
+            coords_range<E, W, I>(a.x, maps + c.map_off, c, c.tb, c.te, jt);
             if (c.flags & kChunkRelease)
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             held = !(c.flags & kChunkRelease);
@@ -485,7 +484,7 @@ __global__ __launch_bounds__(256) void wave_kernel(XArgs a)
             load_map<E, W, I>(maps + c.map_off, c.hb, c.he, j0);
             if (c.wait_a || c.wait_b)
                 wave_wait(a, a.fcnt, a.fneed, pf, c.wait_a, c.S * P, c.wait_b, c.R * P, bump);
-            forces_range<E, W, I>(a.f, maps, c, c.hb, c.he, j0);
+            forces_range<E, W, I>(a.f, maps + c.map_off, c, c.hb, c.he, j0);
             if (c.flags & kChunkRelease)
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             held = !(c.flags & kChunkRelease);
@@ -511,7 +510,10 @@ __global__ __launch_bounds__(256) void wave_kernel(XArgs a)
 struct PArgs {
     float* x;
     float* f;
-    const void* maps;  // map entries in the kernel's index type
+    const void* pad;   // chunk-aligned map entries in the kernel's index type
+    int32_t chunk;     // entries per chunk slot of pad
+    int32_t xpad;      // pad slot of the launch's first coordinate chunk
+    int32_t fpad;      // pad slot of the launch's first force chunk
     const DChunk* xchunks;
     const DChunk* fchunks;
     int32_t xbegin, nxb, fbegin;
@@ -540,25 +542,29 @@ __device__ __forceinline__ void publish_done(const PArgs& a)
 template <int E, int B, typename I>
 __global__ __launch_bounds__(B) void pulse_kernel(PArgs a)
 {
-    const I* maps = static_cast<const I*>(a.maps);
+    const I* pad = static_cast<const I*>(a.pad);
     publish_done(a);
     for (int b = (int)blockIdx.x; b < a.nb; b += (int)gridDim.x) {
-        if (b < a.nxb) {
-            const DChunk c = a.xchunks[a.xbegin + b];
-            int j0[E];
-            load_map<E, B, I>(maps + c.map_off, c.hb, c.he, j0);
-            coords_range<E, B, I>(a.x, maps, c, c.hb, c.he, j0, a.stage);
-            if (c.te > c.tb) {
-                int jt[E];
-                load_map<E, B, I>(maps + c.map_off, c.tb, c.te, jt);
-                coords_range<E, B, I>(a.x, maps, c, c.tb, c.te, jt, a.stage);
-            }
-        } else {
-            const DChunk c = a.fchunks[a.fbegin + b - a.nxb];
-            int j0[E];
-            load_map<E, B, I>(maps + c.map_off, c.hb, c.he, j0);
-            forces_range<E, B, I>(a.f, maps, c, c.hb, c.he, j0, a.stage);
-        }
+        const bool xs = b < a.nxb;
+        // the first round's map entries come from the chunk's pad slot,
+        // located by the chunk index alone, so their loads are in flight
+        // before the descriptor arrives (the pad holds zeros past every
+        // chunk and after the last one, so the loads stay in bounds)
+        const I* m = pad + (int64_t)(xs ? a.xpad + b : a.fpad + (b - a.nxb)) * a.chunk;
+        int j0[E];
+#pragma unroll
+        for (int e = 0; e < E; e++)
+            j0[e] = (int)m[e * B + (int)threadIdx.x];
+        const DChunk c = xs ? a.xchunks[a.xbegin + b] : a.fchunks[a.fbegin + (b - a.nxb)];
+#pragma unroll
+        for (int e = 0; e < E; e++)
+            if (e * B + (int)threadIdx.x >= c.he - c.hb)
+                j0[e] = -1;
+        // entry i of the chunk's map is at m[i - hb]
+        if (xs)
+            coords_range<E, B, I>(a.x, m - c.hb, c, c.hb, c.he, j0, a.stage);
+        else
+            forces_range<E, B, I>(a.f, m - c.hb, c, c.hb, c.he, j0, a.stage);
     }
 }
 
@@ -750,7 +756,20 @@ int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, 
     a.x = x;
     a.f = f;
     const bool narrow = use_narrow_maps(p);
-    a.maps = narrow ? (const void*)p->d_maps16 : (const void*)p->d_maps;
+    a.pad = narrow ? (const void*)t.d_pad16 : (const void*)t.d_pad;
+    a.chunk = t.chunk;
+    // pad slots: coordinate chunk k owns slot k; a force chunk uses the slot
+    // of the coordinate chunk of the same map slice (the tables slice every
+    // map alike, and list a pulse's chunks in the same order in both passes)
+    a.xpad = xb;
+    a.fpad = 0;
+    if (fe > fb) {
+        const int P = p->g.P;
+        int r = 0;
+        while (r + 1 < P && t.fpulse_begin[r + 1] <= fb)
+            r++;
+        a.fpad = t.xpulse_begin[P - 1 - r] + (fb - t.fpulse_begin[r]);
+    }
     a.xchunks = t.d_xch;
     a.fchunks = t.d_fch;
     a.xbegin = xb;

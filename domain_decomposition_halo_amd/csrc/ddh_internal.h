@@ -123,7 +123,16 @@ struct WorkTable {
     std::vector<int32_t> xpulse_begin, fpulse_begin;  // per pulse ranges (+1)
     DChunk* d_xch = nullptr;        // device copies
     DChunk* d_fch = nullptr;
+    // per-pulse launches: the map entries of coordinate chunk k at
+    // [k * chunk, k * chunk + size) (then zeros), so a block finds its
+    // entries from its chunk index alone and loads them while its
+    // descriptor is still in flight; kPadTail zero entries follow the last
+    // chunk. Force chunks use the slots of the coordinate chunk of the same
+    // map slice. 32-bit, and 16-bit when the maps have a 16-bit copy.
+    int32_t* d_pad = nullptr;
+    uint16_t* d_pad16 = nullptr;
 };
+constexpr int kPadTail = 4096;      // >= entries per round of any block
 
 struct Plan {
     int device = 0;
