@@ -154,7 +154,8 @@ def run_gpu(args, w):
     # pulse mode: a step pairs coordinate pulse q with force pulse P-1-q in
     # one launch, then one flag launch
     launches_per_step = {"step": 1, "split": 2,
-                         "staged": 2 * lay["n_pulses"] + 1}.get(variant, lay["n_pulses"] + 1)
+                         "staged": 2 * lay["n_pulses"] + 1}.get(
+        variant, lay["n_pulses"] + (0 if args.no_flags else 1))
     for _ in range(args.warmup):
         for _, fn, _ in calls:
             fn()
@@ -312,6 +313,28 @@ def run_gpu(args, w):
         del graph
         assert plan.check() == ddh.DDH_OK
 
+    # the latency floor of the same number of dependent launches: tiny
+    # one-block kernels (a one-element add) replayed from a graph
+    launch_floor = None
+    if not args.cold and not args.eager and variant != "staged":
+        tiny = torch.zeros(1, dtype=torch.float32, device=dev)
+        G = 50
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(G * launches_per_step):
+                tiny.add_(1.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(4):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        launch_floor = e0.elapsed_time(e1) * 1e3 / (4 * G)
+        del graph
+
     durs = sorted(durs)
     avg_step_gpu = sum(durs) / len(durs)
     step_bytes = sum(nb for _, _, nb in calls)
@@ -360,6 +383,13 @@ def run_gpu(args, w):
                       frac_at_min_bytes=round(min_bytes / avg_step_gpu / 1e9 / HBM_PEAK_GBS, 4),
                       avg_launch_us=round(avg_launch * 1e6, 3),
                       traffic_GBps=(round(traffic / avg_step_gpu / 1e9, 2) if traffic else None),
+                      latency=dict(
+                          hop_count=2 * lay["n_pulses"],
+                          dependent_stages=lay["n_pulses"] if variant in ("pulse", "step")
+                          else 2 * lay["n_pulses"],
+                          launches_per_step=launches_per_step,
+                          launch_floor_us=(round(launch_floor, 3) if launch_floor else None),
+                          hbm_floor_us=round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 3)),
                       median_step_us=round(durs[len(durs) // 2] * 1e6, 3),
                       p10_step_us=round(durs[len(durs) // 10] * 1e6, 3),
                       p90_step_us=round(durs[(9 * len(durs)) // 10] * 1e6, 3)),
@@ -669,6 +699,7 @@ def main():
                 "roofline_frac": g2["roofline"]["frac"], "achieved_GBps": g2["roofline"]["achieved"],
                 "map_entry_bytes": g2["roofline"]["map_entry_bytes"],
                 "frac_at_min_bytes": g2["roofline"]["frac_at_min_bytes"],
+                "latency": g2["roofline"]["latency"],
                 "passes": g2["passes"], "single_launch": g2["single"],
                 "without_flags": g2["without_flags"]}
     cpu = None
