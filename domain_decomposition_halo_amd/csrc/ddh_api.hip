@@ -13,9 +13,20 @@
 #include <cstring>
 #include <new>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "ddh_internal.h"
 
 namespace ddh {
+
+// A named host range around an entry point, seen by rocprofv3 --marker-trace
+// (a no-op without a profiler).
+struct Range {
+    explicit Range(const char* name) { roctxRangePushA(name); }
+    ~Range() { roctxRangePop(); }
+    Range(const Range&) = delete;
+    Range& operator=(const Range&) = delete;
+};
 
 static thread_local std::string g_last_error;
 
@@ -161,6 +172,7 @@ void ddh_plan_destroy(ddh_plan* p)
 
 int ddh_build_maps(ddh_plan* p, const float* xg, int32_t n_atoms, void* stream)
 {
+    Range range("ddh_build_maps");
     if (!p)
         return fail(DDH_EINVAL, "ddh_build_maps: null plan");
     return build_maps(p, xg, n_atoms, (hipStream_t)stream);
@@ -311,6 +323,7 @@ int ddh_local_ids(const ddh_plan* p, int32_t* ids_dev, int64_t capacity, void* s
 
 int ddh_gather_home(ddh_plan* p, const float* xg, float* x, int64_t cap, void* stream)
 {
+    Range range("ddh_gather_home");
     int rc = check_built(p);
     if (rc)
         return rc;
@@ -324,6 +337,7 @@ int ddh_gather_home(ddh_plan* p, const float* xg, float* x, int64_t cap, void* s
 
 int ddh_exchange_coords(ddh_plan* p, float* x, int64_t cap, void* stream)
 {
+    Range range("ddh_exchange_coords");
     int rc = check_built(p);
     if (rc)
         return rc;
@@ -335,6 +349,7 @@ int ddh_exchange_coords(ddh_plan* p, float* x, int64_t cap, void* stream)
 
 int ddh_exchange_forces(ddh_plan* p, float* f, int64_t cap, void* stream)
 {
+    Range range("ddh_exchange_forces");
     int rc = check_built(p);
     if (rc)
         return rc;
@@ -346,6 +361,7 @@ int ddh_exchange_forces(ddh_plan* p, float* f, int64_t cap, void* stream)
 
 int ddh_exchange_step(ddh_plan* p, float* x, float* f, int64_t cap, void* stream)
 {
+    Range range("ddh_exchange_step");
     int rc = check_built(p);
     if (rc)
         return rc;
@@ -380,6 +396,7 @@ int ddh_set_mode(ddh_plan* p, int32_t mode)
 
 int ddh_check(ddh_plan* p, void* stream)
 {
+    Range range("ddh_check");
     if (!p)
         return fail(DDH_EINVAL, "ddh_check: null plan");
     DDH_HIP(hipStreamSynchronize((hipStream_t)stream));
