@@ -13,8 +13,8 @@ without static first tickets); exact dyadic boxes with multi-pulse relay up
 to the most pulses a grid allows; seeded random decompositions; rebuilds for
 moving atoms; two plans on two streams; completion flags (counts, consumer
 streams waiting on them, turned off); device memory released by destroyed
-plans; empty and one-sided inputs, error paths and the bounded-wait timeout
-paths.
+plans; the exchange beside a compute load on another stream; empty and
+one-sided inputs, error paths and the bounded-wait timeout paths.
 """
 
 import numpy as np
@@ -218,7 +218,7 @@ def random_configs(n, seed):
     return out
 
 
-@pytest.mark.parametrize("cfg", random_configs(12, 2024))
+@pytest.mark.parametrize("cfg", random_configs(24, 2024))
 def test_random_decompositions(cfg):
     """Random grids, boxes, cutoffs (one to several pulses per dimension) and
     atom counts: layout, maps, ids, coordinates and forces bit-identical to
@@ -232,6 +232,42 @@ def test_random_decompositions(cfg):
         check_steps(g, ref, n, steps=2)
         check_steps(g, ref, n + 1, steps=1, fused_step=True)
         g.close()
+
+
+@pytest.mark.parametrize("mode,wave", [("fused", 0), ("fused", 1), ("pulse", 0)])
+def test_exchange_beside_a_compute_load(mode, wave, workload_plan):
+    """The exchange on one stream while a chain of matrix products (the local
+    non-bonded work's stand-in) holds compute units on another, both at
+    default priority: the fused launch's claimed tickets must still drain,
+    and every result stays bit-identical to the oracle."""
+    w, x, ref = workload_plan(2)
+    g = GpuPlan(x, **w.params(), mode=MODES[mode], wave=wave)
+    xl = g.new_coords()
+    fl = torch.empty((g.n_slots, 3), dtype=torch.float32, device="cuda")
+    a = torch.randn(2048, 2048, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(2048, 2048, device="cuda", dtype=torch.bfloat16)
+    side = torch.cuda.Stream()
+    rng = np.random.default_rng(500)
+    for r in range(5):
+        f0 = rng.normal(0, 10, size=(g.n_slots, 3)).astype(np.float32)
+        fl.copy_(torch.from_numpy(f0))
+        xl.copy_(g.new_coords())
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            c = a
+            for _ in range(4):
+                c = torch.mm(c, b)
+        for _ in range(3):                      # several steps overlap the load
+            g.plan.exchange_step(xl, fl)
+            if _ < 2:
+                fl.copy_(torch.from_numpy(f0))
+        torch.cuda.synchronize()
+        assert g.plan.check() == ddh.DDH_OK
+        assert np.array_equal(bits(xl.cpu().numpy()), bits(ref.x_local)), r
+        fr = f0.copy()
+        ref.exchange_forces(fr)
+        assert np.array_equal(bits(fl.cpu().numpy()), bits(fr)), r
+    g.close()
 
 
 def test_rebuild_after_atoms_move():
