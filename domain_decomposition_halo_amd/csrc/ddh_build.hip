@@ -37,6 +37,7 @@ namespace ddh {
 namespace {
 
 constexpr int kScanBlock = 1024;  // elements per scan block (4 per thread)
+constexpr int kSelTile = 1024;    // candidate slots per block of the slab selection
 
 struct AGeom {
     int n[3];
@@ -171,6 +172,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ bu
     if (a >= n_atoms)
         return;
     const int bk = bucket[a];
+    if (bk < 0)
+        return;  // a position outside the box: reported by the build
     const uint32_t pos = start[bk] + atomicAdd(fill + bk, 1u);
     sorted[pos] = a;
 }
@@ -261,73 +264,6 @@ __device__ bool selected(const SArgs& a, int S, int j, int& gid, int& mask)
     return (v - a.lo[S]) < a.rc;
 }
 
-__global__ __launch_bounds__(256) void select_count_kernel(SArgs a)
-{
-    __shared__ int s_send, s_split;
-    const int S = blockIdx.x;
-    if (threadIdx.x == 0) {
-        s_send = 0;
-        s_split = 0;
-    }
-    __syncthreads();
-    int c = 0, below = 0;
-    const int nh = a.nhome[S];
-    for (int j = a.first[S] + threadIdx.x; j < a.last[S]; j += 256) {
-        int gid, mask;
-        if (selected(a, S, j, gid, mask)) {
-            c++;
-            below += j < nh;
-        }
-    }
-    atomicAdd(&s_send, c);
-    atomicAdd(&s_split, below);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        a.cnt_send[S] = s_send;
-        a.cnt_split[S] = s_split;
-    }
-}
-
-// Ordered compaction of the selected candidates of sender S.
-__global__ __launch_bounds__(256) void select_write_kernel(SArgs a)
-{
-    __shared__ int wave_tot[4];
-    __shared__ int s_run;
-    const int S = blockIdx.x;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (threadIdx.x == 0)
-        s_run = 0;
-    __syncthreads();
-    const int first = a.first[S], last = a.last[S];
-    const int sbit = a.shiftbit[S] << a.d;
-    for (int base = first; base < last; base += 256) {
-        const int j = base + threadIdx.x;
-        int gid = -1, mask = 0;
-        const bool pred = j < last && selected(a, S, j, gid, mask);
-        const unsigned long long bal = __ballot(pred);
-        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0)
-            wave_tot[w] = __popcll(bal);
-        __syncthreads();
-        int off = s_run, tot = 0;
-        for (int q = 0; q < 4; q++) {
-            if (q < w)
-                off += wave_tot[q];
-            tot += wave_tot[q];
-        }
-        if (pred) {
-            const int idx = off + pre;
-            a.map_out[a.map_pos[S] + idx] = j;
-            a.out_gid[a.out_pos[S] + idx] = gid;
-            a.out_mask[a.out_pos[S] + idx] = mask | sbit;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0)
-            s_run += tot;
-        __syncthreads();
-    }
-}
-
 // slot_gid / home_slot for the home slots: r -> domain by binary search.
 __global__ __launch_bounds__(256) void fill_home_kernel(const int* __restrict__ home_gid,
                                                         const int* __restrict__ hs, int ndom,
@@ -365,6 +301,112 @@ __device__ __forceinline__ int segment_of(const int* prefix, int n, int e)
             hi = mid;
     }
     return lo;
+}
+
+// Slab selection of pulse p in tiles: sender S's candidate slots
+// [first[S], last[S]) are cut into tiles of kSelTile slots, and tile b of the
+// pulse (tiles of S numbered from tprefix[S]) is one block. Counting and
+// writing by tile fills the GPU whatever the number of domains; an exclusive
+// scan of the tile counts (in S order, then slot order) gives every tile its
+// first entry in the pulse's map buffer, so the compaction stays in slot
+// order.
+__device__ __forceinline__ void tile_of(const SArgs& a, const int* tprefix, int ndom, int b,
+                                        int& S, int& j0, int& j1)
+{
+    S = segment_of(tprefix, ndom, b);
+    j0 = a.first[S] + (b - tprefix[S]) * kSelTile;
+    j1 = min(j0 + kSelTile, a.last[S]);
+}
+
+__global__ __launch_bounds__(256) void select_count_kernel(SArgs a, const int* __restrict__ tprefix,
+                                                           int ndom, uint32_t* __restrict__ cnt,
+                                                           uint32_t* __restrict__ below)
+{
+    __shared__ int s_send, s_split;
+    int S, j0, j1;
+    tile_of(a, tprefix, ndom, blockIdx.x, S, j0, j1);
+    if (threadIdx.x == 0) {
+        s_send = 0;
+        s_split = 0;
+    }
+    __syncthreads();
+    int c = 0, bl = 0;
+    const int nh = a.nhome[S];
+    for (int j = j0 + threadIdx.x; j < j1; j += 256) {
+        int gid, mask;
+        if (selected(a, S, j, gid, mask)) {
+            c++;
+            bl += j < nh;
+        }
+    }
+    atomicAdd(&s_send, c);
+    atomicAdd(&s_split, bl);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        cnt[blockIdx.x] = (uint32_t)s_send;
+        below[blockIdx.x] = (uint32_t)s_split;
+    }
+}
+
+// Per-sender totals from the tile scan: entries sent and entries below the
+// split (home slots).
+__global__ __launch_bounds__(256) void select_totals_kernel(const int* __restrict__ tprefix,
+                                                            int ndom,
+                                                            const uint32_t* __restrict__ scan,
+                                                            const uint32_t* __restrict__ below,
+                                                            int* __restrict__ cnt_send,
+                                                            int* __restrict__ cnt_split)
+{
+    for (int S = blockIdx.x * 256 + threadIdx.x; S < ndom; S += gridDim.x * 256) {
+        cnt_send[S] = (int)(scan[tprefix[S + 1]] - scan[tprefix[S]]);
+        uint32_t bl = 0;
+        for (int b = tprefix[S]; b < tprefix[S + 1]; b++)
+            bl += below[b];
+        cnt_split[S] = (int)bl;
+    }
+}
+
+// Ordered compaction of one tile: its selected slots go to the sender's map
+// from the tile's scanned offset on, in slot order.
+__global__ __launch_bounds__(256) void select_write_kernel(SArgs a, const int* __restrict__ tprefix,
+                                                           int ndom,
+                                                           const uint32_t* __restrict__ scan)
+{
+    __shared__ int wave_tot[4];
+    __shared__ int s_run;
+    int S, j0, j1;
+    tile_of(a, tprefix, ndom, blockIdx.x, S, j0, j1);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (threadIdx.x == 0)
+        s_run = (int)(scan[blockIdx.x] - scan[tprefix[S]]);  // entries of S's earlier tiles
+    __syncthreads();
+    const int sbit = a.shiftbit[S] << a.d;
+    for (int base = j0; base < j1; base += 256) {
+        const int j = base + threadIdx.x;
+        int gid = -1, mask = 0;
+        const bool pred = j < j1 && selected(a, S, j, gid, mask);
+        const unsigned long long bal = __ballot(pred);
+        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0)
+            wave_tot[w] = __popcll(bal);
+        __syncthreads();
+        int off = s_run, tot = 0;
+        for (int q = 0; q < 4; q++) {
+            if (q < w)
+                off += wave_tot[q];
+            tot += wave_tot[q];
+        }
+        if (pred) {
+            const int idx = off + pre;
+            a.map_out[a.map_pos[S] + idx] = j;
+            a.out_gid[a.out_pos[S] + idx] = gid;
+            a.out_mask[a.out_pos[S] + idx] = mask | sbit;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_run += tot;
+        __syncthreads();
+    }
 }
 
 // Region q of every receiver: global id of each received slot, and the pulse
@@ -515,16 +557,67 @@ struct Scratch {
     }
 };
 
+// Device memory of the built state. Slot k of the plan's kept list serves the
+// k-th allocation of every build and is reused while it is large enough, so a
+// rebuild (every neighbour-search step) allocates nothing once sizes settle.
+// The plan frees the list when it is destroyed.
 template <class T>
 hipError_t owned_alloc(Plan* p, T** out, size_t n)
 {
+    const size_t bytes = (std::max<size_t>(n, 1) * sizeof(T) + 255) & ~size_t(255);
+    auto& kept = p->kept;
+    const size_t k = p->kept_next++;
+    if (k < kept.size() && kept[k].second >= bytes) {
+        *out = (T*)kept[k].first;
+        return hipSuccess;
+    }
     void* q = nullptr;
-    hipError_t e = hipMalloc(&q, std::max<size_t>(n, 1) * sizeof(T));
-    if (e == hipSuccess)
-        p->owned.push_back(q);
+    hipError_t e = hipMalloc(&q, bytes);
+    if (e != hipSuccess) {
+        *out = nullptr;
+        return e;
+    }
+    if (k < kept.size()) {
+        (void)hipFree(kept[k].first);
+        kept[k] = {q, bytes};
+    } else {
+        kept.emplace_back(q, bytes);
+    }
     *out = (T*)q;
-    return e;
+    return hipSuccess;
 }
+
+// Small host arrays gathered into one host-to-device copy: add() appends a
+// section (8-byte aligned) and returns its byte offset; send() copies the
+// whole blob into a scratch buffer, after which section k sits at
+// base + offset k. The host storage must live until the stream has run the
+// copy (the build synchronizes before it goes out of scope).
+struct Blob {
+    std::vector<uint64_t> words;
+    size_t bytes = 0;
+    template <class T>
+    size_t add(const T* src, size_t n)
+    {
+        const size_t off = (bytes + 7) & ~size_t(7);
+        bytes = off + n * sizeof(T);
+        words.resize((bytes + 7) / 8);
+        if (n)
+            std::memcpy(reinterpret_cast<char*>(words.data()) + off, src, n * sizeof(T));
+        return off;
+    }
+    template <class T>
+    size_t add(const std::vector<T>& v)
+    {
+        return add(v.data(), v.size());
+    }
+    hipError_t send(Scratch& sc, char** base, hipStream_t s)
+    {
+        hipError_t e = sc.alloc(base, std::max<size_t>(bytes, 8));
+        if (e != hipSuccess || bytes == 0)
+            return e;
+        return hipMemcpyAsync(*base, words.data(), bytes, hipMemcpyHostToDevice, s);
+    }
+};
 
 template <class T>
 hipError_t upload(T* dst, const std::vector<T>& src, hipStream_t s)
@@ -557,6 +650,10 @@ void free_scratch(Plan* p)
     for (auto& kv : p->scratch)
         (void)hipFree(kv.first);
     p->scratch.clear();
+    for (auto& kv : p->kept)
+        (void)hipFree(kv.first);
+    p->kept.clear();
+    p->kept_next = 0;
 }
 
 void free_built(Plan* p)
@@ -567,6 +664,7 @@ void free_built(Plan* p)
     for (void* q : p->owned)
         (void)hipFree(q);
     p->owned.clear();
+    p->kept_next = 0;
     p->d_maps = p->d_slot_gid = p->d_home_gid = p->d_home_slot = nullptr;
     p->d_maps16 = nullptr;
     p->fused = WorkTable{};
@@ -769,16 +867,13 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         cellbase[D] = (int)acc;
     }
     const int nb = cellbase[D];
-    float* d_b;
-    int *d_ncell, *d_cellbase;
-    DDH_HIP(sc.alloc(&d_b, bcat.size()));
-    DDH_HIP(sc.alloc(&d_ncell, ncat.size()));
-    DDH_HIP(sc.alloc(&d_cellbase, cellbase.size()));
-    DDH_HIP(upload(d_b, bcat, s));
-    DDH_HIP(upload(d_ncell, ncat, s));
-    DDH_HIP(upload(d_cellbase, cellbase, s));
-    ag.b = d_b;
-    ag.ncell = d_ncell;
+    Blob geo;  // alive until the first sync below
+    const size_t o_b = geo.add(bcat), o_ncell = geo.add(ncat), o_cellbase = geo.add(cellbase);
+    char* d_geo;
+    DDH_HIP(geo.send(sc, &d_geo, s));
+    const int* d_cellbase = (const int*)(d_geo + o_cellbase);
+    ag.b = (const float*)(d_geo + o_b);
+    ag.ncell = (const int*)(d_geo + o_ncell);
     ag.cellbase = d_cellbase;
 
     // ---- 1-2: home assignment and cell sort
@@ -798,11 +893,8 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         hipLaunchKernelGGL(assign_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s, xg, n_atoms, ag,
                            d_bucket, d_count, d_err);
     DDH_HIP(hipGetLastError());
-    uint32_t herr = 0;
-    DDH_HIP(hipMemcpyAsync(&herr, d_err, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-    DDH_HIP(hipStreamSynchronize(s));
-    if (herr)
-        return fail(DDH_EINVAL, "ddh_build_maps: a position is outside [0, L) or not a number");
+    // atoms outside the box have no bucket and are skipped until the error
+    // word is read with the home counts below
     int rcode = scan_exclusive(sc, d_count, nb, d_start, s);
     if (rcode)
         return rcode;
@@ -816,8 +908,12 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                        D, d_hs);
     DDH_HIP(hipGetLastError());
     std::vector<int> hs((size_t)D + 1);
+    uint32_t herr = 0;
     DDH_HIP(hipMemcpyAsync(hs.data(), d_hs, sizeof(int) * (D + 1), hipMemcpyDeviceToHost, s));
+    DDH_HIP(hipMemcpyAsync(&herr, d_err, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
     DDH_HIP(hipStreamSynchronize(s));
+    if (herr)
+        return fail(DDH_EINVAL, "ddh_build_maps: a position is outside [0, L) or not a number");
 
     p->nhome.assign(D, 0);
     p->ntotal.assign(D, 0);
@@ -841,24 +937,13 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     std::vector<int*> mapp((size_t)std::max(P, 1), nullptr);
     std::vector<std::vector<int>> mpos((size_t)P), rsprefix((size_t)P);
     std::vector<int> total((size_t)P, 0);
-    int *d_roff_at, *d_rsize_at, *d_rstart, *d_cnt_send, *d_cnt_split;
-    int *d_first, *d_last, *d_shiftbit, *d_map_pos, *d_out_pos;
-    float* d_lo;
-    int **d_rgid, **d_rmask;
-    DDH_HIP(sc.alloc(&d_roff_at, DP));
-    DDH_HIP(sc.alloc(&d_rsize_at, DP));
-    DDH_HIP(sc.alloc(&d_rstart, DP));
+    int *d_cnt_send, *d_cnt_split;
     DDH_HIP(sc.alloc(&d_cnt_send, (size_t)D));
     DDH_HIP(sc.alloc(&d_cnt_split, (size_t)D));
-    DDH_HIP(sc.alloc(&d_first, (size_t)D));
-    DDH_HIP(sc.alloc(&d_last, (size_t)D));
-    DDH_HIP(sc.alloc(&d_shiftbit, (size_t)D));
-    DDH_HIP(sc.alloc(&d_map_pos, (size_t)D));
-    DDH_HIP(sc.alloc(&d_out_pos, (size_t)D));
-    DDH_HIP(sc.alloc(&d_lo, (size_t)D));
-    DDH_HIP(sc.alloc(&d_rgid, (size_t)std::max(P, 1)));
-    DDH_HIP(sc.alloc(&d_rmask, (size_t)std::max(P, 1)));
 
+    // the pulses' upload blobs stay alive until the layout's sync
+    std::vector<Blob> blobs;
+    blobs.reserve(2 * (size_t)P);
     for (int q = 0; q < P; q++) {
         const int d = g.pdim[q], k = g.pk[q];
         std::vector<float> lo(D);
@@ -879,15 +964,30 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                 last[S] = first[S] + rsize_at[S * P + q - 1];
             }
         }
-        DDH_HIP(upload(d_lo, lo, s));
-        DDH_HIP(upload(d_first, first, s));
-        DDH_HIP(upload(d_last, last, s));
-        DDH_HIP(upload(d_shiftbit, sbit, s));
-        DDH_HIP(upload(d_roff_at, roff_at, s));
-        DDH_HIP(upload(d_rsize_at, rsize_at, s));
-        DDH_HIP(upload(d_rstart, rstart, s));
-        DDH_HIP(upload(d_rgid, rgid, s));
-        DDH_HIP(upload(d_rmask, rmask, s));
+        // tiles of kSelTile candidate slots, numbered sender by sender
+        std::vector<int> tprefix((size_t)D + 1, 0);
+        for (int S = 0; S < D; S++)
+            tprefix[S + 1] = tprefix[S] + (last[S] - first[S] + kSelTile - 1) / kSelTile;
+        const int T = tprefix[D];
+        // the pulse's small tables in one copy
+        blobs.emplace_back();
+        Blob& in = blobs.back();
+        const size_t o_lo = in.add(lo), o_first = in.add(first), o_last = in.add(last);
+        const size_t o_sbit = in.add(sbit), o_roff = in.add(roff_at), o_rsize = in.add(rsize_at);
+        const size_t o_rstart = in.add(rstart), o_rgid = in.add(rgid), o_rmask = in.add(rmask);
+        const size_t o_tprefix = in.add(tprefix);
+        char* d_in;
+        DDH_HIP(in.send(sc, &d_in, s));
+        const float* d_lo = (const float*)(d_in + o_lo);
+        const int* d_first = (const int*)(d_in + o_first);
+        const int* d_last = (const int*)(d_in + o_last);
+        const int* d_shiftbit = (const int*)(d_in + o_sbit);
+        const int* d_roff_at = (const int*)(d_in + o_roff);
+        const int* d_rsize_at = (const int*)(d_in + o_rsize);
+        const int* d_rstart = (const int*)(d_in + o_rstart);
+        int* const* d_rgid = (int* const*)(d_in + o_rgid);
+        int* const* d_rmask = (int* const*)(d_in + o_rmask);
+        const int* d_tprefix = (const int*)(d_in + o_tprefix);
 
         SArgs a{};
         a.p = q;
@@ -910,7 +1010,19 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         a.shiftbit = d_shiftbit;
         a.cnt_send = d_cnt_send;
         a.cnt_split = d_cnt_split;
-        hipLaunchKernelGGL(select_count_kernel, dim3(D), dim3(256), 0, s, a);
+        uint32_t *d_tcnt, *d_tbelow, *d_tscan;
+        DDH_HIP(sc.alloc(&d_tcnt, (size_t)T + 1));
+        DDH_HIP(sc.alloc(&d_tbelow, (size_t)T + 1));
+        DDH_HIP(sc.alloc(&d_tscan, (size_t)T + 1));
+        if (T > 0)
+            hipLaunchKernelGGL(select_count_kernel, dim3(T), dim3(256), 0, s, a, d_tprefix, D,
+                               d_tcnt, d_tbelow);
+        DDH_HIP(hipGetLastError());
+        rcode = scan_exclusive(sc, d_tcnt, T, d_tscan, s);
+        if (rcode)
+            return rcode;
+        hipLaunchKernelGGL(select_totals_kernel, dim3(std::min(blocks(D), 1024)), dim3(256), 0, s,
+                           d_tprefix, D, d_tscan, d_tbelow, d_cnt_send, d_cnt_split);
         DDH_HIP(hipGetLastError());
         std::vector<int> cs(D), cp(D);
         DDH_HIP(hipMemcpyAsync(cs.data(), d_cnt_send, sizeof(int) * D, hipMemcpyDeviceToHost, s));
@@ -952,16 +1064,20 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         std::vector<int> opos(D);
         for (int S = 0; S < D; S++)
             opos[S] = rstart[rcv[S] * P + q];
-        DDH_HIP(upload(d_map_pos, mpos[q], s));
-        DDH_HIP(upload(d_out_pos, opos, s));
-        a.map_pos = d_map_pos;
+        blobs.emplace_back();
+        Blob& pos = blobs.back();
+        const size_t o_mpos = pos.add(mpos[q]), o_opos = pos.add(opos);
+        char* d_pos;
+        DDH_HIP(pos.send(sc, &d_pos, s));
+        a.map_pos = (const int*)(d_pos + o_mpos);
         a.map_out = mapp[q];
-        a.out_pos = d_out_pos;
+        a.out_pos = (const int*)(d_pos + o_opos);
         a.out_gid = rgid[q];
         a.out_mask = rmask[q];
-        hipLaunchKernelGGL(select_write_kernel, dim3(D), dim3(256), 0, s, a);
+        if (T > 0)
+            hipLaunchKernelGGL(select_write_kernel, dim3(T), dim3(256), 0, s, a, d_tprefix, D,
+                               d_tscan);
         DDH_HIP(hipGetLastError());
-        DDH_HIP(hipStreamSynchronize(s));  // per-pulse host arrays are reused
     }
 
     // ---- 4: final layout
@@ -1014,31 +1130,34 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     DDH_HIP(sc.alloc(&d_rid, (size_t)p->n_slots));
     DDH_HIP(hipMemsetAsync(d_rid, 0xff, (size_t)p->n_slots, s));
     std::vector<int> base32(D);
-    int* d_base;
+    const int* d_base;
+    Blob lay;  // alive until the sync below
     {
         for (int Dm = 0; Dm < D; Dm++)
             base32[Dm] = (int)p->base[Dm];
-        DDH_HIP(sc.alloc(&d_base, (size_t)D));
-        DDH_HIP(upload(d_base, base32, s));
+        // slot bases, and per pulse the region prefix and the receivers'
+        // first region slots, in one copy
+        const size_t o_base = lay.add(base32);
+        std::vector<size_t> o_rs((size_t)P), o_dst((size_t)P);
+        std::vector<int> dst(D);
+        for (int q = 0; q < P; q++) {
+            for (int R = 0; R < D; R++)
+                dst[R] = base32[R] + roff_at[R * P + q];
+            o_rs[q] = lay.add(rsprefix[q]);
+            o_dst[q] = lay.add(dst);
+        }
+        char* d_lay;
+        DDH_HIP(lay.send(sc, &d_lay, s));
+        d_base = (const int*)(d_lay + o_base);
         if (n_atoms > 0)
             hipLaunchKernelGGL(fill_home_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s,
                                p->d_home_gid, d_hs, D, d_base, n_atoms, p->d_slot_gid,
                                p->d_home_slot);
-        std::vector<int*> d_rs((size_t)P), d_dst((size_t)P);
-        std::vector<std::vector<int>> dsts((size_t)P);  // alive until the sync below
         for (int q = 0; q < P; q++) {
-            std::vector<int>& dst = dsts[q];
-            dst.resize(D);
-            for (int R = 0; R < D; R++)
-                dst[R] = base32[R] + roff_at[R * P + q];
-            DDH_HIP(sc.alloc(&d_rs[q], (size_t)D + 1));
-            DDH_HIP(sc.alloc(&d_dst[q], (size_t)D));
-            DDH_HIP(upload(d_rs[q], rsprefix[q], s));
-            DDH_HIP(upload(d_dst[q], dst, s));
             if (total[q] > 0)
                 hipLaunchKernelGGL(fill_region_kernel, dim3(blocks(total[q])), dim3(256), 0, s,
-                                   rgid[q], total[q], d_rs[q], D, d_dst[q], p->d_slot_gid, d_rid,
-                                   q);
+                                   rgid[q], total[q], (const int*)(d_lay + o_rs[q]), D,
+                                   (const int*)(d_lay + o_dst[q]), p->d_slot_gid, d_rid, q);
         }
         DDH_HIP(hipGetLastError());
         DDH_HIP(hipStreamSynchronize(s));
@@ -1128,8 +1247,9 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     p->d_xneed = p->d_fcnt + DP;
     p->d_fneed = p->d_xneed + DP;
     p->d_pflag = p->d_fneed + DP;
+    // d_fneed follows d_xneed: one copy of both
+    xneed.insert(xneed.end(), fneed.begin(), fneed.end());
     DDH_HIP(upload(p->d_xneed, xneed, s));
-    DDH_HIP(upload(p->d_fneed, fneed, s));
     DDH_HIP(hipStreamSynchronize(s));
     p->built = true;
     p->build_failed = false;

@@ -193,7 +193,9 @@ struct Plan {
     uint32_t* d_pflag = nullptr;   // per-pulse completion flags: [p] coordinates,
                                    // [DDH_MAX_PULSES + p] forces (epoch values)
     float* d_stage = nullptr;      // staging buffer of DDH_MODE_STAGED (first use)
-    std::vector<void*> owned;      // every hipMalloc of the built state
+    std::vector<void*> owned;      // allocations made after the build (staging buffer)
+    std::vector<std::pair<void*, size_t>> kept;     // built state, reused by later builds
+    size_t kept_next = 0;          // next slot of kept during a build
     std::vector<std::pair<void*, size_t>> scratch;  // build scratch, kept between builds
     bool build_failed = false;     // the last build returned an error midway
 
