@@ -52,6 +52,7 @@ struct AGeom {
 
 __global__ __launch_bounds__(256) void assign_kernel(const float* __restrict__ xg, int n_atoms,
                                                      AGeom g, int* __restrict__ bucket,
+                                                     uint32_t* __restrict__ rank,
                                                      uint32_t* __restrict__ count,
                                                      uint32_t* __restrict__ err)
 {
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256) void assign_kernel(const float* __restrict__ x
     const int key = cc[0] + nc[0] * (cc[1] + nc[1] * cc[2]);
     const int bk = g.cellbase[D] + key;
     bucket[a] = bk;
-    atomicAdd(count + bk, 1u);
+    rank[a] = atomicAdd(count + bk, 1u);  // arrival order in the bucket
 }
 
 // ---- exclusive scan of uint32 counts: out[i] = sum(in[0..i)), out[n] = total
@@ -163,9 +164,12 @@ __global__ __launch_bounds__(256) void scan_apply_kernel(const uint32_t* __restr
     }
 }
 
-__global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ bucket, int n_atoms,
+// Every atom to its bucket's range, at its arrival rank (an arbitrary order
+// inside the bucket: the per-cell sort by global id fixes it).
+__global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ bucket,
+                                                      const uint32_t* __restrict__ rank,
+                                                      int n_atoms,
                                                       const uint32_t* __restrict__ start,
-                                                      uint32_t* __restrict__ fill,
                                                       int* __restrict__ sorted)
 {
     const int a = blockIdx.x * 256 + threadIdx.x;
@@ -174,8 +178,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ bu
     const int bk = bucket[a];
     if (bk < 0)
         return;  // a position outside the box: reported by the build
-    const uint32_t pos = start[bk] + atomicAdd(fill + bk, 1u);
-    sorted[pos] = a;
+    sorted[start[bk] + rank[a]] = a;
 }
 
 // Order each cell's atoms by global id (cells hold ~10 atoms: insertion sort).
@@ -210,7 +213,7 @@ __global__ void home_start_kernel(const uint32_t* __restrict__ start, const int*
 struct SArgs {
     int p, d, P;
     float L_d, rc;
-    const float* xg;
+    const float* xhome;   // home positions in slot order (float3)
     const int* home_gid;
     const int* home_start;
     const int* nhome;
@@ -218,7 +221,8 @@ struct SArgs {
     const int* rsize_at;  // [S * P + q] size of S's region q
     const int* rstart;    // [S * P + q] index of S's region q in pulse q's storage
     int* const* rgid;     // per pulse q: global ids of received records
-    int* const* rmask;    // per pulse q: shift masks of received records
+    float* const* rxyz;   // per pulse q: positions of received records (float3,
+                          // periodic shifts applied)
     const float* lo;      // per S: lower boundary along d
     const int* first;     // per S: candidate slot range
     const int* last;
@@ -229,15 +233,19 @@ struct SArgs {
     int* map_out;
     const int* out_pos;   // per S: first record of its region at R
     int* out_gid;
-    int* out_mask;
+    float* out_xyz;
 };
 
-__device__ void resolve(const SArgs& a, int S, int j, int& gid, int& mask)
+// Candidate slot j of sender S: its global id and its coordinates. Home
+// slots read the slot-ordered home positions, received slots the records of
+// the pulse that delivered them, where the periodic shift is already applied
+// (the value the coordinate pass leaves in the slot).
+__device__ const float* resolve(const SArgs& a, int S, int j, int& gid)
 {
     if (j < a.nhome[S]) {
-        gid = a.home_gid[a.home_start[S] + j];
-        mask = 0;
-        return;
+        const int r = a.home_start[S] + j;
+        gid = a.home_gid[r];
+        return a.xhome + 3ll * r;
     }
     for (int q = 0; q < a.p; q++) {
         const int o = a.roff_at[S * a.P + q];
@@ -245,23 +253,20 @@ __device__ void resolve(const SArgs& a, int S, int j, int& gid, int& mask)
         if (j >= o && j < o + n) {
             const int idx = a.rstart[S * a.P + q] + (j - o);
             gid = a.rgid[q][idx];
-            mask = a.rmask[q][idx];
-            return;
+            return a.rxyz[q] + 3ll * idx;
         }
     }
     gid = -1;
-    mask = 0;
+    return nullptr;
 }
 
-__device__ bool selected(const SArgs& a, int S, int j, int& gid, int& mask)
+// The slab test of the pulse's dimension d: fl(x_d - lo_d(S)) < rc.
+__device__ bool selected(const SArgs& a, int S, int j, int& gid, const float*& pos)
 {
-    resolve(a, S, j, gid, mask);
-    if (gid < 0)
+    pos = resolve(a, S, j, gid);
+    if (!pos)
         return false;
-    float v = a.xg[3ll * gid + a.d];
-    if ((mask >> a.d) & 1)
-        v = v + a.L_d;
-    return (v - a.lo[S]) < a.rc;
+    return (pos[a.d] - a.lo[S]) < a.rc;
 }
 
 // slot_gid / home_slot for the home slots: r -> domain by binary search.
@@ -333,8 +338,9 @@ __global__ __launch_bounds__(256) void select_count_kernel(SArgs a, const int* _
     int c = 0, bl = 0;
     const int nh = a.nhome[S];
     for (int j = j0 + threadIdx.x; j < j1; j += 256) {
-        int gid, mask;
-        if (selected(a, S, j, gid, mask)) {
+        int gid;
+        const float* pos;
+        if (selected(a, S, j, gid, pos)) {
             c++;
             bl += j < nh;
         }
@@ -380,11 +386,12 @@ __global__ __launch_bounds__(256) void select_write_kernel(SArgs a, const int* _
     if (threadIdx.x == 0)
         s_run = (int)(scan[blockIdx.x] - scan[tprefix[S]]);  // entries of S's earlier tiles
     __syncthreads();
-    const int sbit = a.shiftbit[S] << a.d;
+    const bool shift = a.shiftbit[S] != 0;
     for (int base = j0; base < j1; base += 256) {
         const int j = base + threadIdx.x;
-        int gid = -1, mask = 0;
-        const bool pred = j < j1 && selected(a, S, j, gid, mask);
+        int gid = -1;
+        const float* pos = nullptr;
+        const bool pred = j < j1 && selected(a, S, j, gid, pos);
         const unsigned long long bal = __ballot(pred);
         const int pre = __popcll(bal & ((1ull << lane) - 1ull));
         if (lane == 0)
@@ -400,7 +407,15 @@ __global__ __launch_bounds__(256) void select_write_kernel(SArgs a, const int* _
             const int idx = off + pre;
             a.map_out[a.map_pos[S] + idx] = j;
             a.out_gid[a.out_pos[S] + idx] = gid;
-            a.out_mask[a.out_pos[S] + idx] = mask | sbit;
+            // the record as the receiver gets it: + L_d on component d when
+            // the sender sits at index 0 of d
+            float* o = a.out_xyz + 3ll * (a.out_pos[S] + idx);
+            for (int c = 0; c < 3; c++) {
+                float v = pos[c];
+                if (c == a.d && shift)
+                    v = v + a.L_d;
+                o[c] = v;
+            }
         }
         __syncthreads();
         if (threadIdx.x == 0)
@@ -434,6 +449,21 @@ __global__ __launch_bounds__(256) void narrow_maps_kernel(const int32_t* __restr
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n)
         out[i] = (uint16_t)maps[i];
+}
+
+// Home positions in slot order: xhome[r] = xg[home_gid[r]] (float3).
+__global__ __launch_bounds__(256) void gather_xhome_kernel(const float* __restrict__ xg,
+                                                           const int* __restrict__ home_gid,
+                                                           int n, float* __restrict__ xhome)
+{
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= n)
+        return;
+    const float* src = xg + 3ll * home_gid[r];
+    float* dst = xhome + 3ll * r;
+    dst[0] = src[0];
+    dst[1] = src[1];
+    dst[2] = src[2];
 }
 
 // Chunk-aligned copy of the maps for the per-pulse launches: block b writes
@@ -878,20 +908,19 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
 
     // ---- 1-2: home assignment and cell sort
     int *d_bucket, *d_hs;
-    uint32_t *d_count, *d_start, *d_fill, *d_err;
+    uint32_t *d_count, *d_start, *d_rank, *d_err;
     DDH_HIP(sc.alloc(&d_bucket, (size_t)n_atoms));
+    DDH_HIP(sc.alloc(&d_rank, (size_t)n_atoms));
     DDH_HIP(sc.alloc(&d_count, (size_t)nb + 1));
     DDH_HIP(sc.alloc(&d_start, (size_t)nb + 1));
-    DDH_HIP(sc.alloc(&d_fill, (size_t)nb + 1));
     DDH_HIP(sc.alloc(&d_err, 1));
     DDH_HIP(sc.alloc(&d_hs, (size_t)D + 1));
     DDH_HIP(owned_alloc(p, &p->d_home_gid, (size_t)n_atoms));
     DDH_HIP(hipMemsetAsync(d_count, 0, sizeof(uint32_t) * ((size_t)nb + 1), s));
-    DDH_HIP(hipMemsetAsync(d_fill, 0, sizeof(uint32_t) * ((size_t)nb + 1), s));
     DDH_HIP(hipMemsetAsync(d_err, 0, sizeof(uint32_t), s));
     if (n_atoms > 0)
         hipLaunchKernelGGL(assign_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s, xg, n_atoms, ag,
-                           d_bucket, d_count, d_err);
+                           d_bucket, d_rank, d_count, d_err);
     DDH_HIP(hipGetLastError());
     // atoms outside the box have no bucket and are skipped until the error
     // word is read with the home counts below
@@ -899,8 +928,8 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     if (rcode)
         return rcode;
     if (n_atoms > 0) {
-        hipLaunchKernelGGL(scatter_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s, d_bucket, n_atoms,
-                           d_start, d_fill, p->d_home_gid);
+        hipLaunchKernelGGL(scatter_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s, d_bucket, d_rank,
+                           n_atoms, d_start, p->d_home_gid);
         hipLaunchKernelGGL(sort_cells_kernel, dim3(blocks(nb)), dim3(256), 0, s, d_start, nb,
                            p->d_home_gid);
     }
@@ -914,6 +943,13 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     DDH_HIP(hipStreamSynchronize(s));
     if (herr)
         return fail(DDH_EINVAL, "ddh_build_maps: a position is outside [0, L) or not a number");
+    // home positions in slot order: the slab tests read them in order
+    float* d_xhome;
+    DDH_HIP(sc.alloc(&d_xhome, 3 * (size_t)n_atoms));
+    if (n_atoms > 0)
+        hipLaunchKernelGGL(gather_xhome_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s, xg,
+                           p->d_home_gid, n_atoms, d_xhome);
+    DDH_HIP(hipGetLastError());
 
     p->nhome.assign(D, 0);
     p->ntotal.assign(D, 0);
@@ -933,7 +969,8 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     p->roff.assign(DP, 0);
     p->shift.assign(DP, 0);
     std::vector<int> roff_at(DP, 0), rsize_at(DP, 0), rstart(DP, 0);
-    std::vector<int*> rgid((size_t)std::max(P, 1), nullptr), rmask((size_t)std::max(P, 1), nullptr);
+    std::vector<int*> rgid((size_t)std::max(P, 1), nullptr);
+    std::vector<float*> rxyz((size_t)std::max(P, 1), nullptr);
     std::vector<int*> mapp((size_t)std::max(P, 1), nullptr);
     std::vector<std::vector<int>> mpos((size_t)P), rsprefix((size_t)P);
     std::vector<int> total((size_t)P, 0);
@@ -974,7 +1011,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         Blob& in = blobs.back();
         const size_t o_lo = in.add(lo), o_first = in.add(first), o_last = in.add(last);
         const size_t o_sbit = in.add(sbit), o_roff = in.add(roff_at), o_rsize = in.add(rsize_at);
-        const size_t o_rstart = in.add(rstart), o_rgid = in.add(rgid), o_rmask = in.add(rmask);
+        const size_t o_rstart = in.add(rstart), o_rgid = in.add(rgid), o_rxyz = in.add(rxyz);
         const size_t o_tprefix = in.add(tprefix);
         char* d_in;
         DDH_HIP(in.send(sc, &d_in, s));
@@ -986,7 +1023,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         const int* d_rsize_at = (const int*)(d_in + o_rsize);
         const int* d_rstart = (const int*)(d_in + o_rstart);
         int* const* d_rgid = (int* const*)(d_in + o_rgid);
-        int* const* d_rmask = (int* const*)(d_in + o_rmask);
+        float* const* d_rxyz = (float* const*)(d_in + o_rxyz);
         const int* d_tprefix = (const int*)(d_in + o_tprefix);
 
         SArgs a{};
@@ -995,7 +1032,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         a.P = P;
         a.L_d = g.L[d];
         a.rc = g.rc;
-        a.xg = xg;
+        a.xhome = d_xhome;
         a.home_gid = p->d_home_gid;
         a.home_start = d_hs;
         a.nhome = d_nhome;
@@ -1003,7 +1040,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         a.rsize_at = d_rsize_at;
         a.rstart = d_rstart;
         a.rgid = d_rgid;
-        a.rmask = d_rmask;
+        a.rxyz = d_rxyz;
         a.lo = d_lo;
         a.first = d_first;
         a.last = d_last;
@@ -1059,7 +1096,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         if (mt > INT32_MAX)
             return fail(DDH_ECAPACITY, "ddh_build_maps: a pulse exceeds 2^31 entries");
         DDH_HIP(sc.alloc(&rgid[q], (size_t)mt));
-        DDH_HIP(sc.alloc(&rmask[q], (size_t)mt));
+        DDH_HIP(sc.alloc(&rxyz[q], 3 * (size_t)mt));
         DDH_HIP(sc.alloc(&mapp[q], (size_t)mt));
         std::vector<int> opos(D);
         for (int S = 0; S < D; S++)
@@ -1073,7 +1110,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         a.map_out = mapp[q];
         a.out_pos = (const int*)(d_pos + o_opos);
         a.out_gid = rgid[q];
-        a.out_mask = rmask[q];
+        a.out_xyz = rxyz[q];
         if (T > 0)
             hipLaunchKernelGGL(select_write_kernel, dim3(T), dim3(256), 0, s, a, d_tprefix, D,
                                d_tscan);
