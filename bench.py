@@ -398,6 +398,37 @@ def run_gpu(args, w):
     return res
 
 
+# ------------------------------------------------------------- map builds
+
+def run_builds(args, w):
+    """The map build alone, as at every neighbour-search step: one plan
+    rebuilt --steps times from the same positions (after one warm-up build);
+    host wall time per build, the device work included."""
+    import torch
+
+    import domain_decomposition_halo_amd as ddh
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    xg = torch.from_numpy(W.positions(w)).to(dev)
+    plan = ddh.Plan(**w.params())
+    plan.build_maps(xg)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.steps):
+        t0 = time.perf_counter()
+        plan.build_maps(xg)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    plan.close()
+    times.sort()
+    return {"workload": w.name, "builds": len(times),
+            "median_ms": round(times[len(times) // 2] * 1e3, 3),
+            "mean_ms": round(sum(times) / len(times) * 1e3, 3),
+            "min_ms": round(times[0] * 1e3, 3)}
+
+
 # ------------------------------------------------------ overlap with compute
 
 def run_overlap(args, w):
@@ -633,6 +664,8 @@ def main():
     ap.add_argument("--cold", action="store_true", help="evict caches before every step")
     ap.add_argument("--eager", action="store_true",
                     help="enqueue every step from the host (no graph replay)")
+    ap.add_argument("--build-only", action="store_true",
+                    help="time the map build alone (--steps builds of one plan)")
     ap.add_argument("--overlap", action="store_true",
                     help="time the step beside a compute load on a second stream "
                          "(prints one JSON object of its own)")
@@ -680,6 +713,9 @@ def main():
 
     if args.overlap:
         print(json.dumps({"overlap": run_overlap(args, w)}), flush=True)
+        return
+    if args.build_only:
+        print(json.dumps({"map_build": run_builds(args, w)}), flush=True)
         return
     gpu = run_gpu(args, w)
     also = {}

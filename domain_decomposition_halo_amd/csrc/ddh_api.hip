@@ -13,20 +13,9 @@
 #include <cstring>
 #include <new>
 
-#include <rocprofiler-sdk-roctx/roctx.h>
-
 #include "ddh_internal.h"
 
 namespace ddh {
-
-// A named host range around an entry point, seen by rocprofv3 --marker-trace
-// (a no-op without a profiler).
-struct Range {
-    explicit Range(const char* name) { roctxRangePushA(name); }
-    ~Range() { roctxRangePop(); }
-    Range(const Range&) = delete;
-    Range& operator=(const Range&) = delete;
-};
 
 static thread_local std::string g_last_error;
 

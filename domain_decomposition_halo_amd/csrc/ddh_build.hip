@@ -858,8 +858,26 @@ static int pulse_chunk(const Plan* p)
     return smallest / 512 >= p->n_cu / 2 ? 512 : 256;
 }
 
+// Consecutive named host ranges for the phases of one build.
+struct Phases {
+    bool open = false;
+    void next(const char* name)
+    {
+        if (open)
+            roctxRangePop();
+        roctxRangePushA(name);
+        open = true;
+    }
+    ~Phases()
+    {
+        if (open)
+            roctxRangePop();
+    }
+};
+
 int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
 {
+    Phases ph;
     free_built(p);
     Geometry& g = p->g;
     const int D = g.ndom, P = g.P;
@@ -871,6 +889,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     Scratch sc(p);
 
     // ---- geometry tables
+    ph.next("build: geometry");
     std::vector<float> bcat;
     std::vector<int> ncat;
     AGeom ag{};
@@ -907,6 +926,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     ag.cellbase = d_cellbase;
 
     // ---- 1-2: home assignment and cell sort
+    ph.next("build: assign and sort");
     int *d_bucket, *d_hs;
     uint32_t *d_count, *d_start, *d_rank, *d_err;
     DDH_HIP(sc.alloc(&d_bucket, (size_t)n_atoms));
@@ -962,6 +982,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     DDH_HIP(upload(d_nhome, p->nhome, s));
 
     // ---- 3: pulses
+    ph.next("build: pulses");
     const size_t DP = (size_t)D * P;
     p->send.assign(DP, 0);
     p->split.assign(DP, 0);
@@ -1118,6 +1139,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     }
 
     // ---- 4: final layout
+    ph.next("build: layout");
     p->base.assign(D, 0);
     int64_t acc = 0;
     for (int Dm = 0; Dm < D; Dm++) {
@@ -1201,6 +1223,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     }
 
     // ---- 5: chunk tables (wait masks computed on the device), counters
+    ph.next("build: chunk tables");
     p->fused.chunk = p->chunk_req > 0 ? p->chunk_req : fused_chunk(p);
     p->fused.wave = p->wave_chunks != 0;
     p->pulse.chunk = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p);

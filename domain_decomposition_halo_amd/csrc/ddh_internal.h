@@ -11,9 +11,20 @@
 #include <utility>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "../../include/ddh.h"
 
 namespace ddh {
+
+// A named host range (an entry point, a phase of the map build), seen by
+// rocprofv3 --marker-trace; a no-op without a profiler.
+struct Range {
+    explicit Range(const char* name) { roctxRangePushA(name); }
+    ~Range() { roctxRangePop(); }
+    Range(const Range&) = delete;
+    Range& operator=(const Range&) = delete;
+};
 
 // Work-group size of the per-pulse and helper kernels (four 64-wide
 // wavefronts); the fused launch picks 256 or 1024.
