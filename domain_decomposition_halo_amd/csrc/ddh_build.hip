@@ -181,7 +181,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ bu
     sorted[start[bk] + rank[a]] = a;
 }
 
-// Order each cell's atoms by global id (cells hold ~10 atoms: insertion sort).
+// Order each cell's atoms by global id (cells hold ~10 atoms: insertion
+// sort). A cell of at most kCellRegs atoms is loaded once, sorted in
+// registers and stored once; a larger one is sorted in place in memory.
+constexpr int kCellRegs = 32;
 __global__ __launch_bounds__(256) void sort_cells_kernel(const uint32_t* __restrict__ start, int nb,
                                                          int* __restrict__ sorted)
 {
@@ -189,6 +192,28 @@ __global__ __launch_bounds__(256) void sort_cells_kernel(const uint32_t* __restr
     if (bk >= nb)
         return;
     const uint32_t s = start[bk], e = start[bk + 1];
+    const int n = (int)(e - s);
+    if (n <= kCellRegs) {
+        int v[kCellRegs];
+#pragma unroll
+        for (int i = 0; i < kCellRegs; i++)
+            v[i] = i < n ? sorted[s + i] : INT32_MAX;
+        // insertion sort with fixed trip counts keeps v[] in registers
+#pragma unroll
+        for (int i = 1; i < kCellRegs; i++) {
+#pragma unroll
+            for (int j = i; j > 0; j--) {
+                const int lo = min(v[j - 1], v[j]), hi = max(v[j - 1], v[j]);
+                v[j - 1] = lo;
+                v[j] = hi;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kCellRegs; i++)
+            if (i < n)
+                sorted[s + i] = v[i];
+        return;
+    }
     for (uint32_t i = s + 1; i < e; i++) {
         const int v = sorted[i];
         uint32_t j = i;
