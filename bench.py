@@ -195,9 +195,11 @@ def run_gpu(args, w):
         durs = [e0.elapsed_time(e1) * 1e-3 / args.steps]
     else:
         # G steps captured in one graph and replayed: the host enqueues one
-        # graph per G steps, so the GPU never waits for the host
-        G = max(1, min(args.graph_steps, args.steps))
-        n_rep = max(1, args.steps // G)
+        # graph per G steps, so the GPU never waits for the host. G divides
+        # the step count, so exactly --steps steps are timed.
+        G = max(d for d in range(1, max(1, min(args.graph_steps, args.steps)) + 1)
+                if args.steps % d == 0)
+        n_rep = args.steps // G
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for _ in range(G):
