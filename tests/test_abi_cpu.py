@@ -215,3 +215,12 @@ def test_header_is_c99_and_links(tmp_path):
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     assert len(names) >= 19
+
+
+def test_bench_runs_on_one_gpu_only():
+    # every domain is a virtual rank inside one GPU: more GPUs is an error
+    # that names the reason, before any device is touched
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
