@@ -141,8 +141,11 @@ const char *ddh_last_error(void);
  * follow "Accelerating GROMACS using Device-initiated Remote Memory Access"
  * and "Enabling parallelism across pulses through kernel fusion" (the
  * dependency offset of each map is the sender's home count).
- * Replaces any previous maps of the plan. Errors: DDH_EINVAL (bad pointer or
- * position), DDH_ECAPACITY (layout too large), DDH_EHIP.
+ * Replaces any previous maps of the plan. Meant to run at every
+ * neighbour-search step: the plan keeps its device memory and reuses it in
+ * later builds while it is large enough (ddh_plan_destroy releases it).
+ * Errors: DDH_EINVAL (bad pointer or position), DDH_ECAPACITY (layout too
+ * large), DDH_EHIP.
  */
 int ddh_build_maps(ddh_plan *plan, const float *x_global_dev, int32_t n_atoms, void *stream);
 
