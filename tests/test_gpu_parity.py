@@ -306,6 +306,28 @@ def test_rebuild_after_atoms_move():
         plan.close()
 
 
+def test_rebuilds_that_grow_and_shrink():
+    """One plan rebuilt for 2000, 40000, 500 and 40000 atoms: the build's
+    device memory grows, is reused while large enough, and every build and
+    exchange matches a fresh oracle plan in both main modes."""
+    grid, box, rc = (2, 2, 2), (8.0, 8.0, 8.0), 1.25
+    plan = ddh.Plan(grid, box, rc)
+    for n in (2000, 40000, 500, 40000):
+        x = W.uniform_positions(n, box, seed=700 + n)
+        ref = oracle.OraclePlan(x, grid, box, rc)
+        g = GpuPlan.__new__(GpuPlan)
+        g.plan = plan
+        g.xg = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        g.lay = plan.build_maps(g.xg)
+        g.n_slots = g.lay["n_slots"]
+        g.D, g.P = g.lay["n_domains"], g.lay["n_pulses"]
+        check_layout(g, ref)
+        for mode in (ddh.DDH_MODE_FUSED, ddh.DDH_MODE_PULSE):
+            plan.set_mode(mode)
+            check_steps(g, ref, n + mode, steps=1)
+    plan.close()
+
+
 def test_two_plans_on_two_streams(workload_plan):
     """Two plans (different decompositions) exchanging at the same time on
     two streams, fused and per-pulse: each keeps its own tickets, counters
