@@ -828,6 +828,42 @@ static void make_work_table(const Plan* p, bool waits, WorkTable& t)
     t.fpulse_begin[P] = (int)t.fch.size();
 }
 
+// Device form of set_release_flags (below), for masks computed on the
+// device: read[S * P + q] marks a coordinate counter, read[DP + S * P + q] a
+// force counter that some chunk waits on (every writer stores 1).
+__global__ __launch_bounds__(256) void release_marks_kernel(const DChunk* __restrict__ xch, int nx,
+                                                            const DChunk* __restrict__ fch, int nf,
+                                                            int P, int DP,
+                                                            uint32_t* __restrict__ read)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < nx) {
+        const DChunk& c = xch[i];
+        for (uint32_t m = c.wait_a; m; m &= m - 1)
+            read[c.S * P + __builtin_ctz(m)] = 1u;
+    } else if (i < nx + nf) {
+        const DChunk& c = fch[i - nx];
+        for (uint32_t m = c.wait_a; m; m &= m - 1)
+            read[DP + c.S * P + __builtin_ctz(m)] = 1u;
+        for (uint32_t m = c.wait_b; m; m &= m - 1)
+            read[DP + c.R * P + __builtin_ctz(m)] = 1u;
+    }
+}
+
+__global__ __launch_bounds__(256) void release_apply_kernel(DChunk* __restrict__ xch, int nx,
+                                                            DChunk* __restrict__ fch, int nf, int DP,
+                                                            const uint32_t* __restrict__ read)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < nx) {
+        if (read[xch[i].ctr])
+            xch[i].flags |= kChunkRelease;
+    } else if (i < nx + nf) {
+        if (read[DP + fch[i - nx].ctr])
+            fch[i - nx].flags |= kChunkRelease;
+    }
+}
+
 // A chunk of the fused launch publishes with a release fence only if a
 // later chunk of the same launch waits on its counter (and so reads what it
 // wrote). Needs the final wait masks.
@@ -1303,19 +1339,25 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
             pb += total[q];
         }
         const int nx = (int)t.xch.size(), nf = (int)t.fch.size();
-        if (nx + nf > 0)
+        // the release flags follow from the masks, on the device as well
+        // (the host copies of the fused table keep neither)
+        uint32_t* d_read;
+        DDH_HIP(sc.alloc(&d_read, 2 * DP));
+        DDH_HIP(hipMemsetAsync(d_read, 0, sizeof(uint32_t) * 2 * DP, s));
+        if (nx + nf > 0) {
             hipLaunchKernelGGL(chunk_masks_kernel, dim3(nx + nf), dim3(256), 0, s, t.d_xch, nx,
                                t.d_fch, nf, p->d_maps, d_rid, d_inmap, P);
+            hipLaunchKernelGGL(release_marks_kernel, dim3(blocks(nx + nf)), dim3(256), 0, s,
+                               t.d_xch, nx, t.d_fch, nf, P, (int)DP, d_read);
+            hipLaunchKernelGGL(release_apply_kernel, dim3(blocks(nx + nf)), dim3(256), 0, s,
+                               t.d_xch, nx, t.d_fch, nf, (int)DP, d_read);
+        }
         DDH_HIP(hipGetLastError());
-        DDH_HIP(hipMemcpyAsync(t.xch.data(), t.d_xch, sizeof(DChunk) * nx, hipMemcpyDeviceToHost,
-                               s));
-        DDH_HIP(hipMemcpyAsync(t.fch.data(), t.d_fch, sizeof(DChunk) * nf, hipMemcpyDeviceToHost,
-                               s));
-        DDH_HIP(hipStreamSynchronize(s));
+    } else {
+        set_release_flags(p, p->fused);
+        DDH_HIP(upload(p->fused.d_xch, p->fused.xch, s));
+        DDH_HIP(upload(p->fused.d_fch, p->fused.fch, s));
     }
-    set_release_flags(p, p->fused);
-    DDH_HIP(upload(p->fused.d_xch, p->fused.xch, s));
-    DDH_HIP(upload(p->fused.d_fch, p->fused.fch, s));
 
     std::vector<uint32_t> xneed(DP, 0u), fneed(DP, 0u);
     for (int S = 0; S < D; S++)
