@@ -896,10 +896,11 @@ static void set_release_flags(const Plan* p, WorkTable& t)
 // smaller slices multiply the serialized ticket claims and releases).
 static int fused_chunk(const Plan* p) { return p->wave_chunks ? 1024 : 8192; }
 
-// Entries per block of the per-pulse launches: the largest of 2048, 1024 and
-// 512 that still gives every pulse's launch at least two blocks per compute
-// unit (a launch with fewer blocks than compute units leaves bandwidth idle),
-// or 256 for small pulses.
+// Entries per block of the per-pulse launches: a whole map (4096) when the
+// maps are many and short; else the largest of 2048, 1024 and 512 that still
+// gives every pulse's launch at least two blocks per compute unit (a launch
+// with fewer blocks than compute units leaves bandwidth idle), or 256 for
+// small pulses.
 static int pulse_chunk(const Plan* p)
 {
     const int D = p->g.ndom, P = p->g.P;
