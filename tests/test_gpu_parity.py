@@ -14,7 +14,8 @@ to the most pulses a grid allows; seeded random decompositions; rebuilds for
 moving atoms; two plans on two streams; completion flags (counts, consumer
 streams waiting on them, turned off); device memory released by destroyed
 plans; the exchange beside a compute load on another stream; empty and
-one-sided inputs, error paths and the bounded-wait timeout paths.
+one-sided inputs, many domains with short or empty maps, error paths and the
+bounded-wait timeout paths.
 """
 
 import numpy as np
@@ -651,6 +652,21 @@ def test_empty_and_one_sided_inputs():
     ref = oracle.OraclePlan(x, (2, 2, 2), box, 1.25, cell=0.0)
     g = GpuPlan(x, (2, 2, 2), box, 1.25, cell=0.0)
     check_layout(g, ref)
+    g.close()
+
+
+@pytest.mark.parametrize("mode", ["pulse", "pulse_graph", "fused", "auto"])
+@pytest.mark.parametrize("grid,n", [((16, 4, 4), 3000), ((8, 8, 8), 1500), ((16, 4, 4), 40000)])
+def test_many_small_maps(grid, n, mode):
+    """At least one domain per compute unit and short maps, many of them
+    empty: the per-pulse launches then take one chunk per map."""
+    box = (15.66, 15.66, 15.66)
+    x = W.uniform_positions(n, box, seed=n + grid[0])
+    ref = oracle.OraclePlan(x, grid, box, 1.2)
+    g = GpuPlan(x, grid, box, 1.2, mode=MODES[mode])
+    check_layout(g, ref)
+    check_steps(g, ref, n, steps=2)
+    check_steps(g, ref, n + 1, steps=1, fused_step=True)
     g.close()
 
 
