@@ -896,8 +896,8 @@ static void set_release_flags(const Plan* p, WorkTable& t)
 // smaller slices multiply the serialized ticket claims and releases).
 static int fused_chunk(const Plan* p) { return p->wave_chunks ? 1024 : 8192; }
 
-// Entries per block of the per-pulse launches: a whole map (4096) when the
-// maps are many and short; else the largest of 2048, 1024 and 512 that still
+// Entries per block of the per-pulse launches: a whole map (the longest,
+// up to 4096) when the maps are many and short; else the largest of 2048, 1024 and 512 that still
 // gives every pulse's launch at least two blocks per compute unit (a launch
 // with fewer blocks than compute units leaves bandwidth idle), or 256 for
 // small pulses.
@@ -920,9 +920,12 @@ static int pulse_chunk(const Plan* p)
     // blocks are spread evenly over the compute units (384k atoms on 16x4x4
     // domains: 23.6 -> 22.4 us per step, force pass 18.3 -> 15.4 us; splitting
     // the 2560-entry maps into 512-entry chunks leaves some units with more
-    // blocks than others)
+    // blocks than others). The chunk is the longest map rounded up to 64
+    // entries: the chunk-aligned map copy holds one chunk per map, empty maps
+    // included, so a fixed 4096 would cost 24 KB per map where tiny domains
+    // have a few entries each.
     if (D >= p->n_cu && largest <= 4096)
-        return 4096;
+        return std::max(64, (largest + 63) / 64 * 64);
     for (int ch = 2048; ch > 512; ch /= 2)
         if (smallest / ch >= 2ll * p->n_cu)
             return ch;
