@@ -26,8 +26,7 @@
  *    earlier pulses; entries at or above it are atoms forwarded from earlier
  *    pulses.
  *
- * Readings taken where the guide is silent (each also recorded in the design
- * notes of the repository):
+ * Readings taken where the guide is silent:
  *  - one-sided halo: in every pulse a domain sends to its -d neighbour and
  *    receives from its +d neighbour, so each domain's halo lies on its +d side;
  *  - candidates of pulse k of dimension d: for k == 0 the sender's home slots
