@@ -92,8 +92,8 @@ def test_workload_forces(k, workload_plan):
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4])
 def test_workload_copies_bounded(k, workload_plan):
-    # one pulse per dimension: at most 7 halo copies per atom; workload 4
-    # (two X pulses) allows (2+1)*(1+1)*(1+1) - 1 = 11
+    # one pulse per dimension: at most 7 halo copies per atom; 384k atoms on
+    # 16x4x4 domains (two X pulses) allow (2+1)*(1+1)*(1+1) - 1 = 11
     w, x, plan = workload_plan(k)
     counts = np.bincount(plan.slot_ids, minlength=w.n_atoms)
     bound = 1
