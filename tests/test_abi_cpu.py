@@ -224,3 +224,18 @@ def test_bench_runs_on_one_gpu_only():
                          cwd=ROOT, capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_bench_reports_counter_traffic_only_for_current_sources(tmp_path, monkeypatch):
+    # the HBM traffic of a stored counter summary is reported only while the
+    # kernel sources hash to the value stored with it
+    import bench
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    path = tmp_path / "traffic_pulse_demo.md"
+    path.write_text(f"- kernel_source_sha256: `{bench.kernel_hash()}`\n"
+                    "- traffic_bytes_per_launch: 12345\n")
+    assert bench.read_traffic("pulse", "demo") == 12345.0
+    path.write_text("- kernel_source_sha256: `0000000000000000`\n"
+                    "- traffic_bytes_per_launch: 12345\n")
+    assert bench.read_traffic("pulse", "demo") is None
+    assert bench.read_traffic("pulse", "absent") is None
