@@ -285,15 +285,6 @@ __device__ const float* resolve(const SArgs& a, int S, int j, int& gid)
     return nullptr;
 }
 
-// The slab test of the pulse's dimension d: fl(x_d - lo_d(S)) < rc.
-__device__ bool selected(const SArgs& a, int S, int j, int& gid, const float*& pos)
-{
-    pos = resolve(a, S, j, gid);
-    if (!pos)
-        return false;
-    return (pos[a.d] - a.lo[S]) < a.rc;
-}
-
 // slot_gid / home_slot for the home slots: r -> domain by binary search.
 __global__ __launch_bounds__(256) void fill_home_kernel(const int* __restrict__ home_gid,
                                                         const int* __restrict__ hs, int ndom,
@@ -333,7 +324,8 @@ __device__ __forceinline__ int segment_of(const int* prefix, int n, int e)
     return lo;
 }
 
-// Slab selection of pulse p in tiles: sender S's candidate slots
+// Slab selection of pulse p in tiles (the slab test of the pulse's dimension
+// d: fl(x_d - lo_d(S)) < rc): sender S's candidate slots
 // [first[S], last[S]) are cut into tiles of kSelTile slots, and tile b of the
 // pulse (tiles of S numbered from tprefix[S]) is one block. Counting and
 // writing by tile fills the GPU whatever the number of domains; an exclusive
@@ -362,10 +354,21 @@ __global__ __launch_bounds__(256) void select_count_kernel(SArgs a, const int* _
     __syncthreads();
     int c = 0, bl = 0;
     const int nh = a.nhome[S];
-    for (int j = j0 + threadIdx.x; j < j1; j += 256) {
+    // the tile's kSelTile / 256 slots per thread: every position load is
+    // issued before the first test, so the loads are in flight together
+    constexpr int U = kSelTile / 256;
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int j = j0 + (int)threadIdx.x + u * 256;
         int gid;
-        const float* pos;
-        if (selected(a, S, j, gid, pos)) {
+        const float* pos = j < j1 ? resolve(a, S, j, gid) : nullptr;
+        v[u] = pos ? pos[a.d] : __builtin_nanf("");
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int j = j0 + (int)threadIdx.x + u * 256;
+        if ((v[u] - a.lo[S]) < a.rc) {  // false for the NaN of a slot out of range
             c++;
             bl += j < nh;
         }
@@ -412,11 +415,25 @@ __global__ __launch_bounds__(256) void select_write_kernel(SArgs a, const int* _
         s_run = (int)(scan[blockIdx.x] - scan[tprefix[S]]);  // entries of S's earlier tiles
     __syncthreads();
     const bool shift = a.shiftbit[S] != 0;
-    for (int base = j0; base < j1; base += 256) {
-        const int j = base + threadIdx.x;
-        int gid = -1;
-        const float* pos = nullptr;
-        const bool pred = j < j1 && selected(a, S, j, gid, pos);
+    // as in the count: every slot's position load is issued before the
+    // first test
+    constexpr int U = kSelTile / 256;
+    const float* pp[U];
+    int gg[U];
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int j = j0 + (int)threadIdx.x + u * 256;
+        gg[u] = -1;
+        pp[u] = j < j1 ? resolve(a, S, j, gg[u]) : nullptr;
+        v[u] = pp[u] ? pp[u][a.d] : __builtin_nanf("");
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int j = j0 + (int)threadIdx.x + u * 256;
+        const int gid = gg[u];
+        const float* pos = pp[u];
+        const bool pred = (v[u] - a.lo[S]) < a.rc;  // false for the NaN of a slot out of range
         const unsigned long long bal = __ballot(pred);
         const int pre = __popcll(bal & ((1ull << lane) - 1ull));
         if (lane == 0)
@@ -436,10 +453,10 @@ __global__ __launch_bounds__(256) void select_write_kernel(SArgs a, const int* _
             // the sender sits at index 0 of d
             float* o = a.out_xyz + 3ll * (a.out_pos[S] + idx);
             for (int c = 0; c < 3; c++) {
-                float v = pos[c];
+                float r = pos[c];
                 if (c == a.d && shift)
-                    v = v + a.L_d;
-                o[c] = v;
+                    r = r + a.L_d;
+                o[c] = r;
             }
         }
         __syncthreads();
