@@ -38,6 +38,7 @@ DDH_TUNE_STATIC_FIRST = 8
 DDH_TUNE_FLAGS = 9
 DDH_TUNE_NARROW_MAPS = 10
 DDH_TUNE_WAVE_CHUNKS = 11
+DDH_TUNE_HOME_SORT = 12
 TRACE_RECORDS = 64
 TRACE_EVENTS = {1: "start", 2: "claim", 3: "head", 4: "waited", 5: "chunk", 6: "publish", 7: "exit"}
 

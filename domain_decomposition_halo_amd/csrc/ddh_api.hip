@@ -458,6 +458,11 @@ int ddh_tune(ddh_plan* p, int32_t key, int64_t value)
             return fail(DDH_EINVAL, "ddh_tune: wave-chunks must be 0 or 1");
         p->wave_chunks = (int)value;
         return DDH_OK;
+    case DDH_TUNE_HOME_SORT:
+        if (value < 0 || value > 2)
+            return fail(DDH_EINVAL, "ddh_tune: home-sort must be 0, 1 or 2");
+        p->home_sort = (int)value;
+        return DDH_OK;
     default:
         return fail(DDH_EINVAL, "ddh_tune: unknown key");
     }

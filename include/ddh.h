@@ -341,8 +341,17 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     guide's per-warp pipelining). Takes effect
                                     at the next build. */
 
-/* Set a tuning knob; takes effect at the next build (CHUNK, WAVE_CHUNKS) or
-   call. */
+#define DDH_TUNE_HOME_SORT 12      /* how the build orders the home atoms (by
+                                    domain, cell, then global id; the result
+                                    is the same): 0 (default) automatic, a
+                                    radix sort from 4,000,000 atoms on, else
+                                    the counting sort; 1 the counting sort
+                                    (per-atom device atomics, then a per-cell
+                                    sort); 2 the radix sort. Takes effect at
+                                    the next build. */
+
+/* Set a tuning knob; takes effect at the next build (CHUNK, WAVE_CHUNKS,
+   HOME_SORT) or call. */
 int ddh_tune(ddh_plan *plan, int32_t key, int64_t value);
 
 #ifdef __cplusplus

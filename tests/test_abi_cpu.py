@@ -145,11 +145,14 @@ def test_mode_and_tune_validation():
     plan.tune(ddh.DDH_TUNE_NARROW_MAPS, 1)
     plan.tune(ddh.DDH_TUNE_WAVE_CHUNKS, 1)
     plan.tune(ddh.DDH_TUNE_WAVE_CHUNKS, 0)
+    for v in (1, 2, 0):
+        plan.tune(ddh.DDH_TUNE_HOME_SORT, v)
     for key, val in [(ddh.DDH_TUNE_CHUNK, 10), (ddh.DDH_TUNE_CHUNK, 70000),
                      (ddh.DDH_TUNE_GRID, -1), (ddh.DDH_TUNE_SPIN_LIMIT, 0), (99, 1),
                      (ddh.DDH_TUNE_BLOCK, 512), (ddh.DDH_TUNE_STATIC_FIRST, 2),
                      (ddh.DDH_TUNE_FLAGS, 2), (ddh.DDH_TUNE_NARROW_MAPS, -1),
-                     (ddh.DDH_TUNE_WAVE_CHUNKS, 3)]:
+                     (ddh.DDH_TUNE_WAVE_CHUNKS, 3), (ddh.DDH_TUNE_HOME_SORT, 3),
+                     (ddh.DDH_TUNE_HOME_SORT, -1)]:
         with pytest.raises(ddh.DDHError) as e:
             plan.tune(key, val)
         assert e.value.code == ddh.DDH_EINVAL

@@ -47,8 +47,9 @@ class GpuPlan:
     """A device plan built from host positions, with host views of its output."""
 
     def __init__(self, x, grid, box, rc, cell=0.5, mode=0, chunk=0, wg=0, refined=1, block=0,
-                 static_first=0, narrow=1, wave=0):
+                 static_first=0, narrow=1, wave=0, home_sort=0):
         self.plan = ddh.Plan(grid, box, rc, cell)
+        self.plan.tune(ddh.DDH_TUNE_HOME_SORT, home_sort)
         self.plan.tune(ddh.DDH_TUNE_STATIC_FIRST, static_first)
         self.plan.tune(ddh.DDH_TUNE_NARROW_MAPS, narrow)
         self.plan.tune(ddh.DDH_TUNE_WAVE_CHUNKS, wave)
@@ -668,6 +669,42 @@ def test_many_small_maps(grid, n, mode):
     check_steps(g, ref, n, steps=2)
     check_steps(g, ref, n + 1, steps=1, fused_step=True)
     g.close()
+
+
+@pytest.mark.parametrize("home_sort", [1, 2])
+def test_home_sort_forms(home_sort, workload_plan):
+    """Both orderings of the home atoms (the counting sort with device
+    atomics, the radix sort) give the oracle's layout, maps and results: on
+    the workloads, exact boxes with multi-pulse relay, random decompositions,
+    many small domains, an empty input and a position outside the box."""
+    for k in (1, 2, 3, 4):
+        w, x, ref = workload_plan(k)
+        g = GpuPlan(x, **w.params(), mode=ddh.DDH_MODE_PULSE, home_sort=home_sort)
+        check_layout(g, ref)
+        check_steps(g, ref, k, steps=1)
+        g.close()
+    cases = [(grid, box, rc, W.lattice_positions(n, box, seed=40 + n)) for grid, box, rc, n in DYADIC]
+    cases += [(grid, box, rc, W.uniform_positions(n, box, seed=n))
+              for grid, box, rc, n in random_configs(6, 77)]
+    cases.append(((16, 4, 4), (15.66, 15.66, 15.66), 1.2,
+                  W.uniform_positions(3000, (15.66, 15.66, 15.66), seed=3016)))
+    for grid, box, rc, x in cases:
+        ref = oracle.OraclePlan(x, grid, box, rc)
+        g = GpuPlan(x, grid, box, rc, mode=ddh.DDH_MODE_AUTO, home_sort=home_sort)
+        check_layout(g, ref)
+        check_steps(g, ref, len(x), steps=1)
+        g.close()
+    g = GpuPlan(np.zeros((0, 3), np.float32), (2, 2, 2), (8.0, 8.0, 8.0), 1.0, home_sort=home_sort)
+    assert g.n_slots == 0 and g.lay["n_halo"] == 0
+    g.close()
+    plan = ddh.Plan((2, 2, 2), (8.0, 8.0, 8.0), 1.0)
+    plan.tune(ddh.DDH_TUNE_HOME_SORT, home_sort)
+    x = W.lattice_positions(200, (8.0, 8.0, 8.0), seed=1)
+    x[7, 2] = 8.0
+    with pytest.raises(ddh.DDHError) as e:
+        plan.build_maps(torch.from_numpy(x).cuda())
+    assert e.value.code == ddh.DDH_EINVAL
+    plan.close()
 
 
 def test_error_paths():
