@@ -288,6 +288,7 @@ __global__ void home_start_kernel(const uint32_t* __restrict__ start, const int*
 struct SArgs {
     int p, d, P;
     float L_d, rc;
+    const int* tile_s;    // [b] sender of selection tile b
     const float* xhome;   // home positions in slot order (float3)
     const int* home_gid;
     const int* home_start;
@@ -382,21 +383,21 @@ __device__ __forceinline__ int segment_of(const int* prefix, int n, int e)
 // scan of the tile counts (in S order, then slot order) gives every tile its
 // first entry in the pulse's map buffer, so the compaction stays in slot
 // order.
-__device__ __forceinline__ void tile_of(const SArgs& a, const int* tprefix, int ndom, int b,
-                                        int& S, int& j0, int& j1)
+__device__ __forceinline__ void tile_of(const SArgs& a, const int* tprefix, int b, int& S,
+                                        int& j0, int& j1)
 {
-    S = segment_of(tprefix, ndom, b);
+    S = a.tile_s[b];  // one load, not a search of tprefix per block
     j0 = a.first[S] + (b - tprefix[S]) * kSelTile;
     j1 = min(j0 + kSelTile, a.last[S]);
 }
 
 __global__ __launch_bounds__(256) void select_count_kernel(SArgs a, const int* __restrict__ tprefix,
-                                                           int ndom, uint32_t* __restrict__ cnt,
+                                                           uint32_t* __restrict__ cnt,
                                                            uint32_t* __restrict__ below)
 {
     __shared__ int s_send, s_split;
     int S, j0, j1;
-    tile_of(a, tprefix, ndom, blockIdx.x, S, j0, j1);
+    tile_of(a, tprefix, blockIdx.x, S, j0, j1);
     if (threadIdx.x == 0) {
         s_send = 0;
         s_split = 0;
@@ -453,13 +454,12 @@ __global__ __launch_bounds__(256) void select_totals_kernel(const int* __restric
 // Ordered compaction of one tile: its selected slots go to the sender's map
 // from the tile's scanned offset on, in slot order.
 __global__ __launch_bounds__(256) void select_write_kernel(SArgs a, const int* __restrict__ tprefix,
-                                                           int ndom,
                                                            const uint32_t* __restrict__ scan)
 {
     __shared__ int wave_tot[4];
     __shared__ int s_run;
     int S, j0, j1;
-    tile_of(a, tprefix, ndom, blockIdx.x, S, j0, j1);
+    tile_of(a, tprefix, blockIdx.x, S, j0, j1);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (threadIdx.x == 0)
         s_run = (int)(scan[blockIdx.x] - scan[tprefix[S]]);  // entries of S's earlier tiles
@@ -1221,6 +1221,11 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         const size_t o_sbit = in.add(sbit), o_roff = in.add(roff_at), o_rsize = in.add(rsize_at);
         const size_t o_rstart = in.add(rstart), o_rgid = in.add(rgid), o_rxyz = in.add(rxyz);
         const size_t o_tprefix = in.add(tprefix);
+        std::vector<int> tile_s((size_t)std::max(T, 1), 0);
+        for (int S = 0; S < D; S++)
+            for (int b = tprefix[S]; b < tprefix[S + 1]; b++)
+                tile_s[b] = S;
+        const size_t o_tile_s = in.add(tile_s);
         char* d_in;
         DDH_HIP(in.send(sc, &d_in, s));
         const float* d_lo = (const float*)(d_in + o_lo);
@@ -1233,6 +1238,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         int* const* d_rgid = (int* const*)(d_in + o_rgid);
         float* const* d_rxyz = (float* const*)(d_in + o_rxyz);
         const int* d_tprefix = (const int*)(d_in + o_tprefix);
+        const int* d_tile_s = (const int*)(d_in + o_tile_s);
 
         SArgs a{};
         a.p = q;
@@ -1240,6 +1246,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         a.P = P;
         a.L_d = g.L[d];
         a.rc = g.rc;
+        a.tile_s = d_tile_s;
         a.xhome = d_xhome;
         a.home_gid = p->d_home_gid;
         a.home_start = d_hs;
@@ -1260,7 +1267,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         DDH_HIP(sc.alloc(&d_tbelow, (size_t)T + 1));
         DDH_HIP(sc.alloc(&d_tscan, (size_t)T + 1));
         if (T > 0)
-            hipLaunchKernelGGL(select_count_kernel, dim3(T), dim3(256), 0, s, a, d_tprefix, D,
+            hipLaunchKernelGGL(select_count_kernel, dim3(T), dim3(256), 0, s, a, d_tprefix,
                                d_tcnt, d_tbelow);
         DDH_HIP(hipGetLastError());
         const int rcode = scan_exclusive(sc, d_tcnt, T, d_tscan, s);
@@ -1320,7 +1327,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         a.out_gid = rgid[q];
         a.out_xyz = rxyz[q];
         if (T > 0)
-            hipLaunchKernelGGL(select_write_kernel, dim3(T), dim3(256), 0, s, a, d_tprefix, D,
+            hipLaunchKernelGGL(select_write_kernel, dim3(T), dim3(256), 0, s, a, d_tprefix,
                                d_tscan);
         DDH_HIP(hipGetLastError());
     }
