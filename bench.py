@@ -5,16 +5,20 @@ forces X->Y->Z with scatter-add), all domains virtual ranks in one GPU's HBM.
 A step is one coordinate pass plus one force pass over the workload's
 synthetic atoms (the whole hot path; the map build runs once before the
 timed region and is reported separately, as a neighbour-search step would
-be). Inputs are resident in HBM when timing starts. Default workload: 96,000
-atoms, 2x2x2 domains, rc 1.0 nm. Variant "auto" (default) runs what the
-library's automatic mode picks: "step" (both passes in one launch, all pulses
-chained on device counters) for a small pass, "pulse" (one launch per pulse)
-for a large one.
+be). Inputs are resident in HBM when timing starts. Default workload: 12,000,000
+atoms, 8x8x8 domains, rc 1.2 nm (the largest one-GPU configuration, the one
+the bandwidth target is stated for); the other four workloads follow under
+`also`. Variant "auto" (default) runs what the library's automatic mode
+picks: "step" (both passes in one launch, all pulses chained on device
+counters) for a small pass, "pulse" (one launch per pulse) for a large one.
 
 Prints one JSON line. `value` is halo atoms moved per second (sum of every
 (domain, pulse) map size, counted once per pass). The timed region replays a
-graph of --graph-steps captured steps, so the host never starves the GPU;
-HIP events on the launch stream bracket every replay. `roofline` compares the
+graph of G captured steps (G at most --graph-steps, and small enough that
+--steps gives at least five replays), so the host never starves the GPU;
+HIP events on the launch stream bracket every replay, and the median, p10
+and p90 are taken over the replays. `cold` times the same workload with a
+1 GiB buffer written before every (eager) step. `roofline` compares the
 step's algorithmic bytes (28 B per halo atom for the coordinate pass, 40 B
 for the force pass) with the 8 TB/s HBM peak over the measured GPU time per
 launch; `cpu_baseline` times the CPU oracle on a bounded sample of the same
@@ -50,6 +54,15 @@ KERNEL_SRCS = [os.path.join(ROOT, "domain_decomposition_halo_amd", "csrc", f)
                for f in ("ddh_exchange.hip", "ddh_build.hip", "ddh_internal.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 VARIANTS = ("auto", "step", "split", "pulse", "staged")
+
+
+def graph_size(steps: int, graph_steps: int, min_replays: int = 5) -> int:
+    """Steps per captured graph in the timed region: the largest divisor of
+    `steps` that is at most `graph_steps` and still leaves `min_replays`
+    replays (one step per graph when `steps` is below that), so exactly
+    `steps` steps are timed and the replays give a spread."""
+    cap = max(1, min(graph_steps, steps // min_replays))
+    return max(d for d in range(1, cap + 1) if steps % d == 0)
 
 
 def kernel_hash() -> str:
@@ -197,8 +210,7 @@ def run_gpu(args, w):
         # G steps captured in one graph and replayed: the host enqueues one
         # graph per G steps, so the GPU never waits for the host. G divides
         # the step count, so exactly --steps steps are timed.
-        G = max(d for d in range(1, max(1, min(args.graph_steps, args.steps)) + 1)
-                if args.steps % d == 0)
+        G = graph_size(args.steps, args.graph_steps)
         n_rep = args.steps // G
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
@@ -526,6 +538,28 @@ def run_overlap(args, w):
 
 # ------------------------------------------------------------- CPU baseline
 
+def host_cpu():
+    """The host's processor model and core counts: os.cpu_count() (what nproc
+    reports without an affinity mask), the cores this process may run on, and
+    the thread count the process is held to by OMP_NUM_THREADS (unset: none)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    omp = int(env) if env.strip().isdigit() and int(env) > 0 else None
+    return dict(model=model, cpu_count=os.cpu_count() or 1, affinity=affinity, omp_num_threads=omp)
+
+
 def run_cpu_baseline(w, seconds: float):
     import numpy as np
 
@@ -534,8 +568,12 @@ def run_cpu_baseline(w, seconds: float):
 
     x = W.positions(w)
     ref = oracle.OraclePlan(x, **w.params())
-    threads = max(1, min(ref.n_domains, os.cpu_count() or 1, 16,
-                         int(os.environ.get("OMP_NUM_THREADS", "16") or 16)))
+    # every core the process may use, unless OMP_NUM_THREADS holds it to fewer
+    # (the share of the host's cores a job is given)
+    cpu = host_cpu()
+    threads = cpu["affinity"] if cpu["omp_num_threads"] is None else min(cpu["affinity"],
+                                                                          cpu["omp_num_threads"])
+    threads = max(1, threads)
     xl = ref.x_local.copy()
     f = W.forces(w, ref.n_slots)
     steps = 0
@@ -562,9 +600,15 @@ def run_cpu_baseline(w, seconds: float):
     return dict(value=round(ref.halo_atoms / per_step, 1), unit="halo atoms/s", cores=threads,
                 kind="oracle",
                 sample=(f"{steps} steps (coordinate + force pass) of workload {w.name} "
-                        f"in {el:.1f} s, OpenMP over domains, maps prebuilt "
-                        f"(oracle map build {ref.build_seconds * 1e3:.0f} ms)"),
+                        f"in {el:.1f} s, OpenMP over the domains of each pulse on {threads} "
+                        f"threads, maps prebuilt (oracle map build "
+                        f"{ref.build_seconds * 1e3:.0f} ms, not timed)"),
                 us_per_step=round(per_step * 1e6, 2),
+                host_cores=cpu["cpu_count"], affinity_cores=cpu["affinity"],
+                omp_num_threads=cpu["omp_num_threads"], cpu_model=cpu["model"],
+                threads_note=("threads = the cores this process may use"
+                              + ("" if cpu["omp_num_threads"] is None else
+                                 ", held to OMP_NUM_THREADS")),
                 single_thread={"value": round(ref.halo_atoms / per_step1, 1),
                                "us_per_step": round(per_step1 * 1e6, 2),
                                "sample": f"{steps1} steps in {el1:.1f} s"})
@@ -650,7 +694,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--variant", default="auto", choices=VARIANTS)
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--grid", type=int, default=0)
@@ -678,9 +722,13 @@ def main():
                          "for profiler runs")
     ap.add_argument("--lib-graph", action="store_true",
                     help="with --eager: each call replays the library's cached hipGraph")
-    ap.add_argument("--also", default="1,3,4,5",
-                    help="comma-separated workload keys timed after the main one and "
-                         "summarized under 'also' (empty: none; skipped with --only-step)")
+    ap.add_argument("--also", default="1,2,3,4,5",
+                    help="comma-separated workload keys timed after the main one (which "
+                         "is skipped there) and "
+                         "summarized under 'also', each with its own default step count "
+                         "(empty: none; skipped with --only-step)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache figure of the main workload")
     ap.add_argument("--graph-steps", type=int, default=50,
                     help="steps captured per graph replay in the timed region")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -709,7 +757,6 @@ def main():
         print(f"bench.py runs on one GPU only: every domain is a virtual rank inside one "
               f"GPU's HBM (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
-    steps_given = args.steps
     if args.steps is None:
         args.steps = 1000 if w.n_atoms <= 100_000 else 200
 
@@ -720,6 +767,23 @@ def main():
         print(json.dumps({"map_build": run_builds(args, w)}), flush=True)
         return
     gpu = run_gpu(args, w)
+    # the same workload with caches evicted before every step (eager steps)
+    cold = None
+    if not args.cold and not args.eager and not args.only_step and not args.copy_probe \
+            and not args.no_cold:
+        sub = argparse.Namespace(**vars(args))
+        sub.cold = True
+        sub.steps = max(5, min(args.steps, 50))
+        sub.warmup = 2
+        gc = run_gpu(sub, w)
+        cold = {"us_per_step": gc["roofline"]["median_step_us"],
+                "p10_step_us": gc["roofline"]["p10_step_us"],
+                "p90_step_us": gc["roofline"]["p90_step_us"],
+                "frac": round((BYTES_X + BYTES_F) * gc["n_halo"]
+                              / (gc["roofline"]["median_step_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "variant": gc["variant"], "steps": gc["steps"],
+                "how": "eager steps, each after a 1 GiB buffer is written (caches evicted); "
+                       "median over the steps"}
     also = {}
     keys = [int(k) for k in args.also.split(",") if k.strip()] if args.also else []
     if not args.only_step and not args.copy_probe:
@@ -728,7 +792,7 @@ def main():
                 continue
             wk = W.WORKLOADS[k]
             sub = argparse.Namespace(**vars(args))
-            sub.steps = steps_given or (1000 if wk.n_atoms <= 100_000 else 200)
+            sub.steps = 1000 if wk.n_atoms <= 100_000 else 200
             g2 = run_gpu(sub, wk)
             also[wk.name] = {
                 "variant": g2["variant"], "halo_atoms_per_pass": g2["n_halo"],
@@ -738,6 +802,10 @@ def main():
                 "map_entry_bytes": g2["roofline"]["map_entry_bytes"],
                 "frac_at_min_bytes": g2["roofline"]["frac_at_min_bytes"],
                 "latency": g2["roofline"]["latency"],
+                "steps": g2["steps"],
+                "median_step_us": g2["roofline"]["median_step_us"],
+                "p10_step_us": g2["roofline"]["p10_step_us"],
+                "p90_step_us": g2["roofline"]["p90_step_us"],
                 "passes": g2["passes"], "single_launch": g2["single"],
                 "without_flags": g2["without_flags"]}
     cpu = None
@@ -774,6 +842,7 @@ def main():
         "passes": gpu["passes"],
         "single_launch": gpu["single"],
         "without_flags": gpu["without_flags"],
+        "cold": cold,
         "roofline": gpu["roofline"],
         "cpu_baseline": cpu,
         "also": also or None,

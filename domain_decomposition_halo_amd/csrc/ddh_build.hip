@@ -38,8 +38,8 @@ namespace ddh {
 namespace {
 
 constexpr int kScanBlock = 1024;  // elements per scan block (4 per thread)
-constexpr int kSelTile = 1024;
-constexpr int kRadixSortMin = 4000000;  // atoms from which the home sort is a radix sort    // candidate slots per block of the slab selection
+constexpr int kSelTile = 1024;    // candidate slots per block of the slab selection
+constexpr int kRadixSortMin = 4000000;  // atoms from which the home sort is a radix sort
 
 struct AGeom {
     int n[3];
@@ -1188,7 +1188,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
 
     // the pulses' upload blobs stay alive until the layout's sync
     std::vector<Blob> blobs;
-    blobs.reserve(2 * (size_t)P);
+    blobs.reserve(2 * (size_t)P + 1);
     for (int q = 0; q < P; q++) {
         const int d = g.pdim[q], k = g.pk[q];
         std::vector<float> lo(D);
@@ -1452,9 +1452,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     if (p->refined_waits && P > 0) {
         WorkTable& t = p->fused;
         uint32_t* d_inmap;
-        int* d_mpos;
         DDH_HIP(sc.alloc(&d_inmap, (size_t)p->n_slots));
-        DDH_HIP(sc.alloc(&d_mpos, ((size_t)D + 1) * P));
         DDH_HIP(hipMemsetAsync(d_inmap, 0, sizeof(uint32_t) * (size_t)p->n_slots, s));
         std::vector<int> mposall(((size_t)D + 1) * P);
         for (int q = 0; q < P; q++) {
@@ -1462,7 +1460,14 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                 mposall[(size_t)q * (D + 1) + S] = mpos[q][S];
             mposall[(size_t)q * (D + 1) + D] = total[q];
         }
-        DDH_HIP(upload(d_mpos, mposall, s));
+        // the host copy goes out in a blob of the function-scope list, which
+        // lives until the build's final sync
+        blobs.emplace_back();
+        Blob& mb = blobs.back();
+        const size_t o_mpos = mb.add(mposall);
+        char* d_mb;
+        DDH_HIP(mb.send(sc, &d_mb, s));
+        const int* d_mpos = (const int*)(d_mb + o_mpos);
         int64_t pb = 0;
         for (int q = 0; q < P; q++) {
             if (total[q] > 0)

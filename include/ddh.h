@@ -120,10 +120,12 @@ typedef struct ddh_plan ddh_plan;
  */
 int ddh_plan_create(const ddh_params *params, ddh_plan **out);
 
-/* Release every device and host resource of the plan (NULL is a no-op). */
+/* Release every device and host resource of the plan (NULL is a no-op).
+   Library utility: the guide defines no such call. */
 void ddh_plan_destroy(ddh_plan *plan);
 
-/* Text for the last failure on the calling thread ("" if none). */
+/* Text for the last failure on the calling thread ("" if none). Library
+   utility: the guide defines no such call. */
 const char *ddh_last_error(void);
 
 /* ------------------------------------------------------------- map build */
@@ -149,11 +151,20 @@ const char *ddh_last_error(void);
  */
 int ddh_build_maps(ddh_plan *plan, const float *x_global_dev, int32_t n_atoms, void *stream);
 
-/* Layout summary. Before ddh_build_maps only the domain count and the pulse
-   schedule are set (slot, halo and atom counts are 0). Errors: DDH_EINVAL. */
+/* Layout summary: the pulse schedule (dimensions Z, then Y, then X, with
+   several pulses in a dimension narrower than the cutoff: "Accelerating
+   GROMACS using Device-initiated Remote Memory Access") and the slot counts
+   of the flat array in which received records land at the receiver's atom
+   offset ("From MPI baseline to optimized GPU-native halo exchange"). Before
+   ddh_build_maps only the domain count and the pulse schedule are set (slot,
+   halo and atom counts are 0). Host output. Errors: DDH_EINVAL. */
 int ddh_query(const ddh_plan *plan, ddh_layout *out);
 
-/* Slot range of domain dom: base, home count, total count (host outputs). */
+/* Slot range of domain dom: base, home count, total count (host outputs).
+   The range is the domain's own coordinate array of "From MPI baseline to
+   optimized GPU-native halo exchange": its home atoms first, then the
+   records received in each pulse at their atom offsets. Errors: DDH_EINVAL
+   (bad domain), DDH_ESTATE (no build yet). */
 int ddh_domain_info(const ddh_plan *plan, int32_t dom, int64_t *base, int32_t *n_home,
                     int32_t *n_total);
 
@@ -162,7 +173,12 @@ int ddh_domain_info(const ddh_plan *plan, int32_t dom, int64_t *base, int32_t *n
  * send_size (entries), split (entries below the sender's home count: the
  * independent head), recv_dom (receiving domain), recv_offset (first slot of
  * the region inside the receiver, relative to its base), shift (1 if the
- * pulse's component gets + L at this sender).
+ * pulse's component gets + L at this sender). These are the per-pulse
+ * arguments of the guide's pack-and-send kernels (send size, receiving rank,
+ * atom offset in the receiver: "From MPI baseline to optimized GPU-native
+ * halo exchange", "Replacing host-side communication with NVSHMEM") and the
+ * dependency offset of "Enabling parallelism across pulses through kernel
+ * fusion". Errors: DDH_EINVAL (bad domain or pulse), DDH_ESTATE.
  */
 int ddh_pulse_info(const ddh_plan *plan, int32_t dom, int32_t pulse, int32_t *send_size,
                    int32_t *split, int32_t *recv_dom, int32_t *recv_offset, int32_t *shift);
@@ -170,7 +186,11 @@ int ddh_pulse_info(const ddh_plan *plan, int32_t dom, int32_t pulse, int32_t *se
 /*
  * Copy every map (sender-local slot indices, int32) to maps_dev, concatenated
  * with the sender outer and the pulse inner; capacity is in int32 elements
- * and must be >= n_halo. Asynchronous on stream.
+ * and must be >= n_halo. These are the index maps through which the pack
+ * kernel of "From MPI baseline to optimized GPU-native halo exchange"
+ * gathers its boundary atoms (entries in increasing slot order). The caller
+ * owns maps_dev. Asynchronous on stream. Errors: DDH_EINVAL, DDH_ECAPACITY,
+ * DDH_ESTATE, DDH_EHIP.
  */
 int ddh_copy_maps(const ddh_plan *plan, int32_t *maps_dev, int64_t capacity, void *stream);
 
@@ -217,13 +237,18 @@ int ddh_copy_flags(const ddh_plan *plan, uint32_t *flags_dev, void *stream);
  */
 int ddh_wait_flag(ddh_plan *plan, int32_t pass_kind, int32_t pulse, uint32_t epoch, void *stream);
 
-/* Global atom id of every slot (int32[n_slots], device). Asynchronous. */
+/* Global atom id of every slot (int32[n_slots], device; capacity in int32
+   elements). Library utility for callers that map slots back to atoms; the
+   guide defines no such call. Asynchronous. Errors: DDH_EINVAL,
+   DDH_ECAPACITY, DDH_ESTATE. */
 int ddh_local_ids(const ddh_plan *plan, int32_t *ids_dev, int64_t capacity, void *stream);
 
 /*
  * Fill the home slots of x_local_dev from x_global_dev (the array given to
  * ddh_build_maps or any array of the same atoms). Halo slots are untouched.
- * Asynchronous.
+ * Library utility: the guide takes each rank's home coordinates as given;
+ * this call places a caller's positions into the layout. Asynchronous.
+ * Errors: DDH_EINVAL, DDH_ECAPACITY, DDH_ESTATE.
  */
 int ddh_gather_home(ddh_plan *plan, const float *x_global_dev, float *x_local_dev,
                     int64_t capacity_slots, void *stream);
@@ -265,13 +290,19 @@ int ddh_exchange_step(ddh_plan *plan, float *x_local_dev, float *f_local_dev,
                       int64_t capacity_slots, void *stream);
 
 /* Select DDH_MODE_FUSED, DDH_MODE_PULSE or DDH_MODE_AUTO, optionally
-   | DDH_MODE_GRAPH, or DDH_MODE_STAGED alone. */
+   | DDH_MODE_GRAPH, or DDH_MODE_STAGED alone: the execution forms of
+   "Enabling parallelism across pulses through kernel fusion" (one launch),
+   "Replacing host-side communication with NVSHMEM" (one launch per pulse)
+   and "From MPI baseline to optimized GPU-native halo exchange" (host
+   orchestrated). All give the same results. Errors: DDH_EINVAL. */
 int ddh_set_mode(ddh_plan *plan, int32_t mode);
 
 /*
  * Wait for stream, then read and clear the plan's device error word.
  * Returns DDH_OK, DDH_ETIMEOUT (a device wait hit its spin limit: the
- * results of that call are not valid) or DDH_EHIP.
+ * results of that call are not valid) or DDH_EHIP. Library utility: the
+ * guide's waits on signals ("Dependency-aware packing") are unbounded; the
+ * library bounds them and reports an expiry here.
  */
 int ddh_check(ddh_plan *plan, void *stream);
 
@@ -351,7 +382,8 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     the next build. */
 
 /* Set a tuning knob; takes effect at the next build (CHUNK, WAVE_CHUNKS,
-   HOME_SORT) or call. */
+   HOME_SORT) or call. Library utility: the guide defines no such call.
+   Errors: DDH_EINVAL (unknown key or value out of range). */
 int ddh_tune(ddh_plan *plan, int32_t key, int64_t value);
 
 #ifdef __cplusplus

@@ -242,3 +242,23 @@ def test_bench_reports_counter_traffic_only_for_current_sources(tmp_path, monkey
                     "- traffic_bytes_per_launch: 12345\n")
     assert bench.read_traffic("pulse", "demo") is None
     assert bench.read_traffic("pulse", "absent") is None
+
+
+def test_bench_timed_graphs_leave_at_least_five_replays():
+    # exactly --steps steps are timed, in graphs of G steps, with at least
+    # five replays whenever there are five steps, so p10 and p90 can differ
+    import bench
+    for steps, cap in [(20, 50), (200, 50), (1000, 50), (7, 50), (5, 50), (3, 50), (20, 1), (97, 50)]:
+        G = bench.graph_size(steps, cap)
+        assert steps % G == 0 and 1 <= G <= max(1, cap)
+        if steps >= 5:
+            assert steps // G >= 5, (steps, G)
+    assert bench.graph_size(20, 50) == 4
+    assert bench.graph_size(200, 50) == 40
+
+
+def test_bench_host_cpu_fields():
+    import bench
+    cpu = bench.host_cpu()
+    assert cpu["cpu_count"] >= 1 and 1 <= cpu["affinity"] <= cpu["cpu_count"]
+    assert isinstance(cpu["model"], str) and cpu["model"]

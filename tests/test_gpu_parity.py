@@ -578,7 +578,7 @@ def test_map_width_threshold(n, wide):
 
 
 @pytest.mark.parametrize("chunk,wg", [(0, 0), (64, 0), (1000, 0), (0, 1), (192, 3), (4096, 0)])
-@pytest.mark.parametrize("k", [1, 2, 4])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
 def test_wave_chunks(k, chunk, wg, workload_plan):
     """Fused launch with wavefront workers (DDH_TUNE_WAVE_CHUNKS): contiguous
     map slices, a wavefront waits only when its slice holds dependent
@@ -767,18 +767,21 @@ def test_repeated_force_passes_are_deterministic(workload_plan):
 
 
 def test_workload5_full_size():
-    """12M atoms, 8x8x8 domains, at full size: the fused launch, the
-    library's graph of per-pulse launches, and the bench's own launch (the
-    automatic mode captured in a caller's graph and replayed twice)."""
+    """12M atoms, 8x8x8 domains, at full size: the fused launch (work-group
+    chunks and wavefront workers), the library's graph of per-pulse launches,
+    the host-orchestrated baseline, and the bench's own launch (the automatic
+    mode captured in a caller's graph and replayed twice)."""
     w = W.WORKLOADS[5]
     x = W.positions(w)
     ref = oracle.OraclePlan(x, **w.params())
     f0 = W.forces(w, ref.n_slots)
     fr = f0.copy()
     ref.exchange_forces(fr)
-    for mode in (ddh.DDH_MODE_FUSED, ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, ddh.DDH_MODE_AUTO):
-        g = GpuPlan(x, **w.params(), mode=mode)
-        if mode == ddh.DDH_MODE_FUSED:
+    for mode, wave in ((ddh.DDH_MODE_FUSED, 0), (ddh.DDH_MODE_FUSED, 1),
+                       (ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, 0), (ddh.DDH_MODE_STAGED, 0),
+                       (ddh.DDH_MODE_AUTO, 0)):
+        g = GpuPlan(x, **w.params(), mode=mode, wave=wave)
+        if mode == ddh.DDH_MODE_FUSED and not wave:
             check_layout(g, ref)
         xl = g.new_coords()
         fl = torch.from_numpy(f0).cuda()
@@ -803,8 +806,8 @@ def test_workload5_full_size():
                 torch.cuda.synchronize()
                 graph.replay()
             assert g.plan.check() == ddh.DDH_OK
-            assert np.array_equal(bits(xl.cpu().numpy()), bits(ref.x_local)), (mode, r)
-            assert np.array_equal(bits(fl.cpu().numpy()), bits(fr)), (mode, r)
+            assert np.array_equal(bits(xl.cpu().numpy()), bits(ref.x_local)), (mode, wave, r)
+            assert np.array_equal(bits(fl.cpu().numpy()), bits(fr)), (mode, wave, r)
         if mode == ddh.DDH_MODE_AUTO:
             del graph
         g.close()

@@ -1,8 +1,9 @@
 """Planted mistakes: the checks that pin the oracle must catch each one.
 
 Each test takes a correct oracle result on an exact (dyadic) box, plants one
-plausible mistake in it on the CPU (a dropped pulse, a duplicated or wrong map
-entry, a missing periodic shift, a lost or doubled force term, a wrong add
+plausible mistake in it on the CPU (a dropped pulse, a duplicated map entry, a
+missing periodic shift, `<=` in the slab test, pulses sent to the wrong
+neighbour, no relay of received records, a lost force term, a wrong add
 order) and asserts that the corresponding independent check fails.
 """
 
@@ -126,3 +127,79 @@ def test_wrong_add_order_is_caught(base):
     h = fn.copy()
     plan.exchange_forces(h)
     assert np.array_equal(h[rows], tree[rows])
+
+
+def _relaid_view(plan, per_domain):
+    """A view whose domain R holds its home slots and then the halo records
+    per_domain(R) returns (ids, coordinates), packed domain after domain."""
+    v = _View(plan)
+    ids, xs, bases, ntot = [], [], [], []
+    pos = 0
+    for R in range(plan.n_domains):
+        b, nh = int(plan.base[R]), int(plan.nhome[R])
+        hid, hx = per_domain(R)
+        ids += [plan.slot_ids[b:b + nh], hid]
+        xs += [plan.x_local[b:b + nh], hx]
+        bases.append(pos)
+        ntot.append(nh + len(hid))
+        pos += nh + len(hid)
+    v.slot_ids = np.concatenate(ids).astype(np.int32)
+    v.x_local = np.concatenate(xs).astype(np.float32)
+    v.base = np.asarray(bases, np.int64)
+    v.ntotal = np.asarray(ntot, np.int32)
+    v.n_slots = pos
+    return v
+
+
+def _mirror_domain(D, grid):
+    c = [D % grid[0], (D // grid[0]) % grid[1], D // (grid[0] * grid[1])]
+    c = [grid[d] - 1 - c[d] for d in range(3)]
+    return c[0] + grid[0] * (c[1] + grid[1] * c[2])
+
+
+def test_wrong_send_side_is_caught(base):
+    # an oracle that sent every pulse to the +d neighbour (not -d) would
+    # leave each domain the slab below its lower faces: exactly what the
+    # correct oracle gives for the mirror image of the system, read back
+    x, plan, bounds = base
+    L = np.asarray(BOX, dtype=np.float32)
+    xm = np.mod(L - x, L).astype(np.float32)  # exact on the 2^-12 nm lattice
+    mp = oracle.OraclePlan(xm, GRID, BOX, RC)
+
+    def halo(R):
+        M = _mirror_domain(R, GRID)
+        mb, mnh, mnt = int(mp.base[M]), int(mp.nhome[M]), int(mp.ntotal[M])
+        return mp.slot_ids[mb + mnh:mb + mnt], L - mp.x_local[mb + mnh:mb + mnt]
+
+    v = _relaid_view(plan, halo)
+    with pytest.raises(AssertionError):
+        bf.check_halo_against(v, x, GRID, BOX, RC, bounds)
+
+
+def test_no_relay_is_caught(base):
+    # an oracle whose pulses sent home atoms only (no forwarding of records
+    # received in earlier pulses) leaves out every edge and corner copy
+    x, plan, bounds = base
+    keep = np.ones(plan.n_slots, dtype=bool)
+    relayed = 0
+    for S in range(plan.n_domains):
+        for p in range(plan.n_pulses):
+            R = int(plan.recv[S, p])
+            o = int(plan.base[R] + plan.roff[S, p])
+            keep[o + int(plan.split[S, p]):o + int(plan.send[S, p])] = False
+            relayed += int(plan.send[S, p] - plan.split[S, p])
+    assert relayed > 0
+
+    def halo(R):
+        b, nh, nt = int(plan.base[R]), int(plan.nhome[R]), int(plan.ntotal[R])
+        k = keep[b + nh:b + nt]
+        return plan.slot_ids[b + nh:b + nt][k], plan.x_local[b + nh:b + nt][k]
+
+    v = _relaid_view(plan, halo)
+    with pytest.raises(AssertionError):
+        bf.check_halo_against(v, x, GRID, BOX, RC, bounds)
+    # the unmutated view passes the same check
+    full = _relaid_view(plan, lambda R: (
+        plan.slot_ids[int(plan.base[R] + plan.nhome[R]):int(plan.base[R] + plan.ntotal[R])],
+        plan.x_local[int(plan.base[R] + plan.nhome[R]):int(plan.base[R] + plan.ntotal[R])]))
+    bf.check_halo_against(full, x, GRID, BOX, RC, bounds)
