@@ -133,6 +133,10 @@ def run_gpu(args, w):
         plan.tune(ddh.DDH_TUNE_NARROW_MAPS, 0)
     if args.wave_chunks:
         plan.tune(ddh.DDH_TUNE_WAVE_CHUNKS, 1)
+    if args.exit_publish:
+        plan.tune(ddh.DDH_TUNE_EXIT_PUBLISH, args.exit_publish)
+    if args.pad_maps:
+        plan.tune(ddh.DDH_TUNE_PAD_MAPS, args.pad_maps)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -158,7 +162,11 @@ def run_gpu(args, w):
     fl = torch.from_numpy(W.forces(w, n_slots)).to(dev)
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
 
-    if variant == "split":
+    if args.pass_ == "coords":
+        calls = [("coords", lambda: plan.exchange_coords(xl), BYTES_X * n_halo)]
+    elif args.pass_ == "forces":
+        calls = [("forces", lambda: plan.exchange_forces(fl), BYTES_F * n_halo)]
+    elif variant == "split":
         calls = [("coords", lambda: plan.exchange_coords(xl), BYTES_X * n_halo),
                  ("forces", lambda: plan.exchange_forces(fl), BYTES_F * n_halo)]
     else:
@@ -166,9 +174,11 @@ def run_gpu(args, w):
 
     # pulse mode: a step pairs coordinate pulse q with force pulse P-1-q in
     # one launch, then one flag launch
+    # (a call whose last launch publishes its own flags needs no flag launch)
+    exit_pub = args.exit_publish == 1
     launches_per_step = {"step": 1, "split": 2,
                          "staged": 2 * lay["n_pulses"] + 1}.get(
-        variant, lay["n_pulses"] + (0 if args.no_flags else 1))
+        variant, lay["n_pulses"] + (0 if (args.no_flags or exit_pub) else 1))
     for _ in range(args.warmup):
         for _, fn, _ in calls:
             fn()
@@ -356,7 +366,8 @@ def run_gpu(args, w):
     achieved = step_bytes / avg_step_gpu / 1e9
     # the stored counters were taken with the default settings
     tuned = (args.chunk or args.grid or args.block or args.static_first or args.no_flags
-             or args.wide_maps or args.wave_chunks or args.cold)
+             or args.wide_maps or args.wave_chunks or args.cold or args.exit_publish
+             or args.pad_maps or args.pass_ != "step")
     traffic = None if tuned else read_traffic(variant, w.name)
     fused_name = "wave_kernel" if args.wave_chunks else "exchange_kernel"
     kernel = {"step": f"{fused_name} (fused step, one launch)",
@@ -698,7 +709,7 @@ def main():
     ap.add_argument("--variant", default="auto", choices=VARIANTS)
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--grid", type=int, default=0)
-    ap.add_argument("--block", type=int, default=0, choices=[0, 256, 1024])
+    ap.add_argument("--block", type=int, default=0, choices=[0, 256, 512, 1024])
     ap.add_argument("--static-first", action="store_true",
                     help="fused launch: first tickets unclaimed (DDH_TUNE_STATIC_FIRST)")
     ap.add_argument("--no-flags", action="store_true",
@@ -707,6 +718,13 @@ def main():
                     help="fused launch with wavefront workers (DDH_TUNE_WAVE_CHUNKS = 1)")
     ap.add_argument("--wide-maps", action="store_true",
                     help="kernels read the 32-bit maps (DDH_TUNE_NARROW_MAPS = 0)")
+    ap.add_argument("--exit-publish", type=int, default=0, choices=[0, 1, 2],
+                    help="DDH_TUNE_EXIT_PUBLISH (0 automatic)")
+    ap.add_argument("--pad-maps", type=int, default=0, choices=[0, 1, 2],
+                    help="DDH_TUNE_PAD_MAPS (0 automatic)")
+    ap.add_argument("--pass", dest="pass_", default="step", choices=["step", "coords", "forces"],
+                    help="time one pass alone (coordinate or force pass) instead of the step; "
+                         "with --only-step, for per-pass profiler runs")
     ap.add_argument("--cold", action="store_true", help="evict caches before every step")
     ap.add_argument("--eager", action="store_true",
                     help="enqueue every step from the host (no graph replay)")

@@ -431,8 +431,8 @@ int ddh_tune(ddh_plan* p, int32_t key, int64_t value)
         p->refined_waits = value != 0;
         return DDH_OK;
     case DDH_TUNE_BLOCK:
-        if (value != 0 && value != 256 && value != 1024)
-            return fail(DDH_EINVAL, "ddh_tune: block must be 0, 256 or 1024");
+        if (value != 0 && value != 256 && value != 512 && value != 1024)
+            return fail(DDH_EINVAL, "ddh_tune: block must be 0, 256, 512 or 1024");
         p->block_req = (int)value;
         return DDH_OK;
     case DDH_TUNE_TRACE:
@@ -457,6 +457,16 @@ int ddh_tune(ddh_plan* p, int32_t key, int64_t value)
         if (value != 0 && value != 1)
             return fail(DDH_EINVAL, "ddh_tune: wave-chunks must be 0 or 1");
         p->wave_chunks = (int)value;
+        return DDH_OK;
+    case DDH_TUNE_EXIT_PUBLISH:
+        if (value < 0 || value > 2)
+            return fail(DDH_EINVAL, "ddh_tune: exit-publish must be 0, 1 or 2");
+        p->exit_publish = (int)value;
+        return DDH_OK;
+    case DDH_TUNE_PAD_MAPS:
+        if (value < 0 || value > 2)
+            return fail(DDH_EINVAL, "ddh_tune: pad-maps must be 0, 1 or 2");
+        p->pad_maps = (int)value;
         return DDH_OK;
     case DDH_TUNE_HOME_SORT:
         if (value < 0 || value > 2)

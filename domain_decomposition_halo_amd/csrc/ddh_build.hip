@@ -791,6 +791,7 @@ void free_built(Plan* p)
     p->d_maps16 = nullptr;
     p->fused = WorkTable{};
     p->pulse = WorkTable{};
+    p->pulse1 = WorkTable{};
     p->d_ctrl = p->d_xcnt = p->d_fcnt = p->d_xneed = p->d_fneed = p->d_pflag = nullptr;
     p->d_stage = nullptr;
     p->built = false;
@@ -963,43 +964,59 @@ static void set_release_flags(const Plan* p, WorkTable& t)
 // smaller slices multiply the serialized ticket claims and releases).
 static int fused_chunk(const Plan* p) { return p->wave_chunks ? 1024 : 8192; }
 
-// Entries per block of the per-pulse launches: a whole map (the longest,
-// up to 4096) when the maps are many and short; else the largest of 2048, 1024 and 512 that still
-// gives every pulse's launch at least two blocks per compute unit (a launch
-// with fewer blocks than compute units leaves bandwidth idle), or 256 for
-// small pulses.
-static int pulse_chunk(const Plan* p)
+// Entries per chunk of the per-pulse launches (256-lane blocks, up to eight
+// entries per lane and round), from the average entries of a pulse per
+// compute unit, a. Measured on MI355X (graph replay, us per step; each pass
+// alone in brackets):
+//   - a >= 4096 (12M atoms on 8x8x8 domains, a = 11000): steps 2048 (111.0;
+//     1024: 118.0, 1536: 114.7, 2560: 117.8, 3072: 115.4); a pass alone 1024
+//     (coordinates 47.8 against 49.0 at 2048; forces 68.0 against 67.9);
+//   - a >= 256 (1M atoms on 4x4x4, a = 1080; 384k atoms on 16x4x4, a = 1050):
+//     768 (1M: 17.15, 512: 17.15, 1024: 17.44; 384k: 22.85, 1024: 22.82, 512:
+//     23.46, the former one chunk per map of up to 2752 entries: 27.4);
+//   - smaller (96k atoms on 2x2x2, a = 93): 256 (8.95; 128: 9.32, 512: 9.18).
+// step: the table of step calls (both passes share each launch), else the
+// one of single-pass calls.
+static int pulse_chunk(const Plan* p, bool step)
 {
-    const int D = p->g.ndom, P = p->g.P;
-    int64_t smallest = INT64_MAX;
-    int32_t largest = 0;
-    for (int q = 0; q < P; q++) {
-        int64_t n = 0;
-        for (int S = 0; S < D; S++) {
-            n += p->send[S * P + q];
-            largest = std::max(largest, p->send[S * P + q]);
-        }
-        smallest = std::min(smallest, n);
+    const int P = p->g.P;
+    int64_t total = 0;
+    for (int32_t n : p->send)
+        total += n;
+    const int64_t a = P > 0 ? total / P / std::max(1, p->n_cu) : 0;
+    if (a >= 4096)
+        return step ? 2048 : 1024;
+    if (a >= 256)
+        return 768;
+    return 256;
+}
+
+// Device copies of a per-pulse table and its chunk-aligned maps (coordinate
+// chunk k's entries at slot k * chunk, force chunks sharing the slot of the
+// coordinate chunk of the same map slice), 32-bit and, when the maps have a
+// 16-bit copy, 16-bit.
+static int upload_pulse_table(Plan* p, WorkTable& t, hipStream_t s)
+{
+    DDH_HIP(owned_alloc(p, &t.d_xch, t.xch.size()));
+    DDH_HIP(owned_alloc(p, &t.d_fch, t.fch.size()));
+    DDH_HIP(upload(t.d_xch, t.xch, s));
+    DDH_HIP(upload(t.d_fch, t.fch, s));
+    const int nch = (int)t.xch.size();
+    const size_t npad = (size_t)nch * t.chunk + kPadTail;
+    DDH_HIP(owned_alloc(p, &t.d_pad, npad));
+    DDH_HIP(hipMemsetAsync(t.d_pad, 0, sizeof(int32_t) * npad, s));
+    if (nch > 0)
+        hipLaunchKernelGGL(pad_maps_kernel<int32_t>, dim3(nch), dim3(256), 0, s, p->d_maps, t.d_xch,
+                           t.chunk, t.d_pad);
+    if (p->d_maps16) {
+        DDH_HIP(owned_alloc(p, &t.d_pad16, npad));
+        DDH_HIP(hipMemsetAsync(t.d_pad16, 0, sizeof(uint16_t) * npad, s));
+        if (nch > 0)
+            hipLaunchKernelGGL(pad_maps_kernel<uint16_t>, dim3(nch), dim3(256), 0, s, p->d_maps16,
+                               t.d_xch, t.chunk, t.d_pad16);
     }
-    // many small maps (every pulse has a map per compute unit, and none is
-    // longer than one round of a 1024-wide block at four entries per lane):
-    // one chunk per map, so each block carries a whole map and a launch's
-    // blocks are spread evenly over the compute units (384k atoms on 16x4x4
-    // domains: 23.6 -> 22.4 us per step, force pass 18.3 -> 15.4 us; splitting
-    // the 2560-entry maps into 512-entry chunks leaves some units with more
-    // blocks than others). The chunk is the longest map rounded up to 64
-    // entries: the chunk-aligned map copy holds one chunk per map, empty maps
-    // included, so a fixed 4096 would cost 24 KB per map where tiny domains
-    // have a few entries each.
-    if (D >= p->n_cu && largest <= 4096)
-        return std::max(64, (largest + 63) / 64 * 64);
-    for (int ch = 2048; ch > 512; ch /= 2)
-        if (smallest / ch >= 2ll * p->n_cu)
-            return ch;
-    // small pulses (at 512 entries, chunks for fewer than half the compute
-    // units): 256-entry chunks, one round per block (96k atoms:
-    // 9.04 -> 8.63 us per step; from 1M atoms on, 512 is faster)
-    return smallest / 512 >= p->n_cu / 2 ? 512 : 256;
+    DDH_HIP(hipGetLastError());
+    return DDH_OK;
 }
 
 // Consecutive named host ranges for the phases of one build.
@@ -1420,34 +1437,23 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     ph.next("build: chunk tables");
     p->fused.chunk = p->chunk_req > 0 ? p->chunk_req : fused_chunk(p);
     p->fused.wave = p->wave_chunks != 0;
-    p->pulse.chunk = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p);
+    p->pulse.chunk = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p, true);
+    const int chunk1 = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p, false);
     make_work_table(p, true, p->fused);
     make_work_table(p, false, p->pulse);
-    for (WorkTable* t : {&p->fused, &p->pulse}) {
-        DDH_HIP(owned_alloc(p, &t->d_xch, t->xch.size()));
-        DDH_HIP(owned_alloc(p, &t->d_fch, t->fch.size()));
-        DDH_HIP(upload(t->d_xch, t->xch, s));
-        DDH_HIP(upload(t->d_fch, t->fch, s));
-    }
-    {
-        // chunk-aligned maps of the per-pulse launches (every coordinate
-        // chunk of the table is a contiguous slice [hb, he) of one map)
-        WorkTable& t = p->pulse;
-        const int nch = (int)t.xch.size();
-        const size_t npad = (size_t)nch * t.chunk + kPadTail;
-        DDH_HIP(owned_alloc(p, &t.d_pad, npad));
-        DDH_HIP(hipMemsetAsync(t.d_pad, 0, sizeof(int32_t) * npad, s));
-        if (nch > 0)
-            hipLaunchKernelGGL(pad_maps_kernel<int32_t>, dim3(nch), dim3(256), 0, s, p->d_maps,
-                               t.d_xch, t.chunk, t.d_pad);
-        if (p->d_maps16) {
-            DDH_HIP(owned_alloc(p, &t.d_pad16, npad));
-            DDH_HIP(hipMemsetAsync(t.d_pad16, 0, sizeof(uint16_t) * npad, s));
-            if (nch > 0)
-                hipLaunchKernelGGL(pad_maps_kernel<uint16_t>, dim3(nch), dim3(256), 0, s,
-                                   p->d_maps16, t.d_xch, t.chunk, t.d_pad16);
-        }
-        DDH_HIP(hipGetLastError());
+    DDH_HIP(owned_alloc(p, &p->fused.d_xch, p->fused.xch.size()));
+    DDH_HIP(owned_alloc(p, &p->fused.d_fch, p->fused.fch.size()));
+    DDH_HIP(upload(p->fused.d_xch, p->fused.xch, s));
+    DDH_HIP(upload(p->fused.d_fch, p->fused.fch, s));
+    // per-pulse tables: every coordinate chunk is a contiguous slice [hb, he)
+    // of one map
+    if (int rc = upload_pulse_table(p, p->pulse, s))
+        return rc;
+    if (chunk1 != p->pulse.chunk) {
+        p->pulse1.chunk = chunk1;
+        make_work_table(p, false, p->pulse1);
+        if (int rc = upload_pulse_table(p, p->pulse1, s))
+            return rc;
     }
     if (p->refined_waits && P > 0) {
         WorkTable& t = p->fused;

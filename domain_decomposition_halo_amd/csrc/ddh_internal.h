@@ -38,6 +38,8 @@ enum CtrlWord : int {
     kCtrlEpochF = 80,  // force passes completed in any mode
     kCtrlTicket = 96,  // next dynamic work ticket of the running fused launch
     kCtrlDone = 128,   // work-groups that left the running fused launch
+    kCtrlPulseDone = 160,  // blocks that left the running per-pulse launch
+                           // that publishes its own flags at exit
     kCtrlError = 192,  // first device-side error code (0 = none)
     kCtrlWords = 224
 };
@@ -145,6 +147,9 @@ struct WorkTable {
 };
 constexpr int kPadTail = 4096;      // >= entries per round of any block
 
+// The passes an exchange call runs.
+enum Op : int { kOpCoords = 1, kOpForces = 2, kOpStep = 3 };
+
 struct Plan {
     int device = 0;
     int n_cu = 256;
@@ -181,6 +186,13 @@ struct Plan {
                                 // (takes effect at the next build)
     int home_sort = 0;          // home-atom sort of the build: 0 automatic,
                                 // 1 counting sort, 2 radix sort
+    int exit_publish = 0;       // per-pulse mode: 0 automatic, 1 the last
+                                // launch publishes its flags at exit, 2 a
+                                // one-wave launch after it does
+    int pad_maps = 0;           // per-pulse mode: 0 automatic, 1 blocks read
+                                // the chunk-aligned map copy (loads issued
+                                // before the descriptor arrives), 2 the maps
+                                // themselves, after the descriptor
     uint64_t* trace = nullptr;  // caller-owned device buffer (DDH_TUNE_TRACE)
 
     // host copies of the layout
@@ -189,7 +201,16 @@ struct Plan {
     std::vector<int32_t> send, split, recv, roff, shift;  // [S * P + p]
     std::vector<int64_t> map_off;  // [S * P + p]
     WorkTable fused;               // fused launch: waits and release flags set
-    WorkTable pulse;               // per-pulse launches: no waits
+    WorkTable pulse;               // per-pulse launches of step calls (both
+                                   // passes per launch): no waits
+    WorkTable pulse1;              // per-pulse launches of single-pass calls
+                                   // (a launch carries half the work: smaller
+                                   // chunks); unused (chunk 0) when it would
+                                   // equal the step table
+    const WorkTable& pulse_table(int op) const
+    {
+        return (op == kOpStep || pulse1.chunk == 0) ? pulse : pulse1;
+    }
 
     // device state
     int32_t* d_maps = nullptr;     // all maps, pulse-major
@@ -238,7 +259,6 @@ int sort_pairs(void* temp, size_t* temp_bytes, const uint32_t* keys_in, uint32_t
                const int32_t* vals_in, int32_t* vals_out, int n, int end_bit, hipStream_t s);
 
 // exchange launches (ddh_exchange.hip)
-enum Op : int { kOpCoords = 1, kOpForces = 2, kOpStep = 3 };
 int enqueue_exchange(Plan* plan, int op, float* x, float* f, hipStream_t stream);
 int enqueue_gather_home(Plan* plan, const float* xg, float* x, hipStream_t stream);
 int enqueue_wait_flag(Plan* plan, int idx, uint32_t epoch, hipStream_t stream);

@@ -335,7 +335,8 @@ int ddh_check(ddh_plan *plan, void *stream);
 #define DDH_TUNE_BLOCK 7           /* work-group width of the exchange launches:
                                     0 (automatic: fused 1024; per-pulse 1024
                                     for chunks of at least 1024 entries, else
-                                    256), 256 or 1024 */
+                                    256), 256, 512 (per-pulse launches; the
+                                    fused launch then takes 256) or 1024 */
 
 #define DDH_TUNE_STATIC_FIRST 8    /* fused mode: 0 (default) every work-group
                                     claims its tickets in start order, so no
@@ -380,6 +381,22 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     (per-atom device atomics, then a per-cell
                                     sort); 2 the radix sort. Takes effect at
                                     the next build. */
+
+#define DDH_TUNE_EXIT_PUBLISH 13   /* per-pulse mode with completion flags:
+                                    0 (default) automatic; 1 the call's last
+                                    launch publishes its pulses' flags when
+                                    its last block leaves (every block
+                                    releases its records first); 2 a one-wave
+                                    launch after the last pulse launch
+                                    publishes them */
+
+#define DDH_TUNE_PAD_MAPS 14       /* per-pulse mode: 0 (default) automatic;
+                                    1 every block loads its first map entries
+                                    from a chunk-aligned copy of the maps
+                                    before its chunk descriptor arrives (reads
+                                    the copy's zero padding too); 2 it loads
+                                    the descriptor first, then only the
+                                    chunk's own entries */
 
 /* Set a tuning knob; takes effect at the next build (CHUNK, WAVE_CHUNKS,
    HOME_SORT) or call. Library utility: the guide defines no such call.

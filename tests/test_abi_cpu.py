@@ -136,7 +136,11 @@ def test_mode_and_tune_validation():
             plan.set_mode(bad)
     plan.tune(ddh.DDH_TUNE_CHUNK, 100)
     plan.tune(ddh.DDH_TUNE_CHUNK, 0)
-    plan.tune(ddh.DDH_TUNE_BLOCK, 1024)
+    for v in (1024, 512, 256, 0):
+        plan.tune(ddh.DDH_TUNE_BLOCK, v)
+    for v in (1, 2, 0):
+        plan.tune(ddh.DDH_TUNE_EXIT_PUBLISH, v)
+        plan.tune(ddh.DDH_TUNE_PAD_MAPS, v)
     plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 1)
     plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 0)
     plan.tune(ddh.DDH_TUNE_FLAGS, 0)
@@ -149,7 +153,8 @@ def test_mode_and_tune_validation():
         plan.tune(ddh.DDH_TUNE_HOME_SORT, v)
     for key, val in [(ddh.DDH_TUNE_CHUNK, 10), (ddh.DDH_TUNE_CHUNK, 70000),
                      (ddh.DDH_TUNE_GRID, -1), (ddh.DDH_TUNE_SPIN_LIMIT, 0), (99, 1),
-                     (ddh.DDH_TUNE_BLOCK, 512), (ddh.DDH_TUNE_STATIC_FIRST, 2),
+                     (ddh.DDH_TUNE_BLOCK, 768), (ddh.DDH_TUNE_STATIC_FIRST, 2),
+                     (ddh.DDH_TUNE_EXIT_PUBLISH, 3), (ddh.DDH_TUNE_PAD_MAPS, -1),
                      (ddh.DDH_TUNE_FLAGS, 2), (ddh.DDH_TUNE_NARROW_MAPS, -1),
                      (ddh.DDH_TUNE_WAVE_CHUNKS, 3), (ddh.DDH_TUNE_HOME_SORT, 3),
                      (ddh.DDH_TUNE_HOME_SORT, -1)]:

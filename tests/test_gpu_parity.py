@@ -421,11 +421,15 @@ def test_without_completion_flags(k, workload_plan):
         g.close()
 
 
-def test_completion_flags_count_passes(workload_plan):
+@pytest.mark.parametrize("exit_pub", [0, 1, 2])
+def test_completion_flags_count_passes(exit_pub, workload_plan):
     """Every mode publishes every pulse's completion flag with the number of
-    passes completed so far; words past the plan's pulses stay zero."""
+    passes completed so far; words past the plan's pulses stay zero. Per-pulse
+    calls publish the last launch's flags from that launch's last block
+    (exit_pub 1) or from a one-wave launch after it (2)."""
     w, x, ref = workload_plan(4)
     g = GpuPlan(x, **w.params())
+    g.plan.tune(ddh.DDH_TUNE_EXIT_PUBLISH, exit_pub)
     P = g.P
     xl = g.new_coords()
     fl = torch.zeros((max(g.n_slots, 1), 3), dtype=torch.float32, device="cuda")
@@ -460,14 +464,17 @@ def test_completion_flags_count_passes(workload_plan):
     g.close()
 
 
-@pytest.mark.parametrize("mode", ["pulse", "fused"])
-def test_wait_flag_orders_a_consumer_stream(mode, workload_plan):
+@pytest.mark.parametrize("mode,exit_pub", [("pulse", 2), ("pulse", 1), ("fused", 0)])
+@pytest.mark.parametrize("k", [2, 3])
+def test_wait_flag_orders_a_consumer_stream(k, mode, exit_pub, workload_plan):
     """A consumer stream that waits on a pulse's flag reads that pulse's
     delivered records: the exchange on one stream, then on a second stream
     a flag wait followed by a gather of every receiver's region of the pulse,
-    for each pulse and two passes."""
-    w, x, ref = workload_plan(2)
+    for each pulse and two passes (per-pulse calls: the last pulse's flag from
+    its launch's last block, or from a one-wave launch after it)."""
+    w, x, ref = workload_plan(k)
     g = GpuPlan(x, **w.params(), mode=MODES[mode])
+    g.plan.tune(ddh.DDH_TUNE_EXIT_PUBLISH, exit_pub)
     base, nhome, ntotal, pul = g.tables()
     xl = g.new_coords()
     prod = torch.cuda.Stream()
@@ -488,6 +495,54 @@ def test_wait_flag_orders_a_consumer_stream(mode, workload_plan):
             torch.cuda.synchronize()
             assert g.plan.check() == ddh.DDH_OK
             assert np.array_equal(bits(got.cpu().numpy()), bits(ref.x_local[idx])), (p, epoch)
+    g.close()
+
+
+@pytest.mark.parametrize("exit_pub,pad", [(1, 1), (1, 2), (2, 2)])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_pulse_publish_and_map_forms(k, exit_pub, pad, workload_plan):
+    """Per-pulse launches whose last launch publishes the flags itself
+    (DDH_TUNE_EXIT_PUBLISH 1) or leaves them to a one-wave launch (2), and
+    whose blocks read the chunk-aligned map copy (DDH_TUNE_PAD_MAPS 1) or the
+    maps after the descriptor (2): several steps, eager and from the library's
+    graphs, then calls captured in a caller's graph and replayed with the
+    halo cleared before each replay."""
+    w, x, ref = workload_plan(k)
+    for mode in (ddh.DDH_MODE_PULSE, ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH):
+        g = GpuPlan(x, **w.params(), mode=mode)
+        g.plan.tune(ddh.DDH_TUNE_EXIT_PUBLISH, exit_pub)
+        g.plan.tune(ddh.DDH_TUNE_PAD_MAPS, pad)
+        check_steps(g, ref, 200 + k, steps=2)
+        check_steps(g, ref, 210 + k, steps=1, fused_step=True)
+        g.close()
+    g = GpuPlan(x, **w.params(), mode=ddh.DDH_MODE_PULSE)
+    g.plan.tune(ddh.DDH_TUNE_EXIT_PUBLISH, exit_pub)
+    g.plan.tune(ddh.DDH_TUNE_PAD_MAPS, pad)
+    xl = g.new_coords()
+    home = g.new_coords()
+    f0 = np.random.default_rng(220 + k).normal(0, 10, size=(g.n_slots, 3)).astype(np.float32)
+    fl = torch.from_numpy(f0).cuda()
+    fr = f0.copy()
+    ref.exchange_forces(fr)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.plan.exchange_step(xl, fl)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.plan.exchange_step(xl, fl)
+    for r in range(3):
+        xl.copy_(home)
+        fl.copy_(torch.from_numpy(f0))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(xl.cpu().numpy()[:g.n_slots]), bits(ref.x_local)), r
+        assert np.array_equal(bits(fl.cpu().numpy()[:g.n_slots]), bits(fr)), r
+    assert g.plan.check() == ddh.DDH_OK
+    del graph
     g.close()
 
 

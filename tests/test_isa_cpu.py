@@ -153,3 +153,32 @@ def test_wave_kernel_takes_no_barrier_and_releases(tmp_path):
     for name, lines in wk.items():
         assert not any("s_barrier" in ln for ln in lines), name
         assert sum("buffer_wbl2" in ln for ln in lines) >= 2, name
+
+
+def _scratch_users(src, tmp_path):
+    """Kernels of `src` that touch private (scratch) memory: register arrays
+    the compiler demoted to the stack, which turn every gathered record into
+    extra memory traffic."""
+    kernels = _isa(src, tmp_path)
+    return sorted(k for k, lines in kernels.items() if any("scratch_" in ln for ln in lines))
+
+
+def test_no_kernel_spills_to_scratch(tmp_path):
+    for name in ("ddh_exchange.hip", "ddh_build.hip"):
+        assert _scratch_users(os.path.join(CSRC, name), tmp_path) == [], name
+
+
+def test_pulse_kernels_gather_without_branches(tmp_path):
+    # a lane's gathers issue back to back: within a per-pulse kernel's first
+    # round no s_waitcnt vmcnt separates the coordinate gathers of one lane
+    kernels = _isa(os.path.join(CSRC, "ddh_exchange.hip"), tmp_path)
+    pk = {k: v for k, v in kernels.items() if "pulse_kernel" in k}
+    assert len(pk) >= 6
+    for name, lines in pk.items():
+        loads = [i for i, ln in enumerate(lines) if "global_load_dwordx3" in ln]
+        assert loads, name
+        # some pair of consecutive record loads with nothing but address
+        # arithmetic between them (the unrolled gather of one round)
+        assert any(all("s_waitcnt" not in lines[k] and "s_cbranch" not in lines[k]
+                       for k in range(a, b))
+                   for a, b in zip(loads, loads[1:])), name
