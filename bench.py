@@ -73,13 +73,14 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_file(variant: str, wname: str) -> str:
-    return os.path.join(PROFILES, f"traffic_{variant}_{wname}.md")
+def traffic_file(variant: str, wname: str, pass_: str = "step") -> str:
+    tag = variant if pass_ == "step" else f"{variant}_{pass_}"
+    return os.path.join(PROFILES, f"traffic_{tag}_{wname}.md")
 
 
-def read_traffic(variant: str, wname: str):
+def read_traffic(variant: str, wname: str, pass_: str = "step"):
     """Counter bytes per launch from a stored summary, if still current."""
-    path = traffic_file(variant, wname)
+    path = traffic_file(variant, wname, pass_)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -220,7 +221,7 @@ def run_gpu(args, w):
         # G steps captured in one graph and replayed: the host enqueues one
         # graph per G steps, so the GPU never waits for the host. G divides
         # the step count, so exactly --steps steps are timed.
-        G = graph_size(args.steps, args.graph_steps)
+        G = graph_size(args.steps, args.graph_steps, args.min_replays)
         n_rep = args.steps // G
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
@@ -369,6 +370,11 @@ def run_gpu(args, w):
              or args.wide_maps or args.wave_chunks or args.cold or args.exit_publish
              or args.pad_maps or args.pass_ != "step")
     traffic = None if tuned else read_traffic(variant, w.name)
+    if passes is not None:
+        # each pass's counter traffic, from its own stored summary
+        for nm in ("coords", "forces"):
+            t = None if tuned else read_traffic(variant, w.name, nm)
+            passes[nm + "_traffic"] = t
     fused_name = "wave_kernel" if args.wave_chunks else "exchange_kernel"
     kernel = {"step": f"{fused_name} (fused step, one launch)",
               "split": f"{fused_name} (coordinate launch + force launch)",
@@ -627,8 +633,8 @@ def run_cpu_baseline(w, seconds: float):
 
 # --------------------------------------------------------- counter summary
 
-def summarize_pmc(fetch_csv, write_csv, variant, wname, copy_mb, command):
-    """Turn two rocprofv3 --pmc runs into profiles/traffic_<variant>_<wname>.md."""
+def summarize_pmc(fetch_csv, write_csv, variant, wname, copy_mb, command, pass_="step"):
+    """Turn two rocprofv3 --pmc runs into profiles/traffic_<variant>[_<pass>]_<wname>.md."""
     def rows(path):
         with open(path) as fh:
             return list(csv.DictReader(fh))
@@ -657,7 +663,8 @@ def summarize_pmc(fetch_csv, write_csv, variant, wname, copy_mb, command):
         f_ex = sum(sum(fk[k]) for k in ex) / n_steps
         w_ex = sum(sum(wk.get(k, [])) for k in ex) / n_steps
         n_disp = sum(len(fk[k]) for k in ex)
-        unit = "step (all per-pulse launches of one step)"
+        unit = ("step (all per-pulse launches of one step)" if pass_ == "step" else
+                f"call (all per-pulse launches of one {pass_} call)")
     else:
         ex = [k for k in fk if "exchange_kernel" in k]
         if not ex or not cp:
@@ -675,10 +682,12 @@ def summarize_pmc(fetch_csv, write_csv, variant, wname, copy_mb, command):
     sf = expect_kib / f_cp if f_cp else 1.0
     sw = expect_kib / w_cp if w_cp else 1.0
     traffic = (f_ex * sf + w_ex * sw) * 1024.0
-    path = traffic_file(variant, wname)
+    path = traffic_file(variant, wname, pass_)
     os.makedirs(os.path.dirname(path), exist_ok=True)
+    what = {"step": "coordinate + force pass", "coords": "coordinate pass alone",
+            "forces": "force pass alone"}[pass_]
     with open(path, "w") as fh:
-        fh.write(f"# HBM traffic of the exchange, variant {variant}, workload {wname}\n\n")
+        fh.write(f"# HBM traffic of the exchange, variant {variant}, {what}, workload {wname}\n\n")
         fh.write("Two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),\n"
                  "scaled by what the same counters read for a plain copy of known size.\n\n")
         fh.write(f"Command (each counter in its own run):\n\n```\n{command}\n```\n\n")
@@ -695,7 +704,77 @@ def summarize_pmc(fetch_csv, write_csv, variant, wname, copy_mb, command):
         fh.write(f"- scale_fetch: {sf:.4f}\n")
         fh.write(f"- scale_write: {sw:.4f}\n")
         fh.write(f"- traffic_bytes_per_launch: {traffic:.0f}\n")
+        fh.write(f"- scaled_FETCH_bytes_per_unit: {f_ex * sf * 1024.0:.0f}\n")
+        fh.write(f"- scaled_WRITE_bytes_per_unit: {w_ex * sw * 1024.0:.0f}\n")
     print(path)
+
+
+def summarize_trace(trace_dir, wname, label, command, bench_line, out_path):
+    """Turn a rocprofv3 --kernel-trace --stats run into a profiles/ summary:
+    the statistics table and, for the exchange's launches, the median
+    duration of each launch position in one step over the last 200 steps."""
+    import glob
+    import statistics
+
+    def find(pattern):
+        hits = sorted(glob.glob(os.path.join(trace_dir, "**", pattern), recursive=True))
+        if not hits:
+            raise SystemExit(f"no {pattern} under {trace_dir}")
+        return hits[-1]
+
+    with open(find("*kernel_stats.csv")) as fh:
+        stats = list(csv.DictReader(fh))
+    with open(find("*kernel_trace.csv")) as fh:
+        trace = list(csv.DictReader(fh))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+
+    def short(name, n=70):
+        name = name.replace("ddh::(anonymous namespace)::", "")
+        return name if len(name) <= n else name[:n]
+
+    # one step: the exchange launches (pulse or fused kernels) from one
+    # signal_kernel (or fused launch) to the next
+    ex = [r for r in trace if any(k in r["Kernel_Name"] for k in
+                                  ("pulse_kernel", "signal_kernel", "exchange_kernel", "wave_kernel"))]
+    steps, cur = [], []
+    for r in ex:
+        cur.append(r)
+        if "signal_kernel" in r["Kernel_Name"] or "exchange_kernel" in r["Kernel_Name"] \
+                or "wave_kernel" in r["Kernel_Name"]:
+            steps.append(cur)
+            cur = []
+    # the timed steps all have the launch count of the last step
+    n_l = len(steps[-1]) if steps else 0
+    steps = [st for st in steps if len(st) == n_l][-200:]
+    rows = []
+    for k in range(n_l):
+        durs = [(int(st[k]["End_Timestamp"]) - int(st[k]["Start_Timestamp"])) / 1e3 for st in steps]
+        gaps = [(int(st[k]["Start_Timestamp"]) - int(st[k - 1]["End_Timestamp"])) / 1e3
+                for st in steps] if k > 0 else [0.0]
+        r = steps[-1][k]
+        grid = r.get("Grid_Size_X") or r.get("Grid_Size") or ""
+        vgpr = r.get("VGPR_Count") or r.get("Arch_VGPR_Count") or ""
+        rows.append((short(r["Kernel_Name"], 60), grid, vgpr, statistics.median(durs),
+                     statistics.median(gaps)))
+    with open(out_path, "w") as fh:
+        fh.write(f"# Kernel trace: {label}, workload {wname}\n\n")
+        fh.write("Command (run from the repository root on one MI355X):\n\n")
+        fh.write(f"```\n{command}\n```\n\n")
+        if bench_line:
+            fh.write(f"bench line of the same run: {bench_line}\n\n")
+        fh.write("## Kernel statistics (rocprofv3 `--stats`, all dispatches of the run)\n\n")
+        fh.write("| kernel | calls | avg us | min us | max us | share % |\n|---|---|---|---|---|---|\n")
+        for r in stats[:10]:
+            fh.write(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |\n")
+        fh.write(f"\n## Launches of one step (kernel trace, median over the last {len(steps)} steps)\n\n")
+        fh.write("| # | kernel | grid (threads) | VGPRs | median us | median gap before (us) |\n"
+                 "|---|---|---|---|---|---|\n")
+        for k, (name, grid, vgpr, d, g) in enumerate(rows):
+            fh.write(f"| {k} | `{name}` | {grid} | {vgpr} | {d:.2f} | {g:.2f} |\n")
+        fh.write(f"| | sum of durations | | | {sum(r[3] for r in rows):.2f} | |\n")
+    print(out_path)
 
 
 # ------------------------------------------------------------------- main
@@ -754,7 +833,15 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
                     help="after timing, copy a buffer of this size (counter scaling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
-    ap.add_argument("--pmc-command", default="")
+    ap.add_argument("--pmc-command", default="",
+                    help="the profiler command, recorded in a --summarize-* output")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "OUT_MD", "LABEL"),
+                    help="write a kernel-trace summary from a rocprofv3 --kernel-trace --stats "
+                         "output directory")
+    ap.add_argument("--bench-line", default="",
+                    help="with --summarize-trace: the bench result of the profiled run")
+    ap.add_argument("--min-replays", type=int, default=5,
+                    help="timed graphs hold at most --steps / this many steps")
     args = ap.parse_args()
     if args.variant == "staged":
         # the host-orchestrated baseline waits on the host inside every call:
@@ -769,7 +856,11 @@ def main():
             sys.exit("--summarize-pmc names the variant the counters were taken on: "
                      "pass --variant step|split|pulse")
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.variant, w.name,
-                      args.copy_probe, args.pmc_command)
+                      args.copy_probe, args.pmc_command, args.pass_)
+        return
+    if args.summarize_trace:
+        tdir, out_path, label = args.summarize_trace
+        summarize_trace(tdir, w.name, label, args.pmc_command, args.bench_line, out_path)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: every domain is a virtual rank inside one "
