@@ -49,7 +49,9 @@ EXPORTS = ("ddh_plan_create", "ddh_plan_destroy", "ddh_last_error", "ddh_build_m
            "ddh_domain_info", "ddh_pulse_info", "ddh_copy_maps", "ddh_local_ids",
            "ddh_flags", "ddh_copy_flags", "ddh_wait_flag",
            "ddh_gather_home", "ddh_exchange_coords", "ddh_exchange_forces",
-           "ddh_exchange_step", "ddh_set_mode", "ddh_check", "ddh_tune")
+           "ddh_exchange_step", "ddh_exchange_staged_static", "ddh_set_mode", "ddh_check",
+           "ddh_tune")
+DDH_STATIC_STAGE_BYTES = 64 << 20
 
 
 class ddh_params(ctypes.Structure):
@@ -103,6 +105,7 @@ def _load():
         "ddh_exchange_coords": ([V, P, I64, V], ctypes.c_int),
         "ddh_exchange_forces": ([V, P, I64, V], ctypes.c_int),
         "ddh_exchange_step": ([V, P, P, I64, V], ctypes.c_int),
+        "ddh_exchange_staged_static": ([V, P, P, I64, V], ctypes.c_int),
         "ddh_set_mode": ([V, I32], ctypes.c_int),
         "ddh_check": ([V, V], ctypes.c_int),
         "ddh_tune": ([V, I32, I64], ctypes.c_int),
@@ -243,6 +246,15 @@ class Plan:
         _check(_lib.ddh_exchange_step(self._h, _dev_ptr(x_local, "float32", "x_local"),
                                       _dev_ptr(f_local, "float32", "f_local"), cap,
                                       _stream(stream)), "ddh_exchange_step")
+
+    def exchange_staged_static(self, x_local=None, f_local=None, stream=None):
+        """The host-orchestrated exchange with its staging in the library's
+        static device buffer (no allocation); either array may be None."""
+        caps = [t.numel() // 3 for t in (x_local, f_local) if t is not None]
+        xp = _dev_ptr(x_local, "float32", "x_local") if x_local is not None else None
+        fp = _dev_ptr(f_local, "float32", "f_local") if f_local is not None else None
+        _check(_lib.ddh_exchange_staged_static(self._h, xp, fp, min(caps) if caps else 0,
+                                               _stream(stream)), "ddh_exchange_staged_static")
 
     # -- control
     def set_mode(self, mode: int):

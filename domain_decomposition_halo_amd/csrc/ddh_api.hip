@@ -368,6 +368,26 @@ int ddh_exchange_step(ddh_plan* p, float* x, float* f, int64_t cap, void* stream
     return enqueue_exchange(p, kOpStep, x, f, (hipStream_t)stream);
 }
 
+int ddh_exchange_staged_static(ddh_plan* p, float* x, float* f, int64_t cap, void* stream)
+{
+    Range range("ddh_exchange_staged_static");
+    int rc = check_built(p);
+    if (rc)
+        return rc;
+    if (!x && !f)
+        return fail(DDH_EINVAL, "ddh_exchange_staged_static: no coordinate or force array");
+    if (x && (rc = check_buffer(p, x, cap, "ddh_exchange_staged_static (coordinates)")))
+        return rc;
+    if (f && (rc = check_buffer(p, f, cap, "ddh_exchange_staged_static (forces)")))
+        return rc;
+    const uintptr_t xb = (uintptr_t)x, fb = (uintptr_t)f;
+    const uintptr_t nb = (uintptr_t)p->n_slots * 3u * sizeof(float);
+    if (x && f && nb > 0 && xb < fb + nb && fb < xb + nb)
+        return fail(DDH_EINVAL, "ddh_exchange_staged_static: coordinate and force arrays overlap");
+    const int op = (x ? kOpCoords : 0) | (f ? kOpForces : 0);
+    return enqueue_staged_static(p, op, x, f, (hipStream_t)stream);
+}
+
 int ddh_set_mode(ddh_plan* p, int32_t mode)
 {
     if (!p)

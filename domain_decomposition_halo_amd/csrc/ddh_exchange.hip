@@ -56,6 +56,8 @@
 // the control block and the work-group carries on, so every launch drains.
 #pragma clang fp contract(off)
 
+#include <mutex>
+
 #include "ddh_internal.h"
 
 namespace ddh {
@@ -1114,13 +1116,10 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s, int mode)
 // order): one copy per sender of the receiver's region into the staging
 // buffer, a host wait, one unpack launch that adds, a host wait. The staging
 // buffer holds every map entry once (entry i of map (S, p) at map_off + i).
-int enqueue_staged(Plan* p, int op, float* x, float* f, hipStream_t s)
+// stage: a device buffer of at least 3 * n_halo floats.
+int enqueue_staged(Plan* p, int op, float* x, float* f, hipStream_t s, float* stage)
 {
     const int P = p->g.P, D = p->g.ndom;
-    if (!p->d_stage && p->n_halo > 0) {
-        DDH_HIP(hipMalloc((void**)&p->d_stage, sizeof(float) * 3 * (size_t)p->n_halo));
-        p->owned.push_back(p->d_stage);
-    }
     const WorkTable& t = p->pulse;
     const auto& xb = t.xpulse_begin;
     const auto& fb = t.fpulse_begin;
@@ -1132,7 +1131,7 @@ int enqueue_staged(Plan* p, int op, float* x, float* f, hipStream_t s)
             if (n == 0)
                 continue;
             float* region = arr + 3 * (p->base[p->recv[it]] + p->roff[it]);
-            float* staged = p->d_stage + 3 * p->map_off[it];
+            float* staged = stage + 3 * p->map_off[it];
             DDH_HIP(hipMemcpyAsync(to_region ? region : staged, to_region ? staged : region,
                                    sizeof(float) * 3 * n, hipMemcpyDeviceToDevice, s));
         }
@@ -1141,7 +1140,7 @@ int enqueue_staged(Plan* p, int op, float* x, float* f, hipStream_t s)
     int rc = DDH_OK;
     if (op & kOpCoords)
         for (int q = 0; q < P; q++) {
-            if ((rc = launch_pulse(p, x, f, t, xb[q], xb[q + 1], 0, 0, s, none, none, p->d_stage)))
+            if ((rc = launch_pulse(p, x, f, t, xb[q], xb[q + 1], 0, 0, s, none, none, stage)))
                 return rc;
             DDH_HIP(hipStreamSynchronize(s));
             if ((rc = copies(q, x, true)))
@@ -1153,7 +1152,7 @@ int enqueue_staged(Plan* p, int op, float* x, float* f, hipStream_t s)
             if ((rc = copies(P - 1 - r, f, false)))
                 return rc;
             DDH_HIP(hipStreamSynchronize(s));
-            if ((rc = launch_pulse(p, x, f, t, 0, 0, fb[r], fb[r + 1], s, none, none, p->d_stage)))
+            if ((rc = launch_pulse(p, x, f, t, 0, 0, fb[r], fb[r + 1], s, none, none, stage)))
                 return rc;
             DDH_HIP(hipStreamSynchronize(s));
         }
@@ -1184,7 +1183,12 @@ int enqueue_exchange(Plan* p, int op, float* x, float* f, hipStream_t s)
         if (p->mode == DDH_MODE_STAGED) {
             if (captured)
                 return fail(DDH_EINVAL, "DDH_MODE_STAGED waits on the host: it cannot be captured");
-            return enqueue_staged(p, op, x, f, s);
+            // the staging buffer is allocated at the first staged call
+            if (!p->d_stage && p->n_halo > 0) {
+                DDH_HIP(hipMalloc((void**)&p->d_stage, sizeof(float) * 3 * (size_t)p->n_halo));
+                p->owned.push_back(p->d_stage);
+            }
+            return enqueue_staged(p, op, x, f, s, p->d_stage);
         }
         return enqueue_raw(p, op, x, f, s, p->effective_mode(captured));
     }
@@ -1217,6 +1221,60 @@ int enqueue_exchange(Plan* p, int op, float* x, float* f, hipStream_t s)
     }
     DDH_HIP(hipGraphLaunch(found->second, s));
     return DDH_OK;
+}
+
+// ---- the host-orchestrated exchange without allocation
+//
+// Its staging buffer lives in the file-scope device array below instead of
+// device memory allocated at the first staged call, for callers that cannot
+// allocate. Each device that loads the library holds one copy of the array
+// until the process ends. In host code the array's name is only a host-side
+// stand-in: kernels and copies get its per-device address, resolved once per
+// device with hipGetSymbolAddress while that device is current.
+static __device__ __align__(256) unsigned char scratch[kStaticStageBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int enqueue_staged_static(Plan* p, int op, float* x, float* f, hipStream_t s)
+{
+    const size_t need = sizeof(float) * 3 * (size_t)p->n_halo;
+    if (need > kStaticStageBytes)
+        return fail(DDH_ECAPACITY, "ddh_exchange_staged_static: the layout's " +
+                                       std::to_string(p->n_halo) + " halo entries need " +
+                                       std::to_string(need) + " bytes of staging, above the " +
+                                       std::to_string(kStaticStageBytes) + "-byte static buffer");
+    if (s) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+            (void)hipGetLastError();
+            cs = hipStreamCaptureStatusNone;
+        }
+        if (cs == hipStreamCaptureStatusActive)
+            return fail(DDH_EINVAL,
+                        "ddh_exchange_staged_static waits on the host: it cannot be captured");
+    }
+    int dev = -1;
+    DDH_HIP(hipGetDevice(&dev));
+    if (dev != p->device)
+        return fail(DDH_EINVAL, "ddh_exchange_staged_static: the plan's device must be current");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DDH_EINVAL, "ddh_exchange_staged_static: device index out of range");
+    void* ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch_ptr[dev]) {
+            DDH_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+            g_scratch_ptr[dev] = ptr;
+        }
+        ptr = g_scratch_ptr[dev];
+    }
+    if (p->g.P == 0 || p->fused.nchunks.empty())
+        return DDH_OK;
+    return enqueue_staged(p, op, x, f, s, static_cast<float*>(ptr));
 }
 
 int enqueue_wait_flag(Plan* p, int idx, uint32_t epoch, hipStream_t s)

@@ -262,5 +262,9 @@ int sort_pairs(void* temp, size_t* temp_bytes, const uint32_t* keys_in, uint32_t
 int enqueue_exchange(Plan* plan, int op, float* x, float* f, hipStream_t stream);
 int enqueue_gather_home(Plan* plan, const float* xg, float* x, hipStream_t stream);
 int enqueue_wait_flag(Plan* plan, int idx, uint32_t epoch, hipStream_t stream);
+// the host-orchestrated exchange with its staging in the library's static
+// device array (no allocation); at most kStaticStageBytes of staging
+constexpr size_t kStaticStageBytes = (size_t)DDH_STATIC_STAGE_BYTES;
+int enqueue_staged_static(Plan* plan, int op, float* x, float* f, hipStream_t stream);
 
 }  // namespace ddh

@@ -289,6 +289,26 @@ int ddh_exchange_forces(ddh_plan *plan, float *f_local_dev, int64_t capacity_slo
 int ddh_exchange_step(ddh_plan *plan, float *x_local_dev, float *f_local_dev,
                       int64_t capacity_slots, void *stream);
 
+/*
+ * The host-orchestrated exchange of DDH_MODE_STAGED (the same launches,
+ * copies and host waits, and the same results, whatever mode the plan is
+ * set to), for callers that cannot allocate device memory: harnesses that
+ * forbid it and tight serving loops. The staging buffer that DDH_MODE_STAGED
+ * allocates at its first call is here a static device array of the library
+ * (DDH_STATIC_STAGE_BYTES, one per device, held until the process ends), so
+ * the call allocates nothing. x_local_dev (coordinate pass) and/or
+ * f_local_dev (force pass, after the coordinate pass when both are given)
+ * may be NULL, not both; the two must not overlap. The plan's device must be
+ * current. Returns when the passes are complete; it cannot be captured.
+ * Every call on a device shares that device's array: calls that overlap in
+ * time on one device (other host threads, other plans) race. Errors:
+ * DDH_EINVAL, DDH_ESTATE, DDH_ECAPACITY (a buffer smaller than the layout,
+ * or 12 * n_halo above DDH_STATIC_STAGE_BYTES), DDH_EHIP.
+ */
+#define DDH_STATIC_STAGE_BYTES 67108864 /* 64 MiB */
+int ddh_exchange_staged_static(ddh_plan *plan, float *x_local_dev, float *f_local_dev,
+                               int64_t capacity_slots, void *stream);
+
 /* Select DDH_MODE_FUSED, DDH_MODE_PULSE or DDH_MODE_AUTO, optionally
    | DDH_MODE_GRAPH, or DDH_MODE_STAGED alone: the execution forms of
    "Enabling parallelism across pulses through kernel fusion" (one launch),
