@@ -715,7 +715,7 @@ def test_empty_and_one_sided_inputs():
 @pytest.mark.parametrize("grid,n", [((16, 4, 4), 3000), ((8, 8, 8), 1500), ((16, 4, 4), 40000)])
 def test_many_small_maps(grid, n, mode):
     """At least one domain per compute unit and short maps, many of them
-    empty: the per-pulse launches then take one chunk per map."""
+    empty (chunks of empty maps, chunks holding a whole map)."""
     box = (15.66, 15.66, 15.66)
     x = W.uniform_positions(n, box, seed=n + grid[0])
     ref = oracle.OraclePlan(x, grid, box, 1.2)
