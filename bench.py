@@ -138,6 +138,8 @@ def run_gpu(args, w):
         plan.tune(ddh.DDH_TUNE_EXIT_PUBLISH, args.exit_publish)
     if args.pad_maps:
         plan.tune(ddh.DDH_TUNE_PAD_MAPS, args.pad_maps)
+    if args.heads_first:
+        plan.tune(ddh.DDH_TUNE_HEADS_FIRST, 1)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -368,7 +370,7 @@ def run_gpu(args, w):
     # the stored counters were taken with the default settings
     tuned = (args.chunk or args.grid or args.block or args.static_first or args.no_flags
              or args.wide_maps or args.wave_chunks or args.cold or args.exit_publish
-             or args.pad_maps or args.pass_ != "step")
+             or args.pad_maps or args.heads_first or args.pass_ != "step")
     traffic = None if tuned else read_traffic(variant, w.name)
     if passes is not None:
         # each pass's counter traffic, from its own stored summary
@@ -551,6 +553,151 @@ def run_overlap(args, w):
     out["workload"] = w.name
     out["mode"] = args.variant
     return out
+
+
+# ------------------------------------------------------ fused launch events
+
+def run_event_trace(args, w, out_path):
+    """One fused step with the library's device event log (DDH_TUNE_TRACE):
+    per work-group, the ticket claims, independent part done, wait done,
+    chunk done, release and exit, on the 100 MHz wall clock. Writes a summary
+    per stage (pass and pulse): when its chunks start and end, and the
+    medians of their work, wait and release times."""
+    import collections
+
+    import numpy as np
+    import torch
+
+    import domain_decomposition_halo_amd as ddh
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    xg = torch.from_numpy(W.positions(w)).to(dev)
+    plan = ddh.Plan(**w.params())
+    plan.set_mode(ddh.DDH_MODE_FUSED)
+    grid = args.grid or torch.cuda.get_device_properties(dev).multi_processor_count
+    if args.grid:
+        plan.tune(ddh.DDH_TUNE_GRID, args.grid)
+    if args.heads_first:
+        plan.tune(ddh.DDH_TUNE_HEADS_FIRST, 1)
+    lay = plan.build_maps(xg)
+    n = lay["n_slots"]
+    xl = torch.zeros((n, 3), dtype=torch.float32, device=dev)
+    plan.gather_home(xg, xl)
+    fl = torch.from_numpy(W.forces(w, n)).to(dev)
+    for _ in range(max(args.warmup, 3)):
+        plan.exchange_step(xl, fl)
+    torch.cuda.synchronize()
+    buf = torch.zeros(2 * 64 * grid, dtype=torch.int64, device=dev)
+    plan.tune(ddh.DDH_TUNE_TRACE, buf.data_ptr())
+    plan.exchange_step(xl, fl)
+    torch.cuda.synchronize()
+    plan.tune(ddh.DDH_TUNE_TRACE, 0)
+    assert plan.check() == ddh.DDH_OK
+    D, P = lay["n_domains"], lay["n_pulses"]
+    # tickets: coordinate chunks pulse by pulse (with --heads-first: every
+    # pulse's heads, then every pulse's tails), then force chunks in
+    # decreasing pulse order. At the fused launch's default chunk size of
+    # 8192 entries a map of n entries has max(1, ceil(n / 8192)) chunks, or
+    # ceil(head / 8192) + ceil(tail / 8192) (at least one) heads first.
+    CH = 8192
+    info = [[plan.pulse_info(S, q) for q in range(P)] for S in range(D)]
+    def n_head(S, q):
+        n, h = info[S][q][0], info[S][q][1]
+        nh, nt = -(-h // CH), -(-(n - h) // CH)
+        return nh if nh + nt else 1
+    def n_tail(S, q):
+        n, h = info[S][q][0], info[S][q][1]
+        return -(-(n - h) // CH)
+    def n_all(S, q):
+        return n_head(S, q) + n_tail(S, q) if args.heads_first else max(1, -(-info[S][q][0] // CH))
+    bounds = []
+    acc = 0
+    if args.heads_first:
+        for q in range(P):
+            m = sum(n_head(S, q) for S in range(D))
+            bounds.append((acc, acc + m, f"coords heads pulse {q}"))
+            acc += m
+        for q in range(P):
+            m = sum(n_tail(S, q) for S in range(D))
+            bounds.append((acc, acc + m, f"coords tails pulse {q}"))
+            acc += m
+    else:
+        for q in range(P):
+            m = sum(n_all(S, q) for S in range(D))
+            bounds.append((acc, acc + m, f"coords pulse {q}"))
+            acc += m
+    for q in range(P - 1, -1, -1):
+        m = sum(n_all(S, q) for S in range(D))
+        bounds.append((acc, acc + m, f"forces pulse {q}"))
+        acc += m
+    rec = buf.cpu().numpy().view(np.uint64).reshape(grid, 64, 2)
+    starts = [int(rec[b, 0, 1]) for b in range(grid) if int(rec[b, 0, 0]) >> 32 == 1]
+    t0 = min(starts)
+    chunks, exits = [], []
+    for b in range(grid):
+        cur = None
+        for r in rec[b]:
+            code, info, t = int(r[0]) >> 32, int(r[0]) & 0xFFFFFFFF, (int(r[1]) - t0) * 10
+            if code == 2:
+                if cur:
+                    chunks.append(cur)
+                cur = dict(wg=b, ticket=info, claim=t)
+            elif code in (3, 4, 5, 6) and cur is not None:
+                cur[{3: "head", 4: "waited", 5: "done", 6: "released"}[code]] = t
+                if code == 5:
+                    cur["n"] = info
+            elif code == 7:
+                if cur:
+                    chunks.append(cur)
+                cur = None
+                exits.append(t)
+    plan.close()
+    if not exits:
+        # a work-group that logged more than 64 events stops logging: its
+        # exit is then the last event it logged
+        exits = [max(c.get("released", c.get("done", c["claim"])) for c in chunks)]
+
+    def stage(t):
+        return next((name for lo, hi, name in bounds if lo <= t < hi), "other")
+    by = collections.defaultdict(list)
+    for c in chunks:
+        by[stage(c["ticket"])].append(c)
+    span = max(exits) / 1e3
+
+    def q3(vals):
+        a = np.asarray(vals, dtype=np.float64) / 1e3
+        return "%.2f / %.2f / %.2f" % (np.percentile(a, 10), np.median(a), np.percentile(a, 90))
+    order = [name for _, _, name in bounds]
+    busy = collections.defaultdict(float)
+    for c in chunks:
+        busy[c["wg"]] += c.get("released", c.get("done", c["claim"])) - c["claim"]
+    with open(out_path, "w") as fh:
+        fh.write(f"# Fused launch event log, workload {w.name}\n\n")
+        fh.write("One fused step (`exchange_kernel`, both passes, all pulses) with the "
+                 "library's device event log (`DDH_TUNE_TRACE`), after warm-up steps. "
+                 "Times in us from the first work-group's start (100 MHz wall clock). "
+                 "Command (repository root, one MI355X):\n\n")
+        fh.write(f"```\n{args.pmc_command}\n```\n\n")
+        fh.write(f"- work-groups: {grid} (1024 lanes); chunks: {len(chunks)}; "
+                 f"span to the last exit: {span:.1f} us\n")
+        fh.write(f"- median work-group busy fraction (claim to release, summed): "
+                 f"{np.median([busy[b] * 1e-3 / span for b in busy]):.2f}\n\n")
+        fh.write("| stage | chunks | entries (median) | chunk start (p10 / median / p90) | "
+                 "chunk end | work: claim to done | wait | release |\n"
+                 "|---|---|---|---|---|---|---|---|\n")
+        for k in order:
+            v = by.get(k, [])
+            if not v:
+                continue
+            fh.write(f"| {k} | {len(v)} | {int(np.median([c.get('n', 0) for c in v]))} | "
+                     f"{q3([c['claim'] for c in v])} | "
+                     f"{q3([c.get('released', c.get('done', c['claim'])) for c in v])} | "
+                     f"{q3([c.get('done', c['claim']) - c['claim'] for c in v])} | "
+                     f"{q3([(c['waited'] - c.get('head', c['claim'])) if 'waited' in c else 0 for c in v])} | "
+                     f"{q3([c.get('released', c.get('done', 0)) - c.get('done', 0) for c in v])} |\n")
+    print(out_path)
 
 
 # ------------------------------------------------------------- CPU baseline
@@ -801,6 +948,8 @@ def main():
                     help="DDH_TUNE_EXIT_PUBLISH (0 automatic)")
     ap.add_argument("--pad-maps", type=int, default=0, choices=[0, 1, 2],
                     help="DDH_TUNE_PAD_MAPS (0 automatic)")
+    ap.add_argument("--heads-first", action="store_true",
+                    help="fused launch: heads-first ticket order (DDH_TUNE_HEADS_FIRST = 1)")
     ap.add_argument("--pass", dest="pass_", default="step", choices=["step", "coords", "forces"],
                     help="time one pass alone (coordinate or force pass) instead of the step; "
                          "with --only-step, for per-pass profiler runs")
@@ -838,6 +987,9 @@ def main():
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "OUT_MD", "LABEL"),
                     help="write a kernel-trace summary from a rocprofv3 --kernel-trace --stats "
                          "output directory")
+    ap.add_argument("--event-log", metavar="OUT_MD", default="",
+                    help="run one fused step with the device event log and write its "
+                         "per-stage summary (give the command line with --pmc-command)")
     ap.add_argument("--bench-line", default="",
                     help="with --summarize-trace: the bench result of the profiled run")
     ap.add_argument("--min-replays", type=int, default=5,
@@ -861,6 +1013,9 @@ def main():
     if args.summarize_trace:
         tdir, out_path, label = args.summarize_trace
         summarize_trace(tdir, w.name, label, args.pmc_command, args.bench_line, out_path)
+        return
+    if args.event_log:
+        run_event_trace(args, w, args.event_log)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: every domain is a virtual rank inside one "

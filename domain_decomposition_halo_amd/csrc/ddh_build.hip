@@ -877,12 +877,58 @@ static void make_work_table(const Plan* p, bool waits, WorkTable& t)
     t.fch.clear();
     t.xpulse_begin.assign((size_t)P + 1, 0);
     t.fpulse_begin.assign((size_t)P + 1, 0);
-    // coordinates in pulse order (a chunk waits only on earlier pulses)
-    for (int q = 0; q < P; q++) {
-        t.xpulse_begin[q] = (int)t.xch.size();
-        for (int S = 0; S < D; S++)
-            for (int k = 0; k < t.nchunks[S * P + q]; k++)
-                t.xch.push_back(xchunk(S * P + q, k));
+    if (waits && t.heads_first && !t.wave) {
+        // heads first: every map's independent head in chunks of its own,
+        // all of them (pulse order) before any dependent tail (pulse
+        // order), so no head ever waits and the tails follow the regions
+        // they read. A map has ceil(h / CH) head and ceil(tl / CH) tail
+        // chunks (an empty map one empty head chunk), and the force pass
+        // slices it into the same number of chunks. xpulse_begin marks the
+        // heads of each pulse only (the fused launch does not use it).
+        std::vector<int> nh((size_t)D * P), nt((size_t)D * P);
+        for (int it = 0; it < D * P; it++) {
+            const int h = p->split[it], tl = p->send[it] - h;
+            nh[it] = (h + CH - 1) / CH;
+            nt[it] = (tl + CH - 1) / CH;
+            if (nh[it] + nt[it] == 0)
+                nh[it] = 1;
+            t.nchunks[it] = nh[it] + nt[it];
+        }
+        for (int q = 0; q < P; q++) {
+            t.xpulse_begin[q] = (int)t.xch.size();
+            for (int S = 0; S < D; S++) {
+                const int it = S * P + q, h = p->split[it];
+                for (int k = 0; k < nh[it]; k++) {
+                    DChunk d = base_chunk(it);
+                    d.ctr = d.R * P + d.p;
+                    d.hb = (int32_t)((int64_t)h * k / nh[it]);
+                    d.he = (int32_t)((int64_t)h * (k + 1) / nh[it]);
+                    d.tb = d.te = d.he;
+                    t.xch.push_back(d);
+                }
+            }
+        }
+        for (int q = 0; q < P; q++)
+            for (int S = 0; S < D; S++) {
+                const int it = S * P + q, h = p->split[it], tl = p->send[it] - h;
+                for (int k = 0; k < nt[it]; k++) {
+                    DChunk d = base_chunk(it);
+                    d.ctr = d.R * P + d.p;
+                    d.hb = d.he = h;
+                    d.tb = h + (int32_t)((int64_t)tl * k / nt[it]);
+                    d.te = h + (int32_t)((int64_t)tl * (k + 1) / nt[it]);
+                    d.wait_a = conservative ? (1u << d.p) - 1u : 0u;
+                    t.xch.push_back(d);
+                }
+            }
+    } else {
+        // coordinates in pulse order (a chunk waits only on earlier pulses)
+        for (int q = 0; q < P; q++) {
+            t.xpulse_begin[q] = (int)t.xch.size();
+            for (int S = 0; S < D; S++)
+                for (int k = 0; k < t.nchunks[S * P + q]; k++)
+                    t.xch.push_back(xchunk(S * P + q, k));
+        }
     }
     t.xpulse_begin[P] = (int)t.xch.size();
     // forces in decreasing pulse order (a chunk waits only on later pulses)
@@ -1437,6 +1483,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     ph.next("build: chunk tables");
     p->fused.chunk = p->chunk_req > 0 ? p->chunk_req : fused_chunk(p);
     p->fused.wave = p->wave_chunks != 0;
+    p->fused.heads_first = p->heads_first != 0;
     p->pulse.chunk = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p, true);
     const int chunk1 = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p, false);
     make_work_table(p, true, p->fused);

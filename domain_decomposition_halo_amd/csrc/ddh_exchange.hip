@@ -151,6 +151,23 @@ __device__ void wave_wait(const XArgs& a, const uint32_t* cnt, const uint32_t* n
     wait_vm_idle();
 }
 
+// A chunk descriptor through the scalar cache: the tables are read-only
+// for the whole launch and the index is uniform across the block, so one
+// s_load fetches all 64 bytes without occupying the vector memory counter.
+typedef const __attribute__((address_space(4))) uint32_t* ConstWordPtr;
+
+__device__ __forceinline__ DChunk load_chunk(const DChunk* table, int k)
+{
+    const ConstWordPtr w = (ConstWordPtr)(table + k);
+    uint32_t words[sizeof(DChunk) / 4];
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(DChunk) / 4); i++)
+        words[i] = w[i];
+    DChunk c;
+    __builtin_memcpy(&c, words, sizeof(DChunk));
+    return c;
+}
+
 // Map entries of one round: entry i0 + e * B + tid for e < E. B threads
 // share a round: a whole work-group (B = its width, tid = threadIdx.x) or one
 // wavefront (B = 64, tid = its lane). I is the stored index type: int32, or
@@ -163,78 +180,6 @@ __device__ __forceinline__ void load_map(const I* map, int i0, int end, int (&j)
     for (int e = 0; e < E; e++) {
         const int i = i0 + e * B + (int)threadIdx.x % B;
         j[e] = i < end ? (int)map[i] : -1;
-    }
-}
-
-// Coordinates, one round: x[dst + i] = x[src + map[i]] (+ L on the pulse's
-// component). All E gathers are issued before any store, so a wavefront
-// keeps 3E independent requests in flight. Stores are non-temporal: a region
-// is written once per pass and not re-read by the writing work-group.
-template <int E, int B>
-__device__ __forceinline__ void coords_round(const float* src, float* dst, const DChunk& c, int i0,
-                                             int end, const int (&j)[E])
-{
-    float v[E][3];
-#pragma unroll
-    for (int e = 0; e < E; e++) {
-        if (j[e] >= 0) {
-            const float* s = src + 3ll * j[e];
-            v[e][0] = s[0];
-            v[e][1] = s[1];
-            v[e][2] = s[2];
-        }
-    }
-    // uniform per-component branches keep v[][] in registers
-    if (c.flags & kChunkShift) {
-#pragma unroll
-        for (int k = 0; k < 3; k++)
-            if ((c.flags & 0xff) == k) {
-#pragma unroll
-                for (int e = 0; e < E; e++)
-                    v[e][k] = v[e][k] + c.shift;
-            }
-    }
-#pragma unroll
-    for (int e = 0; e < E; e++) {
-        const int i = i0 + e * B + (int)threadIdx.x % B;
-        if (i < end) {
-            float* d = dst + 3ll * i;
-            __builtin_nontemporal_store(v[e][0], d);
-            __builtin_nontemporal_store(v[e][1], d + 1);
-            __builtin_nontemporal_store(v[e][2], d + 2);
-        }
-    }
-}
-
-// Forces, one round: f[src + map[i]] += f[dst + i] (the receiver's region
-// back into the sender's slots).
-template <int E, int B>
-__device__ __forceinline__ void forces_round(const float* from, float* tgt, int i0, int end,
-                                             const int (&j)[E])
-{
-    float s[E][3], t[E][3];
-#pragma unroll
-    for (int e = 0; e < E; e++) {
-        const int i = i0 + e * B + (int)threadIdx.x % B;
-        if (j[e] >= 0) {
-            const float* r = from + 3ll * i;
-            s[e][0] = r[0];
-            s[e][1] = r[1];
-            s[e][2] = r[2];
-            const float* q = tgt + 3ll * j[e];
-            t[e][0] = q[0];
-            t[e][1] = q[1];
-            t[e][2] = q[2];
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < E; e++) {
-        if (j[e] >= 0) {
-            float* q = tgt + 3ll * j[e];
-            __builtin_nontemporal_store(t[e][0] + s[e][0], q);
-            __builtin_nontemporal_store(t[e][1] + s[e][1], q + 1);
-            __builtin_nontemporal_store(t[e][2] + s[e][2], q + 2);
-        }
     }
 }
 
@@ -318,9 +263,34 @@ __device__ __forceinline__ void forces_put(float* tgt, const int (&j)[E], const 
     }
 }
 
+// One round of a range: x[dst + i] = x[src + map[i]] (+ L on the pulse's
+// component) for the round's entries; all gathers are issued before any
+// store. Stores are non-temporal: a region is written once per pass and not
+// re-read by the writing work-group.
+template <int E, int B>
+__device__ __forceinline__ void coords_round(const float* src, float* dst, const DChunk& c, int i0,
+                                             int end, const int (&j)[E])
+{
+    float v[E][3];
+    coords_gather<E, B>(src, j, v);
+    coords_put<E, B>(dst, c, i0, end, v);
+}
+
+// Forces, one round: f[src + map[i]] += f[dst + i] (the receiver's region
+// back into the sender's slots).
+template <int E, int B>
+__device__ __forceinline__ void forces_round(const float* from, float* tgt, int i0, int end,
+                                             const int (&j)[E])
+{
+    float sv[E][3], tv[E][3];
+    forces_gather<E, B>(from, tgt, i0, j, sv, tv);
+    forces_put<E, B>(tgt, j, sv, tv);
+}
+
 // Entries [begin, end) of a chunk's map (map: the chunk's (sender, pulse)
 // map, entry i at map[i]); j0 holds the first round's map entries (loaded by
-// the caller, possibly before a wait).
+// the caller, possibly before a wait). An empty range touches nothing (its
+// sender may hold no slot for the unconditional reads of a round).
 // With a staging buffer (the host-orchestrated baseline), entry i of a map
 // goes to / comes from stage[map_off + i] instead of the receiver's region.
 // With load_first, the first round's entries are loaded here too (j0 unused).
@@ -328,6 +298,8 @@ template <int E, int B, typename I>
 __device__ void coords_range(float* x, const I* map, const DChunk& c, int begin, int end,
                              const int (&j0)[E], float* stage = nullptr, bool load_first = false)
 {
+    if (begin >= end)
+        return;
     const float* src = x + 3ll * c.src_base;
     float* dst = stage ? stage + 3ll * c.map_off : x + 3ll * c.dst_base;
     if (load_first) {
@@ -349,6 +321,8 @@ __device__ void forces_range(float* f, const I* map, const DChunk& c, int begin,
                              const int (&j0)[E], const float* stage = nullptr,
                              bool load_first = false)
 {
+    if (begin >= end)
+        return;
     float* tgt = f + 3ll * c.src_base;
     const float* from = stage ? stage + 3ll * c.map_off : f + 3ll * c.dst_base;
     if (load_first) {
@@ -444,7 +418,7 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
         if (threadIdx.x == 0)
             trace_rec(a, ntr, kTrClaim, (uint32_t)t);
         if (t < a.nx) {
-            const DChunk c = a.xchunks[t];
+            const DChunk c = load_chunk(a.xchunks, t);
             // the guide's two-pass pack at work-group level: the independent
             // slice goes out first; the map entries of the dependent slice
             // are loaded before the wait, its records packed after it
@@ -478,7 +452,7 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
             }
             __syncthreads();
         } else {
-            const DChunk c = a.fchunks[t - a.nx];
+            const DChunk c = load_chunk(a.fchunks, t - a.nx);
             int j0[E];
             load_map<E, B, I>(maps + c.map_off, c.hb, c.he, j0);  // static: before any wait
             // a step's force chunks do not wait for its coordinate chunks:
@@ -557,7 +531,7 @@ __global__ __launch_bounds__(256) void wave_kernel(XArgs a)
         if (t >= nt)
             break;
         if (t < a.nx) {
-            const DChunk c = a.xchunks[t];
+            const DChunk c = load_chunk(a.xchunks, t);
             int jh[E], jt[E];
             load_map<E, W, I>(maps + c.map_off, c.hb, c.he, jh);
             load_map<E, W, I>(maps + c.map_off, c.tb, c.te, jt);
@@ -575,7 +549,7 @@ __global__ __launch_bounds__(256) void wave_kernel(XArgs a)
             if (lead)
                 add_relaxed(a.xcnt + c.ctr, 1u);
         } else {
-            const DChunk c = a.fchunks[t - a.nx];
+            const DChunk c = load_chunk(a.fchunks, t - a.nx);
             int j0[E];
             load_map<E, W, I>(maps + c.map_off, c.hb, c.he, j0);
             if (c.wait_a || c.wait_b)
@@ -680,23 +654,6 @@ __device__ void exit_publish(const PArgs& a)
 // after the last one, so the loads stay in bounds); without it, from the
 // maps, after the descriptor. m receives the chunk's map base (entry i at
 // m[i]).
-// A chunk descriptor through the scalar cache: the tables are read-only
-// for the whole launch and the index is uniform across the block, so one
-// s_load fetches all 64 bytes without occupying the vector memory counter.
-typedef const __attribute__((address_space(4))) uint32_t* ConstWordPtr;
-
-__device__ __forceinline__ DChunk load_chunk(const DChunk* table, int k)
-{
-    const ConstWordPtr w = (ConstWordPtr)(table + k);
-    uint32_t words[sizeof(DChunk) / 4];
-#pragma unroll
-    for (int i = 0; i < (int)(sizeof(DChunk) / 4); i++)
-        words[i] = w[i];
-    DChunk c;
-    __builtin_memcpy(&c, words, sizeof(DChunk));
-    return c;
-}
-
 template <int E, int B, typename I>
 __device__ __forceinline__ void pulse_fetch(const PArgs& a, int b, DChunk& c, int (&j)[E],
                                             const I*& m)

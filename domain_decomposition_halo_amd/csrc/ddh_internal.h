@@ -131,6 +131,8 @@ struct Geometry {
 struct WorkTable {
     int chunk = 0;                  // entries per chunk
     bool wave = false;              // fused: built for wavefront workers
+    bool heads_first = false;       // fused: every map's head in chunks of its
+                                    // own, all heads before any tail
     std::vector<int32_t> nchunks;   // [S * P + p] chunks of the map
     std::vector<DChunk> xch, fch;
     std::vector<int32_t> xpulse_begin, fpulse_begin;  // per pulse ranges (+1)
@@ -186,6 +188,7 @@ struct Plan {
                                 // (takes effect at the next build)
     int home_sort = 0;          // home-atom sort of the build: 0 automatic,
                                 // 1 counting sort, 2 radix sort
+    int heads_first = 0;        // fused: heads-first ticket order (next build)
     int exit_publish = 0;       // per-pulse mode: 0 automatic, 1 the last
                                 // launch publishes its flags at exit, 2 a
                                 // one-wave launch after it does

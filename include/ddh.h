@@ -418,8 +418,18 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     the descriptor first, then only the
                                     chunk's own entries */
 
+#define DDH_TUNE_HEADS_FIRST 15    /* fused mode: 0 (default) a coordinate
+                                    chunk packs a slice of its map's
+                                    independent head, waits, then packs a
+                                    slice of its dependent tail; 1 heads and
+                                    tails are chunks of their own, and every
+                                    head (pulse order) is ticketed before any
+                                    tail (pulse order), so no head waits.
+                                    Same results. Takes effect at the next
+                                    build. */
+
 /* Set a tuning knob; takes effect at the next build (CHUNK, WAVE_CHUNKS,
-   HOME_SORT) or call. Library utility: the guide defines no such call.
+   HOME_SORT, HEADS_FIRST) or call. Library utility: the guide defines no such call.
    Errors: DDH_EINVAL (unknown key or value out of range). */
 int ddh_tune(ddh_plan *plan, int32_t key, int64_t value);
 

@@ -141,6 +141,8 @@ def test_mode_and_tune_validation():
     for v in (1, 2, 0):
         plan.tune(ddh.DDH_TUNE_EXIT_PUBLISH, v)
         plan.tune(ddh.DDH_TUNE_PAD_MAPS, v)
+    for v in (1, 0):
+        plan.tune(ddh.DDH_TUNE_HEADS_FIRST, v)
     plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 1)
     plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 0)
     plan.tune(ddh.DDH_TUNE_FLAGS, 0)

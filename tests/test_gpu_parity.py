@@ -47,9 +47,10 @@ class GpuPlan:
     """A device plan built from host positions, with host views of its output."""
 
     def __init__(self, x, grid, box, rc, cell=0.5, mode=0, chunk=0, wg=0, refined=1, block=0,
-                 static_first=0, narrow=1, wave=0, home_sort=0):
+                 static_first=0, narrow=1, wave=0, home_sort=0, heads_first=0):
         self.plan = ddh.Plan(grid, box, rc, cell)
         self.plan.tune(ddh.DDH_TUNE_HOME_SORT, home_sort)
+        self.plan.tune(ddh.DDH_TUNE_HEADS_FIRST, heads_first)
         self.plan.tune(ddh.DDH_TUNE_STATIC_FIRST, static_first)
         self.plan.tune(ddh.DDH_TUNE_NARROW_MAPS, narrow)
         self.plan.tune(ddh.DDH_TUNE_WAVE_CHUNKS, wave)
@@ -228,8 +229,10 @@ def test_random_decompositions(cfg):
     grid, box, rc, n = cfg
     x = W.uniform_positions(n, box, seed=n)
     ref = oracle.OraclePlan(x, grid, box, rc)
-    for mode, wave in [(m, 0) for m in MODES.values()] + [(ddh.DDH_MODE_FUSED, 1)]:
-        g = GpuPlan(x, grid, box, rc, mode=mode, wave=wave)
+    runs = [(m, 0, 0) for m in MODES.values()] + [(ddh.DDH_MODE_FUSED, 1, 0),
+                                                  (ddh.DDH_MODE_FUSED, 0, 1)]
+    for mode, wave, heads_first in runs:
+        g = GpuPlan(x, grid, box, rc, mode=mode, wave=wave, heads_first=heads_first)
         check_layout(g, ref)
         check_steps(g, ref, n, steps=2)
         check_steps(g, ref, n + 1, steps=1, fused_step=True)
@@ -521,6 +524,52 @@ def test_pulse_publish_and_map_forms(k, exit_pub, pad, workload_plan):
     xl = g.new_coords()
     home = g.new_coords()
     f0 = np.random.default_rng(220 + k).normal(0, 10, size=(g.n_slots, 3)).astype(np.float32)
+    fl = torch.from_numpy(f0).cuda()
+    fr = f0.copy()
+    ref.exchange_forces(fr)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.plan.exchange_step(xl, fl)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.plan.exchange_step(xl, fl)
+    for r in range(3):
+        xl.copy_(home)
+        fl.copy_(torch.from_numpy(f0))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(xl.cpu().numpy()[:g.n_slots]), bits(ref.x_local)), r
+        assert np.array_equal(bits(fl.cpu().numpy()[:g.n_slots]), bits(fr)), r
+    assert g.plan.check() == ddh.DDH_OK
+    del graph
+    g.close()
+
+
+@pytest.mark.parametrize("chunk,wg", [(0, 0), (64, 0), (1000, 3), (0, 1)])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_heads_first_tickets(k, chunk, wg, workload_plan):
+    """The fused launch with heads-first tickets (DDH_TUNE_HEADS_FIRST): every
+    map's independent head in chunks of its own, all heads before any tail.
+    Ragged and many-chunk tables, grids down to one work-group, the
+    conservative waits, and calls captured in a caller's graph replayed with
+    the halo cleared (a missing wait or release cannot hide behind stale
+    values)."""
+    w, x, ref = workload_plan(k)
+    g = GpuPlan(x, **w.params(), mode=ddh.DDH_MODE_FUSED, chunk=chunk, wg=wg, heads_first=1)
+    check_steps(g, ref, 500 + k, steps=2)
+    check_steps(g, ref, 510 + k, steps=1, fused_step=True)
+    g.plan.tune(ddh.DDH_TUNE_REFINED_WAITS, 0)
+    g.plan.build_maps(g.xg)
+    check_steps(g, ref, 520 + k, steps=1, fused_step=True)
+    g.plan.tune(ddh.DDH_TUNE_REFINED_WAITS, 1)
+    g.plan.build_maps(g.xg)
+    home = g.new_coords()
+    xl = g.new_coords()
+    f0 = np.random.default_rng(530 + k).normal(0, 10, size=(g.n_slots, 3)).astype(np.float32)
     fl = torch.from_numpy(f0).cuda()
     fr = f0.copy()
     ref.exchange_forces(fr)

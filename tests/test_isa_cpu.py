@@ -37,9 +37,12 @@ def _isa(src, tmp_path):
             kernels[cur] = []
             continue
         if cur is not None:
-            kernels[cur].append(line)
-            if "s_endpgm" in line:
+            # a kernel may end early (s_endpgm) before its main loop: the body
+            # runs to the function's end label
+            if line.startswith(".Lfunc_end"):
                 cur = None
+                continue
+            kernels[cur].append(line)
     return kernels
 
 
