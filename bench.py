@@ -140,6 +140,8 @@ def run_gpu(args, w):
         plan.tune(ddh.DDH_TUNE_PAD_MAPS, args.pad_maps)
     if args.heads_first:
         plan.tune(ddh.DDH_TUNE_HEADS_FIRST, 1)
+    if args.home_sort:
+        plan.tune(ddh.DDH_TUNE_HOME_SORT, args.home_sort)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -446,6 +448,8 @@ def run_builds(args, w):
     torch.cuda.set_device(dev)
     xg = torch.from_numpy(W.positions(w)).to(dev)
     plan = ddh.Plan(**w.params())
+    if args.home_sort:
+        plan.tune(ddh.DDH_TUNE_HOME_SORT, args.home_sort)
     plan.build_maps(xg)
     torch.cuda.synchronize()
     times = []
@@ -950,6 +954,8 @@ def main():
                     help="DDH_TUNE_PAD_MAPS (0 automatic)")
     ap.add_argument("--heads-first", action="store_true",
                     help="fused launch: heads-first ticket order (DDH_TUNE_HEADS_FIRST = 1)")
+    ap.add_argument("--home-sort", type=int, default=0, choices=[0, 1, 2],
+                    help="DDH_TUNE_HOME_SORT (0 automatic, 1 counting, 2 partition)")
     ap.add_argument("--pass", dest="pass_", default="step", choices=["step", "coords", "forces"],
                     help="time one pass alone (coordinate or force pass) instead of the step; "
                          "with --only-step, for per-pass profiler runs")

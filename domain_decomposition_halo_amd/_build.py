@@ -8,7 +8,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libddh.so")
-SOURCES = ["ddh_api.hip", "ddh_build.hip", "ddh_exchange.hip", "ddh_sort.hip"]
+SOURCES = ["ddh_api.hip", "ddh_build.hip", "ddh_exchange.hip"]
 
 # -ffp-contract=off: every fp32 add and multiply is one rounded IEEE operation,
 # as the bit-exact results require. Packed fp32 instructions are disabled.

@@ -11,9 +11,12 @@
 //   1. every atom goes to the domain whose half-open interval [b_d[i],
 //      b_d[i+1]) holds it in each dimension (fp32 compares decide);
 //   2. home atoms of a domain are ordered by sort cell (key cx + ncx * (cy +
-//      ncy * cz)) and then by global id: a counting sort over all cells of
-//      all domains, made deterministic by sorting each cell by id, or (from
-//      kRadixSortMin atoms on) a stable radix sort of (cell, id) pairs;
+//      ncy * cz)) and then by global id: a partition of the atoms by domain
+//      (block histograms in LDS, one scan, a scatter with LDS counters), a
+//      counting sort of each domain's atoms by cell in LDS, then each cell
+//      sorted by id; or, where a domain or a cell table is too large for
+//      LDS, a counting sort over all cells of all domains with device
+//      atomics, made deterministic the same way;
 //   3. pulse p along d, sender S: candidates are S's home slots and every
 //      slot it received in earlier pulses (first pulse of d), or the slots it
 //      received in the previous pulse of d (later pulses); slot j is selected
@@ -39,7 +42,15 @@ namespace {
 
 constexpr int kScanBlock = 1024;  // elements per scan block (4 per thread)
 constexpr int kSelTile = 1024;    // candidate slots per block of the slab selection
-constexpr int kRadixSortMin = 4000000;  // atoms from which the home sort is a radix sort
+// the partition sort: atoms per block of the domain partition, and the
+// largest domain count and cells per domain its LDS tables hold
+// atoms per thread of the partition's first two passes (256 threads): the
+// largest of 16, 4 and 1 that still gives at least kPartMinBlocks blocks
+constexpr int kPartMinBlocks = 512;
+constexpr int kPartMaxDomains = 2048;
+constexpr int kPartMaxCells = 4096;
+constexpr int kDomCap = 32768;           // atoms of a domain sorted in LDS
+constexpr int kDomBatch = 8;             // record loads a thread issues together
 
 struct AGeom {
     int n[3];
@@ -52,59 +63,45 @@ struct AGeom {
     const int* cellbase;  // first bucket of each domain
 };
 
-// Bucket of one atom: its domain's first bucket plus its sort cell's key, or
-// -1 when a coordinate lies outside [0, L) (or is not a number).
-__device__ __forceinline__ int bucket_of(const float* __restrict__ xg, int a, const AGeom& g)
+// Domain and sort cell of one position from the boundary and cell-count
+// tables b and nc (laid out as in AGeom: dimension d at boff[d] and noff[d]);
+// false when a coordinate lies outside [0, L) or is not a number. key is the
+// cell's index inside the domain, x fastest.
+__device__ __forceinline__ bool locate(const float v[3], const AGeom& g, const float* b,
+                                       const int* nc, int& dom, int& key)
 {
-    int ci[3], cc[3], nc[3];
+    int ci[3], cc[3], ncd[3];
+#pragma unroll
     for (int d = 0; d < 3; d++) {
-        const float v = xg[3ll * a + d];
-        if (!(v >= 0.0f && v < g.L[d]))
-            return -1;
-        const float* b = g.b + g.boff[d];
+        if (!(v[d] >= 0.0f && v[d] < g.L[d]))
+            return false;
+        const float* bd = b + g.boff[d];
         const int n = g.n[d];
-        int i = (int)(v * ((float)n / g.L[d]));
+        int i = (int)(v[d] * ((float)n / g.L[d]));
         i = i < 0 ? 0 : (i > n - 1 ? n - 1 : i);
-        while (i > 0 && v < b[i])
+        while (i > 0 && v[d] < bd[i])
             i--;
-        while (i < n - 1 && v >= b[i + 1])
+        while (i < n - 1 && v[d] >= bd[i + 1])
             i++;
         ci[d] = i;
-        nc[d] = g.ncell[g.noff[d] + i];
+        ncd[d] = nc[g.noff[d] + i];
         int c = 0;
-        if (nc[d] > 1) {
-            const float t = (v - b[i]) * g.inv_c;
+        if (ncd[d] > 1) {
+            const float t = (v[d] - bd[i]) * g.inv_c;
             c = (int)floorf(t);
-            c = c < 0 ? 0 : (c > nc[d] - 1 ? nc[d] - 1 : c);
+            c = c < 0 ? 0 : (c > ncd[d] - 1 ? ncd[d] - 1 : c);
         }
         cc[d] = c;
     }
-    const int D = ci[0] + g.n[0] * (ci[1] + g.n[1] * ci[2]);
-    const int key = cc[0] + nc[0] * (cc[1] + nc[1] * cc[2]);
-    return g.cellbase[D] + key;
+    dom = ci[0] + g.n[0] * (ci[1] + g.n[1] * ci[2]);
+    key = cc[0] + ncd[0] * (cc[1] + ncd[1] * cc[2]);
+    return true;
 }
 
-// Sort keys of the home assignment: the bucket (domain-major, then cell) of
-// every atom, its global id as the value. An atom outside the box gets the
-// largest key and raises the error word.
-__global__ __launch_bounds__(256) void assign_key_kernel(const float* __restrict__ xg, int n_atoms,
-                                                         AGeom g, uint32_t* __restrict__ key,
-                                                         int* __restrict__ gid,
-                                                         uint32_t* __restrict__ err)
-{
-    const int a = blockIdx.x * 256 + threadIdx.x;
-    if (a >= n_atoms)
-        return;
-    const int bk = bucket_of(xg, a, g);
-    if (bk < 0)
-        atomicOr(err, 1u);
-    key[a] = bk < 0 ? 0xFFFFFFFFu : (uint32_t)bk;
-    gid[a] = a;
-}
-
-// Counting form of the same assignment: each atom's bucket and its arrival
-// rank in the bucket from the count's atomic add (an arbitrary order inside
-// the bucket, which the per-cell sort by global id then fixes).
+// Counting form of the assignment: each atom's bucket (its domain's first
+// bucket plus its cell key, -1 outside the box) and its arrival rank in the
+// bucket from the count's atomic add (an arbitrary order inside the bucket,
+// which the per-cell sort by global id then fixes).
 __global__ __launch_bounds__(256) void assign_count_kernel(const float* __restrict__ xg,
                                                            int n_atoms, AGeom g,
                                                            int* __restrict__ bucket,
@@ -115,31 +112,292 @@ __global__ __launch_bounds__(256) void assign_count_kernel(const float* __restri
     const int a = blockIdx.x * 256 + threadIdx.x;
     if (a >= n_atoms)
         return;
-    const int bk = bucket_of(xg, a, g);
-    bucket[a] = bk;
-    if (bk < 0)
+    const float v[3] = {xg[3ll * a], xg[3ll * a + 1], xg[3ll * a + 2]};
+    int dom, key;
+    if (!locate(v, g, g.b, g.ncell, dom, key)) {
+        bucket[a] = -1;
         atomicOr(err, 1u);
-    else
-        rank[a] = atomicAdd(count + bk, 1u);
+        return;
+    }
+    const int bk = g.cellbase[dom] + key;
+    bucket[a] = bk;
+    rank[a] = atomicAdd(count + bk, 1u);
 }
 
-// First sorted position of every bucket b in [0, nb]: the lower bound of b
-// in the sorted keys (start[nb] = atoms inside the box).
-__global__ __launch_bounds__(256) void bucket_start_kernel(const uint32_t* __restrict__ keys, int n,
-                                                           int nb, uint32_t* __restrict__ start)
+// ---- partition sort of the home atoms (LDS counters only)
+
+__device__ uint32_t block_scan_excl(uint32_t v, uint32_t* sh, uint32_t& total);
+
+constexpr uint32_t kPartNone = 0xFFFFFFFFu;  // code of an atom outside the box
+constexpr int kKeyBits = 12;                 // cell key bits of a code
+static_assert((1 << kKeyBits) >= kPartMaxCells, "cell keys must fit their bits");
+
+// Partition, pass 1: block b takes atoms [b T, (b + 1) T), T = 256 * ITEMS,
+// with the geometry tables copied to LDS; stores each atom's code (domain <<
+// kKeyBits | cell key, kPartNone outside the box, reported on the error word) and
+// counts its atoms per domain in LDS. hist[d * nblk + b] receives block b's
+// count of domain d (domain-major, so one exclusive scan gives every
+// (domain, block) its first position).
+template <int ITEMS>
+__global__ __launch_bounds__(256) void part_count_kernel(const float* __restrict__ xg, int n_atoms,
+                                                         AGeom g, int ndom, int nblk,
+                                                         uint32_t* __restrict__ code,
+                                                         uint32_t* __restrict__ hist,
+                                                         uint32_t* __restrict__ err)
 {
-    const int b = blockIdx.x * 256 + threadIdx.x;
-    if (b > nb)
-        return;
-    int lo = 0, hi = n;  // first index with keys[index] >= b
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (keys[mid] < (uint32_t)b)
-            lo = mid + 1;
-        else
-            hi = mid;
+    extern __shared__ uint32_t sh[];  // counts [ndom], boundaries [nbt], cell counts [nnt]
+    const int nbt = g.boff[2] + g.n[2] + 1, nnt = g.noff[2] + g.n[2];
+    uint32_t* cnt = sh;
+    float* b = (float*)(sh + ndom);
+    int* nc = (int*)(sh + ndom + nbt);
+    const int tid = (int)threadIdx.x;
+    for (int d = tid; d < ndom; d += 256)
+        cnt[d] = 0u;
+    for (int k = tid; k < nbt; k += 256)
+        b[k] = g.b[k];
+    for (int k = tid; k < nnt; k += 256)
+        nc[k] = g.ncell[k];
+    const int64_t a0 = (int64_t)blockIdx.x * (256 * ITEMS);
+    // every position load of the thread is issued before the first test
+    float v[ITEMS][3];
+#pragma unroll
+    for (int i = 0; i < ITEMS; i++) {
+        const int64_t a = a0 + (int64_t)i * 256 + tid;
+        const int64_t ac = a < n_atoms ? a : 0;
+#pragma unroll
+        for (int d = 0; d < 3; d++)
+            v[i][d] = xg[3 * ac + d];
     }
-    start[b] = (uint32_t)lo;
+    __syncthreads();
+    uint32_t bad = 0u;
+#pragma unroll
+    for (int i = 0; i < ITEMS; i++) {
+        const int64_t a = a0 + (int64_t)i * 256 + tid;
+        if (a < n_atoms) {
+            int dom, key;
+            uint32_t c = kPartNone;
+            if (locate(v[i], g, b, nc, dom, key)) {
+                c = ((uint32_t)dom << kKeyBits) | (uint32_t)key;
+                atomicAdd(&cnt[dom], 1u);
+            } else {
+                bad = 1u;
+            }
+            code[a] = c;
+        }
+    }
+    if (bad)
+        atomicOr(err, 1u);
+    __syncthreads();
+    for (int d = tid; d < ndom; d += 256)
+        hist[(int64_t)d * nblk + blockIdx.x] = cnt[d];
+}
+
+// Partition, pass 2: the block's atoms grouped by domain in LDS (at an LDS
+// counter's rank: any order inside a domain's share, which the per-domain
+// cell sort and the per-cell sort by id then fix), then written out in that
+// order, so each domain's share leaves as one contiguous run. rec[pos] gets
+// (cell key inside the domain, global id) at the (domain, block)'s first
+// position from hscan plus the rank.
+template <int ITEMS>
+__global__ __launch_bounds__(256) void part_scatter_kernel(const uint32_t* __restrict__ code,
+                                                           int n_atoms,
+                                                           const uint32_t* __restrict__ hscan,
+                                                           int ndom, int nblk,
+                                                           uint2* __restrict__ rec)
+{
+    extern __shared__ uint32_t sh[];  // staged (code, id) [(256 * ITEMS)], offset [ndom], rank [ndom]
+    __shared__ uint32_t scan_sh[256];
+    uint2* stage = (uint2*)sh;
+    int* off = (int*)(sh + 2 * (256 * ITEMS));
+    uint32_t* rnk = sh + 2 * (256 * ITEMS) + ndom;
+    const int tid = (int)threadIdx.x, blk = (int)blockIdx.x;
+    const int64_t a0 = (int64_t)blk * (256 * ITEMS);
+    uint32_t c[ITEMS];
+#pragma unroll
+    for (int i = 0; i < ITEMS; i++) {
+        const int64_t a = a0 + (int64_t)i * 256 + tid;
+        c[i] = a < n_atoms ? code[a] : kPartNone;
+    }
+    // the block's local start of each domain: a scan of its counts (each
+    // thread a contiguous run of domains); off = global first - local start
+    const int per = (ndom + 255) / 256;
+    const int d0 = min(ndom, tid * per), d1 = min(ndom, d0 + per);
+    uint32_t sum = 0u;
+    for (int d = d0; d < d1; d++) {
+        const int64_t h = (int64_t)d * nblk + blk;
+        sum += hscan[h + 1] - hscan[h];
+    }
+    uint32_t total;
+    uint32_t run = block_scan_excl(sum, scan_sh, total);
+    for (int d = d0; d < d1; d++) {
+        const int64_t h = (int64_t)d * nblk + blk;
+        off[d] = (int)(hscan[h] - run);
+        rnk[d] = run;
+        run += hscan[h + 1] - hscan[h];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ITEMS; i++) {
+        if (c[i] != kPartNone) {
+            const uint32_t r = atomicAdd(&rnk[c[i] >> kKeyBits], 1u);
+            stage[r] = make_uint2(c[i], (uint32_t)(a0 + (int64_t)i * 256 + tid));
+        }
+    }
+    __syncthreads();
+    for (uint32_t r = tid; r < total; r += 256) {
+        const uint2 e = stage[r];
+        const int d = (int)(e.x >> kKeyBits);
+        rec[(int64_t)off[d] + r] = make_uint2(e.x & ((1u << kKeyBits) - 1u), e.y);
+    }
+}
+
+// Exclusive scan of v over the 1024 threads of a block (wave scans, then
+// the sixteen wave totals); returns this thread's prefix.
+__device__ uint32_t scan1024_excl(uint32_t v, uint32_t* wsum)
+{
+    const int lane = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o)
+            x += y;
+    }
+    if (lane == 63)
+        wsum[w] = x;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int q = 0; q < w; q++)
+        before += wsum[q];
+    __syncthreads();
+    return before + x - v;
+}
+
+// Order the n = e - s global ids at out[s, e) (one cell, ~10 atoms):
+// insertion sort in registers for up to kCellRegs ids, loaded and stored
+// once, else in place.
+constexpr int kCellRegs = 32;
+__device__ __forceinline__ void sort_cell(int* __restrict__ out, uint32_t s, uint32_t e)
+{
+    const int n = (int)(e - s);
+    if (n <= kCellRegs) {
+        int v[kCellRegs];
+#pragma unroll
+        for (int i = 0; i < kCellRegs; i++)
+            v[i] = i < n ? out[s + i] : INT32_MAX;
+        // fixed trip counts keep v[] in registers
+#pragma unroll
+        for (int i = 1; i < kCellRegs; i++) {
+#pragma unroll
+            for (int j = i; j > 0; j--) {
+                const int lo = min(v[j - 1], v[j]), hi = max(v[j - 1], v[j]);
+                v[j - 1] = lo;
+                v[j] = hi;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kCellRegs; i++)
+            if (i < n)
+                out[s + i] = v[i];
+        return;
+    }
+    for (uint32_t i = s + 1; i < e; i++) {
+        const int v = out[i];
+        uint32_t j = i;
+        while (j > s && out[j - 1] > v) {
+            out[j] = out[j - 1];
+            j--;
+        }
+        out[j] = v;
+    }
+}
+
+// Place every id of rec[h0, h1) at its cell's next position in out (c[k]
+// holds cell k's first position and ends as its end), then order each cell
+// by global id. out is the block's LDS copy of the domain or the domain's
+// part of home_gid.
+template <typename Out>
+__device__ __forceinline__ void place_and_sort(const uint2* __restrict__ rec, uint32_t h0,
+                                               uint32_t h1, uint32_t* c, int nc, Out* out)
+{
+    const int tid = (int)threadIdx.x;
+    for (uint32_t i0 = h0; i0 < h1; i0 += 1024 * kDomBatch) {
+        uint2 r[kDomBatch];
+#pragma unroll
+        for (int j = 0; j < kDomBatch; j++) {
+            const uint32_t i = i0 + j * 1024 + tid;
+            r[j] = i < h1 ? rec[i] : make_uint2(kPartNone, 0u);
+        }
+#pragma unroll
+        for (int j = 0; j < kDomBatch; j++)
+            if (r[j].x != kPartNone)
+                out[atomicAdd(&c[r[j].x], 1u)] = (int)r[j].y;
+    }
+    // cell k now ends at c[k] and starts where cell k - 1 ends
+    __syncthreads();
+    for (int k = tid; k < nc; k += 1024)
+        sort_cell(out, k ? c[k - 1] : 0u, c[k]);
+}
+
+// One block per domain D, whose atoms are rec[h0, h1): count them per cell
+// in LDS, scan, store the buckets' first positions (start[cellbase[D] + k],
+// and start[nb] = every atom inside the box from the last domain), place
+// every id at its cell's position and order each cell by global id. A
+// domain of at most kDomCap atoms is placed and sorted in LDS and leaves in
+// one coalesced copy; a larger one is placed and sorted in home_gid.
+__global__ __launch_bounds__(1024) void domain_sort_kernel(const uint2* __restrict__ rec,
+                                                           const uint32_t* __restrict__ hscan,
+                                                           int nblk, const int* __restrict__ cellbase,
+                                                           int ndom, int* __restrict__ home_gid,
+                                                           uint32_t* __restrict__ start)
+{
+    __shared__ uint32_t c[kPartMaxCells];
+    __shared__ int ids[kDomCap];
+    __shared__ uint32_t wsum[16];
+    const int D = (int)blockIdx.x, tid = (int)threadIdx.x;
+    const uint32_t h0 = hscan[(int64_t)D * nblk], h1 = hscan[(int64_t)(D + 1) * nblk];
+    const int cb = cellbase[D], nc = cellbase[D + 1] - cb;
+    for (int k = tid; k < nc; k += 1024)
+        c[k] = 0u;
+    __syncthreads();
+    for (uint32_t i0 = h0; i0 < h1; i0 += 1024 * kDomBatch) {
+        uint32_t k[kDomBatch];
+#pragma unroll
+        for (int j = 0; j < kDomBatch; j++) {
+            const uint32_t i = i0 + j * 1024 + tid;
+            k[j] = i < h1 ? rec[i].x : kPartNone;
+        }
+#pragma unroll
+        for (int j = 0; j < kDomBatch; j++)
+            if (k[j] != kPartNone)
+                atomicAdd(&c[k[j]], 1u);
+    }
+    __syncthreads();
+    // each thread scans a contiguous run of cells
+    const int per = (nc + 1023) / 1024;
+    const int k0 = min(nc, tid * per), k1 = min(nc, k0 + per);
+    uint32_t sum = 0;
+    for (int k = k0; k < k1; k++)
+        sum += c[k];
+    uint32_t run = scan1024_excl(sum, wsum);
+    for (int k = k0; k < k1; k++) {
+        const uint32_t v = c[k];
+        c[k] = run;
+        start[cb + k] = h0 + run;
+        run += v;
+    }
+    if (D == ndom - 1 && tid == 0)
+        start[cellbase[ndom]] = h1;
+    __syncthreads();
+    const uint32_t n = h1 - h0;
+    if (n <= (uint32_t)kDomCap) {
+        place_and_sort(rec, h0, h1, c, nc, ids);
+        __syncthreads();
+        for (uint32_t i = tid; i < n; i += 1024)
+            home_gid[h0 + i] = ids[i];
+    } else {
+        place_and_sort(rec, h0, h1, c, nc, home_gid + h0);
+    }
 }
 
 // ---- exclusive scan of uint32 counts: out[i] = sum(in[0..i)), out[n] = total
@@ -231,48 +489,13 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ bu
     sorted[start[bk] + rank[a]] = a;
 }
 
-// Order each cell's atoms by global id (cells hold ~10 atoms: insertion
-// sort). A cell of at most kCellRegs atoms is loaded once, sorted in
-// registers and stored once; a larger one is sorted in place in memory.
-constexpr int kCellRegs = 32;
+// Order each cell's atoms by global id (one thread per cell).
 __global__ __launch_bounds__(256) void sort_cells_kernel(const uint32_t* __restrict__ start, int nb,
                                                          int* __restrict__ sorted)
 {
     const int bk = blockIdx.x * 256 + threadIdx.x;
-    if (bk >= nb)
-        return;
-    const uint32_t s = start[bk], e = start[bk + 1];
-    const int n = (int)(e - s);
-    if (n <= kCellRegs) {
-        int v[kCellRegs];
-#pragma unroll
-        for (int i = 0; i < kCellRegs; i++)
-            v[i] = i < n ? sorted[s + i] : INT32_MAX;
-        // insertion sort with fixed trip counts keeps v[] in registers
-#pragma unroll
-        for (int i = 1; i < kCellRegs; i++) {
-#pragma unroll
-            for (int j = i; j > 0; j--) {
-                const int lo = min(v[j - 1], v[j]), hi = max(v[j - 1], v[j]);
-                v[j - 1] = lo;
-                v[j] = hi;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kCellRegs; i++)
-            if (i < n)
-                sorted[s + i] = v[i];
-        return;
-    }
-    for (uint32_t i = s + 1; i < e; i++) {
-        const int v = sorted[i];
-        uint32_t j = i;
-        while (j > s && sorted[j - 1] > v) {
-            sorted[j] = sorted[j - 1];
-            j--;
-        }
-        sorted[j] = v;
-    }
+    if (bk < nb)
+        sort_cell(sorted, start[bk], start[bk + 1]);
 }
 
 __global__ void home_start_kernel(const uint32_t* __restrict__ start, const int* __restrict__ cellbase,
@@ -336,27 +559,40 @@ __device__ const float* resolve(const SArgs& a, int S, int j, int& gid)
     return nullptr;
 }
 
-// slot_gid / home_slot for the home slots: r -> domain by binary search.
+// slot_gid and home_slot of the home atoms: work item b (of ndom * cpd,
+// grid-strided) fills chunk b % cpd (kFillTile home ranks) of domain b /
+// cpd, whose ranks [hs[D], hs[D + 1]) take slots from base[D] on.
+constexpr int kFillItems = 8;
+constexpr int kFillTile = 256 * kFillItems;
+constexpr int kFillMaxBlocks = 1 << 20;
 __global__ __launch_bounds__(256) void fill_home_kernel(const int* __restrict__ home_gid,
-                                                        const int* __restrict__ hs, int ndom,
-                                                        const int* __restrict__ base, int n_atoms,
-                                                        int* __restrict__ slot_gid,
+                                                        const int* __restrict__ hs,
+                                                        const int* __restrict__ base, int ndom,
+                                                        int cpd, int* __restrict__ slot_gid,
                                                         int* __restrict__ home_slot)
 {
-    const int r = blockIdx.x * 256 + threadIdx.x;
-    if (r >= n_atoms)
-        return;
-    int lo = 0, hi = ndom;  // find D with hs[D] <= r < hs[D+1]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (hs[mid] <= r)
-            lo = mid;
-        else
-            hi = mid;
+    for (int64_t b = blockIdx.x; b < (int64_t)ndom * cpd; b += gridDim.x) {
+        const int D = (int)(b / cpd), c = (int)(b % cpd);
+        const int64_t r0 = hs[D] + (int64_t)c * kFillTile;
+        const int64_t r1 = min((int64_t)hs[D + 1], r0 + kFillTile);
+        if (r0 >= r1)
+            continue;
+        const int64_t off = (int64_t)base[D] - hs[D];
+        int g[kFillItems];
+#pragma unroll
+        for (int j = 0; j < kFillItems; j++) {
+            const int64_t r = r0 + j * 256 + (int)threadIdx.x;
+            g[j] = r < r1 ? home_gid[r] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < kFillItems; j++) {
+            const int64_t r = r0 + j * 256 + (int)threadIdx.x;
+            if (r < r1) {
+                slot_gid[r + off] = g[j];
+                home_slot[r] = (int)(r + off);
+            }
+        }
     }
-    const int slot = base[lo] + (r - hs[lo]);
-    slot_gid[slot] = home_gid[r];
-    home_slot[r] = slot;
 }
 
 // slot_gid for the region records of one pulse (stored receiver-major).
@@ -1134,15 +1370,21 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
 
     // ---- 1-2: home assignment and cell sort
     ph.next("build: assign and sort");
-    // Two forms, same order. Counting: an atomic count per bucket gives each
-    // atom its arrival rank, a scan the bucket starts, a scatter the
-    // positions, and a sort of each cell by global id the final order.
-    // Radix: a stable radix sort of (bucket, global id) pairs, the ids in
-    // increasing order, and the bucket starts by binary search. The device
-    // atomics of the counting form dominate a large build (12M atoms: 2.53
-    // -> 2.18 ms with the radix sort); the sort's fixed passes cost more on
-    // small ones (1M atoms: 0.67 -> 0.76 ms).
-    const bool radix = p->home_sort == 2 || (p->home_sort == 0 && n_atoms >= kRadixSortMin);
+    // Two forms, same order. Partition (the default wherever its LDS tables
+    // fit): block histograms of the atoms per domain in LDS, one scan, a
+    // scatter into per-domain segments with LDS counters, then one block per
+    // domain counting its atoms per cell in LDS and placing them; no device
+    // atomic on any atom. Counting (any size): a device atomic count per
+    // bucket gives each atom its arrival rank, a scan the bucket starts, a
+    // scatter the positions. Both then sort each cell by global id.
+    int max_cells = 0;
+    for (int Dm = 0; Dm < D; Dm++)
+        max_cells = std::max(max_cells, cellbase[Dm + 1] - cellbase[Dm]);
+    const bool fits = D <= kPartMaxDomains && max_cells <= kPartMaxCells;
+    const bool partition = p->home_sort == 2 ? true : (p->home_sort == 0 && fits);
+    if (partition && !fits)
+        return fail(DDH_EINVAL, "ddh_build_maps: the partition sort (DDH_TUNE_HOME_SORT 2) needs "
+                                "at most 2048 domains and 4096 sort cells per domain");
     int* d_hs;
     uint32_t *d_start, *d_err;
     DDH_HIP(sc.alloc(&d_start, (size_t)nb + 1));
@@ -1150,36 +1392,37 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     DDH_HIP(sc.alloc(&d_hs, (size_t)D + 1));
     DDH_HIP(owned_alloc(p, &p->d_home_gid, (size_t)n_atoms));
     DDH_HIP(hipMemsetAsync(d_err, 0, sizeof(uint32_t), s));
-    if (radix) {
-        int* d_iota;
-        uint32_t *d_key, *d_key_sorted;
-        DDH_HIP(sc.alloc(&d_key, (size_t)n_atoms));
-        DDH_HIP(sc.alloc(&d_key_sorted, (size_t)n_atoms));
-        DDH_HIP(sc.alloc(&d_iota, (size_t)n_atoms));
-        if (n_atoms > 0) {
-            hipLaunchKernelGGL(assign_key_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s, xg,
-                               n_atoms, ag, d_key, d_iota, d_err);
-            DDH_HIP(hipGetLastError());
-            // key bits: enough for every bucket below nb (nb <= 2^30); the key
-            // of an atom outside the box then sorts last, and the build fails
-            // on the error word read with the home counts below
-            int end_bit = 1;
-            while (end_bit < 31 && (1ll << end_bit) <= (int64_t)nb)
-                end_bit++;
-            size_t temp_bytes = 0;
-            int rc = sort_pairs(nullptr, &temp_bytes, d_key, d_key_sorted, d_iota, p->d_home_gid,
-                                n_atoms, end_bit, s);
-            if (rc)
-                return rc;
-            unsigned char* d_temp;
-            DDH_HIP(sc.alloc(&d_temp, temp_bytes));
-            rc = sort_pairs(d_temp, &temp_bytes, d_key, d_key_sorted, d_iota, p->d_home_gid,
-                            n_atoms, end_bit, s);
-            if (rc)
-                return rc;
-        }
-        hipLaunchKernelGGL(bucket_start_kernel, dim3(blocks((int64_t)nb + 1)), dim3(256), 0, s,
-                           d_key_sorted, n_atoms, nb, d_start);
+    if (partition) {
+        const int items = (int64_t)n_atoms >= 16ll * 256 * kPartMinBlocks ? 16
+                          : (int64_t)n_atoms >= 4ll * 256 * kPartMinBlocks ? 4 : 1;
+        const int tile = 256 * items;
+        const int nblk = (int)(((int64_t)n_atoms + tile - 1) / tile);
+        const size_t geo_words = (size_t)D + (ag.boff[2] + ag.n[2] + 1) + (ag.noff[2] + ag.n[2]);
+        uint32_t *d_code, *d_hist, *d_hscan;
+        uint2* d_rec;
+        DDH_HIP(sc.alloc(&d_code, (size_t)n_atoms));
+        DDH_HIP(sc.alloc(&d_hist, (size_t)D * nblk + 1));
+        DDH_HIP(sc.alloc(&d_hscan, (size_t)D * nblk + 1));
+        DDH_HIP(sc.alloc(&d_rec, (size_t)n_atoms));
+        const auto count_k = items == 16 ? part_count_kernel<16>
+                             : items == 4 ? part_count_kernel<4> : part_count_kernel<1>;
+        const auto scatter_k = items == 16 ? part_scatter_kernel<16>
+                               : items == 4 ? part_scatter_kernel<4> : part_scatter_kernel<1>;
+        if (nblk > 0)
+            hipLaunchKernelGGL(count_k, dim3(nblk), dim3(256), sizeof(uint32_t) * geo_words, s, xg,
+                               n_atoms, ag, D, nblk, d_code, d_hist, d_err);
+        DDH_HIP(hipGetLastError());
+        // (domain, block) first positions; hscan[D * nblk] = atoms in the box
+        const int rc = scan_exclusive(sc, d_hist, (int64_t)D * nblk, d_hscan, s);
+        if (rc)
+            return rc;
+        if (nblk > 0)
+            hipLaunchKernelGGL(scatter_k, dim3(nblk), dim3(256),
+                               sizeof(uint32_t) * (2 * (size_t)tile + 2 * (size_t)D), s, d_code,
+                               n_atoms, d_hscan, D, nblk, d_rec);
+        hipLaunchKernelGGL(domain_sort_kernel, dim3(D), dim3(1024), 0, s, d_rec, d_hscan, nblk,
+                           d_cellbase, D, p->d_home_gid, d_start);
+        DDH_HIP(hipGetLastError());
     } else {
         int* d_bucket;
         uint32_t *d_count, *d_rank;
@@ -1465,10 +1708,15 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         char* d_lay;
         DDH_HIP(lay.send(sc, &d_lay, s));
         d_base = (const int*)(d_lay + o_base);
-        if (n_atoms > 0)
-            hipLaunchKernelGGL(fill_home_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s,
-                               p->d_home_gid, d_hs, D, d_base, n_atoms, p->d_slot_gid,
-                               p->d_home_slot);
+        int max_home = 0;
+        for (int Dm = 0; Dm < D; Dm++)
+            max_home = std::max(max_home, hs[Dm + 1] - hs[Dm]);
+        const int cpd = (max_home + kFillTile - 1) / kFillTile;
+        if (cpd > 0)
+            hipLaunchKernelGGL(fill_home_kernel,
+                               dim3((unsigned)std::min<int64_t>((int64_t)D * cpd, kFillMaxBlocks)),
+                               dim3(256), 0, s, p->d_home_gid, d_hs, d_base, D, cpd,
+                               p->d_slot_gid, p->d_home_slot);
         for (int q = 0; q < P; q++) {
             if (total[q] > 0)
                 hipLaunchKernelGGL(fill_region_kernel, dim3(blocks(total[q])), dim3(256), 0, s,

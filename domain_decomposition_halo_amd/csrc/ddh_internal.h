@@ -187,7 +187,7 @@ struct Plan {
     int wave_chunks = 0;        // fused: wavefront workers on contiguous slices
                                 // (takes effect at the next build)
     int home_sort = 0;          // home-atom sort of the build: 0 automatic,
-                                // 1 counting sort, 2 radix sort
+                                // 1 counting sort, 2 partition sort
     int heads_first = 0;        // fused: heads-first ticket order (next build)
     int exit_publish = 0;       // per-pulse mode: 0 automatic, 1 the last
                                 // launch publishes its flags at exit, 2 a
@@ -255,11 +255,6 @@ int hip_fail(hipError_t e, const char* what);
 int build_maps(Plan* plan, const float* xg, int32_t n_atoms, hipStream_t stream);
 void free_built(Plan* plan);
 void free_scratch(Plan* plan);
-
-// stable radix sort of (key, value) pairs by the low end_bit bits of the key
-// (ddh_sort.hip). With temp null, sets *temp_bytes to the storage it needs.
-int sort_pairs(void* temp, size_t* temp_bytes, const uint32_t* keys_in, uint32_t* keys_out,
-               const int32_t* vals_in, int32_t* vals_out, int n, int end_bit, hipStream_t s);
 
 // exchange launches (ddh_exchange.hip)
 int enqueue_exchange(Plan* plan, int op, float* x, float* f, hipStream_t stream);

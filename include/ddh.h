@@ -395,12 +395,17 @@ int ddh_check(ddh_plan *plan, void *stream);
 
 #define DDH_TUNE_HOME_SORT 12      /* how the build orders the home atoms (by
                                     domain, cell, then global id; the result
-                                    is the same): 0 (default) automatic, a
-                                    radix sort from 4,000,000 atoms on, else
-                                    the counting sort; 1 the counting sort
-                                    (per-atom device atomics, then a per-cell
-                                    sort); 2 the radix sort. Takes effect at
-                                    the next build. */
+                                    is the same): 0 (default) automatic, the
+                                    partition sort where its tables fit (at
+                                    most 2048 domains and 4096 sort cells per
+                                    domain), else the counting sort; 1 the
+                                    counting sort (per-atom device atomics,
+                                    then a per-cell sort); 2 the partition
+                                    sort (per-block domain histograms and one
+                                    block per domain counting by cell, all in
+                                    LDS; the build fails with DDH_EINVAL where
+                                    it does not fit). Takes effect at the
+                                    next build. */
 
 #define DDH_TUNE_EXIT_PUBLISH 13   /* per-pulse mode with completion flags:
                                     0 (default) automatic; 1 the call's last

@@ -775,12 +775,14 @@ def test_many_small_maps(grid, n, mode):
     g.close()
 
 
-@pytest.mark.parametrize("home_sort", [1, 2])
+@pytest.mark.parametrize("home_sort", [0, 1, 2])
 def test_home_sort_forms(home_sort, workload_plan):
     """Both orderings of the home atoms (the counting sort with device
-    atomics, the radix sort) give the oracle's layout, maps and results: on
-    the workloads, exact boxes with multi-pulse relay, random decompositions,
-    many small domains, an empty input and a position outside the box."""
+    atomics, the partition sort with LDS counters) give the oracle's layout,
+    maps and results: on the workloads, exact boxes with multi-pulse relay,
+    random decompositions, many small domains, domains too large for the
+    partition's LDS copy (40,000 atoms each), an empty input and a position
+    outside the box."""
     for k in (1, 2, 3, 4):
         w, x, ref = workload_plan(k)
         g = GpuPlan(x, **w.params(), mode=ddh.DDH_MODE_PULSE, home_sort=home_sort)
@@ -792,6 +794,8 @@ def test_home_sort_forms(home_sort, workload_plan):
               for grid, box, rc, n in random_configs(6, 77)]
     cases.append(((16, 4, 4), (15.66, 15.66, 15.66), 1.2,
                   W.uniform_positions(3000, (15.66, 15.66, 15.66), seed=3016)))
+    cases.append(((2, 1, 1), (7.0, 7.0, 7.0), 1.0,
+                  W.uniform_positions(80_000, (7.0, 7.0, 7.0), seed=8011)))
     for grid, box, rc, x in cases:
         ref = oracle.OraclePlan(x, grid, box, rc)
         g = GpuPlan(x, grid, box, rc, mode=ddh.DDH_MODE_AUTO, home_sort=home_sort)
@@ -801,6 +805,24 @@ def test_home_sort_forms(home_sort, workload_plan):
     g = GpuPlan(np.zeros((0, 3), np.float32), (2, 2, 2), (8.0, 8.0, 8.0), 1.0, home_sort=home_sort)
     assert g.n_slots == 0 and g.lay["n_halo"] == 0
     g.close()
+    # more sort cells per domain than the partition's tables hold (13 x 25 x
+    # 25 = 8125 at 2 x 1 x 1, box 12.5, cell 0.5) or more domains (2304): the
+    # forced partition refuses, the automatic choice and the counting sort
+    # build
+    for grid, box in (((2, 1, 1), (12.5, 12.5, 12.5)), ((16, 16, 9), (40.0, 40.0, 22.5))):
+        x = W.uniform_positions(4000, box, seed=77)
+        if home_sort == 2:
+            plan = ddh.Plan(grid, box, 1.0)
+            plan.tune(ddh.DDH_TUNE_HOME_SORT, 2)
+            with pytest.raises(ddh.DDHError) as e:
+                plan.build_maps(torch.from_numpy(x).cuda())
+            assert e.value.code == ddh.DDH_EINVAL
+            plan.close()
+        else:
+            ref = oracle.OraclePlan(x, grid, box, 1.0)
+            g = GpuPlan(x, grid, box, 1.0, mode=ddh.DDH_MODE_AUTO, home_sort=home_sort)
+            check_layout(g, ref)
+            g.close()
     plan = ddh.Plan((2, 2, 2), (8.0, 8.0, 8.0), 1.0)
     plan.tune(ddh.DDH_TUNE_HOME_SORT, home_sort)
     x = W.lattice_positions(200, (8.0, 8.0, 8.0), seed=1)
