@@ -22,7 +22,10 @@ and p90 are taken over the replays. `cold` times the same workload with a
 step's algorithmic bytes (28 B per halo atom for the coordinate pass, 40 B
 for the force pass) with the 8 TB/s HBM peak over the measured GPU time per
 launch; `cpu_baseline` times the CPU oracle on a bounded sample of the same
-workload.
+workload. The 96k and 1M entries under `also` carry `overlap`: the step
+beside a bf16 matrix-product load on a second stream (per-pulse launches,
+and the fused launch at one work-group per compute unit, at half and at a
+quarter of them).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
        [--variant auto|step|split|pulse|staged] [--cold] [--eager]
@@ -49,6 +52,8 @@ if ROOT not in sys.path:
 METRIC = "halo exchange µs/step + halo atoms/s & HBM GB/s fraction (1 MI355X)"
 HBM_PEAK_GBS = 8000.0
 BYTES_X, BYTES_F = 28, 40
+# workloads whose entry under `also` carries the overlap figures (96k, 1M)
+OVERLAP_WORKLOADS = (2, 3)
 # the sources that decide what the exchange launches read and write
 KERNEL_SRCS = [os.path.join(ROOT, "domain_decomposition_halo_amd", "csrc", f)
                for f in ("ddh_exchange.hip", "ddh_build.hip", "ddh_internal.h")]
@@ -142,6 +147,8 @@ def run_gpu(args, w):
         plan.tune(ddh.DDH_TUNE_HEADS_FIRST, 1)
     if args.home_sort:
         plan.tune(ddh.DDH_TUNE_HOME_SORT, args.home_sort)
+    if args.lds_stage:
+        plan.tune(ddh.DDH_TUNE_LDS_STAGE, args.lds_stage)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -372,7 +379,7 @@ def run_gpu(args, w):
     # the stored counters were taken with the default settings
     tuned = (args.chunk or args.grid or args.block or args.static_first or args.no_flags
              or args.wide_maps or args.wave_chunks or args.cold or args.exit_publish
-             or args.pad_maps or args.heads_first or args.pass_ != "step")
+             or args.pad_maps or args.heads_first or args.lds_stage or args.pass_ != "step")
     traffic = None if tuned else read_traffic(variant, w.name)
     if passes is not None:
         # each pass's counter traffic, from its own stored summary
@@ -468,15 +475,18 @@ def run_builds(args, w):
 
 # ------------------------------------------------------ overlap with compute
 
-def run_overlap(args, w):
+def overlap_once(w, mode_name, grid=0, static_first=False, no_flags=False, wide_maps=False,
+                 wave_chunks=False, dim=2048, reps=4):
     """Exchange step beside a CU-filling compute load on a second stream.
 
     The load stands in for the local non-bonded work that runs while the
-    halo exchange is in flight: a chain of bf16 matrix products, sized by
-    --overlap-dim and --overlap-reps. Every stream keeps the default
-    priority. Each of (load alone, exchange alone, both) is captured as G
-    iterations in one graph (the two streams forked and joined inside it)
-    and replayed; exposed = both - load alone."""
+    halo exchange is in flight: a chain of `reps` bf16 matrix products of
+    size dim. Every stream keeps the default priority. Each of (load alone,
+    exchange alone, both) is captured as G iterations in one graph (the two
+    streams forked and joined inside it) and replayed; exposed = both - load
+    alone, hidden = 1 - exposed / exchange alone. grid > 0 caps the fused
+    launch's work-groups (DDH_TUNE_GRID), leaving compute units to the
+    load."""
     import torch
 
     import domain_decomposition_halo_amd as ddh
@@ -489,30 +499,31 @@ def run_overlap(args, w):
     xg = torch.from_numpy(x).to(dev)
     plan = ddh.Plan(**w.params())
     mode = {"auto": ddh.DDH_MODE_AUTO, "step": ddh.DDH_MODE_FUSED,
-            "pulse": ddh.DDH_MODE_PULSE}.get(args.variant, ddh.DDH_MODE_AUTO)
+            "pulse": ddh.DDH_MODE_PULSE}.get(mode_name, ddh.DDH_MODE_AUTO)
     plan.set_mode(mode)
-    if args.static_first:
+    if grid:
+        plan.tune(ddh.DDH_TUNE_GRID, grid)
+    if static_first:
         plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 1)
-    if args.no_flags:
+    if no_flags:
         plan.tune(ddh.DDH_TUNE_FLAGS, 0)
-    if args.wide_maps:
+    if wide_maps:
         plan.tune(ddh.DDH_TUNE_NARROW_MAPS, 0)
-    if args.wave_chunks:
+    if wave_chunks:
         plan.tune(ddh.DDH_TUNE_WAVE_CHUNKS, 1)
     lay = plan.build_maps(xg)
-    n_slots, n_halo = lay["n_slots"], lay["n_halo"]
+    n_slots = lay["n_slots"]
     xl = torch.zeros((n_slots, 3), dtype=torch.float32, device=dev)
     plan.gather_home(xg, xl)
     fl = torch.from_numpy(W.forces(w, n_slots)).to(dev)
-    n = args.overlap_dim
     g = torch.Generator(device="cpu").manual_seed(7)
-    a = torch.randn((n, n), generator=g).to(dev, torch.bfloat16)
-    b = torch.randn((n, n), generator=g).to(dev, torch.bfloat16)
-    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    a = torch.randn((dim, dim), generator=g).to(dev, torch.bfloat16)
+    b = torch.randn((dim, dim), generator=g).to(dev, torch.bfloat16)
+    c = torch.empty((dim, dim), dtype=torch.bfloat16, device=dev)
     side = torch.cuda.Stream()
 
     def load():
-        for _ in range(args.overlap_reps):
+        for _ in range(reps):
             torch.mm(a, b, out=c)
 
     def exchange():
@@ -553,9 +564,40 @@ def run_overlap(args, w):
     exposed = out["both_us"] - out["load_us"]
     out["exposed_exchange_us"] = round(exposed, 3)
     out["hidden_frac"] = round(1.0 - exposed / out["exchange_us"], 4) if out["exchange_us"] else None
-    out["load"] = f"{args.overlap_reps} x bf16 mm {n}x{n}x{n} on a second stream (default priority)"
+    return out
+
+
+def overlap_set(w, dim=2048, reps=4):
+    """The overlap of the per-pulse launches and of the fused launch, the
+    latter at its automatic grid (one work-group per compute unit) and
+    capped at half and a quarter of the compute units."""
+    import torch
+
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {"load": f"{reps} x bf16 mm {dim}x{dim}x{dim} on a second stream (default priority)",
+           "how": "graphs of 20 iterations, best of 5 replays; exposed = both - load alone, "
+                  "hidden = 1 - exposed / exchange alone"}
+    for key, mode, grid in (("per_pulse", "pulse", 0), ("fused", "step", 0),
+                            ("fused_grid_half", "step", n_cu // 2),
+                            ("fused_grid_quarter", "step", n_cu // 4)):
+        o = overlap_once(w, mode, grid=grid, dim=dim, reps=reps)
+        if grid:
+            o["grid"] = grid
+        res[key] = o
+    return res
+
+
+def run_overlap(args, w):
+    """--overlap: one exchange mode beside the compute load (its own JSON)."""
+    out = overlap_once(w, args.variant, grid=args.grid, static_first=args.static_first,
+                       no_flags=args.no_flags, wide_maps=args.wide_maps,
+                       wave_chunks=args.wave_chunks, dim=args.overlap_dim, reps=args.overlap_reps)
+    out["load"] = (f"{args.overlap_reps} x bf16 mm {args.overlap_dim}x{args.overlap_dim}x"
+                   f"{args.overlap_dim} on a second stream (default priority)")
     out["workload"] = w.name
     out["mode"] = args.variant
+    if args.grid:
+        out["grid"] = args.grid
     return out
 
 
@@ -954,6 +996,9 @@ def main():
                     help="DDH_TUNE_PAD_MAPS (0 automatic)")
     ap.add_argument("--heads-first", action="store_true",
                     help="fused launch: heads-first ticket order (DDH_TUNE_HEADS_FIRST = 1)")
+    ap.add_argument("--lds-stage", type=int, default=0, choices=[0, 1, 2],
+                    help="per-pulse coordinate stores staged through LDS (DDH_TUNE_LDS_STAGE: "
+                         "1 gathered in registers, 2 by LDS loads)")
     ap.add_argument("--home-sort", type=int, default=0, choices=[0, 1, 2],
                     help="DDH_TUNE_HOME_SORT (0 automatic, 1 counting, 2 partition)")
     ap.add_argument("--pass", dest="pass_", default="step", choices=["step", "coords", "forces"],
@@ -967,6 +1012,8 @@ def main():
     ap.add_argument("--overlap", action="store_true",
                     help="time the step beside a compute load on a second stream "
                          "(prints one JSON object of its own)")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the overlap figures of the 96k and 1M entries under 'also'")
     ap.add_argument("--overlap-dim", type=int, default=2048)
     ap.add_argument("--overlap-reps", type=int, default=4)
     ap.add_argument("--only-step", action="store_true",
@@ -1078,6 +1125,8 @@ def main():
                 "p90_step_us": g2["roofline"]["p90_step_us"],
                 "passes": g2["passes"], "single_launch": g2["single"],
                 "without_flags": g2["without_flags"]}
+            if k in OVERLAP_WORKLOADS and not args.no_overlap:
+                also[wk.name]["overlap"] = overlap_set(wk, args.overlap_dim, args.overlap_reps)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(w, args.cpu_seconds)

@@ -42,6 +42,7 @@ DDH_TUNE_HOME_SORT = 12
 DDH_TUNE_EXIT_PUBLISH = 13
 DDH_TUNE_PAD_MAPS = 14
 DDH_TUNE_HEADS_FIRST = 15
+DDH_TUNE_LDS_STAGE = 16
 TRACE_RECORDS = 64
 TRACE_EVENTS = {1: "start", 2: "claim", 3: "head", 4: "waited", 5: "chunk", 6: "publish", 7: "exit"}
 

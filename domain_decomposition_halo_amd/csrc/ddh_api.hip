@@ -488,6 +488,11 @@ int ddh_tune(ddh_plan* p, int32_t key, int64_t value)
             return fail(DDH_EINVAL, "ddh_tune: heads-first must be 0 or 1");
         p->heads_first = (int)value;
         return DDH_OK;
+    case DDH_TUNE_LDS_STAGE:
+        if (value < 0 || value > 2)
+            return fail(DDH_EINVAL, "ddh_tune: lds-stage must be 0, 1 or 2");
+        p->lds_stage = (int)value;
+        return DDH_OK;
     case DDH_TUNE_PAD_MAPS:
         if (value < 0 || value > 2)
             return fail(DDH_EINVAL, "ddh_tune: pad-maps must be 0, 1 or 2");

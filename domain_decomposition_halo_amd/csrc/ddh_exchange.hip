@@ -227,6 +227,156 @@ __device__ __forceinline__ void coords_put(float* dst, const DChunk& c, int i0, 
     }
 }
 
+// LDS-staged form of coords_put: per round, each wavefront's 64 records
+// form one contiguous run of the destination (768 bytes). The wavefront
+// writes the runs of all its rounds into its LDS tile, each at the run's
+// 16-byte alignment, then stores every run from the tile in 16-byte groups:
+// one aligned dwordx4 per lane for the groups the run fills, and one dword
+// store instruction for the at most six dwords of the two groups the run
+// starts and ends inside (lanes 56-61, which no group uses: a run touches at
+// most 49 groups). tile holds E * kStageTile floats per wavefront, 16-byte
+// aligned.
+constexpr int kStageTile = 196;  // 192 dwords of a run + up to 3 of alignment, rounded to 16 B
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int E, int B>
+__device__ __forceinline__ void coords_put_lds(float* dst, const DChunk& c, int i0, int end,
+                                               float (&v)[E][3], float* tile)
+{
+    const bool shift = (c.flags & kChunkShift) != 0;
+    const int dd = c.flags & 0xff;
+#pragma unroll
+    for (int e = 0; e < E; e++)
+#pragma unroll
+        for (int k = 0; k < 3; k++)
+            v[e][k] = (shift && dd == k) ? v[e][k] + c.shift : v[e][k];
+    const int lane = (int)threadIdx.x & 63;
+    const int w = ((int)threadIdx.x % B) >> 6;
+    const int seg0 = i0 + w * 64;  // round e's run starts at entry seg0 + e * B
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        const int seg = seg0 + e * B;
+        const int a = (int)(((uintptr_t)(dst + 3ll * seg) >> 2) & 3);  // dwords before it in its group
+        float* t = tile + e * kStageTile + a + 3 * lane;
+        if (seg + lane < end) {
+            t[0] = v[e][0];
+            t[1] = v[e][1];
+            t[2] = v[e][2];
+        }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        const int seg = seg0 + e * B;  // wavefront-uniform
+        if (seg >= end)
+            break;
+        const int nd = 3 * min(64, end - seg);  // the run's dwords
+        float* run = dst + 3ll * seg;
+        const int a = (int)(((uintptr_t)run >> 2) & 3);
+        float* base = run - a;  // 16-byte aligned
+        const float* tl = tile + e * kStageTile;
+        const int ng = (a + nd + 3) >> 2;  // 16-byte groups the run touches
+        const bool head = a > 0 || nd < 4;          // group 0 is partial
+        const bool tail = ng > 1 && ((a + nd) & 3);  // group ng - 1 is partial (and not group 0)
+        if (lane < ng && !(lane == 0 && head) && !(lane == ng - 1 && tail)) {
+            const float4v q = *reinterpret_cast<const float4v*>(tl + 4 * lane);
+            __builtin_nontemporal_store(q, reinterpret_cast<float4v*>(base + 4 * lane));
+        }
+        // the partial groups' dwords, one lane each
+        const int hn = head ? min(4, a + nd) - a : 0;
+        const int tn = tail ? (a + nd) - 4 * (ng - 1) : 0;
+        const int p = lane - 56;
+        if (p >= 0 && p < hn + tn) {
+            const int d = p < hn ? a + p : 4 * (ng - 1) + (p - hn);
+            __builtin_nontemporal_store(tl[d], base + d);
+        }
+    }
+    // the tile's reads are issued before a later round's writes
+    wave_lds_sync();
+}
+
+// The same staging with the gathers done by the LDS's own loads
+// (global_load_lds_dwordx3): each lane's 12-byte record goes from HBM into
+// the wavefront's LDS tile without passing through registers. The load
+// writes lane L's record at 16 L bytes of the round's tile (a 16-byte lane
+// stride, the fourth dword untouched), so the stores read every dword of a
+// 16-byte group from its record's place: dword r of a run is component r % 3
+// of record r / 3, at tile float 4 (r / 3) + r % 3. Unconditional as in
+// coords_gather (an entry past the end reads the sender's first slot). tile
+// holds E * kDmaTile floats per wavefront.
+constexpr int kDmaTile = 256;  // 64 lanes x 16 bytes
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int E>
+__device__ __forceinline__ void coords_dma_issue(const float* src, const int (&j)[E], float* tile)
+{
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        const float* s = src + 3ll * (j[e] < 0 ? 0 : j[e]);
+        __builtin_amdgcn_global_load_lds((global_void*)s, (lds_void*)(tile + e * kDmaTile), 12, 0,
+                                         0);
+    }
+}
+
+template <int E, int B>
+__device__ __forceinline__ void coords_dma_put(float* dst, const DChunk& c, int i0, int end,
+                                               const float* tile)
+{
+    // vmcnt(0): every LDS load of the wavefront has landed (later loads
+    // of the next chunk's maps are waited for too)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    wave_lds_sync();
+    const bool shift = (c.flags & kChunkShift) != 0;
+    const int dd = c.flags & 0xff;
+    const int lane = (int)threadIdx.x & 63;
+    const int w = ((int)threadIdx.x % B) >> 6;
+    const int seg0 = i0 + w * 64;
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        const int seg = seg0 + e * B;  // wavefront-uniform
+        if (seg >= end)
+            break;
+        const int nd = 3 * min(64, end - seg);
+        float* run = dst + 3ll * seg;
+        const int a = (int)(((uintptr_t)run >> 2) & 3);
+        float* base = run - a;
+        const float* tl = tile + e * kDmaTile;
+        // dword d of the aligned groups (run dword d - a), shifted on the
+        // pulse's component at a shifting sender
+        auto rd = [&](int d) {
+            const int r = d - a;
+            const int rec = r / 3, k = r - 3 * rec;
+            const float v = tl[4 * rec + k];
+            return (shift && k == dd) ? v + c.shift : v;
+        };
+        const int ng = (a + nd + 3) >> 2;
+        const bool head = a > 0 || nd < 4;
+        const bool tail = ng > 1 && ((a + nd) & 3);
+        if (lane < ng && !(lane == 0 && head) && !(lane == ng - 1 && tail)) {
+            const int d = 4 * lane;
+            const float4v q = {rd(d), rd(d + 1), rd(d + 2), rd(d + 3)};
+            __builtin_nontemporal_store(q, reinterpret_cast<float4v*>(base + d));
+        }
+        const int hn = head ? min(4, a + nd) - a : 0;
+        const int tn = tail ? (a + nd) - 4 * (ng - 1) : 0;
+        const int p = lane - 56;
+        if (p >= 0 && p < hn + tn) {
+            const int d = p < hn ? a + p : 4 * (ng - 1) + (p - hn);
+            __builtin_nontemporal_store(rd(d), base + d);
+        }
+    }
+    // the tile's reads are issued before a later round's loads land
+    wave_lds_sync();
+}
+
 // Unconditional as in coords_gather: an entry past the chunk's end reads the
 // chunk's first region record and the sender's first slot.
 template <int E, int B>
@@ -267,13 +417,23 @@ __device__ __forceinline__ void forces_put(float* tgt, const int (&j)[E], const 
 // component) for the round's entries; all gathers are issued before any
 // store. Stores are non-temporal: a region is written once per pass and not
 // re-read by the writing work-group.
-template <int E, int B>
+// STG 1: the stores are staged as in coords_put_lds; 2: the gathers are
+// LDS loads as in coords_dma_put (tile: the wavefront's LDS tile).
+template <int E, int B, int STG = 0>
 __device__ __forceinline__ void coords_round(const float* src, float* dst, const DChunk& c, int i0,
-                                             int end, const int (&j)[E])
+                                             int end, const int (&j)[E], float* tile = nullptr)
 {
-    float v[E][3];
-    coords_gather<E, B>(src, j, v);
-    coords_put<E, B>(dst, c, i0, end, v);
+    if constexpr (STG == 2) {
+        coords_dma_issue<E>(src, j, tile);
+        coords_dma_put<E, B>(dst, c, i0, end, tile);
+    } else {
+        float v[E][3];
+        coords_gather<E, B>(src, j, v);
+        if constexpr (STG == 1)
+            coords_put_lds<E, B>(dst, c, i0, end, v, tile);
+        else
+            coords_put<E, B>(dst, c, i0, end, v);
+    }
 }
 
 // Forces, one round: f[src + map[i]] += f[dst + i] (the receiver's region
@@ -294,9 +454,10 @@ __device__ __forceinline__ void forces_round(const float* from, float* tgt, int 
 // With a staging buffer (the host-orchestrated baseline), entry i of a map
 // goes to / comes from stage[map_off + i] instead of the receiver's region.
 // With load_first, the first round's entries are loaded here too (j0 unused).
-template <int E, int B, typename I>
+template <int E, int B, typename I, int STG = 0>
 __device__ void coords_range(float* x, const I* map, const DChunk& c, int begin, int end,
-                             const int (&j0)[E], float* stage = nullptr, bool load_first = false)
+                             const int (&j0)[E], float* stage = nullptr, bool load_first = false,
+                             float* tile = nullptr)
 {
     if (begin >= end)
         return;
@@ -305,14 +466,14 @@ __device__ void coords_range(float* x, const I* map, const DChunk& c, int begin,
     if (load_first) {
         int j[E];
         load_map<E, B, I>(map, begin, end, j);
-        coords_round<E, B>(src, dst, c, begin, end, j);
+        coords_round<E, B, STG>(src, dst, c, begin, end, j, tile);
     } else {
-        coords_round<E, B>(src, dst, c, begin, end, j0);
+        coords_round<E, B, STG>(src, dst, c, begin, end, j0, tile);
     }
     for (int i0 = begin + B * E; i0 < end; i0 += B * E) {
         int j[E];
         load_map<E, B, I>(map, i0, end, j);
-        coords_round<E, B>(src, dst, c, i0, end, j);
+        coords_round<E, B, STG>(src, dst, c, i0, end, j, tile);
     }
 }
 
@@ -674,9 +835,15 @@ __device__ __forceinline__ void pulse_fetch(const PArgs& a, int b, DChunk& c, in
     }
 }
 
-template <int E, int B, typename I>
+// STG: the coordinate chunks stage their stores through LDS, gathered
+// into registers (1, coords_put_lds) or by LDS loads (2, coords_dma_put);
+// the force chunks are the same in every form.
+template <int E, int B, typename I, int STG = 0>
 __global__ __launch_bounds__(B) void pulse_kernel(PArgs a)
 {
+    constexpr int kTile = STG == 2 ? E * kDmaTile : STG == 1 ? E * kStageTile : 0;
+    __shared__ __align__(16) float stile[STG ? B / 64 * kTile : 1];
+    float* tile = STG ? stile + (((int)threadIdx.x >> 6) * kTile) : nullptr;
     publish_done(a);
     // Software pipeline over the block's chunks b, b + grid, ...: chunk b's
     // gathers are issued first, then the descriptor and map entries of the
@@ -706,13 +873,24 @@ __global__ __launch_bounds__(B) void pulse_kernel(PArgs a)
         } else if (b < a.nxb) {
             const float* src = a.x + 3ll * cc.src_base;
             float* dst = a.stage ? a.stage + 3ll * cc.map_off : a.x + 3ll * cc.dst_base;
-            float v[E][3];
-            coords_gather<E, B>(src, j0, v);
-            if (bn < a.nb)
-                pulse_fetch<E, B, I>(a, bn, c, jr, m);
-            coords_put<E, B>(dst, cc, cc.hb, cc.he, v);
+            if constexpr (STG == 2) {
+                coords_dma_issue<E>(src, j0, tile);
+                if (bn < a.nb)
+                    pulse_fetch<E, B, I>(a, bn, c, jr, m);
+                coords_dma_put<E, B>(dst, cc, cc.hb, cc.he, tile);
+            } else {
+                float v[E][3];
+                coords_gather<E, B>(src, j0, v);
+                if (bn < a.nb)
+                    pulse_fetch<E, B, I>(a, bn, c, jr, m);
+                if constexpr (STG == 1)
+                    coords_put_lds<E, B>(dst, cc, cc.hb, cc.he, v, tile);
+                else
+                    coords_put<E, B>(dst, cc, cc.hb, cc.he, v);
+            }
             if (n > E * B)
-                coords_range<E, B, I>(a.x, mc, cc, cc.hb + E * B, cc.he, j0, a.stage, true);
+                coords_range<E, B, I, STG>(a.x, mc, cc, cc.hb + E * B, cc.he, j0, a.stage, true,
+                                           tile);
         } else {
             float* tgt = a.f + 3ll * cc.src_base;
             const float* from = a.stage ? a.stage + 3ll * cc.map_off : a.f + 3ll * cc.dst_base;
@@ -830,10 +1008,24 @@ void launch_wave_t(const XArgs& a, int grid, int per, hipStream_t s)
 
 // The per-pulse kernel instance for the block width and entries per lane.
 template <typename I>
-void launch_pulse_t(const PArgs& a, dim3 grid, int lanes, int per, hipStream_t s)
+void launch_pulse_t(const PArgs& a, dim3 grid, int lanes, int per, int stg, hipStream_t s)
 {
     const dim3 block(lanes);
-    if (lanes == 512) {
+    if (stg == 1) {  // 256 lanes, at most eight entries per lane and round (sixteen spill)
+        if (per > 4)
+            hipLaunchKernelGGL((pulse_kernel<8, 256, I, 1>), grid, block, 0, s, a);
+        else if (per > 2)
+            hipLaunchKernelGGL((pulse_kernel<4, 256, I, 1>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((pulse_kernel<2, 256, I, 1>), grid, block, 0, s, a);
+    } else if (stg == 2) {
+        if (per > 4)
+            hipLaunchKernelGGL((pulse_kernel<8, 256, I, 2>), grid, block, 0, s, a);
+        else if (per > 2)
+            hipLaunchKernelGGL((pulse_kernel<4, 256, I, 2>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((pulse_kernel<2, 256, I, 2>), grid, block, 0, s, a);
+    } else if (lanes == 512) {
         if (per > 4)
             hipLaunchKernelGGL((pulse_kernel<8, 512, I>), grid, block, 0, s, a);
         else if (per > 2)
@@ -992,10 +1184,11 @@ int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, 
     a.nb = nb;
     const int resident = p->n_cu * (2048 / lanes);
     const dim3 grid(std::min(nb, resident));
+    const int stg = lanes == 256 && a.nxb > 0 ? p->lds_stage : 0;
     if (narrow)
-        launch_pulse_t<uint16_t>(a, grid, lanes, per, s);
+        launch_pulse_t<uint16_t>(a, grid, lanes, per, stg, s);
     else
-        launch_pulse_t<int32_t>(a, grid, lanes, per, s);
+        launch_pulse_t<int32_t>(a, grid, lanes, per, stg, s);
     DDH_HIP(hipGetLastError());
     return DDH_OK;
 }

@@ -353,8 +353,7 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     (DDH_TUNE_GRID); the buffer is not cleared. */
 
 #define DDH_TUNE_BLOCK 7           /* work-group width of the exchange launches:
-                                    0 (automatic: fused 1024; per-pulse 1024
-                                    for chunks of at least 1024 entries, else
+                                    0 (automatic: fused 1024; per-pulse
                                     256), 256, 512 (per-pulse launches; the
                                     fused launch then takes 256) or 1024 */
 
@@ -432,6 +431,19 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     tail (pulse order), so no head waits.
                                     Same results. Takes effect at the next
                                     build. */
+
+#define DDH_TUNE_LDS_STAGE 16      /* per-pulse mode: 0 (default) coordinate
+                                    records are stored from registers (one
+                                    12-byte store per lane); 1 each
+                                    wavefront stages its 64 gathered records
+                                    in LDS and stores the contiguous run in
+                                    16-byte aligned groups (the guide's
+                                    shared-memory staging before its bulk
+                                    stores, "NVLink path: TMA-based direct
+                                    stores"); 2 the same, with the records
+                                    gathered straight into LDS by the LDS's
+                                    own loads (global_load_lds). Applies to
+                                    256-wide blocks; same results. */
 
 /* Set a tuning knob; takes effect at the next build (CHUNK, WAVE_CHUNKS,
    HOME_SORT, HEADS_FIRST) or call. Library utility: the guide defines no such call.

@@ -143,6 +143,8 @@ def test_mode_and_tune_validation():
         plan.tune(ddh.DDH_TUNE_PAD_MAPS, v)
     for v in (1, 0):
         plan.tune(ddh.DDH_TUNE_HEADS_FIRST, v)
+        plan.tune(ddh.DDH_TUNE_LDS_STAGE, v)
+    plan.tune(ddh.DDH_TUNE_LDS_STAGE, 2)
     plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 1)
     plan.tune(ddh.DDH_TUNE_STATIC_FIRST, 0)
     plan.tune(ddh.DDH_TUNE_FLAGS, 0)
@@ -159,7 +161,7 @@ def test_mode_and_tune_validation():
                      (ddh.DDH_TUNE_EXIT_PUBLISH, 3), (ddh.DDH_TUNE_PAD_MAPS, -1),
                      (ddh.DDH_TUNE_FLAGS, 2), (ddh.DDH_TUNE_NARROW_MAPS, -1),
                      (ddh.DDH_TUNE_WAVE_CHUNKS, 3), (ddh.DDH_TUNE_HOME_SORT, 3),
-                     (ddh.DDH_TUNE_HOME_SORT, -1)]:
+                     (ddh.DDH_TUNE_HOME_SORT, -1), (ddh.DDH_TUNE_LDS_STAGE, 3)]:
         with pytest.raises(ddh.DDHError) as e:
             plan.tune(key, val)
         assert e.value.code == ddh.DDH_EINVAL

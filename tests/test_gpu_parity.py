@@ -47,8 +47,9 @@ class GpuPlan:
     """A device plan built from host positions, with host views of its output."""
 
     def __init__(self, x, grid, box, rc, cell=0.5, mode=0, chunk=0, wg=0, refined=1, block=0,
-                 static_first=0, narrow=1, wave=0, home_sort=0, heads_first=0):
+                 static_first=0, narrow=1, wave=0, home_sort=0, heads_first=0, lds_stage=0):
         self.plan = ddh.Plan(grid, box, rc, cell)
+        self.plan.tune(ddh.DDH_TUNE_LDS_STAGE, lds_stage)
         self.plan.tune(ddh.DDH_TUNE_HOME_SORT, home_sort)
         self.plan.tune(ddh.DDH_TUNE_HEADS_FIRST, heads_first)
         self.plan.tune(ddh.DDH_TUNE_STATIC_FIRST, static_first)
@@ -892,21 +893,59 @@ def test_repeated_force_passes_are_deterministic(workload_plan):
     g.close()
 
 
+@pytest.mark.parametrize("stage", [1, 2])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_lds_staged_stores(k, stage, workload_plan):
+    """Coordinate stores staged through LDS (DDH_TUNE_LDS_STAGE 1: records
+    gathered into registers, 2: gathered by LDS loads) give the oracle's
+    coordinates and forces: per-pulse launches eager and from the
+    library's graphs, with 16- and 32-bit maps, with chunks of several rounds
+    (DDH_TUNE_CHUNK 4096), in the host-orchestrated baseline, and into
+    coordinate arrays that start 4, 8 or 12 bytes past a 16-byte boundary
+    (every alignment of a run), with nothing written outside them."""
+    w, x, ref = workload_plan(k)
+    forms = ((ddh.DDH_MODE_PULSE, 1, 0), (ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, 1, 0),
+             (ddh.DDH_MODE_PULSE, 0, 0), (ddh.DDH_MODE_PULSE, 1, 4096),
+             (ddh.DDH_MODE_STAGED, 1, 0))
+    for mode, narrow, chunk in forms:
+        g = GpuPlan(x, **w.params(), mode=mode, narrow=narrow, chunk=chunk, lds_stage=stage)
+        check_steps(g, ref, 300 + k, steps=2)
+        check_steps(g, ref, 310 + k, steps=1, fused_step=True)
+        g.close()
+    g = GpuPlan(x, **w.params(), mode=ddh.DDH_MODE_PULSE, lds_stage=stage)
+    n = g.n_slots
+    for off in (1, 2, 3):
+        buf = torch.full((3 * n + 8,), -7.0, dtype=torch.float32, device="cuda")
+        xl = buf[off:off + 3 * n].view(n, 3)
+        xl.zero_()
+        g.plan.gather_home(g.xg, xl)
+        g.plan.exchange_coords(xl)
+        assert g.plan.check() == ddh.DDH_OK
+        assert np.array_equal(bits(xl.cpu().numpy()), bits(ref.x_local)), off
+        rest = torch.cat([buf[:off], buf[off + 3 * n:]]).cpu().numpy()
+        assert np.all(rest == -7.0), off
+    g.close()
+
+
 def test_workload5_full_size():
     """12M atoms, 8x8x8 domains, at full size: the fused launch (work-group
-    chunks and wavefront workers), the library's graph of per-pulse launches,
-    the host-orchestrated baseline, and the bench's own launch (the automatic
-    mode captured in a caller's graph and replayed twice)."""
+    chunks and wavefront workers), the library's graph of per-pulse launches
+    (stores from registers, staged through LDS from registers and by LDS
+    loads), the host-orchestrated
+    baseline, and the bench's own launch (the automatic mode captured in a
+    caller's graph and replayed twice)."""
     w = W.WORKLOADS[5]
     x = W.positions(w)
     ref = oracle.OraclePlan(x, **w.params())
     f0 = W.forces(w, ref.n_slots)
     fr = f0.copy()
     ref.exchange_forces(fr)
-    for mode, wave in ((ddh.DDH_MODE_FUSED, 0), (ddh.DDH_MODE_FUSED, 1),
-                       (ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, 0), (ddh.DDH_MODE_STAGED, 0),
-                       (ddh.DDH_MODE_AUTO, 0)):
-        g = GpuPlan(x, **w.params(), mode=mode, wave=wave)
+    for mode, wave, stg in ((ddh.DDH_MODE_FUSED, 0, 0), (ddh.DDH_MODE_FUSED, 1, 0),
+                            (ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, 0, 0),
+                            (ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, 0, 1),
+                            (ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, 0, 2),
+                            (ddh.DDH_MODE_STAGED, 0, 0), (ddh.DDH_MODE_AUTO, 0, 0)):
+        g = GpuPlan(x, **w.params(), mode=mode, wave=wave, lds_stage=stg)
         if mode == ddh.DDH_MODE_FUSED and not wave:
             check_layout(g, ref)
         xl = g.new_coords()
@@ -932,8 +971,8 @@ def test_workload5_full_size():
                 torch.cuda.synchronize()
                 graph.replay()
             assert g.plan.check() == ddh.DDH_OK
-            assert np.array_equal(bits(xl.cpu().numpy()), bits(ref.x_local)), (mode, wave, r)
-            assert np.array_equal(bits(fl.cpu().numpy()), bits(fr)), (mode, wave, r)
+            assert np.array_equal(bits(xl.cpu().numpy()), bits(ref.x_local)), (mode, wave, stg, r)
+            assert np.array_equal(bits(fl.cpu().numpy()), bits(fr)), (mode, wave, stg, r)
         if mode == ddh.DDH_MODE_AUTO:
             del graph
         g.close()
