@@ -552,10 +552,15 @@ __device__ __forceinline__ int claim_ticket(const XArgs& a)
 // back edge: a region that did (finish at the end of one iteration, claim at
 // the start of the next) lets the compiler park lane 0 outside the loop while
 // the other lanes pass the barrier and re-read a stale ticket forever.
-template <int E, int B, typename I>
+template <int E, int B, typename I, int STG = 0>
 __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
 {
     __shared__ int s_ticket;
+    // STG: coordinate stores staged through each wavefront's LDS tile, as
+    // in the per-pulse kernel (1: register gathers, 2: LDS loads)
+    constexpr int kTile = STG == 2 ? E * kDmaTile : STG == 1 ? E * kStageTile : 0;
+    __shared__ __align__(16) float stile[STG ? B / 64 * kTile : 1];
+    float* tile = STG ? stile + (((int)threadIdx.x >> 6) * kTile) : nullptr;
     const I* maps = static_cast<const I*>(a.maps);
     const int P = a.P;
     const int nt = a.nx + a.nf;
@@ -586,7 +591,8 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
             int jh[E], jt[E];
             load_map<E, B, I>(maps + c.map_off, c.hb, c.he, jh);
             load_map<E, B, I>(maps + c.map_off, c.tb, c.te, jt);
-            coords_range<E, B, I>(a.x, maps + c.map_off, c, c.hb, c.he, jh);
+            coords_range<E, B, I, STG>(a.x, maps + c.map_off, c, c.hb, c.he, jh, nullptr, false,
+                                       tile);
             if (c.wait_a) {
                 if (wave == 0) {
                     if (threadIdx.x == 0)
@@ -597,7 +603,8 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
                 }
                 __syncthreads();
             }
-            coords_range<E, B, I>(a.x, maps + c.map_off, c, c.tb, c.te, jt);
+            coords_range<E, B, I, STG>(a.x, maps + c.map_off, c, c.tb, c.te, jt, nullptr, false,
+                                       tile);
             // every wave's records are in L2 before thread 0 releases them
             if (c.flags & kChunkRelease)
                 wait_vm_idle();
@@ -977,9 +984,19 @@ bool use_narrow_maps(const Plan* p) { return p->narrow_maps && p->d_maps16; }
 
 // The fused kernel instance for the work-group width and entries per lane.
 template <typename I>
-void launch_fused_t(const XArgs& a, int grid, bool wide, int per, hipStream_t s)
+void launch_fused_t(const XArgs& a, int grid, bool wide, int per, int stg, hipStream_t s)
 {
-    if (wide) {
+    if (stg && wide) {  // 1024 lanes; the staged forms are built for the wide block only
+        if (per > 2)
+            hipLaunchKernelGGL((stg == 1 ? exchange_kernel<4, 1024, I, 1> : exchange_kernel<4, 1024, I, 2>),
+                               dim3(grid), dim3(1024), 0, s, a);
+        else if (per > 1)
+            hipLaunchKernelGGL((stg == 1 ? exchange_kernel<2, 1024, I, 1> : exchange_kernel<2, 1024, I, 2>),
+                               dim3(grid), dim3(1024), 0, s, a);
+        else
+            hipLaunchKernelGGL((stg == 1 ? exchange_kernel<1, 1024, I, 1> : exchange_kernel<1, 1024, I, 2>),
+                               dim3(grid), dim3(1024), 0, s, a);
+    } else if (wide) {
         if (per > 2)
             hipLaunchKernelGGL((exchange_kernel<4, 1024, I>), dim3(grid), dim3(1024), 0, s, a);
         else if (per > 1)
@@ -1094,10 +1111,10 @@ int launch_fused(const Plan* p, XArgs a, hipStream_t s)
     const int per = (p->fused.chunk + (wide ? 1023 : 255)) / (wide ? 1024 : 256);
     if (use_narrow_maps(p)) {
         a.maps = p->d_maps16;
-        launch_fused_t<uint16_t>(a, grid, wide, per, s);
+        launch_fused_t<uint16_t>(a, grid, wide, per, p->lds_stage, s);
     } else {
         a.maps = p->d_maps;
-        launch_fused_t<int32_t>(a, grid, wide, per, s);
+        launch_fused_t<int32_t>(a, grid, wide, per, p->lds_stage, s);
     }
     DDH_HIP(hipGetLastError());
     return DDH_OK;

@@ -192,7 +192,7 @@ struct Plan {
     int exit_publish = 0;       // per-pulse mode: 0 automatic, 1 the last
                                 // launch publishes its flags at exit, 2 a
                                 // one-wave launch after it does
-    int lds_stage = 0;          // per-pulse mode: coordinate stores staged through LDS
+    int lds_stage = 0;          // per-pulse and fused: coordinate stores staged through LDS
                                 // (1 gathered in registers, 2 by LDS loads)
     int pad_maps = 0;           // per-pulse mode: 0 automatic, 1 blocks read
                                 // the chunk-aligned map copy (loads issued

@@ -432,7 +432,7 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     Same results. Takes effect at the next
                                     build. */
 
-#define DDH_TUNE_LDS_STAGE 16      /* per-pulse mode: 0 (default) coordinate
+#define DDH_TUNE_LDS_STAGE 16      /* per-pulse and fused modes: 0 (default) coordinate
                                     records are stored from registers (one
                                     12-byte store per lane); 1 each
                                     wavefront stages its 64 gathered records
@@ -443,7 +443,9 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     stores"); 2 the same, with the records
                                     gathered straight into LDS by the LDS's
                                     own loads (global_load_lds). Applies to
-                                    256-wide blocks; same results. */
+                                    the per-pulse launches' 256-wide blocks
+                                    and the fused launch's 1024-wide
+                                    work-groups; same results. */
 
 /* Set a tuning knob; takes effect at the next build (CHUNK, WAVE_CHUNKS,
    HOME_SORT, HEADS_FIRST) or call. Library utility: the guide defines no such call.

@@ -898,15 +898,17 @@ def test_repeated_force_passes_are_deterministic(workload_plan):
 def test_lds_staged_stores(k, stage, workload_plan):
     """Coordinate stores staged through LDS (DDH_TUNE_LDS_STAGE 1: records
     gathered into registers, 2: gathered by LDS loads) give the oracle's
-    coordinates and forces: per-pulse launches eager and from the
-    library's graphs, with 16- and 32-bit maps, with chunks of several rounds
-    (DDH_TUNE_CHUNK 4096), in the host-orchestrated baseline, and into
+    coordinates and forces: per-pulse launches and the fused launch, eager
+    and from the library's graphs, with 16- and 32-bit maps, with chunks of
+    several rounds (DDH_TUNE_CHUNK 4096 and 8192), in the host-orchestrated
+    baseline, and into
     coordinate arrays that start 4, 8 or 12 bytes past a 16-byte boundary
     (every alignment of a run), with nothing written outside them."""
     w, x, ref = workload_plan(k)
     forms = ((ddh.DDH_MODE_PULSE, 1, 0), (ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, 1, 0),
              (ddh.DDH_MODE_PULSE, 0, 0), (ddh.DDH_MODE_PULSE, 1, 4096),
-             (ddh.DDH_MODE_STAGED, 1, 0))
+             (ddh.DDH_MODE_STAGED, 1, 0), (ddh.DDH_MODE_FUSED, 1, 0),
+             (ddh.DDH_MODE_FUSED | ddh.DDH_MODE_GRAPH, 0, 0), (ddh.DDH_MODE_FUSED, 1, 8192))
     for mode, narrow, chunk in forms:
         g = GpuPlan(x, **w.params(), mode=mode, narrow=narrow, chunk=chunk, lds_stage=stage)
         check_steps(g, ref, 300 + k, steps=2)
@@ -941,6 +943,7 @@ def test_workload5_full_size():
     fr = f0.copy()
     ref.exchange_forces(fr)
     for mode, wave, stg in ((ddh.DDH_MODE_FUSED, 0, 0), (ddh.DDH_MODE_FUSED, 1, 0),
+                            (ddh.DDH_MODE_FUSED, 0, 2),
                             (ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, 0, 0),
                             (ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, 0, 1),
                             (ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH, 0, 2),
