@@ -51,6 +51,9 @@ constexpr int kPartMaxDomains = 2048;
 constexpr int kPartMaxCells = 4096;
 constexpr int kDomCap = 32768;           // atoms of a domain sorted in LDS
 constexpr int kDomBatch = 8;             // record loads a thread issues together
+// the home selection goes by cells while no domain averages more home atoms
+// per sort cell than this
+constexpr int kCellMaxAvg = 64;
 
 struct AGeom {
     int n[3];
@@ -533,7 +536,19 @@ struct SArgs {
     const int* out_pos;   // per S: first record of its region at R
     int* out_gid;
     float* out_xyz;
+    // The pulse's counting units, sender-major: sender S's candidate home
+    // cells (with the selection by cells, CArgs; hcprefix null otherwise),
+    // then its tiles, at ubase[S] on; one exclusive scan of the units' counts
+    // gives each its first entry.
+    const int* ubase;
+    const int* hcprefix;
 };
+
+// Units of sender S before its tiles (its candidate home cells).
+__device__ __forceinline__ int home_units(const SArgs& a, int S)
+{
+    return a.hcprefix ? a.hcprefix[S + 1] - a.hcprefix[S] : 0;
+}
 
 // Candidate slot j of sender S: its global id and its coordinates. Home
 // slots read the slot-ordered home positions, received slots the records of
@@ -627,13 +642,212 @@ __device__ __forceinline__ void tile_of(const SArgs& a, const int* tprefix, int 
     j1 = min(j0 + kSelTile, a.last[S]);
 }
 
-__global__ __launch_bounds__(256) void select_count_kernel(SArgs a, const int* __restrict__ tprefix,
-                                                           uint32_t* __restrict__ cnt,
+// ---- slab selection of the home slots by cells (a dimension's first pulse)
+//
+// A home atom's cell coordinate along d is floor(fl(u * inv_c)), clamped to
+// the domain's cells, of the same u = fl(x_d - lo_d(S)) that the slab test
+// fl(x_d - lo_d(S)) < rc compares, and fl(u * inv_c) is monotone in u. So
+// from the host's thresholds, a sender's cells with coordinate >= cfail
+// along d hold only failing positions and are never visited, and those
+// below cpass hold only passing ones and are taken whole without reading a
+// position. Only the cells in between are tested atom by atom. The
+// candidate cells of a sender, numbered m = 0, 1, ... in key order (= slot
+// order), are one thread each.
+struct CArgs {
+    int d;
+    float L_d, rc;
+    const int* ctile_s;    // [b] sender of cell tile b (256 candidate cells)
+    const int* ctprefix;   // [S] first cell tile of S
+    const int* hcprefix;   // [S] first candidate cell of S in the pulse's numbering
+    const int4* cls;       // [S] cells along x, along y, certain-pass and candidate cells along d
+    const int* cellbase;   // first bucket of each domain
+    const uint32_t* start; // home rank where each bucket starts
+    const int* home_start;
+    const float* xhome;
+    const int* home_gid;
+    const float* lo;
+    const int* shiftbit;
+    int nblocks;           // cell tiles (the launch's first blocks)
+    const int* map_pos;
+    int* map_out;
+    const int* out_pos;
+    int* out_gid;
+    float* out_xyz;
+};
+
+// Candidate cell m of a sender: its key (cx + ncx (cy + ncy cz)) and its
+// coordinate along d. Along z the candidates are the layers cz < cf, along
+// y the rows cy < cf of every layer, along x the first cf cells of every row.
+__device__ __forceinline__ int cand_cell(int m, int d, int ncx, int ncy, int cf, int& cd)
+{
+    if (d == 2) {
+        cd = m / (ncx * ncy);
+        return m;
+    }
+    if (d == 1) {
+        const int per = ncx * cf, cz = m / per, r = m - cz * per;
+        cd = r / ncx;
+        return r + cz * ncx * ncy;
+    }
+    const int row = m / cf, cx = m - row * cf;
+    cd = cx;
+    return cx + ncx * row;
+}
+
+constexpr int kCellBatch = 16;  // positions of a cell a thread loads together
+
+// The home ranks [r0, r1) of candidate cell m of cell tile cb's sender and
+// whether they pass whole; false when m is past the sender's candidates.
+__device__ __forceinline__ bool cand_range(const CArgs& a, int cb, int& S, int& m, uint32_t& r0,
+                                           uint32_t& r1, bool& whole)
+{
+    S = a.ctile_s[cb];
+    m = (cb - a.ctprefix[S]) * 256 + (int)threadIdx.x;
+    if (m >= a.hcprefix[S + 1] - a.hcprefix[S])
+        return false;
+    const int4 k = a.cls[S];
+    int cd;
+    const int key = cand_cell(m, a.d, k.x, k.y, k.w, cd);
+    const int bk = a.cellbase[S] + key;
+    r0 = a.start[bk];
+    r1 = a.start[bk + 1];
+    whole = cd < k.z;
+    return true;
+}
+
+// Count of cell tile cb: each candidate cell's entries, at its unit.
+__device__ void cell_count_block(const CArgs& a, int cb, const int* ubase, uint32_t* ucnt)
+{
+    int S, m;
+    uint32_t r0, r1;
+    bool whole;
+    if (!cand_range(a, cb, S, m, r0, r1, whole))
+        return;
+    uint32_t n = r1 - r0;
+    if (!whole) {
+        const float lo = a.lo[S];
+        n = 0;
+        for (uint32_t b = r0; b < r1; b += kCellBatch) {
+            float v[kCellBatch];
+#pragma unroll
+            for (int i = 0; i < kCellBatch; i++)
+                v[i] = b + i < r1 ? a.xhome[3ll * (b + i) + a.d] : __builtin_nanf("");
+#pragma unroll
+            for (int i = 0; i < kCellBatch; i++)
+                n += (v[i] - lo) < a.rc;  // false for NaN
+        }
+    }
+    ucnt[ubase[S] + m] = n;
+}
+
+// Write of cell tile cb: its candidate cells (256 consecutive ones of one sender) as one
+// run of home slots: each thread loads its cell's range into LDS, a block
+// scan lays the cells end to end, and the block walks that run 256 slots
+// at a time. Every slot of a whole cell is selected, every other one is
+// tested; a ballot prefix over the block gives each selected slot its entry,
+// so consecutive lanes read consecutive slots and write consecutive entries.
+__device__ void cell_write_block(const CArgs& a, int cb, const int* ubase, const uint32_t* uscan)
+{
+    __shared__ uint32_t cr0[256];
+    __shared__ int cst[257];
+    __shared__ unsigned char cwhole[256];
+    __shared__ uint32_t scan_sh[256];
+    __shared__ int wt[4];
+    const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int S = a.ctile_s[cb];
+    const int m0 = (cb - a.ctprefix[S]) * 256;
+    const int ncb = min(256, a.hcprefix[S + 1] - a.hcprefix[S] - m0);  // cells of the block
+    uint32_t r0 = 0, r1 = 0;
+    bool whole = false;
+    if (tid < ncb) {
+        const int4 k = a.cls[S];
+        int cd;
+        const int key = cand_cell(m0 + tid, a.d, k.x, k.y, k.w, cd);
+        const int bk = a.cellbase[S] + key;
+        r0 = a.start[bk];
+        r1 = a.start[bk + 1];
+        whole = cd < k.z;
+    }
+    uint32_t nslots;
+    const uint32_t off = block_scan_excl(r1 - r0, scan_sh, nslots);
+    cr0[tid] = r0;
+    cst[tid] = (int)off;
+    cwhole[tid] = whole;
+    if (tid == 0)
+        cst[ncb] = (int)nslots;
+    __syncthreads();
+    const float lo = a.lo[S];
+    const int hs = a.home_start[S];
+    const bool shift = a.shiftbit[S] != 0;
+    // the block's first entry: S's entries of the cells before the block
+    int run = (int)(uscan[ubase[S] + m0] - uscan[ubase[S]]);
+    int* map = a.map_out + a.map_pos[S];
+    int* gid = a.out_gid + a.out_pos[S];
+    float* xyz = a.out_xyz + 3ll * a.out_pos[S];
+    for (int base = 0; base < (int)nslots; base += 256) {
+        const int t = base + tid;
+        bool pass = false;
+        uint32_t r = 0;
+        float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f;
+        int g = 0;
+        if (t < (int)nslots) {
+            int l = 0, h = ncb;  // the cell c with cst[c] <= t < cst[c + 1]
+            while (h - l > 1) {
+                const int mid = (l + h) >> 1;
+                if (cst[mid] <= t)
+                    l = mid;
+                else
+                    h = mid;
+            }
+            r = cr0[l] + (uint32_t)(t - cst[l]);
+            v0 = a.xhome[3ll * r];
+            v1 = a.xhome[3ll * r + 1];
+            v2 = a.xhome[3ll * r + 2];
+            g = a.home_gid[r];
+            const float vd = a.d == 0 ? v0 : a.d == 1 ? v1 : v2;
+            pass = cwhole[l] || (vd - lo) < a.rc;
+        }
+        const unsigned long long bal = __ballot(pass);
+        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0)
+            wt[w] = __popcll(bal);
+        __syncthreads();
+        int before = 0, tot = 0;
+        for (int q = 0; q < 4; q++) {
+            before += q < w ? wt[q] : 0;
+            tot += wt[q];
+        }
+        if (pass) {
+            const int idx = run + before + pre;
+            map[idx] = (int)r - hs;
+            gid[idx] = g;
+            // the record as the receiver gets it: + L_d on component d when
+            // the sender sits at index 0 of d
+            xyz[3ll * idx] = (a.d == 0 && shift) ? v0 + a.L_d : v0;
+            xyz[3ll * idx + 1] = (a.d == 1 && shift) ? v1 + a.L_d : v1;
+            xyz[3ll * idx + 2] = (a.d == 2 && shift) ? v2 + a.L_d : v2;
+        }
+        run += tot;
+        __syncthreads();  // wt is rewritten next round
+    }
+}
+
+// Counts of the pulse's units: the first ca.nblocks blocks are cell tiles
+// (cell_count_block), the others slot tiles, each counting its selected
+// slots and those below the split (home slots).
+__global__ __launch_bounds__(256) void select_count_kernel(SArgs a, CArgs ca,
+                                                           const int* __restrict__ tprefix,
+                                                           uint32_t* __restrict__ ucnt,
                                                            uint32_t* __restrict__ below)
 {
+    if ((int)blockIdx.x < ca.nblocks) {
+        cell_count_block(ca, (int)blockIdx.x, a.ubase, ucnt);
+        return;
+    }
+    const int tb = (int)blockIdx.x - ca.nblocks;
     __shared__ int s_send, s_split;
     int S, j0, j1;
-    tile_of(a, tprefix, blockIdx.x, S, j0, j1);
+    tile_of(a, tprefix, tb, S, j0, j1);
     if (threadIdx.x == 0) {
         s_send = 0;
         s_split = 0;
@@ -664,14 +878,14 @@ __global__ __launch_bounds__(256) void select_count_kernel(SArgs a, const int* _
     atomicAdd(&s_split, bl);
     __syncthreads();
     if (threadIdx.x == 0) {
-        cnt[blockIdx.x] = (uint32_t)s_send;
-        below[blockIdx.x] = (uint32_t)s_split;
+        ucnt[a.ubase[S] + home_units(a, S) + (tb - tprefix[S])] = (uint32_t)s_send;
+        below[tb] = (uint32_t)s_split;
     }
 }
 
 // Per-sender totals from the tile scan: entries sent and entries below the
 // split (home slots).
-__global__ __launch_bounds__(256) void select_totals_kernel(const int* __restrict__ tprefix,
+__global__ __launch_bounds__(256) void select_totals_kernel(SArgs a, const int* __restrict__ tprefix,
                                                             int ndom,
                                                             const uint32_t* __restrict__ scan,
                                                             const uint32_t* __restrict__ below,
@@ -679,8 +893,9 @@ __global__ __launch_bounds__(256) void select_totals_kernel(const int* __restric
                                                             int* __restrict__ cnt_split)
 {
     for (int S = blockIdx.x * 256 + threadIdx.x; S < ndom; S += gridDim.x * 256) {
-        cnt_send[S] = (int)(scan[tprefix[S + 1]] - scan[tprefix[S]]);
-        uint32_t bl = 0;
+        const int u0 = a.ubase[S];
+        cnt_send[S] = (int)(scan[a.ubase[S + 1]] - scan[u0]);
+        uint32_t bl = scan[u0 + home_units(a, S)] - scan[u0];  // home cells: all below
         for (int b = tprefix[S]; b < tprefix[S + 1]; b++)
             bl += below[b];
         cnt_split[S] = (int)bl;
@@ -689,16 +904,22 @@ __global__ __launch_bounds__(256) void select_totals_kernel(const int* __restric
 
 // Ordered compaction of one tile: its selected slots go to the sender's map
 // from the tile's scanned offset on, in slot order.
-__global__ __launch_bounds__(256) void select_write_kernel(SArgs a, const int* __restrict__ tprefix,
+__global__ __launch_bounds__(256) void select_write_kernel(SArgs a, CArgs ca,
+                                                           const int* __restrict__ tprefix,
                                                            const uint32_t* __restrict__ scan)
 {
+    if ((int)blockIdx.x < ca.nblocks) {
+        cell_write_block(ca, (int)blockIdx.x, a.ubase, scan);
+        return;
+    }
+    const int tb = (int)blockIdx.x - ca.nblocks;
     __shared__ int wave_tot[4];
     __shared__ int s_run;
     int S, j0, j1;
-    tile_of(a, tprefix, blockIdx.x, S, j0, j1);
+    tile_of(a, tprefix, tb, S, j0, j1);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (threadIdx.x == 0)
-        s_run = (int)(scan[blockIdx.x] - scan[tprefix[S]]);  // entries of S's earlier tiles
+    if (threadIdx.x == 0)  // S's entries of the units before this tile
+        s_run = (int)(scan[a.ubase[S] + home_units(a, S) + (tb - tprefix[S])] - scan[a.ubase[S]]);
     __syncthreads();
     const bool shift = a.shiftbit[S] != 0;
     // as in the count: every slot's position load is issued before the
@@ -946,7 +1167,7 @@ hipError_t owned_alloc(Plan* p, T** out, size_t n)
 }
 
 // Small host arrays gathered into one host-to-device copy: add() appends a
-// section (8-byte aligned) and returns its byte offset; send() copies the
+// section (16-byte aligned) and returns its byte offset; send() copies the
 // whole blob into a scratch buffer, after which section k sits at
 // base + offset k. The host storage must live until the stream has run the
 // copy (the build synchronizes before it goes out of scope).
@@ -956,7 +1177,7 @@ struct Blob {
     template <class T>
     size_t add(const T* src, size_t n)
     {
-        const size_t off = (bytes + 7) & ~size_t(7);
+        const size_t off = (bytes + 15) & ~size_t(15);
         bytes = off + n * sizeof(T);
         words.resize((bytes + 7) / 8);
         if (n)
@@ -1492,6 +1713,38 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     DDH_HIP(sc.alloc(&d_cnt_send, (size_t)D));
     DDH_HIP(sc.alloc(&d_cnt_split, (size_t)D));
 
+    // Cell thresholds of the home selection (cell_count_kernel): umin(c) is
+    // the smallest u >= 0 whose cell coordinate floor(fl(u * inv_c))
+    // reaches c. Along d, cell c holds only passing positions when
+    // umin(c + 1) <= rc (and it is not the domain's last cell, which also
+    // takes every larger u), only failing ones when umin(c) >= rc.
+    int cpass0 = 0, cfail0 = 1;
+    if (g.inv_c > 0.0f) {
+        auto umin = [&](int c) {
+            uint32_t lo = 0u, hi = 0x7F800000u;  // +inf reaches every c
+            while (lo < hi) {
+                const uint32_t mid = lo + (hi - lo) / 2;
+                float u;
+                std::memcpy(&u, &mid, 4);
+                if (u * g.inv_c >= (float)c)
+                    hi = mid;
+                else
+                    lo = mid + 1;
+            }
+            float u;
+            std::memcpy(&u, &lo, 4);
+            return u;
+        };
+        while (cpass0 < (1 << 20) && umin(cpass0 + 1) <= g.rc)
+            cpass0++;
+        while (cfail0 < (1 << 20) && umin(cfail0) < g.rc)
+            cfail0++;
+    }
+    // by cells while cells are small (a thread walks each candidate cell)
+    bool cell_mode = g.inv_c > 0.0f;
+    for (int Dm = 0; Dm < D && cell_mode; Dm++)
+        cell_mode = p->nhome[Dm] <= (int64_t)kCellMaxAvg * (cellbase[Dm + 1] - cellbase[Dm]);
+
     // the pulses' upload blobs stay alive until the layout's sync
     std::vector<Blob> blobs;
     blobs.reserve(2 * (size_t)P + 1);
@@ -1499,6 +1752,11 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         const int d = g.pdim[q], k = g.pk[q];
         std::vector<float> lo(D);
         std::vector<int> first(D), last(D), sbit(D), rcv(D);
+        // the home slots by cells: per sender its cell shape and thresholds,
+        // and its candidate cells in tiles of 256
+        const bool by_cells = cell_mode && k == 0;
+        std::vector<int> cls(by_cells ? 4 * (size_t)D : 0), hcprefix(by_cells ? (size_t)D + 1 : 0);
+        std::vector<int> ctprefix(by_cells ? (size_t)D + 1 : 0);
         for (int S = 0; S < D; S++) {
             int c[3];
             g.coords(S, c);
@@ -1507,8 +1765,20 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
             int cr[3] = {c[0], c[1], c[2]};
             cr[d] = (c[d] - 1 + g.n[d]) % g.n[d];
             rcv[S] = g.index(cr);
+            if (by_cells) {
+                const int nx = g.ncell[0][c[0]], ny = g.ncell[1][c[1]], nz = g.ncell[2][c[2]];
+                const int ncd = g.ncell[d][c[d]];
+                const int cf = std::min(cfail0, ncd);
+                cls[4 * S] = nx;
+                cls[4 * S + 1] = ny;
+                cls[4 * S + 2] = std::min(cpass0, ncd - 1);
+                cls[4 * S + 3] = cf;
+                const int hc = (int)((int64_t)nx * ny * nz / ncd * cf);
+                hcprefix[S + 1] = hcprefix[S] + hc;
+                ctprefix[S + 1] = ctprefix[S] + (hc + 255) / 256;
+            }
             if (k == 0) {
-                first[S] = 0;
+                first[S] = by_cells ? p->nhome[S] : 0;
                 last[S] = p->ntotal[S];
             } else {
                 first[S] = roff_at[S * P + q - 1];
@@ -1532,6 +1802,20 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
             for (int b = tprefix[S]; b < tprefix[S + 1]; b++)
                 tile_s[b] = S;
         const size_t o_tile_s = in.add(tile_s);
+        const int CT = by_cells ? ctprefix[D] : 0;
+        std::vector<int> ctile_s((size_t)std::max(CT, 1), 0);
+        for (int S = 0; by_cells && S < D; S++)
+            for (int b = ctprefix[S]; b < ctprefix[S + 1]; b++)
+                ctile_s[b] = S;
+        const size_t o_cls = in.add(cls), o_hcprefix = in.add(hcprefix);
+        const size_t o_ctprefix = in.add(ctprefix), o_ctile_s = in.add(ctile_s);
+        // counting units, sender-major: S's candidate home cells, then its tiles
+        std::vector<int> ubase((size_t)D + 1, 0);
+        for (int S = 0; S < D; S++)
+            ubase[S + 1] = ubase[S] + (by_cells ? hcprefix[S + 1] - hcprefix[S] : 0) +
+                           (tprefix[S + 1] - tprefix[S]);
+        const int U = ubase[D];
+        const size_t o_ubase = in.add(ubase);
         char* d_in;
         DDH_HIP(in.send(sc, &d_in, s));
         const float* d_lo = (const float*)(d_in + o_lo);
@@ -1568,19 +1852,39 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         a.shiftbit = d_shiftbit;
         a.cnt_send = d_cnt_send;
         a.cnt_split = d_cnt_split;
-        uint32_t *d_tcnt, *d_tbelow, *d_tscan;
-        DDH_HIP(sc.alloc(&d_tcnt, (size_t)T + 1));
+        a.ubase = (const int*)(d_in + o_ubase);
+        CArgs ca{};
+        if (by_cells) {
+            ca.d = d;
+            ca.L_d = g.L[d];
+            ca.rc = g.rc;
+            ca.ctile_s = (const int*)(d_in + o_ctile_s);
+            ca.ctprefix = (const int*)(d_in + o_ctprefix);
+            ca.hcprefix = (const int*)(d_in + o_hcprefix);
+            ca.cls = (const int4*)(d_in + o_cls);
+            ca.cellbase = d_cellbase;
+            ca.start = d_start;
+            ca.home_start = d_hs;
+            ca.xhome = d_xhome;
+            ca.home_gid = p->d_home_gid;
+            ca.lo = d_lo;
+            ca.shiftbit = d_shiftbit;
+            ca.nblocks = CT;
+            a.hcprefix = ca.hcprefix;
+        }
+        uint32_t *d_ucnt, *d_tbelow, *d_uscan;
+        DDH_HIP(sc.alloc(&d_ucnt, (size_t)U + 1));
         DDH_HIP(sc.alloc(&d_tbelow, (size_t)T + 1));
-        DDH_HIP(sc.alloc(&d_tscan, (size_t)T + 1));
-        if (T > 0)
-            hipLaunchKernelGGL(select_count_kernel, dim3(T), dim3(256), 0, s, a, d_tprefix,
-                               d_tcnt, d_tbelow);
+        DDH_HIP(sc.alloc(&d_uscan, (size_t)U + 1));
+        if (CT + T > 0)
+            hipLaunchKernelGGL(select_count_kernel, dim3(CT + T), dim3(256), 0, s, a, ca, d_tprefix,
+                               d_ucnt, d_tbelow);
         DDH_HIP(hipGetLastError());
-        const int rcode = scan_exclusive(sc, d_tcnt, T, d_tscan, s);
+        const int rcode = scan_exclusive(sc, d_ucnt, U, d_uscan, s);
         if (rcode)
             return rcode;
         hipLaunchKernelGGL(select_totals_kernel, dim3(std::min(blocks(D), 1024)), dim3(256), 0, s,
-                           d_tprefix, D, d_tscan, d_tbelow, d_cnt_send, d_cnt_split);
+                           a, d_tprefix, D, d_uscan, d_tbelow, d_cnt_send, d_cnt_split);
         DDH_HIP(hipGetLastError());
         std::vector<int> cs(D), cp(D);
         DDH_HIP(hipMemcpyAsync(cs.data(), d_cnt_send, sizeof(int) * D, hipMemcpyDeviceToHost, s));
@@ -1632,9 +1936,14 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         a.out_pos = (const int*)(d_pos + o_opos);
         a.out_gid = rgid[q];
         a.out_xyz = rxyz[q];
-        if (T > 0)
-            hipLaunchKernelGGL(select_write_kernel, dim3(T), dim3(256), 0, s, a, d_tprefix,
-                               d_tscan);
+        ca.map_pos = a.map_pos;
+        ca.map_out = a.map_out;
+        ca.out_pos = a.out_pos;
+        ca.out_gid = a.out_gid;
+        ca.out_xyz = a.out_xyz;
+        if (CT + T > 0)
+            hipLaunchKernelGGL(select_write_kernel, dim3(CT + T), dim3(256), 0, s, a, ca, d_tprefix,
+                               d_uscan);
         DDH_HIP(hipGetLastError());
     }
 
