@@ -902,6 +902,24 @@ def summarize_pmc(fetch_csv, write_csv, variant, wname, copy_mb, command, pass_=
     print(path)
 
 
+def summarize_markers(trace_dir, title, command):
+    """A markdown section from a rocprofv3 --marker-trace --stats run: the
+    host ranges (entry points and the map build's phases) with their calls
+    and average, minimum and maximum durations."""
+    import glob
+
+    hits = sorted(glob.glob(os.path.join(trace_dir, "**", "*marker_api_stats.csv"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no marker statistics under {trace_dir}")
+    rows = list(csv.DictReader(open(hits[-1])))
+    lines = [f"## {title}", "", "```", command, "```", "",
+             "| range | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    return "\n".join(lines) + "\n"
+
+
 def summarize_trace(trace_dir, wname, label, command, bench_line, out_path):
     """Turn a rocprofv3 --kernel-trace --stats run into a profiles/ summary:
     the statistics table and, for the exchange's launches, the median
@@ -1043,6 +1061,9 @@ def main():
     ap.add_argument("--event-log", metavar="OUT_MD", default="",
                     help="run one fused step with the device event log and write its "
                          "per-stage summary (give the command line with --pmc-command)")
+    ap.add_argument("--summarize-markers", nargs=2, metavar=("TRACE_DIR", "TITLE"),
+                    help="print a markdown section of the host ranges of a rocprofv3 "
+                         "--marker-trace --stats run (give the command with --pmc-command)")
     ap.add_argument("--bench-line", default="",
                     help="with --summarize-trace: the bench result of the profiled run")
     ap.add_argument("--min-replays", type=int, default=5,
@@ -1062,6 +1083,10 @@ def main():
                      "pass --variant step|split|pulse")
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.variant, w.name,
                       args.copy_probe, args.pmc_command, args.pass_)
+        return
+    if args.summarize_markers:
+        print(summarize_markers(args.summarize_markers[0], args.summarize_markers[1],
+                                args.pmc_command), end="")
         return
     if args.summarize_trace:
         tdir, out_path, label = args.summarize_trace
