@@ -342,17 +342,74 @@ __device__ __forceinline__ void place_and_sort(const uint2* __restrict__ rec, ui
         sort_cell(out, k ? c[k - 1] : 0u, c[k]);
 }
 
+// Positions of a sorted domain's home ranks: out[i] = xg[ids[i]] for every
+// rank i whose cell the first pulses' selection by cells may read, i.e. with
+// a coordinate below g.w along some dimension (cells along x, y, z in g.x,
+// g.y, g.z; cell k ends at c[k]). The loads of kDomBatch ranks per thread
+// are issued together.
+template <typename Ids>
+__device__ __forceinline__ void gather_home_positions(const Ids* ids, uint32_t n, const uint32_t* c,
+                                                      int nc, const int4 g,
+                                                      const float* __restrict__ xg,
+                                                      float* __restrict__ out)
+{
+    const int tid = (int)threadIdx.x;
+    const int cfx = min(g.w, g.x), cfy = min(g.w, g.y), cfz = min(g.w, g.z);
+    for (uint32_t i0 = 0; i0 < n; i0 += 1024 * kDomBatch) {
+        int id[kDomBatch];
+#pragma unroll
+        for (int j = 0; j < kDomBatch; j++) {
+            const uint32_t i = i0 + j * 1024 + tid;
+            id[j] = -1;
+            if (i < n) {
+                int lo = 0, hi = nc - 1;  // the cell k with c[k - 1] <= i < c[k]
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (c[mid] > i)
+                        hi = mid;
+                    else
+                        lo = mid + 1;
+                }
+                const int cx = lo % g.x, cy = (lo / g.x) % g.y, cz = lo / (g.x * g.y);
+                if (cx < cfx || cy < cfy || cz < cfz)
+                    id[j] = (int)ids[i];
+            }
+        }
+        float v[kDomBatch][3];
+#pragma unroll
+        for (int j = 0; j < kDomBatch; j++) {
+            const float* q = xg + 3ll * (id[j] < 0 ? 0 : id[j]);
+            v[j][0] = q[0];
+            v[j][1] = q[1];
+            v[j][2] = q[2];
+        }
+#pragma unroll
+        for (int j = 0; j < kDomBatch; j++) {
+            if (id[j] >= 0) {
+                float* o = out + 3ll * (i0 + j * 1024 + tid);
+                o[0] = v[j][0];
+                o[1] = v[j][1];
+                o[2] = v[j][2];
+            }
+        }
+    }
+}
+
 // One block per domain D, whose atoms are rec[h0, h1): count them per cell
 // in LDS, scan, store the buckets' first positions (start[cellbase[D] + k],
 // and start[nb] = every atom inside the box from the last domain), place
-// every id at its cell's position and order each cell by global id. A
-// domain of at most kDomCap atoms is placed and sorted in LDS and leaves in
-// one coalesced copy; a larger one is placed and sorted in home_gid.
+// every id at its cell's position and order each cell by global id, then
+// gather the home positions the selection reads into xhome. A domain of at
+// most kDomCap atoms is placed and sorted in LDS and leaves in one coalesced
+// copy; a larger one is placed and sorted in home_gid.
 __global__ __launch_bounds__(1024) void domain_sort_kernel(const uint2* __restrict__ rec,
                                                            const uint32_t* __restrict__ hscan,
                                                            int nblk, const int* __restrict__ cellbase,
                                                            int ndom, int* __restrict__ home_gid,
-                                                           uint32_t* __restrict__ start)
+                                                           uint32_t* __restrict__ start,
+                                                           const float* __restrict__ xg,
+                                                           const int4* __restrict__ dgeo,
+                                                           float* __restrict__ xhome)
 {
     __shared__ uint32_t c[kPartMaxCells];
     __shared__ int ids[kDomCap];
@@ -398,8 +455,13 @@ __global__ __launch_bounds__(1024) void domain_sort_kernel(const uint2* __restri
         __syncthreads();
         for (uint32_t i = tid; i < n; i += 1024)
             home_gid[h0 + i] = ids[i];
+        gather_home_positions(ids, n, c, nc, dgeo[D], xg, xhome + 3ll * h0);
     } else {
         place_and_sort(rec, h0, h1, c, nc, home_gid + h0);
+        // this block's stores to home_gid are visible to its own threads
+        // after the barrier
+        __syncthreads();
+        gather_home_positions(home_gid + h0, n, c, nc, dgeo[D], xg, xhome + 3ll * h0);
     }
 }
 
@@ -1580,11 +1642,52 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         cellbase[D] = (int)acc;
     }
     const int nb = cellbase[D];
+    // Cell thresholds of the home selection (cell_count_kernel): umin(c) is
+    // the smallest u >= 0 whose cell coordinate floor(fl(u * inv_c))
+    // reaches c. Along d, cell c holds only passing positions when
+    // umin(c + 1) <= rc (and it is not the domain's last cell, which also
+    // takes every larger u), only failing ones when umin(c) >= rc.
+    int cpass0 = 0, cfail0 = 1;
+    if (g.inv_c > 0.0f) {
+        auto umin = [&](int c) {
+            uint32_t lo = 0u, hi = 0x7F800000u;  // +inf reaches every c
+            while (lo < hi) {
+                const uint32_t mid = lo + (hi - lo) / 2;
+                float u;
+                std::memcpy(&u, &mid, 4);
+                if (u * g.inv_c >= (float)c)
+                    hi = mid;
+                else
+                    lo = mid + 1;
+            }
+            float u;
+            std::memcpy(&u, &lo, 4);
+            return u;
+        };
+        while (cpass0 < (1 << 20) && umin(cpass0 + 1) <= g.rc)
+            cpass0++;
+        while (cfail0 < (1 << 20) && umin(cfail0) < g.rc)
+            cfail0++;
+    }
+    // per domain: cells along x, y, z, and the first cell index along any
+    // dimension that no first pulse's selection reads (cfail0: the home sort
+    // gathers only the positions of the other cells; a huge value gathers all)
+    std::vector<int> dgeo(4 * (size_t)D);
+    for (int Dm = 0; Dm < D; Dm++) {
+        int c[3];
+        g.coords(Dm, c);
+        dgeo[4 * Dm] = g.ncell[0][c[0]];
+        dgeo[4 * Dm + 1] = g.ncell[1][c[1]];
+        dgeo[4 * Dm + 2] = g.ncell[2][c[2]];
+        dgeo[4 * Dm + 3] = g.inv_c > 0.0f ? cfail0 : INT32_MAX;
+    }
     Blob geo;  // alive until the first sync below
     const size_t o_b = geo.add(bcat), o_ncell = geo.add(ncat), o_cellbase = geo.add(cellbase);
+    const size_t o_dgeo = geo.add(dgeo);
     char* d_geo;
     DDH_HIP(geo.send(sc, &d_geo, s));
     const int* d_cellbase = (const int*)(d_geo + o_cellbase);
+    const int4* d_dgeo = (const int4*)(d_geo + o_dgeo);
     ag.b = (const float*)(d_geo + o_b);
     ag.ncell = (const int*)(d_geo + o_ncell);
     ag.cellbase = d_cellbase;
@@ -1612,6 +1715,9 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     DDH_HIP(sc.alloc(&d_err, 1));
     DDH_HIP(sc.alloc(&d_hs, (size_t)D + 1));
     DDH_HIP(owned_alloc(p, &p->d_home_gid, (size_t)n_atoms));
+    // home positions in slot order: the slab tests read them in order
+    float* d_xhome;
+    DDH_HIP(sc.alloc(&d_xhome, 3 * (size_t)n_atoms));
     DDH_HIP(hipMemsetAsync(d_err, 0, sizeof(uint32_t), s));
     if (partition) {
         const int items = (int64_t)n_atoms >= 16ll * 256 * kPartMinBlocks ? 16
@@ -1642,7 +1748,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                                sizeof(uint32_t) * (2 * (size_t)tile + 2 * (size_t)D), s, d_code,
                                n_atoms, d_hscan, D, nblk, d_rec);
         hipLaunchKernelGGL(domain_sort_kernel, dim3(D), dim3(1024), 0, s, d_rec, d_hscan, nblk,
-                           d_cellbase, D, p->d_home_gid, d_start);
+                           d_cellbase, D, p->d_home_gid, d_start, xg, d_dgeo, d_xhome);
         DDH_HIP(hipGetLastError());
     } else {
         int* d_bucket;
@@ -1677,20 +1783,23 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     DDH_HIP(hipStreamSynchronize(s));
     if (herr)
         return fail(DDH_EINVAL, "ddh_build_maps: a position is outside [0, L) or not a number");
-    // home positions in slot order: the slab tests read them in order
-    float* d_xhome;
-    DDH_HIP(sc.alloc(&d_xhome, 3 * (size_t)n_atoms));
-    if (n_atoms > 0)
-        hipLaunchKernelGGL(gather_xhome_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s, xg,
-                           p->d_home_gid, n_atoms, d_xhome);
-    DDH_HIP(hipGetLastError());
-
     p->nhome.assign(D, 0);
     p->ntotal.assign(D, 0);
     for (int Dm = 0; Dm < D; Dm++) {
         p->nhome[Dm] = hs[Dm + 1] - hs[Dm];
         p->ntotal[Dm] = p->nhome[Dm];
     }
+    // the first pulses select home slots by cells while cells are small (a
+    // thread walks each candidate cell)
+    bool cell_mode = g.inv_c > 0.0f;
+    for (int Dm = 0; Dm < D && cell_mode; Dm++)
+        cell_mode = p->nhome[Dm] <= (int64_t)kCellMaxAvg * (cellbase[Dm + 1] - cellbase[Dm]);
+    // the partition sort gathered the positions the selection by cells
+    // reads; otherwise every home position is gathered here
+    if (n_atoms > 0 && (!partition || (!cell_mode && g.inv_c > 0.0f)))
+        hipLaunchKernelGGL(gather_xhome_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s, xg,
+                           p->d_home_gid, n_atoms, d_xhome);
+    DDH_HIP(hipGetLastError());
     int* d_nhome;
     DDH_HIP(sc.alloc(&d_nhome, (size_t)D));
     DDH_HIP(upload(d_nhome, p->nhome, s));
@@ -1712,38 +1821,6 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     int *d_cnt_send, *d_cnt_split;
     DDH_HIP(sc.alloc(&d_cnt_send, (size_t)D));
     DDH_HIP(sc.alloc(&d_cnt_split, (size_t)D));
-
-    // Cell thresholds of the home selection (cell_count_kernel): umin(c) is
-    // the smallest u >= 0 whose cell coordinate floor(fl(u * inv_c))
-    // reaches c. Along d, cell c holds only passing positions when
-    // umin(c + 1) <= rc (and it is not the domain's last cell, which also
-    // takes every larger u), only failing ones when umin(c) >= rc.
-    int cpass0 = 0, cfail0 = 1;
-    if (g.inv_c > 0.0f) {
-        auto umin = [&](int c) {
-            uint32_t lo = 0u, hi = 0x7F800000u;  // +inf reaches every c
-            while (lo < hi) {
-                const uint32_t mid = lo + (hi - lo) / 2;
-                float u;
-                std::memcpy(&u, &mid, 4);
-                if (u * g.inv_c >= (float)c)
-                    hi = mid;
-                else
-                    lo = mid + 1;
-            }
-            float u;
-            std::memcpy(&u, &lo, 4);
-            return u;
-        };
-        while (cpass0 < (1 << 20) && umin(cpass0 + 1) <= g.rc)
-            cpass0++;
-        while (cfail0 < (1 << 20) && umin(cfail0) < g.rc)
-            cfail0++;
-    }
-    // by cells while cells are small (a thread walks each candidate cell)
-    bool cell_mode = g.inv_c > 0.0f;
-    for (int Dm = 0; Dm < D && cell_mode; Dm++)
-        cell_mode = p->nhome[Dm] <= (int64_t)kCellMaxAvg * (cellbase[Dm + 1] - cellbase[Dm]);
 
     // the pulses' upload blobs stay alive until the layout's sync
     std::vector<Blob> blobs;
