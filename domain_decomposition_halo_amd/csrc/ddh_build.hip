@@ -1170,7 +1170,50 @@ __global__ __launch_bounds__(256) void chunk_masks_kernel(DChunk* __restrict__ x
 struct Scratch {
     Plan* plan;
     size_t next = 0;
+    size_t pnext = 0;
     explicit Scratch(Plan* p) : plan(p) {}
+    // Pinned host staging for one upload: slot k serves the k-th upload of
+    // every build and is reused while large enough (a build's uploads have
+    // all run by its final sync, before the next build reuses a slot). From
+    // pinned memory hipMemcpyAsync returns at once; from pageable memory the
+    // host would first wait for the stream, leaving the device idle while
+    // it prepares the next work.
+    hipError_t pinned(void** out, size_t n)
+    {
+        const size_t bytes = (std::max<size_t>(n, 1) + 255) & ~size_t(255);
+        auto& cache = plan->pinned;
+        if (pnext < cache.size() && cache[pnext].second >= bytes) {
+            *out = cache[pnext++].first;
+            return hipSuccess;
+        }
+        void* q = nullptr;
+        hipError_t e = hipHostMalloc(&q, bytes, hipHostMallocDefault);
+        if (e != hipSuccess) {
+            *out = nullptr;
+            return e;
+        }
+        if (pnext < cache.size()) {
+            (void)hipHostFree(cache[pnext].first);
+            cache[pnext] = {q, bytes};
+        } else {
+            cache.emplace_back(q, bytes);
+        }
+        pnext++;
+        *out = q;
+        return hipSuccess;
+    }
+    // An asynchronous upload of n bytes through a pinned staging slot.
+    hipError_t upload_bytes(void* dst, const void* src, size_t n, hipStream_t s)
+    {
+        if (n == 0)
+            return hipSuccess;
+        void* h;
+        const hipError_t e = pinned(&h, n);
+        if (e != hipSuccess)
+            return e;
+        std::memcpy(h, src, n);
+        return hipMemcpyAsync(dst, h, n, hipMemcpyHostToDevice, s);
+    }
     template <class T>
     hipError_t alloc(T** out, size_t n)
     {
@@ -1230,9 +1273,9 @@ hipError_t owned_alloc(Plan* p, T** out, size_t n)
 
 // Small host arrays gathered into one host-to-device copy: add() appends a
 // section (16-byte aligned) and returns its byte offset; send() copies the
-// whole blob into a scratch buffer, after which section k sits at
-// base + offset k. The host storage must live until the stream has run the
-// copy (the build synchronizes before it goes out of scope).
+// whole blob into a scratch buffer (staged through pinned memory, so the
+// blob itself may go out of scope at once), after which section k sits at
+// base + offset k.
 struct Blob {
     std::vector<uint64_t> words;
     size_t bytes = 0;
@@ -1256,16 +1299,14 @@ struct Blob {
         hipError_t e = sc.alloc(base, std::max<size_t>(bytes, 8));
         if (e != hipSuccess || bytes == 0)
             return e;
-        return hipMemcpyAsync(*base, words.data(), bytes, hipMemcpyHostToDevice, s);
+        return sc.upload_bytes(*base, words.data(), bytes, s);
     }
 };
 
 template <class T>
-hipError_t upload(T* dst, const std::vector<T>& src, hipStream_t s)
+hipError_t upload(Scratch& sc, T* dst, const std::vector<T>& src, hipStream_t s)
 {
-    if (src.empty())
-        return hipSuccess;
-    return hipMemcpyAsync(dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice, s);
+    return sc.upload_bytes(dst, src.data(), src.size() * sizeof(T), s);
 }
 
 int scan_exclusive(Scratch& sc, const uint32_t* in, int64_t n, uint32_t* out, hipStream_t s)
@@ -1291,6 +1332,9 @@ void free_scratch(Plan* p)
     for (auto& kv : p->scratch)
         (void)hipFree(kv.first);
     p->scratch.clear();
+    for (auto& kv : p->pinned)
+        (void)hipHostFree(kv.first);
+    p->pinned.clear();
     for (auto& kv : p->kept)
         (void)hipFree(kv.first);
     p->kept.clear();
@@ -1560,12 +1604,12 @@ static int pulse_chunk(const Plan* p, bool step)
 // chunk k's entries at slot k * chunk, force chunks sharing the slot of the
 // coordinate chunk of the same map slice), 32-bit and, when the maps have a
 // 16-bit copy, 16-bit.
-static int upload_pulse_table(Plan* p, WorkTable& t, hipStream_t s)
+static int upload_pulse_table(Plan* p, Scratch& sc, WorkTable& t, hipStream_t s)
 {
     DDH_HIP(owned_alloc(p, &t.d_xch, t.xch.size()));
     DDH_HIP(owned_alloc(p, &t.d_fch, t.fch.size()));
-    DDH_HIP(upload(t.d_xch, t.xch, s));
-    DDH_HIP(upload(t.d_fch, t.fch, s));
+    DDH_HIP(upload(sc, t.d_xch, t.xch, s));
+    DDH_HIP(upload(sc, t.d_fch, t.fch, s));
     const int nch = (int)t.xch.size();
     const size_t npad = (size_t)nch * t.chunk + kPadTail;
     DDH_HIP(owned_alloc(p, &t.d_pad, npad));
@@ -1681,7 +1725,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         dgeo[4 * Dm + 2] = g.ncell[2][c[2]];
         dgeo[4 * Dm + 3] = g.inv_c > 0.0f ? cfail0 : INT32_MAX;
     }
-    Blob geo;  // alive until the first sync below
+    Blob geo;
     const size_t o_b = geo.add(bcat), o_ncell = geo.add(ncat), o_cellbase = geo.add(cellbase);
     const size_t o_dgeo = geo.add(dgeo);
     char* d_geo;
@@ -1776,11 +1820,20 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     hipLaunchKernelGGL(home_start_kernel, dim3(blocks(D + 1)), dim3(256), 0, s, d_start, d_cellbase,
                        D, d_hs);
     DDH_HIP(hipGetLastError());
+    // the home starts and the error word, read back through pinned memory
+    // (both copies queued, one wait)
     std::vector<int> hs((size_t)D + 1);
     uint32_t herr = 0;
-    DDH_HIP(hipMemcpyAsync(hs.data(), d_hs, sizeof(int) * (D + 1), hipMemcpyDeviceToHost, s));
-    DDH_HIP(hipMemcpyAsync(&herr, d_err, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-    DDH_HIP(hipStreamSynchronize(s));
+    {
+        void* h;
+        DDH_HIP(sc.pinned(&h, sizeof(int) * ((size_t)D + 2)));
+        int* hp = (int*)h;
+        DDH_HIP(hipMemcpyAsync(hp, d_hs, sizeof(int) * (D + 1), hipMemcpyDeviceToHost, s));
+        DDH_HIP(hipMemcpyAsync(hp + D + 1, d_err, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+        DDH_HIP(hipStreamSynchronize(s));
+        std::memcpy(hs.data(), hp, sizeof(int) * ((size_t)D + 1));
+        std::memcpy(&herr, hp + D + 1, sizeof(uint32_t));
+    }
     if (herr)
         return fail(DDH_EINVAL, "ddh_build_maps: a position is outside [0, L) or not a number");
     p->nhome.assign(D, 0);
@@ -1802,7 +1855,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     DDH_HIP(hipGetLastError());
     int* d_nhome;
     DDH_HIP(sc.alloc(&d_nhome, (size_t)D));
-    DDH_HIP(upload(d_nhome, p->nhome, s));
+    DDH_HIP(upload(sc, d_nhome, p->nhome, s));
 
     // ---- 3: pulses
     ph.next("build: pulses");
@@ -1822,7 +1875,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     DDH_HIP(sc.alloc(&d_cnt_send, (size_t)D));
     DDH_HIP(sc.alloc(&d_cnt_split, (size_t)D));
 
-    // the pulses' upload blobs stay alive until the layout's sync
+    // the pulses' upload blobs
     std::vector<Blob> blobs;
     blobs.reserve(2 * (size_t)P + 1);
     for (int q = 0; q < P; q++) {
@@ -1964,9 +2017,16 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                            a, d_tprefix, D, d_uscan, d_tbelow, d_cnt_send, d_cnt_split);
         DDH_HIP(hipGetLastError());
         std::vector<int> cs(D), cp(D);
-        DDH_HIP(hipMemcpyAsync(cs.data(), d_cnt_send, sizeof(int) * D, hipMemcpyDeviceToHost, s));
-        DDH_HIP(hipMemcpyAsync(cp.data(), d_cnt_split, sizeof(int) * D, hipMemcpyDeviceToHost, s));
-        DDH_HIP(hipStreamSynchronize(s));
+        {
+            void* h;
+            DDH_HIP(sc.pinned(&h, 2 * sizeof(int) * (size_t)D));
+            int* hp = (int*)h;
+            DDH_HIP(hipMemcpyAsync(hp, d_cnt_send, sizeof(int) * D, hipMemcpyDeviceToHost, s));
+            DDH_HIP(hipMemcpyAsync(hp + D, d_cnt_split, sizeof(int) * D, hipMemcpyDeviceToHost, s));
+            DDH_HIP(hipStreamSynchronize(s));
+            std::memcpy(cs.data(), hp, sizeof(int) * (size_t)D);
+            std::memcpy(cp.data(), hp + D, sizeof(int) * (size_t)D);
+        }
 
         // sizes -> offsets; region q of R lands after R's current slots
         mpos[q].assign(D, 0);
@@ -2076,7 +2136,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     DDH_HIP(hipMemsetAsync(d_rid, 0xff, (size_t)p->n_slots, s));
     std::vector<int> base32(D);
     const int* d_base;
-    Blob lay;  // alive until the sync below
+    Blob lay;
     {
         for (int Dm = 0; Dm < D; Dm++)
             base32[Dm] = (int)p->base[Dm];
@@ -2110,7 +2170,6 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                                    (const int*)(d_lay + o_dst[q]), p->d_slot_gid, d_rid, q);
         }
         DDH_HIP(hipGetLastError());
-        DDH_HIP(hipStreamSynchronize(s));
     }
 
     // ---- 5: chunk tables (wait masks computed on the device), counters
@@ -2124,16 +2183,16 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     make_work_table(p, false, p->pulse);
     DDH_HIP(owned_alloc(p, &p->fused.d_xch, p->fused.xch.size()));
     DDH_HIP(owned_alloc(p, &p->fused.d_fch, p->fused.fch.size()));
-    DDH_HIP(upload(p->fused.d_xch, p->fused.xch, s));
-    DDH_HIP(upload(p->fused.d_fch, p->fused.fch, s));
+    DDH_HIP(upload(sc, p->fused.d_xch, p->fused.xch, s));
+    DDH_HIP(upload(sc, p->fused.d_fch, p->fused.fch, s));
     // per-pulse tables: every coordinate chunk is a contiguous slice [hb, he)
     // of one map
-    if (int rc = upload_pulse_table(p, p->pulse, s))
+    if (int rc = upload_pulse_table(p, sc, p->pulse, s))
         return rc;
     if (chunk1 != p->pulse.chunk) {
         p->pulse1.chunk = chunk1;
         make_work_table(p, false, p->pulse1);
-        if (int rc = upload_pulse_table(p, p->pulse1, s))
+        if (int rc = upload_pulse_table(p, sc, p->pulse1, s))
             return rc;
     }
     if (p->refined_waits && P > 0) {
@@ -2147,10 +2206,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                 mposall[(size_t)q * (D + 1) + S] = mpos[q][S];
             mposall[(size_t)q * (D + 1) + D] = total[q];
         }
-        // the host copy goes out in a blob of the function-scope list, which
-        // lives until the build's final sync
-        blobs.emplace_back();
-        Blob& mb = blobs.back();
+        Blob mb;
         const size_t o_mpos = mb.add(mposall);
         char* d_mb;
         DDH_HIP(mb.send(sc, &d_mb, s));
@@ -2180,8 +2236,8 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         DDH_HIP(hipGetLastError());
     } else {
         set_release_flags(p, p->fused);
-        DDH_HIP(upload(p->fused.d_xch, p->fused.xch, s));
-        DDH_HIP(upload(p->fused.d_fch, p->fused.fch, s));
+        DDH_HIP(upload(sc, p->fused.d_xch, p->fused.xch, s));
+        DDH_HIP(upload(sc, p->fused.d_fch, p->fused.fch, s));
     }
 
     std::vector<uint32_t> xneed(DP, 0u), fneed(DP, 0u);
@@ -2201,7 +2257,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     p->d_pflag = p->d_fneed + DP;
     // d_fneed follows d_xneed: one copy of both
     xneed.insert(xneed.end(), fneed.begin(), fneed.end());
-    DDH_HIP(upload(p->d_xneed, xneed, s));
+    DDH_HIP(upload(sc, p->d_xneed, xneed, s));
     DDH_HIP(hipStreamSynchronize(s));
     p->built = true;
     p->build_failed = false;

@@ -236,6 +236,8 @@ struct Plan {
     std::vector<std::pair<void*, size_t>> kept;     // built state, reused by later builds
     size_t kept_next = 0;          // next slot of kept during a build
     std::vector<std::pair<void*, size_t>> scratch;  // build scratch, kept between builds
+    std::vector<std::pair<void*, size_t>> pinned;   // pinned host staging of the build's
+                                                    // uploads, kept between builds
     bool build_failed = false;     // the last build returned an error midway
 
     // graph replay cache: (op, x, f, mode) -> executable graph
