@@ -1610,16 +1610,24 @@ static int upload_pulse_table(Plan* p, Scratch& sc, WorkTable& t, hipStream_t s)
     DDH_HIP(owned_alloc(p, &t.d_fch, t.fch.size()));
     DDH_HIP(upload(sc, t.d_xch, t.xch, s));
     DDH_HIP(upload(sc, t.d_fch, t.fch, s));
+    // the kernel writes every chunk's slot (entries, then zeros); only the
+    // tail after the last slot is cleared here. The 32-bit copy is made only
+    // when the 16-bit maps are off (without it, launches read the maps
+    // after the descriptor).
     const int nch = (int)t.xch.size();
-    const size_t npad = (size_t)nch * t.chunk + kPadTail;
-    DDH_HIP(owned_alloc(p, &t.d_pad, npad));
-    DDH_HIP(hipMemsetAsync(t.d_pad, 0, sizeof(int32_t) * npad, s));
-    if (nch > 0)
-        hipLaunchKernelGGL(pad_maps_kernel<int32_t>, dim3(nch), dim3(256), 0, s, p->d_maps, t.d_xch,
-                           t.chunk, t.d_pad);
+    const size_t body = (size_t)nch * t.chunk, npad = body + kPadTail;
+    t.d_pad = nullptr;
+    t.d_pad16 = nullptr;
+    if (!p->d_maps16 || !p->narrow_maps) {
+        DDH_HIP(owned_alloc(p, &t.d_pad, npad));
+        DDH_HIP(hipMemsetAsync(t.d_pad + body, 0, sizeof(int32_t) * kPadTail, s));
+        if (nch > 0)
+            hipLaunchKernelGGL(pad_maps_kernel<int32_t>, dim3(nch), dim3(256), 0, s, p->d_maps,
+                               t.d_xch, t.chunk, t.d_pad);
+    }
     if (p->d_maps16) {
         DDH_HIP(owned_alloc(p, &t.d_pad16, npad));
-        DDH_HIP(hipMemsetAsync(t.d_pad16, 0, sizeof(uint16_t) * npad, s));
+        DDH_HIP(hipMemsetAsync(t.d_pad16 + body, 0, sizeof(uint16_t) * kPadTail, s));
         if (nch > 0)
             hipLaunchKernelGGL(pad_maps_kernel<uint16_t>, dim3(nch), dim3(256), 0, s, p->d_maps16,
                                t.d_xch, t.chunk, t.d_pad16);
@@ -2181,6 +2189,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     const int chunk1 = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p, false);
     make_work_table(p, true, p->fused);
     make_work_table(p, false, p->pulse);
+    ph.next("build: chunk tables, uploads");
     DDH_HIP(owned_alloc(p, &p->fused.d_xch, p->fused.xch.size()));
     DDH_HIP(owned_alloc(p, &p->fused.d_fch, p->fused.fch.size()));
     DDH_HIP(upload(sc, p->fused.d_xch, p->fused.xch, s));
@@ -2195,6 +2204,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         if (int rc = upload_pulse_table(p, sc, p->pulse1, s))
             return rc;
     }
+    ph.next("build: chunk tables, wait masks");
     if (p->refined_waits && P > 0) {
         WorkTable& t = p->fused;
         uint32_t* d_inmap;
@@ -2240,6 +2250,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         DDH_HIP(upload(sc, p->fused.d_fch, p->fused.fch, s));
     }
 
+    ph.next("build: counters");
     std::vector<uint32_t> xneed(DP, 0u), fneed(DP, 0u);
     for (int S = 0; S < D; S++)
         for (int q = 0; q < P; q++) {

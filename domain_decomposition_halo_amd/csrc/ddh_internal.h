@@ -143,7 +143,8 @@ struct WorkTable {
     // entries from its chunk index alone and loads them while its
     // descriptor is still in flight; kPadTail zero entries follow the last
     // chunk. Force chunks use the slots of the coordinate chunk of the same
-    // map slice. 32-bit, and 16-bit when the maps have a 16-bit copy.
+    // map slice. 16-bit when the maps have a 16-bit copy; 32-bit when they
+    // have none or the build ran with the 16-bit maps off (else null).
     int32_t* d_pad = nullptr;
     uint16_t* d_pad16 = nullptr;
 };

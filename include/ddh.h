@@ -420,7 +420,12 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     before its chunk descriptor arrives (reads
                                     the copy's zero padding too); 2 it loads
                                     the descriptor first, then only the
-                                    chunk's own entries */
+                                    chunk's own entries. The copy of the
+                                    32-bit maps exists only when the build
+                                    ran with DDH_TUNE_NARROW_MAPS 0 (or the
+                                    maps have no 16-bit copy); otherwise a
+                                    later switch to 32-bit maps reads them as
+                                    in 2. */
 
 #define DDH_TUNE_HEADS_FIRST 15    /* fused mode: 0 (default) a coordinate
                                     chunk packs a slice of its map's
