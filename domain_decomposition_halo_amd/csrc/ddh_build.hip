@@ -1077,6 +1077,65 @@ __global__ __launch_bounds__(256) void gather_xhome_kernel(const float* __restri
     dst[2] = src[2];
 }
 
+// Per-map data of a build for the device-made chunk tables: [S * P + q].
+struct MapInfo {
+    const int* send;     // map size
+    const int* recv;     // receiver
+    const int* roff;     // the region's first slot at the receiver
+    const int* map_off;  // first entry in the map array
+    const int* shift;    // 1 if the sender sits at index 0 of the pulse's dimension
+    const int* base;     // [domain] first slot
+    const int* pdim;     // [pulse] dimension
+    float L[3];
+    int D, P;
+};
+
+// The per-pulse launches' chunk table (no waits): chunk k of a map of n
+// entries in c chunks is the slice [n k / c, n (k + 1) / c). Coordinate
+// chunks are listed pulse by pulse, sender by sender (xprefix: first chunk
+// of each (pulse, sender) unit, in that order); force chunks in decreasing
+// pulse order (fprefix). One thread per chunk.
+__global__ __launch_bounds__(256) void pulse_chunks_kernel(MapInfo m, const int* __restrict__ nchunks,
+                                                           const int* __restrict__ xprefix, int nx,
+                                                           const int* __restrict__ fprefix, int nf,
+                                                           DChunk* __restrict__ xch,
+                                                           DChunk* __restrict__ fch)
+{
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= nx + nf)
+        return;
+    const bool force = c >= nx;
+    const int cc = force ? c - nx : c;
+    const int* pre = force ? fprefix : xprefix;
+    int lo = 0, hi = m.D * m.P;  // the unit u with pre[u] <= cc < pre[u + 1]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= cc)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const int r = lo / m.D, S = lo - r * m.D;
+    const int q = force ? m.P - 1 - r : r;
+    const int it = S * m.P + q, k = cc - pre[lo];
+    const int n = m.send[it], nc = nchunks[it];
+    DChunk d{};
+    d.hb = (int32_t)((int64_t)n * k / nc);
+    d.he = (int32_t)((int64_t)n * (k + 1) / nc);
+    d.tb = d.te = d.he;
+    d.src_base = m.base[S];
+    d.R = m.recv[it];
+    d.dst_base = m.base[d.R] + m.roff[it];
+    d.map_off = m.map_off[it];
+    const int dim = m.pdim[q];
+    d.flags = dim | (m.shift[it] ? kChunkShift : 0);
+    d.shift = m.L[dim];
+    d.S = S;
+    d.p = q;
+    d.ctr = force ? S * m.P + q : d.R * m.P + q;
+    (force ? fch : xch)[cc] = d;
+}
+
 // Chunk-aligned copy of the maps for the per-pulse launches: block b writes
 // the entries of chunk b at out[b * CH ...] and zeros up to the next chunk.
 template <typename T>
@@ -1494,6 +1553,7 @@ static void make_work_table(const Plan* p, bool waits, WorkTable& t)
         }
     }
     t.xpulse_begin[P] = (int)t.xch.size();
+    t.nx = (int)t.xch.size();
     // forces in decreasing pulse order (a chunk waits only on later pulses)
     for (int r = 0; r < P; r++) {
         const int q = P - 1 - r;
@@ -1503,6 +1563,7 @@ static void make_work_table(const Plan* p, bool waits, WorkTable& t)
                 t.fch.push_back(fchunk(S * P + q, k));
     }
     t.fpulse_begin[P] = (int)t.fch.size();
+    t.nf = (int)t.fch.size();
 }
 
 // Device form of set_release_flags (below), for masks computed on the
@@ -1600,21 +1661,58 @@ static int pulse_chunk(const Plan* p, bool step)
     return 256;
 }
 
-// Device copies of a per-pulse table and its chunk-aligned maps (coordinate
-// chunk k's entries at slot k * chunk, force chunks sharing the slot of the
-// coordinate chunk of the same map slice), 32-bit and, when the maps have a
-// 16-bit copy, 16-bit.
-static int upload_pulse_table(Plan* p, Scratch& sc, WorkTable& t, hipStream_t s)
+// A per-pulse launches' table of chunk size t.chunk, made on the device:
+// the host counts each map's chunks and the table's pulse ranges, the
+// device writes the descriptors (pulse_chunks_kernel); then the
+// chunk-aligned copies of the maps (coordinate chunk k's entries at slot
+// k * chunk, force chunks sharing the slot of the coordinate chunk of the
+// same map slice).
+static int make_pulse_table(Plan* p, Scratch& sc, const MapInfo& m, WorkTable& t, hipStream_t s)
 {
-    DDH_HIP(owned_alloc(p, &t.d_xch, t.xch.size()));
-    DDH_HIP(owned_alloc(p, &t.d_fch, t.fch.size()));
-    DDH_HIP(upload(sc, t.d_xch, t.xch, s));
-    DDH_HIP(upload(sc, t.d_fch, t.fch, s));
+    const int D = p->g.ndom, P = p->g.P, CH = t.chunk;
+    t.wave = false;
+    t.heads_first = false;
+    t.xch.clear();
+    t.fch.clear();
+    t.nchunks.assign((size_t)D * P, 1);
+    for (int it = 0; it < D * P; it++)
+        t.nchunks[it] = std::max(1, (p->send[it] + CH - 1) / CH);
+    // first chunk of each unit: coordinates (pulse, sender), then forces
+    // (reverse pulse, sender)
+    std::vector<int> pre(2 * ((size_t)D * P + 1), 0);
+    int* xpre = pre.data();
+    int* fpre = pre.data() + (size_t)D * P + 1;
+    t.xpulse_begin.assign((size_t)P + 1, 0);
+    t.fpulse_begin.assign((size_t)P + 1, 0);
+    for (int r = 0; r < P; r++) {
+        t.xpulse_begin[r] = xpre[r * D];
+        t.fpulse_begin[r] = fpre[r * D];
+        for (int S = 0; S < D; S++) {
+            const int u = r * D + S;
+            xpre[u + 1] = xpre[u] + t.nchunks[S * P + r];
+            fpre[u + 1] = fpre[u] + t.nchunks[S * P + (P - 1 - r)];
+        }
+    }
+    t.nx = xpre[D * P];
+    t.nf = fpre[D * P];
+    t.xpulse_begin[P] = t.nx;
+    t.fpulse_begin[P] = t.nf;
+    DDH_HIP(owned_alloc(p, &t.d_xch, (size_t)t.nx));
+    DDH_HIP(owned_alloc(p, &t.d_fch, (size_t)t.nf));
+    int *d_pre, *d_nch;
+    DDH_HIP(sc.alloc(&d_pre, pre.size()));
+    DDH_HIP(sc.alloc(&d_nch, t.nchunks.size()));
+    DDH_HIP(upload(sc, d_pre, pre, s));
+    DDH_HIP(upload(sc, d_nch, t.nchunks, s));
+    if (t.nx + t.nf > 0)
+        hipLaunchKernelGGL(pulse_chunks_kernel, dim3(blocks(t.nx + t.nf)), dim3(256), 0, s, m, d_nch,
+                           d_pre, t.nx, d_pre + (size_t)D * P + 1, t.nf, t.d_xch, t.d_fch);
+    DDH_HIP(hipGetLastError());
     // the kernel writes every chunk's slot (entries, then zeros); only the
     // tail after the last slot is cleared here. The 32-bit copy is made only
     // when the 16-bit maps are off (without it, launches read the maps
     // after the descriptor).
-    const int nch = (int)t.xch.size();
+    const int nch = t.nx;
     const size_t body = (size_t)nch * t.chunk, npad = body + kPadTail;
     t.d_pad = nullptr;
     t.d_pad16 = nullptr;
@@ -2188,21 +2286,50 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     p->pulse.chunk = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p, true);
     const int chunk1 = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p, false);
     make_work_table(p, true, p->fused);
-    make_work_table(p, false, p->pulse);
     ph.next("build: chunk tables, uploads");
     DDH_HIP(owned_alloc(p, &p->fused.d_xch, p->fused.xch.size()));
     DDH_HIP(owned_alloc(p, &p->fused.d_fch, p->fused.fch.size()));
     DDH_HIP(upload(sc, p->fused.d_xch, p->fused.xch, s));
     DDH_HIP(upload(sc, p->fused.d_fch, p->fused.fch, s));
     // per-pulse tables: every coordinate chunk is a contiguous slice [hb, he)
-    // of one map
-    if (int rc = upload_pulse_table(p, sc, p->pulse, s))
-        return rc;
-    if (chunk1 != p->pulse.chunk) {
-        p->pulse1.chunk = chunk1;
-        make_work_table(p, false, p->pulse1);
-        if (int rc = upload_pulse_table(p, sc, p->pulse1, s))
+    // of one map, made on the device from the maps' data
+    {
+        std::vector<int> info(5 * DP + (size_t)D + (size_t)P);
+        int* in = info.data();
+        for (size_t it = 0; it < DP; it++) {
+            in[it] = p->send[it];
+            in[DP + it] = p->recv[it];
+            in[2 * DP + it] = (int)p->roff[it];
+            in[3 * DP + it] = (int)p->map_off[it];
+            in[4 * DP + it] = p->shift[it];
+        }
+        for (int Dm = 0; Dm < D; Dm++)
+            in[5 * DP + Dm] = (int)p->base[Dm];
+        for (int q = 0; q < P; q++)
+            in[5 * DP + D + q] = g.pdim[q];
+        int* d_info;
+        DDH_HIP(sc.alloc(&d_info, info.size()));
+        DDH_HIP(upload(sc, d_info, info, s));
+        MapInfo m{};
+        m.send = d_info;
+        m.recv = d_info + DP;
+        m.roff = d_info + 2 * DP;
+        m.map_off = d_info + 3 * DP;
+        m.shift = d_info + 4 * DP;
+        m.base = d_info + 5 * DP;
+        m.pdim = d_info + 5 * DP + D;
+        for (int d = 0; d < 3; d++)
+            m.L[d] = g.L[d];
+        m.D = D;
+        m.P = P;
+        if (int rc = make_pulse_table(p, sc, m, p->pulse, s))
             return rc;
+        p->pulse1.chunk = 0;
+        if (chunk1 != p->pulse.chunk) {
+            p->pulse1.chunk = chunk1;
+            if (int rc = make_pulse_table(p, sc, m, p->pulse1, s))
+                return rc;
+        }
     }
     ph.next("build: chunk tables, wait masks");
     if (p->refined_waits && P > 0) {

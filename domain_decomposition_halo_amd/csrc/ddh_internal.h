@@ -134,7 +134,9 @@ struct WorkTable {
     bool heads_first = false;       // fused: every map's head in chunks of its
                                     // own, all heads before any tail
     std::vector<int32_t> nchunks;   // [S * P + p] chunks of the map
-    std::vector<DChunk> xch, fch;
+    std::vector<DChunk> xch, fch;   // host copies (fused table only; the
+                                    // per-pulse tables are made on the device)
+    int nx = 0, nf = 0;             // coordinate and force chunks
     std::vector<int32_t> xpulse_begin, fpulse_begin;  // per pulse ranges (+1)
     DChunk* d_xch = nullptr;        // device copies
     DChunk* d_fch = nullptr;
