@@ -678,10 +678,15 @@ __global__ __launch_bounds__(B) void exchange_kernel(XArgs a)
 // relaxed add to the map's counter. Same ticket order, counters and targets
 // as exchange_kernel, hence the same freedom from deadlock; in the exit
 // protocol every wavefront counts as one worker.
-template <int E, typename I>
+template <int E, typename I, int STG = 0>
 __global__ __launch_bounds__(256) void wave_kernel(XArgs a)
 {
     constexpr int W = 64;  // lanes that share a round: one wavefront
+    // STG: coordinate stores staged through the wavefront's LDS tile, as in
+    // the per-pulse kernel (1: register gathers, 2: LDS loads)
+    constexpr int kTile = STG == 2 ? E * kDmaTile : STG == 1 ? E * kStageTile : 0;
+    __shared__ __align__(16) float stile[STG ? 4 * kTile : 1];
+    float* tile = STG ? stile + (((int)threadIdx.x >> 6) * kTile) : nullptr;
     const I* maps = static_cast<const I*>(a.maps);
     const int P = a.P;
     const int nt = a.nx + a.nf;
@@ -703,10 +708,12 @@ __global__ __launch_bounds__(256) void wave_kernel(XArgs a)
             int jh[E], jt[E];
             load_map<E, W, I>(maps + c.map_off, c.hb, c.he, jh);
             load_map<E, W, I>(maps + c.map_off, c.tb, c.te, jt);
-            coords_range<E, W, I>(a.x, maps + c.map_off, c, c.hb, c.he, jh);
+            coords_range<E, W, I, STG>(a.x, maps + c.map_off, c, c.hb, c.he, jh, nullptr, false,
+                                       tile);
             if (c.wait_a)
                 wave_wait(a, a.xcnt, a.xneed, px, c.wait_a, c.S * P, 0u, 0, bump);
-            coords_range<E, W, I>(a.x, maps + c.map_off, c, c.tb, c.te, jt);
+            coords_range<E, W, I, STG>(a.x, maps + c.map_off, c, c.tb, c.te, jt, nullptr, false,
+                                       tile);
             if (c.flags & kChunkRelease)
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             held = !(c.flags & kChunkRelease);
@@ -1015,12 +1022,16 @@ void launch_fused_t(const XArgs& a, int grid, bool wide, int per, int stg, hipSt
 
 // The wavefront-granular fused kernel for the entries per lane.
 template <typename I>
-void launch_wave_t(const XArgs& a, int grid, int per, hipStream_t s)
+void launch_wave_t(const XArgs& a, int grid, int per, int stg, hipStream_t s)
 {
     if (per > 4)
-        hipLaunchKernelGGL((wave_kernel<8, I>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((stg == 2 ? wave_kernel<8, I, 2> : stg == 1 ? wave_kernel<8, I, 1>
+                                                                       : wave_kernel<8, I, 0>),
+                           dim3(grid), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((wave_kernel<4, I>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((stg == 2 ? wave_kernel<4, I, 2> : stg == 1 ? wave_kernel<4, I, 1>
+                                                                       : wave_kernel<4, I, 0>),
+                           dim3(grid), dim3(256), 0, s, a);
 }
 
 // The per-pulse kernel instance for the block width and entries per lane.
@@ -1082,10 +1093,10 @@ int launch_fused(const Plan* p, XArgs a, hipStream_t s)
         const int per = (p->fused.chunk + 63) / 64;
         if (use_narrow_maps(p)) {
             a.maps = p->d_maps16;
-            launch_wave_t<uint16_t>(a, grid, per, s);
+            launch_wave_t<uint16_t>(a, grid, per, p->lds_stage, s);
         } else {
             a.maps = p->d_maps;
-            launch_wave_t<int32_t>(a, grid, per, s);
+            launch_wave_t<int32_t>(a, grid, per, p->lds_stage, s);
         }
         DDH_HIP(hipGetLastError());
         return DDH_OK;

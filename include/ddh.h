@@ -449,8 +449,9 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     gathered straight into LDS by the LDS's
                                     own loads (global_load_lds). Applies to
                                     the per-pulse launches' 256-wide blocks
-                                    and the fused launch's 1024-wide
-                                    work-groups; same results. */
+                                    and the fused launch (1024-wide
+                                    work-groups and wavefront workers); same
+                                    results. */
 
 /* Set a tuning knob; takes effect at the next build (CHUNK, WAVE_CHUNKS,
    HOME_SORT, HEADS_FIRST) or call. Library utility: the guide defines no such call.

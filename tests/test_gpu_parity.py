@@ -898,8 +898,8 @@ def test_repeated_force_passes_are_deterministic(workload_plan):
 def test_lds_staged_stores(k, stage, workload_plan):
     """Coordinate stores staged through LDS (DDH_TUNE_LDS_STAGE 1: records
     gathered into registers, 2: gathered by LDS loads) give the oracle's
-    coordinates and forces: per-pulse launches and the fused launch, eager
-    and from the library's graphs, with 16- and 32-bit maps, with chunks of
+    coordinates and forces: per-pulse launches and the fused launch (work-
+    group chunks and wavefront workers), eager and from the library's graphs, with 16- and 32-bit maps, with chunks of
     several rounds (DDH_TUNE_CHUNK 4096 and 8192), in the host-orchestrated
     baseline, and into
     coordinate arrays that start 4, 8 or 12 bytes past a 16-byte boundary
@@ -913,6 +913,12 @@ def test_lds_staged_stores(k, stage, workload_plan):
         g = GpuPlan(x, **w.params(), mode=mode, narrow=narrow, chunk=chunk, lds_stage=stage)
         check_steps(g, ref, 300 + k, steps=2)
         check_steps(g, ref, 310 + k, steps=1, fused_step=True)
+        g.close()
+    # the fused launch's wavefront workers, slices of 256 and 1024 entries
+    for chunk in (256, 1024):
+        g = GpuPlan(x, **w.params(), mode=ddh.DDH_MODE_FUSED, wave=1, chunk=chunk, lds_stage=stage)
+        check_steps(g, ref, 320 + k, steps=2)
+        check_steps(g, ref, 330 + k, steps=1, fused_step=True)
         g.close()
     g = GpuPlan(x, **w.params(), mode=ddh.DDH_MODE_PULSE, lds_stage=stage)
     n = g.n_slots
