@@ -834,6 +834,27 @@ def test_home_sort_forms(home_sort, workload_plan):
     plan.close()
 
 
+@pytest.mark.parametrize("home_sort", [1, 2])
+def test_selection_by_cells_and_by_slots(home_sort):
+    """The home slots of a dimension's first pulse are selected by cells while
+    the cells hold at most 64 home atoms on average (whole cells taken without
+    a test, partly selected ones tested atom by atom, the partition sort
+    gathering only the cells a selection reads), else by slot tiles with every
+    home position gathered: both give the oracle's layout, maps and results.
+    2 x 1 x 1 domains of 2 x 4 x 4 cells of 0.5 nm hold 60 atoms per cell on
+    average (by cells, cells past 32 atoms taken in several batches) and 94
+    (by slots); a cell size of 0 puts one cell in each domain (by slots)."""
+    box = (2.0, 2.0, 2.0)
+    for n, cell in ((3840, 0.5), (6000, 0.5), (2000, 0.0)):
+        x = W.uniform_positions(n, box, seed=500 + n)
+        ref = oracle.OraclePlan(x, (2, 1, 1), box, 0.5, cell=cell)
+        for mode in (ddh.DDH_MODE_PULSE, ddh.DDH_MODE_FUSED):
+            g = GpuPlan(x, (2, 1, 1), box, 0.5, cell=cell, mode=mode, home_sort=home_sort)
+            check_layout(g, ref)
+            check_steps(g, ref, 600 + n, steps=1)
+            g.close()
+
+
 def test_error_paths():
     box = (8.0, 8.0, 8.0)
     plan = ddh.Plan((2, 2, 2), box, 1.0)
