@@ -1862,8 +1862,9 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     int* d_hs;
     uint32_t *d_start, *d_err;
     DDH_HIP(sc.alloc(&d_start, (size_t)nb + 1));
-    DDH_HIP(sc.alloc(&d_err, 1));
-    DDH_HIP(sc.alloc(&d_hs, (size_t)D + 1));
+    // the home starts, then the error word: read back in one copy
+    DDH_HIP(sc.alloc(&d_hs, (size_t)D + 2));
+    d_err = (uint32_t*)(d_hs + D + 1);
     DDH_HIP(owned_alloc(p, &p->d_home_gid, (size_t)n_atoms));
     // home positions in slot order: the slab tests read them in order
     float* d_xhome;
@@ -1934,8 +1935,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         void* h;
         DDH_HIP(sc.pinned(&h, sizeof(int) * ((size_t)D + 2)));
         int* hp = (int*)h;
-        DDH_HIP(hipMemcpyAsync(hp, d_hs, sizeof(int) * (D + 1), hipMemcpyDeviceToHost, s));
-        DDH_HIP(hipMemcpyAsync(hp + D + 1, d_err, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+        DDH_HIP(hipMemcpyAsync(hp, d_hs, sizeof(int) * (D + 2), hipMemcpyDeviceToHost, s));
         DDH_HIP(hipStreamSynchronize(s));
         std::memcpy(hs.data(), hp, sizeof(int) * ((size_t)D + 1));
         std::memcpy(&herr, hp + D + 1, sizeof(uint32_t));
@@ -1977,9 +1977,9 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     std::vector<int*> mapp((size_t)std::max(P, 1), nullptr);
     std::vector<std::vector<int>> mpos((size_t)P), rsprefix((size_t)P);
     std::vector<int> total((size_t)P, 0);
-    int *d_cnt_send, *d_cnt_split;
-    DDH_HIP(sc.alloc(&d_cnt_send, (size_t)D));
-    DDH_HIP(sc.alloc(&d_cnt_split, (size_t)D));
+    int *d_cnt_send, *d_cnt_split;  // adjacent: read back in one copy
+    DDH_HIP(sc.alloc(&d_cnt_send, 2 * (size_t)D));
+    d_cnt_split = d_cnt_send + D;
 
     // the pulses' upload blobs
     std::vector<Blob> blobs;
@@ -2127,8 +2127,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
             void* h;
             DDH_HIP(sc.pinned(&h, 2 * sizeof(int) * (size_t)D));
             int* hp = (int*)h;
-            DDH_HIP(hipMemcpyAsync(hp, d_cnt_send, sizeof(int) * D, hipMemcpyDeviceToHost, s));
-            DDH_HIP(hipMemcpyAsync(hp + D, d_cnt_split, sizeof(int) * D, hipMemcpyDeviceToHost, s));
+            DDH_HIP(hipMemcpyAsync(hp, d_cnt_send, 2 * sizeof(int) * D, hipMemcpyDeviceToHost, s));
             DDH_HIP(hipStreamSynchronize(s));
             std::memcpy(cs.data(), hp, sizeof(int) * (size_t)D);
             std::memcpy(cp.data(), hp + D, sizeof(int) * (size_t)D);
