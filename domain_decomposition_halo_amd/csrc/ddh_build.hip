@@ -1792,7 +1792,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         cellbase[D] = (int)acc;
     }
     const int nb = cellbase[D];
-    // Cell thresholds of the home selection (cell_count_kernel): umin(c) is
+    // Cell thresholds of the home selection (cell_count_block): umin(c) is
     // the smallest u >= 0 whose cell coordinate floor(fl(u * inv_c))
     // reaches c. Along d, cell c holds only passing positions when
     // umin(c + 1) <= rc (and it is not the domain's last cell, which also
