@@ -52,6 +52,9 @@ if ROOT not in sys.path:
 METRIC = "halo exchange µs/step + halo atoms/s & HBM GB/s fraction (1 MI355X)"
 HBM_PEAK_GBS = 8000.0
 BYTES_X, BYTES_F = 28, 40
+# calls behind each side figure (each pass alone, flags off, the single
+# fused launch), in graphs of --graph-steps calls
+AUX_CALLS = 200
 # workloads whose entry under `also` carries the overlap figures (96k, 1M)
 OVERLAP_WORKLOADS = (2, 3)
 # the sources that decide what the exchange launches read and write
@@ -260,12 +263,14 @@ def run_gpu(args, w):
     assert plan.check() == ddh.DDH_OK
 
     # each pass alone (pack = coordinate pass, unpack = force pass), the same
-    # way: graphs of G calls, replayed
+    # way: graphs of G calls, replayed. These side figures take AUX_CALLS
+    # calls whatever --steps is, so a short headline run does not leave them
+    # to one replay of a small graph.
     passes = None
     if not args.cold and not args.eager and not args.only_step:
         passes = {}
-        G = max(1, min(args.graph_steps, args.steps))
-        n_rep = max(1, min(args.steps // G, 10))
+        G = max(1, args.graph_steps)
+        n_rep = max(1, AUX_CALLS // G)
         for name, fn, nb in (("coords", lambda: plan.exchange_coords(xl), BYTES_X * n_halo),
                              ("forces", lambda: plan.exchange_forces(fl), BYTES_F * n_halo)):
             graph = torch.cuda.CUDAGraph()
@@ -289,7 +294,7 @@ def run_gpu(args, w):
 
     def time_steps(fn, reps):
         """GPU us per call of fn, from graphs of G calls replayed reps times."""
-        G = max(1, min(args.graph_steps, args.steps))
+        G = max(1, args.graph_steps)
         fn()
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
@@ -314,7 +319,8 @@ def run_gpu(args, w):
     if not args.cold and not args.eager and not args.only_step and not args.no_flags:
         plan.tune(ddh.DDH_TUNE_FLAGS, 0)
         us = time_steps(calls[0][1] if len(calls) == 1 else
-                        (lambda: [fn() for _, fn, _ in calls]), max(1, min(args.steps // 50, 10)))
+                        (lambda: [fn() for _, fn, _ in calls]),
+                        max(1, AUX_CALLS // max(1, args.graph_steps)))
         plan.tune(ddh.DDH_TUNE_FLAGS, 1)
         without_flags = {"us_per_step": round(us, 3),
                          "frac": round((BYTES_X + BYTES_F) * n_halo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -325,8 +331,8 @@ def run_gpu(args, w):
     single = None
     if not args.cold and not args.eager and not args.only_step and variant != "step":
         plan.set_mode(ddh.DDH_MODE_FUSED)
-        G = max(1, min(args.graph_steps, args.steps))
-        n_rep = max(1, min(args.steps // G, 4))
+        G = max(1, args.graph_steps)
+        n_rep = max(1, AUX_CALLS // G)
         fn = lambda: plan.exchange_step(xl, fl)
         fn()
         graph = torch.cuda.CUDAGraph()
