@@ -664,6 +664,23 @@ def test_32bit_maps(k, mode, workload_plan):
     g.close()
 
 
+@pytest.mark.parametrize("k", [2, 4])
+def test_map_width_switched_after_build(k, workload_plan):
+    """A build with the 16-bit maps on makes only the 16-bit chunk-aligned
+    map copy; switching to the 32-bit maps afterwards makes the per-pulse
+    launches read the 32-bit maps after each descriptor (whatever
+    DDH_TUNE_PAD_MAPS says), and switching back uses the copy again."""
+    w, x, ref = workload_plan(k)
+    for mode in (ddh.DDH_MODE_PULSE, ddh.DDH_MODE_PULSE | ddh.DDH_MODE_GRAPH):
+        g = GpuPlan(x, **w.params(), mode=mode)
+        for narrow, pad in ((0, 1), (0, 0), (1, 1), (0, 2)):
+            g.plan.tune(ddh.DDH_TUNE_NARROW_MAPS, narrow)
+            g.plan.tune(ddh.DDH_TUNE_PAD_MAPS, pad)
+            check_steps(g, ref, 700 + 10 * narrow + pad, steps=1)
+            check_steps(g, ref, 720 + 10 * narrow + pad, steps=1, fused_step=True)
+        g.close()
+
+
 @pytest.mark.parametrize("n,wide", [(100_000, False), (140_000, True)])
 def test_map_width_threshold(n, wide):
     """Two domains of about 50k and 70k home atoms: the first stays within
