@@ -271,3 +271,21 @@ def test_bench_host_cpu_fields():
     cpu = bench.host_cpu()
     assert cpu["cpu_count"] >= 1 and 1 <= cpu["affinity"] <= cpu["cpu_count"]
     assert isinstance(cpu["model"], str) and cpu["model"]
+
+
+def test_bench_marker_summary(tmp_path):
+    # the host ranges of a rocprofv3 --marker-trace --stats run, largest
+    # total first, durations in microseconds
+    import bench
+    d = tmp_path / "run" / "host"
+    d.mkdir(parents=True)
+    (d / "run_marker_api_stats.csv").write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        '"build: pulses",2,1000000,500000.0,10.0,400000,600000,1.0\n'
+        '"ddh_build_maps",2,3000000,1500000.0,30.0,1200000,1800000,1.0\n')
+    text = bench.summarize_markers(str(tmp_path), "Map build", "cmd --x")
+    lines = text.splitlines()
+    assert lines[0] == "## Map build" and "cmd --x" in lines
+    rows = [ln for ln in lines if ln.startswith("| `")]
+    assert rows[0] == "| `ddh_build_maps` | 2 | 1500.0 | 1200.0 | 1800.0 |"
+    assert rows[1] == "| `build: pulses` | 2 | 500.0 | 400.0 | 600.0 |"
