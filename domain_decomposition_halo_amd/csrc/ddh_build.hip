@@ -713,8 +713,9 @@ __device__ __forceinline__ void tile_of(const SArgs& a, const int* tprefix, int 
 // along d hold only failing positions and are never visited, and those
 // below cpass hold only passing ones and are taken whole without reading a
 // position. Only the cells in between are tested atom by atom. The
-// candidate cells of a sender, numbered m = 0, 1, ... in key order (= slot
-// order), are one thread each.
+// candidate cells of a sender are numbered m = 0, 1, ... in key order (=
+// slot order); the count takes one thread per cell, the write one thread
+// per slot of 256 consecutive cells.
 struct CArgs {
     int d;
     float L_d, rc;
