@@ -672,22 +672,6 @@ __global__ __launch_bounds__(256) void fill_home_kernel(const int* __restrict__ 
     }
 }
 
-// slot_gid for the region records of one pulse (stored receiver-major).
-// Index of the segment of prefix[0..n] (non-decreasing, prefix[0] = 0) that
-// holds e: the largest k < n with prefix[k] <= e.
-__device__ __forceinline__ int segment_of(const int* prefix, int n, int e)
-{
-    int lo = 0, hi = n;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (prefix[mid] <= e)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    return lo;
-}
-
 // Slab selection of pulse p in tiles (the slab test of the pulse's dimension
 // d: fl(x_d - lo_d(S)) < rc): sender S's candidate slots
 // [first[S], last[S]) are cut into tiles of kSelTile slots, and tile b of the
@@ -1036,21 +1020,53 @@ __global__ __launch_bounds__(256) void select_write_kernel(SArgs a, CArgs ca,
     }
 }
 
+// Segmented work for the per-record kernels below: nseg segments, segment
+// k holding items [pre[k], pre[k + 1]). Work item b (of nseg * cps, grid-
+// strided) is chunk b % cps (kSegTile items) of segment b / cps, so a block
+// knows its segment without searching for it. Returns false when the chunk
+// is empty.
+constexpr int kSegItems = 8;
+constexpr int kSegTile = 256 * kSegItems;
+constexpr int kSegMaxBlocks = 1 << 20;
+__device__ __forceinline__ bool seg_chunk(const int* pre, int cps, int64_t b, int& k, int& i0,
+                                          int& i1)
+{
+    k = (int)(b / cps);
+    const int c = (int)(b % cps);
+    i0 = pre[k] + c * kSegTile;
+    i1 = min(pre[k + 1], i0 + kSegTile);
+    return i0 < i1;
+}
+
 // Region q of every receiver: global id of each received slot, and the pulse
-// it was received in (rid).
-__global__ __launch_bounds__(256) void fill_region_kernel(const int* __restrict__ rgid, int total,
+// it was received in (rid). Receiver R's records are rs[R] .. rs[R + 1] of
+// the pulse's storage and land at slots dst[R] on.
+__global__ __launch_bounds__(256) void fill_region_kernel(const int* __restrict__ rgid,
                                                           const int* __restrict__ rs, int ndom,
-                                                          const int* __restrict__ dst,
+                                                          int cps, const int* __restrict__ dst,
                                                           int* __restrict__ slot_gid,
                                                           uint8_t* __restrict__ rid, int q)
 {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= total)
-        return;
-    const int R = segment_of(rs, ndom, idx);  // rs[R] <= idx < rs[R+1]
-    const int slot = dst[R] + (idx - rs[R]);
-    slot_gid[slot] = rgid[idx];
-    rid[slot] = (uint8_t)q;
+    for (int64_t b = blockIdx.x; b < (int64_t)ndom * cps; b += gridDim.x) {
+        int R, i0, i1;
+        if (!seg_chunk(rs, cps, b, R, i0, i1))
+            continue;
+        const int off = dst[R] - rs[R];
+        int g[kSegItems];
+#pragma unroll
+        for (int j = 0; j < kSegItems; j++) {
+            const int i = i0 + j * 256 + (int)threadIdx.x;
+            g[j] = i < i1 ? rgid[i] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < kSegItems; j++) {
+            const int i = i0 + j * 256 + (int)threadIdx.x;
+            if (i < i1) {
+                slot_gid[i + off] = g[j];
+                rid[i + off] = (uint8_t)q;
+            }
+        }
+    }
 }
 
 // out[i] = maps[i] as 16 bits; the caller has checked that every domain has
@@ -1152,21 +1168,30 @@ __global__ __launch_bounds__(256) void pad_maps_kernel(const T* __restrict__ map
 }
 
 // inmap[slot] |= bit for every entry of pulse q's maps (maps_q: the pulse's
-// maps of all senders, sender S's at mpos[S]..mpos[S+1]). Within one pulse
-// every slot appears at most once (a map holds distinct slots of its own
-// sender), so plain read-modify-writes suffice; pulses run one after the
-// other on the stream.
-__global__ __launch_bounds__(256) void inmap_kernel(const int32_t* __restrict__ maps_q, int total,
-                                                    const int* __restrict__ mpos, int ndom,
+// maps of all senders, sender S's at mpos[S]..mpos[S+1], segmented as in
+// fill_region_kernel). Within one pulse every slot appears at most once (a
+// map holds distinct slots of its own sender), so plain read-modify-writes
+// suffice; pulses run one after the other on the stream.
+__global__ __launch_bounds__(256) void inmap_kernel(const int32_t* __restrict__ maps_q,
+                                                    const int* __restrict__ mpos, int ndom, int cps,
                                                     const int* __restrict__ base,
                                                     uint32_t* __restrict__ inmap, uint32_t bit)
 {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= total)
-        return;
-    const int S = segment_of(mpos, ndom, idx);
-    const int slot = base[S] + maps_q[idx];
-    inmap[slot] |= bit;
+    for (int64_t b = blockIdx.x; b < (int64_t)ndom * cps; b += gridDim.x) {
+        int S, i0, i1;
+        if (!seg_chunk(mpos, cps, b, S, i0, i1))
+            continue;
+        int slot[kSegItems];
+#pragma unroll
+        for (int j = 0; j < kSegItems; j++) {
+            const int i = i0 + j * 256 + (int)threadIdx.x;
+            slot[j] = i < i1 ? base[S] + maps_q[i] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < kSegItems; j++)
+            if (slot[j] >= 0)
+                inmap[slot[j]] |= bit;
+    }
 }
 
 // Wait masks of the fused launch's chunks, one block per chunk. Coordinate
@@ -2270,9 +2295,14 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                                dim3(256), 0, s, p->d_home_gid, d_hs, d_base, D, cpd,
                                p->d_slot_gid, p->d_home_slot);
         for (int q = 0; q < P; q++) {
-            if (total[q] > 0)
-                hipLaunchKernelGGL(fill_region_kernel, dim3(blocks(total[q])), dim3(256), 0, s,
-                                   rgid[q], total[q], (const int*)(d_lay + o_rs[q]), D,
+            int max_region = 0;  // the largest region of the pulse, in chunks
+            for (int R = 0; R < D; R++)
+                max_region = std::max(max_region, rsize_at[R * P + q]);
+            const int cps = (max_region + kSegTile - 1) / kSegTile;
+            if (total[q] > 0 && cps > 0)
+                hipLaunchKernelGGL(fill_region_kernel,
+                                   dim3((unsigned)std::min<int64_t>((int64_t)D * cps, kSegMaxBlocks)),
+                                   dim3(256), 0, s, rgid[q], (const int*)(d_lay + o_rs[q]), D, cps,
                                    (const int*)(d_lay + o_dst[q]), p->d_slot_gid, d_rid, q);
         }
         DDH_HIP(hipGetLastError());
@@ -2350,10 +2380,15 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         const int* d_mpos = (const int*)(d_mb + o_mpos);
         int64_t pb = 0;
         for (int q = 0; q < P; q++) {
-            if (total[q] > 0)
-                hipLaunchKernelGGL(inmap_kernel, dim3(blocks(total[q])), dim3(256), 0, s,
-                                   p->d_maps + pb, total[q], d_mpos + (size_t)q * (D + 1), D,
-                                   d_base, d_inmap, 1u << q);
+            int max_map = 0;  // the largest map of the pulse, in chunks
+            for (int S = 0; S < D; S++)
+                max_map = std::max(max_map, p->send[S * P + q]);
+            const int cps = (max_map + kSegTile - 1) / kSegTile;
+            if (total[q] > 0 && cps > 0)
+                hipLaunchKernelGGL(inmap_kernel,
+                                   dim3((unsigned)std::min<int64_t>((int64_t)D * cps, kSegMaxBlocks)),
+                                   dim3(256), 0, s, p->d_maps + pb, d_mpos + (size_t)q * (D + 1), D,
+                                   cps, d_base, d_inmap, 1u << q);
             pb += total[q];
         }
         const int nx = (int)t.xch.size(), nf = (int)t.fch.size();
