@@ -101,6 +101,59 @@ __device__ __forceinline__ bool locate(const float v[3], const AGeom& g, const f
     return true;
 }
 
+// locate() with the boundary and cell-count tables merged per domain index:
+// entry noff[d] + i of tab holds (b_d[i], b_d[i + 1], cells along d of index
+// i as int bits, 0). The estimate's entry usually brackets the position, so
+// one LDS read per dimension decides it (the three issued together); the
+// search steps run only when it does not. Same results as locate().
+__device__ __forceinline__ bool locate_tab(const float v[3], const AGeom& g, const float4* tab,
+                                           int& dom, int& key)
+{
+    int est[3];
+    float4 e[3];
+#pragma unroll
+    for (int d = 0; d < 3; d++) {
+        const float f = v[d] * ((float)g.n[d] / g.L[d]);
+        // no conversion of NaN or of values past the last index
+        int i = f >= 0.0f && f < (float)g.n[d] ? (int)f : (f >= (float)g.n[d] ? g.n[d] - 1 : 0);
+        i = i > g.n[d] - 1 ? g.n[d] - 1 : i;
+        est[d] = i;
+        e[d] = tab[g.noff[d] + i];
+    }
+    int ci[3], cc[3], ncd[3];
+#pragma unroll
+    for (int d = 0; d < 3; d++) {
+        if (!(v[d] >= 0.0f && v[d] < g.L[d]))
+            return false;
+        const int n = g.n[d];
+        int i = est[d];
+        float4 t = e[d];
+        if (i > 0 && v[d] < t.x) {
+            do {
+                i--;
+                t = tab[g.noff[d] + i];
+            } while (i > 0 && v[d] < t.x);
+        } else if (i < n - 1 && v[d] >= t.y) {
+            do {
+                i++;
+                t = tab[g.noff[d] + i];
+            } while (i < n - 1 && v[d] >= t.y);
+        }
+        ci[d] = i;
+        ncd[d] = __float_as_int(t.z);
+        int c = 0;
+        if (ncd[d] > 1) {
+            const float u = (v[d] - t.x) * g.inv_c;
+            c = (int)floorf(u);
+            c = c < 0 ? 0 : (c > ncd[d] - 1 ? ncd[d] - 1 : c);
+        }
+        cc[d] = c;
+    }
+    dom = ci[0] + g.n[0] * (ci[1] + g.n[1] * ci[2]);
+    key = cc[0] + ncd[0] * (cc[1] + ncd[1] * cc[2]);
+    return true;
+}
+
 // Counting form of the assignment: each atom's bucket (its domain's first
 // bucket plus its cell key, -1 outside the box) and its arrival rank in the
 // bucket from the count's atomic add (an arbitrary order inside the bucket,
@@ -148,18 +201,18 @@ __global__ __launch_bounds__(256) void part_count_kernel(const float* __restrict
                                                          uint32_t* __restrict__ hist,
                                                          uint32_t* __restrict__ err)
 {
-    extern __shared__ uint32_t sh[];  // counts [ndom], boundaries [nbt], cell counts [nnt]
-    const int nbt = g.boff[2] + g.n[2] + 1, nnt = g.noff[2] + g.n[2];
-    uint32_t* cnt = sh;
-    float* b = (float*)(sh + ndom);
-    int* nc = (int*)(sh + ndom + nbt);
+    extern __shared__ float4 shq[];  // merged tables [ntab] (locate_tab), counts [ndom]
+    const int ntab = g.noff[2] + g.n[2];
+    float4* tab = shq;
+    uint32_t* cnt = (uint32_t*)(shq + ntab);
     const int tid = (int)threadIdx.x;
     for (int d = tid; d < ndom; d += 256)
         cnt[d] = 0u;
-    for (int k = tid; k < nbt; k += 256)
-        b[k] = g.b[k];
-    for (int k = tid; k < nnt; k += 256)
-        nc[k] = g.ncell[k];
+    for (int k = tid; k < ntab; k += 256) {
+        const int d = k < g.noff[1] ? 0 : (k < g.noff[2] ? 1 : 2), i = k - g.noff[d];
+        const float* bd = g.b + g.boff[d];
+        tab[k] = make_float4(bd[i], bd[i + 1], __int_as_float(g.ncell[k]), 0.0f);
+    }
     const int64_t a0 = (int64_t)blockIdx.x * (256 * ITEMS);
     // every position load of the thread is issued before the first test
     float v[ITEMS][3];
@@ -179,7 +232,7 @@ __global__ __launch_bounds__(256) void part_count_kernel(const float* __restrict
         if (a < n_atoms) {
             int dom, key;
             uint32_t c = kPartNone;
-            if (locate(v[i], g, b, nc, dom, key)) {
+            if (locate_tab(v[i], g, tab, dom, key)) {
                 c = ((uint32_t)dom << kKeyBits) | (uint32_t)key;
                 atomicAdd(&cnt[dom], 1u);
             } else {
@@ -1901,7 +1954,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                           : (int64_t)n_atoms >= 4ll * 256 * kPartMinBlocks ? 4 : 1;
         const int tile = 256 * items;
         const int nblk = (int)(((int64_t)n_atoms + tile - 1) / tile);
-        const size_t geo_words = (size_t)D + (ag.boff[2] + ag.n[2] + 1) + (ag.noff[2] + ag.n[2]);
+        const size_t part_lds = sizeof(float4) * (size_t)(ag.noff[2] + ag.n[2]) + sizeof(uint32_t) * D;
         uint32_t *d_code, *d_hist, *d_hscan;
         uint2* d_rec;
         DDH_HIP(sc.alloc(&d_code, (size_t)n_atoms));
@@ -1913,8 +1966,8 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         const auto scatter_k = items == 16 ? part_scatter_kernel<16>
                                : items == 4 ? part_scatter_kernel<4> : part_scatter_kernel<1>;
         if (nblk > 0)
-            hipLaunchKernelGGL(count_k, dim3(nblk), dim3(256), sizeof(uint32_t) * geo_words, s, xg,
-                               n_atoms, ag, D, nblk, d_code, d_hist, d_err);
+            hipLaunchKernelGGL(count_k, dim3(nblk), dim3(256), part_lds, s, xg, n_atoms, ag, D, nblk,
+                               d_code, d_hist, d_err);
         DDH_HIP(hipGetLastError());
         // (domain, block) first positions; hscan[D * nblk] = atoms in the box
         const int rc = scan_exclusive(sc, d_hist, (int64_t)D * nblk, d_hscan, s);
