@@ -17,8 +17,10 @@ Prints one JSON line. `value` is halo atoms moved per second (sum of every
 graph of G captured steps (G at most --graph-steps, and small enough that
 --steps gives at least five replays), so the host never starves the GPU;
 HIP events on the launch stream bracket every replay, and the median, p10
-and p90 are taken over the replays. `cold` times the same workload with a
-1 GiB buffer written before every (eager) step. `roofline` compares the
+and p90 are taken over the replays. `cold` times the same workload with the
+caches evicted before every (eager) step by reading a 1 GiB buffer (so they
+hold only clean lines), and once more with the buffer written instead (the
+step then also writes back the eviction's dirty lines). `roofline` compares the
 step's algorithmic bytes (28 B per halo atom for the coordinate pass, 40 B
 for the force pass) with the 8 TB/s HBM peak over the measured GPU time per
 launch; `cpu_baseline` times the CPU oracle on a bounded sample of the same
@@ -175,7 +177,10 @@ def run_gpu(args, w):
     xl = torch.zeros((n_slots, 3), dtype=torch.float32, device=dev)
     plan.gather_home(xg, xl)
     fl = torch.from_numpy(W.forces(w, n_slots)).to(dev)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
+    flush = None
+    if args.cold:
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
 
     if args.pass_ == "coords":
         calls = [("coords", lambda: plan.exchange_coords(xl), BYTES_X * n_halo)]
@@ -202,10 +207,15 @@ def run_gpu(args, w):
     torch.cuda.synchronize()
     if args.cold:
         # eager, one step at a time: caches evicted before every step; the
-        # eviction keeps the GPU busy while the host enqueues the step
+        # eviction keeps the GPU busy while the host enqueues the step.
+        # Reading 1 GiB leaves only clean lines behind; writing it leaves
+        # dirty lines that the step's own traffic then writes back.
         durs = []
         for _ in range(args.steps):
-            flush.fill_(1.0)
+            if args.cold_flush == "write":
+                flush.fill_(1.0)
+            else:
+                flush.sum()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -1029,6 +1039,9 @@ def main():
                     help="time one pass alone (coordinate or force pass) instead of the step; "
                          "with --only-step, for per-pass profiler runs")
     ap.add_argument("--cold", action="store_true", help="evict caches before every step")
+    ap.add_argument("--cold-flush", choices=("read", "write"), default="read",
+                    help="how --cold evicts the caches: read a 1 GiB buffer (clean lines "
+                         "left behind) or write it (dirty lines left behind)")
     ap.add_argument("--eager", action="store_true",
                     help="enqueue every step from the host (no graph replay)")
     ap.add_argument("--build-only", action="store_true",
@@ -1123,15 +1136,25 @@ def main():
         sub.cold = True
         sub.steps = max(5, min(args.steps, 50))
         sub.warmup = 2
+        sub.cold_flush = "read"
         gc = run_gpu(sub, w)
+        sub.cold_flush = "write"
+        gw = run_gpu(sub, w)
+        bytes_step = (BYTES_X + BYTES_F) * gc["n_halo"]
         cold = {"us_per_step": gc["roofline"]["median_step_us"],
                 "p10_step_us": gc["roofline"]["p10_step_us"],
                 "p90_step_us": gc["roofline"]["p90_step_us"],
-                "frac": round((BYTES_X + BYTES_F) * gc["n_halo"]
-                              / (gc["roofline"]["median_step_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "frac": round(bytes_step / (gc["roofline"]["median_step_us"] * 1e-6) / 1e9
+                              / HBM_PEAK_GBS, 4),
                 "variant": gc["variant"], "steps": gc["steps"],
-                "how": "eager steps, each after a 1 GiB buffer is written (caches evicted); "
-                       "median over the steps"}
+                "how": "eager steps, each after a 1 GiB buffer is read (caches evicted, "
+                       "only clean lines left in them); median over the steps",
+                "after_write_flush": {
+                    "us_per_step": gw["roofline"]["median_step_us"],
+                    "frac": round(bytes_step / (gw["roofline"]["median_step_us"] * 1e-6) / 1e9
+                                  / HBM_PEAK_GBS, 4),
+                    "how": "the same, with the 1 GiB buffer written instead: the step also "
+                           "writes back the dirty lines the eviction left in the caches"}}
     also = {}
     keys = [int(k) for k in args.also.split(",") if k.strip()] if args.also else []
     if not args.only_step and not args.copy_probe:
