@@ -44,6 +44,7 @@ import csv
 import hashlib
 import json
 import os
+import shlex
 import sys
 import time
 
@@ -741,7 +742,8 @@ def run_event_trace(args, w, out_path):
                  "library's device event log (`DDH_TUNE_TRACE`), after warm-up steps. "
                  "Times in us from the first work-group's start (100 MHz wall clock). "
                  "Command (repository root, one MI355X):\n\n")
-        fh.write(f"```\n{args.pmc_command}\n```\n\n")
+        cmd = args.pmc_command or " ".join(["python3"] + [shlex.quote(a) for a in sys.argv])
+        fh.write(f"```\n{cmd}\n```\n\n")
         fh.write(f"- work-groups: {grid} (1024 lanes); chunks: {len(chunks)}; "
                  f"span to the last exit: {span:.1f} us\n")
         fh.write(f"- median work-group busy fraction (claim to release, summed): "
