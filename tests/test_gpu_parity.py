@@ -872,6 +872,32 @@ def test_selection_by_cells_and_by_slots(home_sort):
             g.close()
 
 
+CELL_CASES = [((2, 2, 2), (4.0, 4.0, 4.0), 1.0, 4000, 11),
+              ((3, 2, 1), (6.0, 3.0, 2.5), 0.75, 5000, 12),
+              ((4, 1, 2), (5.0, 2.0, 4.0), 1.5, 3000, 13)]
+
+
+@pytest.mark.parametrize("cell", [0.3, 0.37, 0.375, 0.7, 1.1, 3.0])
+def test_cell_sizes(cell):
+    """Cell sizes whose reciprocal is inexact in fp32 (0.3, 0.37, 0.7, 1.1),
+    dyadic (0.375), and wider than every domain (3.0, one cell per domain),
+    with positions on a 1/16 nm lattice, so that many atoms lie exactly on
+    cell edges and on the slab thresholds (rc 1.0, 0.75, 1.5; two pulses
+    along x in the last case). The cell coordinate is floor(fl(fl(x - lo) *
+    fl(1/c))), clamped; the home selection's whole-cell decisions rest on it
+    being monotone in fl(x - lo). Both home sorts and both launch forms give
+    the oracle's layout, maps and results."""
+    for grid, box, rc, n, seed in CELL_CASES:
+        x = W.lattice_positions(n, box, seed=seed, frac_bits=4)
+        ref = oracle.OraclePlan(x, grid, box, rc, cell=cell)
+        for home_sort, mode in ((1, ddh.DDH_MODE_PULSE), (2, ddh.DDH_MODE_PULSE),
+                                (2, ddh.DDH_MODE_FUSED)):
+            g = GpuPlan(x, grid, box, rc, cell=cell, mode=mode, home_sort=home_sort)
+            check_layout(g, ref)
+            check_steps(g, ref, n + seed, steps=1)
+            g.close()
+
+
 def test_error_paths():
     box = (8.0, 8.0, 8.0)
     plan = ddh.Plan((2, 2, 2), box, 1.0)
