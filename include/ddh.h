@@ -146,6 +146,10 @@ const char *ddh_last_error(void);
  * Replaces any previous maps of the plan. Meant to run at every
  * neighbour-search step: the plan keeps its device memory and reuses it in
  * later builds while it is large enough (ddh_plan_destroy releases it).
+ * The library's own graphs (DDH_MODE_GRAPH) are recaptured after a build,
+ * but exchange calls captured into a caller's graph keep the launch shapes
+ * and the tables of the build they were captured after: recapture them
+ * after every ddh_build_maps.
  * Errors: DDH_EINVAL (bad pointer or position), DDH_ECAPACITY (layout too
  * large), DDH_EHIP.
  */
