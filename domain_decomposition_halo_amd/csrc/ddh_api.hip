@@ -399,7 +399,16 @@ int ddh_set_mode(ddh_plan* p, int32_t mode)
     if (base == DDH_MODE_STAGED && (mode & DDH_MODE_GRAPH))
         return fail(DDH_EINVAL, "ddh_set_mode: DDH_MODE_STAGED waits on the host and cannot "
                                 "be replayed from a graph");
+    const int32_t old = p->mode;
     p->mode = mode;
+    // a build made under a mode that never runs the fused launch did not
+    // make its table: make it now if the new mode may run it
+    if (p->built && !p->fused_ready && p->may_fuse()) {
+        if (int rc = prepare_fused(p)) {
+            p->mode = old;
+            return rc;
+        }
+    }
     return DDH_OK;
 }
 

@@ -1490,6 +1490,8 @@ void free_built(Plan* p)
     p->kept_next = 0;
     p->d_maps = p->d_slot_gid = p->d_home_gid = p->d_home_slot = nullptr;
     p->d_maps16 = nullptr;
+    p->d_rid = nullptr;
+    p->fused_ready = false;
     p->fused = WorkTable{};
     p->pulse = WorkTable{};
     p->pulse1 = WorkTable{};
@@ -1829,6 +1831,94 @@ struct Phases {
             roctxRangePop();
     }
 };
+
+// The fused launch's chunk table (chunk size, wavefront workers, heads
+// first and refined waits as set at the build), its wait masks and release
+// flags (on the device from the maps, with refined waits), and the counter
+// target of every map. Needs the build's maps, slot bases, slot pulses and
+// counters.
+static int fused_stage(Plan* p, Scratch& sc, hipStream_t s)
+{
+    const int D = p->g.ndom, P = p->g.P;
+    const size_t DP = (size_t)D * P;
+    WorkTable& t = p->fused;
+    make_work_table(p, true, t);
+    DDH_HIP(owned_alloc(p, &t.d_xch, t.xch.size()));
+    DDH_HIP(owned_alloc(p, &t.d_fch, t.fch.size()));
+    if (p->fused_refined && P > 0) {
+        DDH_HIP(upload(sc, t.d_xch, t.xch, s));
+        DDH_HIP(upload(sc, t.d_fch, t.fch, s));
+        // per pulse: each sender's first entry in the pulse's maps, then
+        // the pulse's total; the slot bases
+        std::vector<int> mposall(((size_t)D + 1) * P);
+        int64_t pb = 0;
+        for (int q = 0; q < P; q++) {
+            int64_t tot = 0;
+            for (int S = 0; S < D; S++) {
+                mposall[(size_t)q * (D + 1) + S] = (int)(p->map_off[(size_t)S * P + q] - pb);
+                tot += p->send[(size_t)S * P + q];
+            }
+            mposall[(size_t)q * (D + 1) + D] = (int)tot;
+            pb += tot;
+        }
+        std::vector<int> base32(D);
+        for (int Dm = 0; Dm < D; Dm++)
+            base32[Dm] = (int)p->base[Dm];
+        Blob mb;
+        const size_t o_mpos = mb.add(mposall), o_base = mb.add(base32);
+        char* d_mb;
+        DDH_HIP(mb.send(sc, &d_mb, s));
+        const int* d_mpos = (const int*)(d_mb + o_mpos);
+        const int* d_base = (const int*)(d_mb + o_base);
+        uint32_t* d_inmap;
+        DDH_HIP(sc.alloc(&d_inmap, (size_t)p->n_slots));
+        DDH_HIP(hipMemsetAsync(d_inmap, 0, sizeof(uint32_t) * (size_t)p->n_slots, s));
+        pb = 0;
+        for (int q = 0; q < P; q++) {
+            const int total = mposall[(size_t)q * (D + 1) + D];
+            int max_map = 0;  // the largest map of the pulse, in chunks
+            for (int S = 0; S < D; S++)
+                max_map = std::max(max_map, p->send[(size_t)S * P + q]);
+            const int cps = (max_map + kSegTile - 1) / kSegTile;
+            if (total > 0 && cps > 0)
+                hipLaunchKernelGGL(inmap_kernel,
+                                   dim3((unsigned)std::min<int64_t>((int64_t)D * cps, kSegMaxBlocks)),
+                                   dim3(256), 0, s, p->d_maps + pb, d_mpos + (size_t)q * (D + 1), D,
+                                   cps, d_base, d_inmap, 1u << q);
+            pb += total;
+        }
+        const int nx = (int)t.xch.size(), nf = (int)t.fch.size();
+        // the release flags follow from the masks, on the device as well
+        // (the host copies of the fused table keep neither)
+        uint32_t* d_read;
+        DDH_HIP(sc.alloc(&d_read, 2 * DP));
+        DDH_HIP(hipMemsetAsync(d_read, 0, sizeof(uint32_t) * 2 * DP, s));
+        if (nx + nf > 0) {
+            hipLaunchKernelGGL(chunk_masks_kernel, dim3(nx + nf), dim3(256), 0, s, t.d_xch, nx,
+                               t.d_fch, nf, p->d_maps, p->d_rid, d_inmap, P);
+            hipLaunchKernelGGL(release_marks_kernel, dim3(blocks(nx + nf)), dim3(256), 0, s,
+                               t.d_xch, nx, t.d_fch, nf, P, (int)DP, d_read);
+            hipLaunchKernelGGL(release_apply_kernel, dim3(blocks(nx + nf)), dim3(256), 0, s,
+                               t.d_xch, nx, t.d_fch, nf, (int)DP, d_read);
+        }
+        DDH_HIP(hipGetLastError());
+    } else {
+        set_release_flags(p, t);
+        DDH_HIP(upload(sc, t.d_xch, t.xch, s));
+        DDH_HIP(upload(sc, t.d_fch, t.fch, s));
+    }
+    // counter targets: chunks per map (coordinates at the receiver's row)
+    std::vector<uint32_t> need(2 * DP, 0u);
+    for (int S = 0; S < D; S++)
+        for (int q = 0; q < P; q++) {
+            const size_t it = (size_t)S * P + q;
+            need[(size_t)p->recv[it] * P + q] = (uint32_t)t.nchunks[it];
+            need[DP + it] = (uint32_t)t.nchunks[it];
+        }
+    // d_fneed follows d_xneed: one copy of both
+    DDH_HIP(upload(sc, p->d_xneed, need, s));
+    return DDH_OK;
+}
 
 int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
 {
@@ -2315,9 +2405,8 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     // slot (rid, 0xff for home slots) for the wait masks
     DDH_HIP(owned_alloc(p, &p->d_slot_gid, (size_t)p->n_slots));
     DDH_HIP(owned_alloc(p, &p->d_home_slot, (size_t)n_atoms));
-    uint8_t* d_rid;
-    DDH_HIP(sc.alloc(&d_rid, (size_t)p->n_slots));
-    DDH_HIP(hipMemsetAsync(d_rid, 0xff, (size_t)p->n_slots, s));
+    DDH_HIP(owned_alloc(p, &p->d_rid, (size_t)p->n_slots));
+    DDH_HIP(hipMemsetAsync(p->d_rid, 0xff, (size_t)p->n_slots, s));
     std::vector<int> base32(D);
     const int* d_base;
     Blob lay;
@@ -2356,26 +2445,17 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                 hipLaunchKernelGGL(fill_region_kernel,
                                    dim3((unsigned)std::min<int64_t>((int64_t)D * cps, kSegMaxBlocks)),
                                    dim3(256), 0, s, rgid[q], (const int*)(d_lay + o_rs[q]), D, cps,
-                                   (const int*)(d_lay + o_dst[q]), p->d_slot_gid, d_rid, q);
+                                   (const int*)(d_lay + o_dst[q]), p->d_slot_gid, p->d_rid, q);
         }
         DDH_HIP(hipGetLastError());
     }
 
-    // ---- 5: chunk tables (wait masks computed on the device), counters
+    // ---- 5: per-pulse chunk tables, counters
     ph.next("build: chunk tables");
-    p->fused.chunk = p->chunk_req > 0 ? p->chunk_req : fused_chunk(p);
-    p->fused.wave = p->wave_chunks != 0;
-    p->fused.heads_first = p->heads_first != 0;
     p->pulse.chunk = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p, true);
     const int chunk1 = p->chunk_req > 0 ? p->chunk_req : pulse_chunk(p, false);
-    make_work_table(p, true, p->fused);
-    ph.next("build: chunk tables, uploads");
-    DDH_HIP(owned_alloc(p, &p->fused.d_xch, p->fused.xch.size()));
-    DDH_HIP(owned_alloc(p, &p->fused.d_fch, p->fused.fch.size()));
-    DDH_HIP(upload(sc, p->fused.d_xch, p->fused.xch, s));
-    DDH_HIP(upload(sc, p->fused.d_fch, p->fused.fch, s));
-    // per-pulse tables: every coordinate chunk is a contiguous slice [hb, he)
-    // of one map, made on the device from the maps' data
+    // every coordinate chunk is a contiguous slice [hb, he) of one map, made
+    // on the device from the maps' data
     {
         std::vector<int> info(5 * DP + (size_t)D + (size_t)P);
         int* in = info.data();
@@ -2414,65 +2494,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                 return rc;
         }
     }
-    ph.next("build: chunk tables, wait masks");
-    if (p->refined_waits && P > 0) {
-        WorkTable& t = p->fused;
-        uint32_t* d_inmap;
-        DDH_HIP(sc.alloc(&d_inmap, (size_t)p->n_slots));
-        DDH_HIP(hipMemsetAsync(d_inmap, 0, sizeof(uint32_t) * (size_t)p->n_slots, s));
-        std::vector<int> mposall(((size_t)D + 1) * P);
-        for (int q = 0; q < P; q++) {
-            for (int S = 0; S < D; S++)
-                mposall[(size_t)q * (D + 1) + S] = mpos[q][S];
-            mposall[(size_t)q * (D + 1) + D] = total[q];
-        }
-        Blob mb;
-        const size_t o_mpos = mb.add(mposall);
-        char* d_mb;
-        DDH_HIP(mb.send(sc, &d_mb, s));
-        const int* d_mpos = (const int*)(d_mb + o_mpos);
-        int64_t pb = 0;
-        for (int q = 0; q < P; q++) {
-            int max_map = 0;  // the largest map of the pulse, in chunks
-            for (int S = 0; S < D; S++)
-                max_map = std::max(max_map, p->send[S * P + q]);
-            const int cps = (max_map + kSegTile - 1) / kSegTile;
-            if (total[q] > 0 && cps > 0)
-                hipLaunchKernelGGL(inmap_kernel,
-                                   dim3((unsigned)std::min<int64_t>((int64_t)D * cps, kSegMaxBlocks)),
-                                   dim3(256), 0, s, p->d_maps + pb, d_mpos + (size_t)q * (D + 1), D,
-                                   cps, d_base, d_inmap, 1u << q);
-            pb += total[q];
-        }
-        const int nx = (int)t.xch.size(), nf = (int)t.fch.size();
-        // the release flags follow from the masks, on the device as well
-        // (the host copies of the fused table keep neither)
-        uint32_t* d_read;
-        DDH_HIP(sc.alloc(&d_read, 2 * DP));
-        DDH_HIP(hipMemsetAsync(d_read, 0, sizeof(uint32_t) * 2 * DP, s));
-        if (nx + nf > 0) {
-            hipLaunchKernelGGL(chunk_masks_kernel, dim3(nx + nf), dim3(256), 0, s, t.d_xch, nx,
-                               t.d_fch, nf, p->d_maps, d_rid, d_inmap, P);
-            hipLaunchKernelGGL(release_marks_kernel, dim3(blocks(nx + nf)), dim3(256), 0, s,
-                               t.d_xch, nx, t.d_fch, nf, P, (int)DP, d_read);
-            hipLaunchKernelGGL(release_apply_kernel, dim3(blocks(nx + nf)), dim3(256), 0, s,
-                               t.d_xch, nx, t.d_fch, nf, (int)DP, d_read);
-        }
-        DDH_HIP(hipGetLastError());
-    } else {
-        set_release_flags(p, p->fused);
-        DDH_HIP(upload(sc, p->fused.d_xch, p->fused.xch, s));
-        DDH_HIP(upload(sc, p->fused.d_fch, p->fused.fch, s));
-    }
-
     ph.next("build: counters");
-    std::vector<uint32_t> xneed(DP, 0u), fneed(DP, 0u);
-    for (int S = 0; S < D; S++)
-        for (int q = 0; q < P; q++) {
-            const int it = S * P + q;
-            xneed[(size_t)p->recv[it] * P + q] = (uint32_t)p->fused.nchunks[it];
-            fneed[it] = (uint32_t)p->fused.nchunks[it];
-        }
     const size_t words = (size_t)kCtrlWords + 4 * DP + 2 * (size_t)DDH_MAX_PULSES;
     DDH_HIP(owned_alloc(p, &p->d_ctrl, words));
     DDH_HIP(hipMemsetAsync(p->d_ctrl, 0, sizeof(uint32_t) * words, s));
@@ -2481,12 +2503,38 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     p->d_xneed = p->d_fcnt + DP;
     p->d_fneed = p->d_xneed + DP;
     p->d_pflag = p->d_fneed + DP;
-    // d_fneed follows d_xneed: one copy of both
-    xneed.insert(xneed.end(), fneed.begin(), fneed.end());
-    DDH_HIP(upload(sc, p->d_xneed, xneed, s));
+
+    // ---- 6: the fused launch's table, now if the mode may run that launch,
+    // else at the first switch to such a mode (prepare_fused); its settings
+    // are those of this build
+    p->fused.chunk = p->chunk_req > 0 ? p->chunk_req : fused_chunk(p);
+    p->fused.wave = p->wave_chunks != 0;
+    p->fused.heads_first = p->heads_first != 0;
+    p->fused_refined = p->refined_waits != 0;
+    const bool fuse_now = p->may_fuse();
+    if (fuse_now) {
+        ph.next("build: fused table");
+        if (int rc = fused_stage(p, sc, s))
+            return rc;
+    }
     DDH_HIP(hipStreamSynchronize(s));
     p->built = true;
+    p->fused_ready = fuse_now;
     p->build_failed = false;
+    return DDH_OK;
+}
+
+int prepare_fused(Plan* p)
+{
+    if (!p->built || p->fused_ready)
+        return DDH_OK;
+    if (!p->capture_stream)
+        DDH_HIP(hipStreamCreateWithFlags(&p->capture_stream, hipStreamNonBlocking));
+    Scratch sc(p);
+    if (int rc = fused_stage(p, sc, p->capture_stream))
+        return rc;
+    DDH_HIP(hipStreamSynchronize(p->capture_stream));
+    p->fused_ready = true;
     return DDH_OK;
 }
 

@@ -1226,6 +1226,10 @@ int enqueue_raw(Plan* p, int op, float* x, float* f, hipStream_t s, int mode)
 {
     const int P = p->g.P;
     if (!(mode & DDH_MODE_PULSE)) {
+        // made at the build, or by ddh_set_mode, whenever the mode may
+        // resolve to the fused launch
+        if (!p->fused_ready)
+            return fail(DDH_ESTATE, "the fused launch's table was not made for this build");
         XArgs a{};
         a.x = x;
         a.f = f;
@@ -1347,7 +1351,7 @@ int enqueue_staged(Plan* p, int op, float* x, float* f, hipStream_t s, float* st
 
 int enqueue_exchange(Plan* p, int op, float* x, float* f, hipStream_t s)
 {
-    if (p->g.P == 0 || p->fused.nchunks.empty())
+    if (p->g.P == 0 || p->pulse.nchunks.empty())
         return DDH_OK;
     if (!(p->mode & DDH_MODE_GRAPH)) {
         // a capturing stream means the launches will be replayed from the
@@ -1450,7 +1454,7 @@ int enqueue_staged_static(Plan* p, int op, float* x, float* f, hipStream_t s)
         }
         ptr = g_scratch_ptr[dev];
     }
-    if (p->g.P == 0 || p->fused.nchunks.empty())
+    if (p->g.P == 0 || p->pulse.nchunks.empty())
         return DDH_OK;
     return enqueue_staged(p, op, x, f, s, static_cast<float*>(ptr));
 }

@@ -176,6 +176,14 @@ struct Plan {
                                                                         : DDH_MODE_PULSE;
         return m | (mode & DDH_MODE_GRAPH);
     }
+    // whether some call under the current mode can run the fused launch:
+    // FUSED, or AUTO on eager calls over a small layout
+    bool may_fuse() const
+    {
+        const int32_t base = mode & ~DDH_MODE_GRAPH;
+        return base == DDH_MODE_FUSED ||
+               (base == DDH_MODE_AUTO && !(mode & DDH_MODE_GRAPH) && n_halo <= DDH_AUTO_FUSED_MAX);
+    }
 
     // tuning
     int chunk_req = 0;
@@ -227,6 +235,11 @@ struct Plan {
     int32_t* d_slot_gid = nullptr; // global id per slot
     int32_t* d_home_gid = nullptr; // home atoms in slot order, all domains
     int32_t* d_home_slot = nullptr;
+    uint8_t* d_rid = nullptr;      // per slot: the pulse that delivered it (0xff: home)
+    bool fused_ready = false;      // the fused launch's table and counter targets
+                                   // are made (at the build, or at the first
+                                   // switch to a mode that may run that launch)
+    bool fused_refined = true;     // refined waits, as set at the build
     uint32_t* d_ctrl = nullptr;    // control words, then the arrays below
     uint32_t* d_xcnt = nullptr;
     uint32_t* d_fcnt = nullptr;
@@ -261,6 +274,9 @@ int hip_fail(hipError_t e, const char* what);
 // map builder (ddh_build.hip)
 int build_maps(Plan* plan, const float* xg, int32_t n_atoms, hipStream_t stream);
 void free_built(Plan* plan);
+// the fused launch's table, wait masks and counter targets for the current
+// build, on the plan's own stream (waits for it)
+int prepare_fused(Plan* plan);
 void free_scratch(Plan* plan);
 
 // exchange launches (ddh_exchange.hip)

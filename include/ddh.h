@@ -318,7 +318,12 @@ int ddh_exchange_staged_static(ddh_plan *plan, float *x_local_dev, float *f_loca
    "Enabling parallelism across pulses through kernel fusion" (one launch),
    "Replacing host-side communication with NVSHMEM" (one launch per pulse)
    and "From MPI baseline to optimized GPU-native halo exchange" (host
-   orchestrated). All give the same results. Errors: DDH_EINVAL. */
+   orchestrated). All give the same results. A build makes the single
+   launch's chunk table only when the plan's mode may run that launch
+   (FUSED, or AUTO without GRAPH on at most DDH_AUTO_FUSED_MAX halo atoms);
+   switching a built plan to such a mode makes it then, with the settings of
+   that build, on a stream of the plan's own, and waits for it. Errors:
+   DDH_EINVAL, DDH_EHIP (the mode is then left unchanged). */
 int ddh_set_mode(ddh_plan *plan, int32_t mode);
 
 /*

@@ -872,6 +872,33 @@ def test_selection_by_cells_and_by_slots(home_sort):
             g.close()
 
 
+@pytest.mark.parametrize("k,first", [(3, ddh.DDH_MODE_AUTO), (3, ddh.DDH_MODE_PULSE),
+                                     (2, ddh.DDH_MODE_AUTO | ddh.DDH_MODE_GRAPH)])
+def test_fused_table_made_at_mode_switch(k, first, workload_plan):
+    """A build under a mode that never runs the fused launch (AUTO over more
+    than 200k halo atoms, PULSE, AUTO with GRAPH) leaves its table out;
+    switching to FUSED makes it then. Results stay the oracle's: eager and
+    graph-replayed fused steps after the switch, a rebuild under FUSED, and
+    a switch back and forth."""
+    w, x, ref = workload_plan(k)
+    g = GpuPlan(x, mode=first, **w.params())
+    check_layout(g, ref)
+    check_steps(g, ref, k + 70, steps=1)
+    g.plan.set_mode(ddh.DDH_MODE_FUSED)
+    check_steps(g, ref, k + 71, steps=1, fused_step=True)
+    g.plan.set_mode(ddh.DDH_MODE_PULSE)
+    g.plan.set_mode(ddh.DDH_MODE_FUSED | ddh.DDH_MODE_GRAPH)
+    check_steps(g, ref, k + 72, steps=2)
+    g.lay = g.plan.build_maps(g.xg)
+    g.plan.set_mode(ddh.DDH_MODE_FUSED)
+    check_steps(g, ref, k + 73, steps=1, fused_step=True)
+    g.plan.set_mode(first)
+    g.lay = g.plan.build_maps(g.xg)
+    g.plan.set_mode(ddh.DDH_MODE_FUSED)
+    check_steps(g, ref, k + 74, steps=1)
+    g.close()
+
+
 CELL_CASES = [((2, 2, 2), (4.0, 4.0, 4.0), 1.0, 4000, 11),
               ((3, 2, 1), (6.0, 3.0, 2.5), 0.75, 5000, 12),
               ((4, 1, 2), (5.0, 2.0, 4.0), 1.5, 3000, 13)]
