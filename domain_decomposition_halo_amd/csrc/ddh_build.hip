@@ -699,7 +699,8 @@ __global__ __launch_bounds__(256) void fill_home_kernel(const int* __restrict__ 
                                                         const int* __restrict__ hs,
                                                         const int* __restrict__ base, int ndom,
                                                         int cpd, int* __restrict__ slot_gid,
-                                                        int* __restrict__ home_slot)
+                                                        int* __restrict__ home_slot,
+                                                        uint8_t* __restrict__ rid)
 {
     for (int64_t b = blockIdx.x; b < (int64_t)ndom * cpd; b += gridDim.x) {
         const int D = (int)(b / cpd), c = (int)(b % cpd);
@@ -720,6 +721,7 @@ __global__ __launch_bounds__(256) void fill_home_kernel(const int* __restrict__ 
             if (r < r1) {
                 slot_gid[r + off] = g[j];
                 home_slot[r] = (int)(r + off);
+                rid[r + off] = 0xff;
             }
         }
     }
@@ -1122,14 +1124,30 @@ __global__ __launch_bounds__(256) void fill_region_kernel(const int* __restrict_
     }
 }
 
-// out[i] = maps[i] as 16 bits; the caller has checked that every domain has
-// at most 65536 slots, so every sender-local index fits.
-__global__ __launch_bounds__(256) void narrow_maps_kernel(const int32_t* __restrict__ maps,
-                                                          int64_t n, uint16_t* __restrict__ out)
+// The pulses' maps (written by the selection, one buffer per pulse) joined
+// pulse-major into one array: entry i of pulse q lands at begin[q] + i, in
+// 32 bits and, when out16 is given (every domain has at most 65536 slots, so
+// every sender-local index fits), in 16 bits as well.
+struct MapParts {
+    const int32_t* src[DDH_MAX_PULSES];
+    int64_t begin[DDH_MAX_PULSES + 1];
+    int P;
+};
+
+__global__ __launch_bounds__(256) void join_maps_kernel(MapParts mp, int32_t* __restrict__ out,
+                                                        uint16_t* __restrict__ out16)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n)
-        out[i] = (uint16_t)maps[i];
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int q = 0; q < mp.P; q++) {  // uniform: the pulse's table entries stay scalar
+        const int32_t* src = mp.src[q];
+        const int64_t b0 = mp.begin[q], n = mp.begin[q + 1] - b0;
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+            const int32_t v = src[i];
+            out[b0 + i] = v;
+            if (out16)
+                out16[b0 + i] = (uint16_t)v;
+        }
+    }
 }
 
 // Home positions in slot order: xhome[r] = xg[home_gid[r]] (float3).
@@ -1207,7 +1225,8 @@ __global__ __launch_bounds__(256) void pulse_chunks_kernel(MapInfo m, const int*
 }
 
 // Chunk-aligned copy of the maps for the per-pulse launches: block b writes
-// the entries of chunk b at out[b * CH ...] and zeros up to the next chunk.
+// the entries of chunk b at out[b * CH ...] and zeros up to the next chunk;
+// block 0 also clears the kPadTail entries after the last chunk.
 template <typename T>
 __global__ __launch_bounds__(256) void pad_maps_kernel(const T* __restrict__ maps,
                                                        const DChunk* __restrict__ ch, int CH,
@@ -1218,6 +1237,11 @@ __global__ __launch_bounds__(256) void pad_maps_kernel(const T* __restrict__ map
     T* o = out + (int64_t)blockIdx.x * CH;
     for (int i = threadIdx.x; i < CH; i += 256)
         o[i] = i < n ? maps[c.map_off + c.hb + i] : (T)0;
+    if (blockIdx.x == 0) {
+        T* tail = out + (int64_t)gridDim.x * CH;
+        for (int i = threadIdx.x; i < kPadTail; i += 256)
+            tail[i] = (T)0;
+    }
 }
 
 // inmap[slot] |= bit for every entry of pulse q's maps (maps_q: the pulse's
@@ -1742,13 +1766,10 @@ static int pulse_chunk(const Plan* p, bool step)
     return 256;
 }
 
-// A per-pulse launches' table of chunk size t.chunk, made on the device:
-// the host counts each map's chunks and the table's pulse ranges, the
-// device writes the descriptors (pulse_chunks_kernel); then the
-// chunk-aligned copies of the maps (coordinate chunk k's entries at slot
-// k * chunk, force chunks sharing the slot of the coordinate chunk of the
-// same map slice).
-static int make_pulse_table(Plan* p, Scratch& sc, const MapInfo& m, WorkTable& t, hipStream_t s)
+// A per-pulse launches' table of chunk size t.chunk, made on the device.
+// Host part: each map's chunk count and the table's pulse ranges; returns
+// the first chunk of every (pulse, sender) unit, coordinates then forces.
+static std::vector<int> pulse_table_counts(const Plan* p, WorkTable& t)
 {
     const int D = p->g.ndom, P = p->g.P, CH = t.chunk;
     t.wave = false;
@@ -1778,19 +1799,26 @@ static int make_pulse_table(Plan* p, Scratch& sc, const MapInfo& m, WorkTable& t
     t.nf = fpre[D * P];
     t.xpulse_begin[P] = t.nx;
     t.fpulse_begin[P] = t.nf;
+    return pre;
+}
+
+// Device part (d_pre, d_nch: the host part's output on the device): the
+// descriptors (pulse_chunks_kernel), then the chunk-aligned copies of the
+// maps (coordinate chunk k's entries at slot k * chunk, force chunks sharing
+// the slot of the coordinate chunk of the same map slice).
+static int make_pulse_table(Plan* p, const MapInfo& m, WorkTable& t, const int* d_pre,
+                            const int* d_nch, hipStream_t s)
+{
+    const int D = p->g.ndom, P = p->g.P;
     DDH_HIP(owned_alloc(p, &t.d_xch, (size_t)t.nx));
     DDH_HIP(owned_alloc(p, &t.d_fch, (size_t)t.nf));
-    int *d_pre, *d_nch;
-    DDH_HIP(sc.alloc(&d_pre, pre.size()));
-    DDH_HIP(sc.alloc(&d_nch, t.nchunks.size()));
-    DDH_HIP(upload(sc, d_pre, pre, s));
-    DDH_HIP(upload(sc, d_nch, t.nchunks, s));
     if (t.nx + t.nf > 0)
         hipLaunchKernelGGL(pulse_chunks_kernel, dim3(blocks(t.nx + t.nf)), dim3(256), 0, s, m, d_nch,
                            d_pre, t.nx, d_pre + (size_t)D * P + 1, t.nf, t.d_xch, t.d_fch);
     DDH_HIP(hipGetLastError());
-    // the kernel writes every chunk's slot (entries, then zeros); only the
-    // tail after the last slot is cleared here. The 32-bit copy is made only
+    // the copy kernel writes every chunk's slot (entries, then zeros) and
+    // the tail after the last one (no chunk: nothing reads the copy). The
+    // 32-bit copy is made only
     // when the 16-bit maps are off (without it, launches read the maps
     // after the descriptor).
     const int nch = t.nx;
@@ -1799,14 +1827,12 @@ static int make_pulse_table(Plan* p, Scratch& sc, const MapInfo& m, WorkTable& t
     t.d_pad16 = nullptr;
     if (!p->d_maps16 || !p->narrow_maps) {
         DDH_HIP(owned_alloc(p, &t.d_pad, npad));
-        DDH_HIP(hipMemsetAsync(t.d_pad + body, 0, sizeof(int32_t) * kPadTail, s));
         if (nch > 0)
             hipLaunchKernelGGL(pad_maps_kernel<int32_t>, dim3(nch), dim3(256), 0, s, p->d_maps,
                                t.d_xch, t.chunk, t.d_pad);
     }
     if (p->d_maps16) {
         DDH_HIP(owned_alloc(p, &t.d_pad16, npad));
-        DDH_HIP(hipMemsetAsync(t.d_pad16 + body, 0, sizeof(uint16_t) * kPadTail, s));
         if (nch > 0)
             hipLaunchKernelGGL(pad_maps_kernel<uint16_t>, dim3(nch), dim3(256), 0, s, p->d_maps16,
                                t.d_xch, t.chunk, t.d_pad16);
@@ -2003,8 +2029,13 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     Blob geo;
     const size_t o_b = geo.add(bcat), o_ncell = geo.add(ncat), o_cellbase = geo.add(cellbase);
     const size_t o_dgeo = geo.add(dgeo);
+    // the home starts, then the error word (zero): read back in one copy
+    const std::vector<int> hs0((size_t)D + 2, 0);
+    const size_t o_hs = geo.add(hs0);
     char* d_geo;
     DDH_HIP(geo.send(sc, &d_geo, s));
+    int* d_hs = (int*)(d_geo + o_hs);
+    uint32_t* d_err = (uint32_t*)(d_hs + D + 1);
     const int* d_cellbase = (const int*)(d_geo + o_cellbase);
     const int4* d_dgeo = (const int4*)(d_geo + o_dgeo);
     ag.b = (const float*)(d_geo + o_b);
@@ -2028,17 +2059,12 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     if (partition && !fits)
         return fail(DDH_EINVAL, "ddh_build_maps: the partition sort (DDH_TUNE_HOME_SORT 2) needs "
                                 "at most 2048 domains and 4096 sort cells per domain");
-    int* d_hs;
-    uint32_t *d_start, *d_err;
+    uint32_t* d_start;
     DDH_HIP(sc.alloc(&d_start, (size_t)nb + 1));
-    // the home starts, then the error word: read back in one copy
-    DDH_HIP(sc.alloc(&d_hs, (size_t)D + 2));
-    d_err = (uint32_t*)(d_hs + D + 1);
     DDH_HIP(owned_alloc(p, &p->d_home_gid, (size_t)n_atoms));
     // home positions in slot order: the slab tests read them in order
     float* d_xhome;
     DDH_HIP(sc.alloc(&d_xhome, 3 * (size_t)n_atoms));
-    DDH_HIP(hipMemsetAsync(d_err, 0, sizeof(uint32_t), s));
     if (partition) {
         const int items = (int64_t)n_atoms >= 16ll * 256 * kPartMinBlocks ? 16
                           : (int64_t)n_atoms >= 4ll * 256 * kPartMinBlocks ? 4 : 1;
@@ -2128,9 +2154,6 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         hipLaunchKernelGGL(gather_xhome_kernel, dim3(blocks(n_atoms)), dim3(256), 0, s, xg,
                            p->d_home_gid, n_atoms, d_xhome);
     DDH_HIP(hipGetLastError());
-    int* d_nhome;
-    DDH_HIP(sc.alloc(&d_nhome, (size_t)D));
-    DDH_HIP(upload(sc, d_nhome, p->nhome, s));
 
     // ---- 3: pulses
     ph.next("build: pulses");
@@ -2220,7 +2243,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
             ubase[S + 1] = ubase[S] + (by_cells ? hcprefix[S + 1] - hcprefix[S] : 0) +
                            (tprefix[S + 1] - tprefix[S]);
         const int U = ubase[D];
-        const size_t o_ubase = in.add(ubase);
+        const size_t o_ubase = in.add(ubase), o_nhome = in.add(p->nhome);
         char* d_in;
         DDH_HIP(in.send(sc, &d_in, s));
         const float* d_lo = (const float*)(d_in + o_lo);
@@ -2245,7 +2268,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         a.xhome = d_xhome;
         a.home_gid = p->d_home_gid;
         a.home_start = d_hs;
-        a.nhome = d_nhome;
+        a.nhome = (const int*)(d_in + o_nhome);
         a.roff_at = d_roff_at;
         a.rsize_at = d_rsize_at;
         a.rstart = d_rstart;
@@ -2375,38 +2398,40 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         nh += total[q];
     p->n_halo = nh;
 
-    // maps, pulse-major
+    // maps, pulse-major, and a 16-bit copy when every sender-local slot
+    // index fits (halves the bytes of the map reads in every pass)
     DDH_HIP(owned_alloc(p, &p->d_maps, (size_t)nh));
     p->map_off.assign(DP, 0);
+    MapParts mp{};
+    mp.P = P;
     {
         int64_t pb = 0;
         for (int q = 0; q < P; q++) {
             for (int S = 0; S < D; S++)
                 p->map_off[S * P + q] = pb + mpos[q][S];
-            if (total[q] > 0)
-                DDH_HIP(hipMemcpyAsync(p->d_maps + pb, mapp[q], sizeof(int) * total[q],
-                                       hipMemcpyDeviceToDevice, s));
+            mp.src[q] = mapp[q];
+            mp.begin[q] = pb;
             pb += total[q];
         }
+        mp.begin[P] = pb;
     }
-    // a 16-bit copy when every sender-local slot index fits (halves the
-    // bytes of the map reads in every pass)
     int32_t max_total = 0;
     for (int Dm = 0; Dm < D; Dm++)
         max_total = std::max(max_total, p->ntotal[Dm]);
-    if (nh > 0 && max_total <= 65536) {
+    if (nh > 0 && max_total <= 65536)
         DDH_HIP(owned_alloc(p, &p->d_maps16, (size_t)nh));
-        hipLaunchKernelGGL(narrow_maps_kernel, dim3(blocks(nh)), dim3(256), 0, s, p->d_maps, nh,
-                           p->d_maps16);
-        DDH_HIP(hipGetLastError());
-    }
+    if (nh > 0)
+        hipLaunchKernelGGL(join_maps_kernel, dim3((unsigned)std::min<int64_t>(blocks(nh), 4096)),
+                           dim3(256), 0, s, mp, p->d_maps, p->d_maps16);
+    DDH_HIP(hipGetLastError());
 
     // global id per slot, home slot per home atom; pulse of every received
     // slot (rid, 0xff for home slots) for the wait masks
     DDH_HIP(owned_alloc(p, &p->d_slot_gid, (size_t)p->n_slots));
     DDH_HIP(owned_alloc(p, &p->d_home_slot, (size_t)n_atoms));
+    // every slot is a home slot (fill_home_kernel writes 0xff) or in one
+    // received region (fill_region_kernel writes its pulse)
     DDH_HIP(owned_alloc(p, &p->d_rid, (size_t)p->n_slots));
-    DDH_HIP(hipMemsetAsync(p->d_rid, 0xff, (size_t)p->n_slots, s));
     std::vector<int> base32(D);
     const int* d_base;
     Blob lay;
@@ -2435,7 +2460,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
             hipLaunchKernelGGL(fill_home_kernel,
                                dim3((unsigned)std::min<int64_t>((int64_t)D * cpd, kFillMaxBlocks)),
                                dim3(256), 0, s, p->d_home_gid, d_hs, d_base, D, cpd,
-                               p->d_slot_gid, p->d_home_slot);
+                               p->d_slot_gid, p->d_home_slot, p->d_rid);
         for (int q = 0; q < P; q++) {
             int max_region = 0;  // the largest region of the pulse, in chunks
             for (int R = 0; R < D; R++)
@@ -2470,9 +2495,19 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
             in[5 * DP + Dm] = (int)p->base[Dm];
         for (int q = 0; q < P; q++)
             in[5 * DP + D + q] = g.pdim[q];
-        int* d_info;
-        DDH_HIP(sc.alloc(&d_info, info.size()));
-        DDH_HIP(upload(sc, d_info, info, s));
+        // the tables' chunk counts and first chunks, with the map data, in
+        // one copy
+        p->pulse1.chunk = chunk1 != p->pulse.chunk ? chunk1 : 0;
+        const std::vector<int> pre = pulse_table_counts(p, p->pulse);
+        std::vector<int> pre1;
+        if (p->pulse1.chunk)
+            pre1 = pulse_table_counts(p, p->pulse1);
+        Blob tb;
+        const size_t o_info = tb.add(info), o_pre = tb.add(pre), o_nch = tb.add(p->pulse.nchunks);
+        const size_t o_pre1 = tb.add(pre1), o_nch1 = tb.add(p->pulse1.nchunks);
+        char* d_tb;
+        DDH_HIP(tb.send(sc, &d_tb, s));
+        const int* d_info = (const int*)(d_tb + o_info);
         MapInfo m{};
         m.send = d_info;
         m.recv = d_info + DP;
@@ -2485,14 +2520,13 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
             m.L[d] = g.L[d];
         m.D = D;
         m.P = P;
-        if (int rc = make_pulse_table(p, sc, m, p->pulse, s))
+        if (int rc = make_pulse_table(p, m, p->pulse, (const int*)(d_tb + o_pre),
+                                      (const int*)(d_tb + o_nch), s))
             return rc;
-        p->pulse1.chunk = 0;
-        if (chunk1 != p->pulse.chunk) {
-            p->pulse1.chunk = chunk1;
-            if (int rc = make_pulse_table(p, sc, m, p->pulse1, s))
+        if (p->pulse1.chunk)
+            if (int rc = make_pulse_table(p, m, p->pulse1, (const int*)(d_tb + o_pre1),
+                                          (const int*)(d_tb + o_nch1), s))
                 return rc;
-        }
     }
     ph.next("build: counters");
     const size_t words = (size_t)kCtrlWords + 4 * DP + 2 * (size_t)DDH_MAX_PULSES;
