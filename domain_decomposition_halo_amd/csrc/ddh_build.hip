@@ -329,6 +329,56 @@ __device__ uint32_t scan1024_excl(uint32_t v, uint32_t* wsum)
     return before + x - v;
 }
 
+// Write offsets of one pulse from the senders' counts: map_pos[S], S's first
+// entry in the pulse's maps (exclusive prefix over senders); out_pos[S], the
+// first record of S's region in the pulse's received storage (exclusive
+// prefix of the region sizes in receiver order: S sends to rcv[S], R receives
+// from snd[R]; rstart holds the prefix per receiver); and the pulse's total.
+// One block of 1024 threads.
+__global__ __launch_bounds__(1024) void pulse_offsets_kernel(const int* __restrict__ cnt,
+                                                             const int* __restrict__ rcv,
+                                                             const int* __restrict__ snd, int ndom,
+                                                             int* __restrict__ map_pos,
+                                                             int* __restrict__ rstart,
+                                                             int* __restrict__ out_pos,
+                                                             uint32_t* __restrict__ total)
+{
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t s_tot;
+    const int tid = (int)threadIdx.x;
+    uint32_t carry = 0;
+    for (int b = 0; b < ndom; b += 1024) {
+        const int S = b + tid;
+        const uint32_t v = S < ndom ? (uint32_t)cnt[S] : 0u;
+        const uint32_t e = scan1024_excl(v, wsum);
+        if (S < ndom)
+            map_pos[S] = (int)(carry + e);
+        if (tid == 1023)
+            s_tot = e + v;
+        __syncthreads();
+        carry += s_tot;
+        __syncthreads();
+    }
+    if (tid == 0)
+        *total = carry;
+    carry = 0;
+    for (int b = 0; b < ndom; b += 1024) {
+        const int R = b + tid;
+        const uint32_t v = R < ndom ? (uint32_t)cnt[snd[R]] : 0u;
+        const uint32_t e = scan1024_excl(v, wsum);
+        if (R < ndom)
+            rstart[R] = (int)(carry + e);
+        if (tid == 1023)
+            s_tot = e + v;
+        __syncthreads();
+        carry += s_tot;
+        __syncthreads();
+    }
+    // (the barrier above also orders the rstart stores for the whole block)
+    for (int S = tid; S < ndom; S += 1024)
+        out_pos[S] = rstart[rcv[S]];
+}
+
 // Order the n = e - s global ids at out[s, e) (one cell, ~10 atoms):
 // insertion sort in registers for up to kCellRegs ids, loaded and stored
 // once, else in place.
@@ -651,6 +701,10 @@ struct SArgs {
     const int* out_pos;   // per S: first record of its region at R
     int* out_gid;
     float* out_xyz;
+    // the pulse's entries (pulse_offsets_kernel) and the room of map_out,
+    // out_gid and out_xyz: the write does nothing when they do not fit
+    const uint32_t* total;
+    uint32_t cap;
     // The pulse's counting units, sender-major: sender S's candidate home
     // cells (with the selection by cells, CArgs; hcprefix null otherwise),
     // then its tiles, at ubase[S] on; one exclusive scan of the units' counts
@@ -1010,6 +1064,8 @@ __global__ __launch_bounds__(256) void select_write_kernel(SArgs a, CArgs ca,
                                                            const int* __restrict__ tprefix,
                                                            const uint32_t* __restrict__ scan)
 {
+    if (*a.total > a.cap)  // the same for every block: the host grows the room and repeats
+        return;
     if ((int)blockIdx.x < ca.nblocks) {
         cell_write_block(ca, (int)blockIdx.x, a.ubase, scan);
         return;
@@ -1501,6 +1557,12 @@ void free_scratch(Plan* p)
         (void)hipFree(kv.first);
     p->kept.clear();
     p->kept_next = 0;
+    for (auto& kv : p->selbuf)
+        (void)hipFree(kv.first);
+    p->selbuf.clear();
+    if (p->counts_ready)
+        (void)hipEventDestroy(p->counts_ready);
+    p->counts_ready = nullptr;
 }
 
 void free_built(Plan* p)
@@ -2243,7 +2305,11 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
             ubase[S + 1] = ubase[S] + (by_cells ? hcprefix[S + 1] - hcprefix[S] : 0) +
                            (tprefix[S + 1] - tprefix[S]);
         const int U = ubase[D];
+        std::vector<int> snd(D);  // the sender of each receiver
+        for (int S = 0; S < D; S++)
+            snd[rcv[S]] = S;
         const size_t o_ubase = in.add(ubase), o_nhome = in.add(p->nhome);
+        const size_t o_rcv = in.add(rcv), o_snd = in.add(snd);
         char* d_in;
         DDH_HIP(in.send(sc, &d_in, s));
         const float* d_lo = (const float*)(d_in + o_lo);
@@ -2314,16 +2380,51 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         hipLaunchKernelGGL(select_totals_kernel, dim3(std::min(blocks(D), 1024)), dim3(256), 0, s,
                            a, d_tprefix, D, d_uscan, d_tbelow, d_cnt_send, d_cnt_split);
         DDH_HIP(hipGetLastError());
+        // write offsets on the device; the counts go to the host (one event)
+        // while the write runs into the room left by earlier builds
+        int* d_off;
+        DDH_HIP(sc.alloc(&d_off, 3 * (size_t)D + 1));
+        uint32_t* d_total = (uint32_t*)(d_off + 3 * (size_t)D);
+        hipLaunchKernelGGL(pulse_offsets_kernel, dim3(1), dim3(1024), 0, s, d_cnt_send,
+                           (const int*)(d_in + o_rcv), (const int*)(d_in + o_snd), D, d_off,
+                           d_off + D, d_off + 2 * (size_t)D, d_total);
+        DDH_HIP(hipGetLastError());
+        void* hcnt;
+        DDH_HIP(sc.pinned(&hcnt, 2 * sizeof(int) * (size_t)D));
+        DDH_HIP(hipMemcpyAsync(hcnt, d_cnt_send, 2 * sizeof(int) * D, hipMemcpyDeviceToHost, s));
+        if (!p->counts_ready)
+            DDH_HIP(hipEventCreateWithFlags(&p->counts_ready, hipEventDisableTiming));
+        DDH_HIP(hipEventRecord(p->counts_ready, s));
+        if (p->selbuf.size() < (size_t)P)
+            p->selbuf.resize((size_t)P, {nullptr, 0});
+        a.map_pos = d_off;
+        a.out_pos = d_off + 2 * (size_t)D;
+        a.total = d_total;
+        auto place = [&](int qq) {  // the pulse's outputs in its room
+            char* base = (char*)p->selbuf[qq].first;
+            const size_t cap = p->selbuf[qq].second;
+            mapp[qq] = (int*)base;
+            rgid[qq] = (int*)(base + sizeof(int) * cap);
+            rxyz[qq] = (float*)(base + 2 * sizeof(int) * cap);
+            a.cap = (uint32_t)cap;
+            a.map_out = mapp[qq];
+            a.out_gid = rgid[qq];
+            a.out_xyz = rxyz[qq];
+            ca.map_pos = a.map_pos;
+            ca.map_out = a.map_out;
+            ca.out_pos = a.out_pos;
+            ca.out_gid = a.out_gid;
+            ca.out_xyz = a.out_xyz;
+        };
+        place(q);
+        if (CT + T > 0 && p->selbuf[q].second > 0)
+            hipLaunchKernelGGL(select_write_kernel, dim3(CT + T), dim3(256), 0, s, a, ca, d_tprefix,
+                               d_uscan);
+        DDH_HIP(hipGetLastError());
         std::vector<int> cs(D), cp(D);
-        {
-            void* h;
-            DDH_HIP(sc.pinned(&h, 2 * sizeof(int) * (size_t)D));
-            int* hp = (int*)h;
-            DDH_HIP(hipMemcpyAsync(hp, d_cnt_send, 2 * sizeof(int) * D, hipMemcpyDeviceToHost, s));
-            DDH_HIP(hipStreamSynchronize(s));
-            std::memcpy(cs.data(), hp, sizeof(int) * (size_t)D);
-            std::memcpy(cp.data(), hp + D, sizeof(int) * (size_t)D);
-        }
+        DDH_HIP(hipEventSynchronize(p->counts_ready));
+        std::memcpy(cs.data(), hcnt, sizeof(int) * (size_t)D);
+        std::memcpy(cp.data(), (int*)hcnt + D, sizeof(int) * (size_t)D);
 
         // sizes -> offsets; region q of R lands after R's current slots
         mpos[q].assign(D, 0);
@@ -2354,31 +2455,24 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         total[q] = (int)mt;
         if (mt > INT32_MAX)
             return fail(DDH_ECAPACITY, "ddh_build_maps: a pulse exceeds 2^31 entries");
-        DDH_HIP(sc.alloc(&rgid[q], (size_t)mt));
-        DDH_HIP(sc.alloc(&rxyz[q], 3 * (size_t)mt));
-        DDH_HIP(sc.alloc(&mapp[q], (size_t)mt));
-        std::vector<int> opos(D);
-        for (int S = 0; S < D; S++)
-            opos[S] = rstart[rcv[S] * P + q];
-        blobs.emplace_back();
-        Blob& pos = blobs.back();
-        const size_t o_mpos = pos.add(mpos[q]), o_opos = pos.add(opos);
-        char* d_pos;
-        DDH_HIP(pos.send(sc, &d_pos, s));
-        a.map_pos = (const int*)(d_pos + o_mpos);
-        a.map_out = mapp[q];
-        a.out_pos = (const int*)(d_pos + o_opos);
-        a.out_gid = rgid[q];
-        a.out_xyz = rxyz[q];
-        ca.map_pos = a.map_pos;
-        ca.map_out = a.map_out;
-        ca.out_pos = a.out_pos;
-        ca.out_gid = a.out_gid;
-        ca.out_xyz = a.out_xyz;
-        if (CT + T > 0)
-            hipLaunchKernelGGL(select_write_kernel, dim3(CT + T), dim3(256), 0, s, a, ca, d_tprefix,
-                               d_uscan);
-        DDH_HIP(hipGetLastError());
+        // no room (the first build of the plan, or the pulse grew by more
+        // than the spare quarter): the write above did nothing; grow the
+        // room and write again
+        if ((size_t)mt > p->selbuf[q].second) {
+            const size_t cap = std::max<size_t>(256, (size_t)mt + (size_t)mt / 4);
+            DDH_HIP(hipStreamSynchronize(s));  // the skipped write has ended
+            if (p->selbuf[q].first)
+                DDH_HIP(hipFree(p->selbuf[q].first));
+            p->selbuf[q] = {nullptr, 0};
+            void* q_buf = nullptr;
+            DDH_HIP(hipMalloc(&q_buf, 5 * sizeof(int) * cap));
+            p->selbuf[q] = {q_buf, cap};
+            place(q);
+            if (CT + T > 0)
+                hipLaunchKernelGGL(select_write_kernel, dim3(CT + T), dim3(256), 0, s, a, ca,
+                                   d_tprefix, d_uscan);
+            DDH_HIP(hipGetLastError());
+        }
     }
 
     // ---- 4: final layout

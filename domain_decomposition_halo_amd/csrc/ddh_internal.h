@@ -254,6 +254,12 @@ struct Plan {
     std::vector<std::pair<void*, size_t>> scratch;  // build scratch, kept between builds
     std::vector<std::pair<void*, size_t>> pinned;   // pinned host staging of the build's
                                                     // uploads, kept between builds
+    // per pulse: the selection's output (map entries, received ids and
+    // positions; 20 bytes per entry) and its room in entries, sized from
+    // earlier builds with a quarter to spare, so a pulse's write is enqueued
+    // before its counts reach the host
+    std::vector<std::pair<void*, size_t>> selbuf;
+    hipEvent_t counts_ready = nullptr;  // the build's count read-back has landed
     bool build_failed = false;     // the last build returned an error midway
 
     // graph replay cache: (op, x, f, mode) -> executable graph
