@@ -27,8 +27,10 @@
 //      fl(x + L) or x in each component, exactly what the coordinate pass
 //      stores.
 //
-// The builder runs once per neighbour-search step; it waits for the stream
-// after every pulse to learn the sizes.
+// The builder runs once per neighbour-search step. It learns the sizes from
+// the host's read-back of each pulse's counts (waited for on an event, while
+// the pulse's write already runs on the device), and waits for the stream
+// after the sort and at the end.
 #pragma clang fp contract(off)
 
 #include <algorithm>
@@ -42,10 +44,10 @@ namespace {
 
 constexpr int kScanBlock = 1024;  // elements per scan block (4 per thread)
 constexpr int kSelTile = 1024;    // candidate slots per block of the slab selection
-// the partition sort: atoms per block of the domain partition, and the
-// largest domain count and cells per domain its LDS tables hold
-// atoms per thread of the partition's first two passes (256 threads): the
-// largest of 16, 4 and 1 that still gives at least kPartMinBlocks blocks
+// the partition sort: its first two passes (256 threads) take the largest
+// of 16, 4 and 1 atoms per thread that still gives at least kPartMinBlocks
+// blocks; its LDS tables hold up to kPartMaxDomains domains and
+// kPartMaxCells sort cells per domain
 constexpr int kPartMinBlocks = 512;
 constexpr int kPartMaxDomains = 2048;
 constexpr int kPartMaxCells = 4096;
