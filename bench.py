@@ -76,11 +76,39 @@ def graph_size(steps: int, graph_steps: int, min_replays: int = 5) -> int:
     return max(d for d in range(1, cap + 1) if steps % d == 0)
 
 
+def code_text(src: str) -> str:
+    """C++ source without its comments and with whitespace runs collapsed:
+    what the compiler sees, so that an edit of the comments alone keeps the
+    stored counters current. String literals are kept as written."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        ch = src[i]
+        if ch == '"' or ch == "'":
+            j = i + 1
+            while j < n and src[j] != ch:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(ch)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_hash() -> str:
+    """Hash of the code (comments aside) of the sources that decide what the
+    exchange launches read and write."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as fh:
-            h.update(fh.read())
+        with open(path, encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

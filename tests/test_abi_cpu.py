@@ -253,6 +253,19 @@ def test_bench_reports_counter_traffic_only_for_current_sources(tmp_path, monkey
     assert bench.read_traffic("pulse", "absent") is None
 
 
+def test_kernel_hash_ignores_comments_but_not_code():
+    # the stored counters stay current across comment edits of the kernel
+    # sources, and go stale on any change of the code itself
+    import bench
+    base = 'int f(int a) { return a + 1; } // one\nconst char* s = "x // y /* z */";\n'
+    assert bench.code_text(base) == bench.code_text(
+        "/* lead */ int f(int a) {\n  return a + 1;  // changed comment\n}\n"
+        'const char* s = "x // y /* z */";')
+    assert bench.code_text(base) != bench.code_text(base.replace("a + 1", "a + 2"))
+    assert bench.code_text(base) != bench.code_text(base.replace("x // y", "x / y"))
+    assert "/* z */" in bench.code_text(base)
+
+
 def test_bench_timed_graphs_leave_at_least_five_replays():
     # exactly --steps steps are timed, in graphs of G steps, with at least
     # five replays whenever there are five steps, so p10 and p90 can differ
