@@ -240,6 +240,46 @@ def test_random_decompositions(cfg):
         g.close()
 
 
+def lattice_configs(n, seed):
+    """Seeded random decompositions on a coarse lattice: 1-5 domains per
+    dimension, boxes of 2-8 nm per edge in steps of 1/8 nm, cutoffs up to
+    twice the narrowest domain in steps of 1/16 nm, cell sizes from 0.2 to
+    1.5 nm (any float), 300-5000 atoms on a 1/32 nm lattice, so atoms sit
+    exactly on domain boundaries, cell edges and slab thresholds."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        grid = tuple(int(g) for g in rng.integers(1, 6, size=3))
+        box = tuple(float(b) / 8.0 for b in rng.integers(16, 65, size=3))
+        wmin = min(box[d] / grid[d] for d in range(3))
+        rc = float(rng.integers(2, max(3, int(32 * wmin)))) / 16.0
+        cell = float(np.float32(rng.uniform(0.2, 1.5)))
+        try:
+            P = len(oracle.schedule(grid, box, rc))
+        except oracle.OracleError:
+            continue
+        if P > ddh.DDH_MAX_PULSES:
+            continue
+        out.append((grid, box, rc, cell, int(rng.integers(300, 5000)), int(rng.integers(1, 3))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", lattice_configs(16, 77))
+def test_lattice_decompositions(cfg):
+    """Random grids, dyadic boxes and cutoffs, random cell sizes and a 1/32 nm
+    lattice (ties everywhere the build compares): layout, maps, ids,
+    coordinates and forces bit-identical to the oracle with either home sort,
+    per-pulse and fused."""
+    grid, box, rc, cell, n, home_sort = cfg
+    x = W.lattice_positions(n, box, seed=n + 5, frac_bits=5)
+    ref = oracle.OraclePlan(x, grid, box, rc, cell=cell)
+    for mode in (ddh.DDH_MODE_PULSE, ddh.DDH_MODE_FUSED):
+        g = GpuPlan(x, grid, box, rc, cell=cell, mode=mode, home_sort=home_sort)
+        check_layout(g, ref)
+        check_steps(g, ref, n + 9, steps=1)
+        g.close()
+
+
 @pytest.mark.parametrize("mode,wave", [("fused", 0), ("fused", 1), ("pulse", 0)])
 def test_exchange_beside_a_compute_load(mode, wave, workload_plan):
     """The exchange on one stream while a chain of matrix products (the local
