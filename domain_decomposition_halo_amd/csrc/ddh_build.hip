@@ -331,56 +331,6 @@ __device__ uint32_t scan1024_excl(uint32_t v, uint32_t* wsum)
     return before + x - v;
 }
 
-// Write offsets of one pulse from the senders' counts: map_pos[S], S's first
-// entry in the pulse's maps (exclusive prefix over senders); out_pos[S], the
-// first record of S's region in the pulse's received storage (exclusive
-// prefix of the region sizes in receiver order: S sends to rcv[S], R receives
-// from snd[R]; rstart holds the prefix per receiver); and the pulse's total.
-// One block of 1024 threads.
-__global__ __launch_bounds__(1024) void pulse_offsets_kernel(const int* __restrict__ cnt,
-                                                             const int* __restrict__ rcv,
-                                                             const int* __restrict__ snd, int ndom,
-                                                             int* __restrict__ map_pos,
-                                                             int* __restrict__ rstart,
-                                                             int* __restrict__ out_pos,
-                                                             uint32_t* __restrict__ total)
-{
-    __shared__ uint32_t wsum[16];
-    __shared__ uint32_t s_tot;
-    const int tid = (int)threadIdx.x;
-    uint32_t carry = 0;
-    for (int b = 0; b < ndom; b += 1024) {
-        const int S = b + tid;
-        const uint32_t v = S < ndom ? (uint32_t)cnt[S] : 0u;
-        const uint32_t e = scan1024_excl(v, wsum);
-        if (S < ndom)
-            map_pos[S] = (int)(carry + e);
-        if (tid == 1023)
-            s_tot = e + v;
-        __syncthreads();
-        carry += s_tot;
-        __syncthreads();
-    }
-    if (tid == 0)
-        *total = carry;
-    carry = 0;
-    for (int b = 0; b < ndom; b += 1024) {
-        const int R = b + tid;
-        const uint32_t v = R < ndom ? (uint32_t)cnt[snd[R]] : 0u;
-        const uint32_t e = scan1024_excl(v, wsum);
-        if (R < ndom)
-            rstart[R] = (int)(carry + e);
-        if (tid == 1023)
-            s_tot = e + v;
-        __syncthreads();
-        carry += s_tot;
-        __syncthreads();
-    }
-    // (the barrier above also orders the rstart stores for the whole block)
-    for (int S = tid; S < ndom; S += 1024)
-        out_pos[S] = rstart[rcv[S]];
-}
-
 // Order the n = e - s global ids at out[s, e) (one cell, ~10 atoms):
 // insertion sort in registers for up to kCellRegs ids, loaded and stored
 // once, else in place.
@@ -604,28 +554,25 @@ __global__ __launch_bounds__(256) void scan_sums_kernel(const uint32_t* __restri
         bsum[blockIdx.x] = total;
 }
 
-__global__ __launch_bounds__(256) void scan_top_kernel(uint32_t* bsum, int nblk, uint32_t* out_total)
-{
-    __shared__ uint32_t sh[256];
-    uint32_t carry = 0;
-    for (int base = 0; base < nblk; base += 256) {
-        const int i = base + threadIdx.x;
-        const uint32_t v = i < nblk ? bsum[i] : 0u;
-        uint32_t total;
-        const uint32_t ex = block_scan_excl(v, sh, total);
-        if (i < nblk)
-            bsum[i] = carry + ex;
-        carry += total;
-    }
-    if (threadIdx.x == 0)
-        *out_total = carry;
-}
-
+// Second pass: each block first sums the totals of the blocks before it
+// (strided loads, then wavefront shuffles), then scans its own elements;
+// the last block also stores the grand total at out[n].
 __global__ __launch_bounds__(256) void scan_apply_kernel(const uint32_t* __restrict__ in, int64_t n,
                                                          const uint32_t* __restrict__ bsum,
                                                          uint32_t* __restrict__ out)
 {
     __shared__ uint32_t sh[256];
+    __shared__ uint32_t wred[4];
+    uint32_t part = 0;
+    for (int i = (int)threadIdx.x; i < (int)blockIdx.x; i += 256)
+        part += bsum[i];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        part += __shfl_down(part, o, 64);
+    if ((threadIdx.x & 63) == 0)
+        wred[threadIdx.x >> 6] = part;
+    __syncthreads();
+    const uint32_t pre = wred[0] + wred[1] + wred[2] + wred[3];
     const int64_t b0 = (int64_t)blockIdx.x * kScanBlock + 4ll * threadIdx.x;
     uint32_t v[4];
     uint32_t s = 0;
@@ -634,12 +581,14 @@ __global__ __launch_bounds__(256) void scan_apply_kernel(const uint32_t* __restr
         s += v[k];
     }
     uint32_t total;
-    uint32_t run = bsum[blockIdx.x] + block_scan_excl(s, sh, total);
+    uint32_t run = pre + block_scan_excl(s, sh, total);
     for (int k = 0; k < 4; k++) {
         if (b0 + k < n)
             out[b0 + k] = run;
         run += v[k];
     }
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0)
+        out[n] = pre + total;
 }
 
 // Every atom to its bucket's range, at its arrival rank (an arbitrary order
@@ -703,7 +652,7 @@ struct SArgs {
     const int* out_pos;   // per S: first record of its region at R
     int* out_gid;
     float* out_xyz;
-    // the pulse's entries (pulse_offsets_kernel) and the room of map_out,
+    // the pulse's entries (pulse_totals_kernel) and the room of map_out,
     // out_gid and out_xyz: the write does nothing when they do not fit
     const uint32_t* total;
     uint32_t cap;
@@ -1041,23 +990,69 @@ __global__ __launch_bounds__(256) void select_count_kernel(SArgs a, CArgs ca,
     }
 }
 
-// Per-sender totals from the tile scan: entries sent and entries below the
-// split (home slots).
-__global__ __launch_bounds__(256) void select_totals_kernel(SArgs a, const int* __restrict__ tprefix,
+// Per-sender totals of a pulse from the unit scan: entries sent (cnt_send)
+// and entries below the split (home slots: cnt_split). Then the write
+// offsets: map_pos[S], S's first entry in the pulse's maps (exclusive prefix
+// over senders); out_pos[S], the first record of S's region in the pulse's
+// received storage (exclusive prefix of the region sizes in receiver order:
+// S sends to rcv[S], R receives from snd[R]; rstart holds the prefix per
+// receiver); and the pulse's total. One block of 1024 threads.
+__global__ __launch_bounds__(1024) void pulse_totals_kernel(SArgs a, const int* __restrict__ tprefix,
                                                             int ndom,
                                                             const uint32_t* __restrict__ scan,
                                                             const uint32_t* __restrict__ below,
                                                             int* __restrict__ cnt_send,
-                                                            int* __restrict__ cnt_split)
+                                                            int* __restrict__ cnt_split,
+                                                            const int* __restrict__ rcv,
+                                                            const int* __restrict__ snd,
+                                                            int* __restrict__ map_pos,
+                                                            int* __restrict__ rstart,
+                                                            int* __restrict__ out_pos,
+                                                            uint32_t* __restrict__ total)
 {
-    for (int S = blockIdx.x * 256 + threadIdx.x; S < ndom; S += gridDim.x * 256) {
-        const int u0 = a.ubase[S];
-        cnt_send[S] = (int)(scan[a.ubase[S + 1]] - scan[u0]);
-        uint32_t bl = scan[u0 + home_units(a, S)] - scan[u0];  // home cells: all below
-        for (int b = tprefix[S]; b < tprefix[S + 1]; b++)
-            bl += below[b];
-        cnt_split[S] = (int)bl;
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t s_tot;
+    const int tid = (int)threadIdx.x;
+    uint32_t carry = 0;
+    for (int b = 0; b < ndom; b += 1024) {
+        const int S = b + tid;
+        uint32_t cs = 0;
+        if (S < ndom) {
+            const int u0 = a.ubase[S];
+            cs = scan[a.ubase[S + 1]] - scan[u0];
+            uint32_t bl = scan[u0 + home_units(a, S)] - scan[u0];  // home cells: all below
+            for (int t = tprefix[S]; t < tprefix[S + 1]; t++)
+                bl += below[t];
+            cnt_send[S] = (int)cs;
+            cnt_split[S] = (int)bl;
+        }
+        const uint32_t e = scan1024_excl(cs, wsum);
+        if (S < ndom)
+            map_pos[S] = (int)(carry + e);
+        if (tid == 1023)
+            s_tot = e + cs;
+        __syncthreads();
+        carry += s_tot;
+        __syncthreads();
     }
+    if (tid == 0)
+        *total = carry;
+    // (the barriers above order the cnt_send stores for the whole block)
+    carry = 0;
+    for (int b = 0; b < ndom; b += 1024) {
+        const int R = b + tid;
+        const uint32_t v = R < ndom ? (uint32_t)cnt_send[snd[R]] : 0u;
+        const uint32_t e = scan1024_excl(v, wsum);
+        if (R < ndom)
+            rstart[R] = (int)(carry + e);
+        if (tid == 1023)
+            s_tot = e + v;
+        __syncthreads();
+        carry += s_tot;
+        __syncthreads();
+    }
+    for (int S = tid; S < ndom; S += 1024)
+        out_pos[S] = rstart[rcv[S]];
 }
 
 // Ordered compaction of one tile: its selected slots go to the sender's map
@@ -1536,9 +1531,9 @@ int scan_exclusive(Scratch& sc, const uint32_t* in, int64_t n, uint32_t* out, hi
     DDH_HIP(sc.alloc(&bsum, (size_t)nblk + 1));
     if (nblk > 0)
         hipLaunchKernelGGL(scan_sums_kernel, dim3(nblk), dim3(256), 0, s, in, n, bsum);
-    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, s, bsum, nblk, out + n);
-    if (nblk > 0)
-        hipLaunchKernelGGL(scan_apply_kernel, dim3(nblk), dim3(256), 0, s, in, n, bsum, out);
+    // (one block when n is 0: it stores the total, 0)
+    hipLaunchKernelGGL(scan_apply_kernel, dim3(std::max(nblk, 1)), dim3(256), 0, s, in, n, bsum,
+                       out);
     DDH_HIP(hipGetLastError());
     return DDH_OK;
 }
@@ -2379,17 +2374,15 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         const int rcode = scan_exclusive(sc, d_ucnt, U, d_uscan, s);
         if (rcode)
             return rcode;
-        hipLaunchKernelGGL(select_totals_kernel, dim3(std::min(blocks(D), 1024)), dim3(256), 0, s,
-                           a, d_tprefix, D, d_uscan, d_tbelow, d_cnt_send, d_cnt_split);
-        DDH_HIP(hipGetLastError());
-        // write offsets on the device; the counts go to the host (one event)
-        // while the write runs into the room left by earlier builds
+        // totals and write offsets on the device; the counts go to the host
+        // (one event) while the write runs into the room left by earlier builds
         int* d_off;
         DDH_HIP(sc.alloc(&d_off, 3 * (size_t)D + 1));
         uint32_t* d_total = (uint32_t*)(d_off + 3 * (size_t)D);
-        hipLaunchKernelGGL(pulse_offsets_kernel, dim3(1), dim3(1024), 0, s, d_cnt_send,
-                           (const int*)(d_in + o_rcv), (const int*)(d_in + o_snd), D, d_off,
-                           d_off + D, d_off + 2 * (size_t)D, d_total);
+        hipLaunchKernelGGL(pulse_totals_kernel, dim3(1), dim3(1024), 0, s, a, d_tprefix, D,
+                           d_uscan, d_tbelow, d_cnt_send, d_cnt_split, (const int*)(d_in + o_rcv),
+                           (const int*)(d_in + o_snd), d_off, d_off + D, d_off + 2 * (size_t)D,
+                           d_total);
         DDH_HIP(hipGetLastError());
         void* hcnt;
         DDH_HIP(sc.pinned(&hcnt, 2 * sizeof(int) * (size_t)D));
