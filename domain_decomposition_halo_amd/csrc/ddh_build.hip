@@ -1615,7 +1615,7 @@ static void make_work_table(const Plan* p, bool waits, WorkTable& t)
         d.p = q;
         return d;
     };
-    const bool conservative = waits && !p->refined_waits;
+    const bool conservative = waits && !p->fused_refined;  // as set at the build
     // coordinates: the k-th slice of the independent head and of the
     // dependent tail; the chunk advances the counter of the region it fills
     auto xchunk = [&](int it, int k) {

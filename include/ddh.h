@@ -463,7 +463,9 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     results. */
 
 /* Set a tuning knob; takes effect at the next build (CHUNK, WAVE_CHUNKS,
-   HOME_SORT, HEADS_FIRST) or call. Library utility: the guide defines no such call.
+   HOME_SORT, HEADS_FIRST, REFINED_WAITS: the single launch's table keeps the
+   values of the build it belongs to, also when ddh_set_mode makes it later)
+   or call. Library utility: the guide defines no such call.
    Errors: DDH_EINVAL (unknown key or value out of range). */
 int ddh_tune(ddh_plan *plan, int32_t key, int64_t value);
 

@@ -939,6 +939,20 @@ def test_fused_table_made_at_mode_switch(k, first, workload_plan):
     g.close()
 
 
+@pytest.mark.parametrize("refined", [0, 1])
+def test_fused_table_keeps_the_build_settings(refined, workload_plan):
+    """The fused table made at a later mode switch uses the refined-waits
+    setting of its build, even when the setting changed in between: the
+    conservative masks, or the refined ones, never none."""
+    w, x, ref = workload_plan(3)
+    g = GpuPlan(x, mode=ddh.DDH_MODE_PULSE, refined=refined, **w.params())
+    g.plan.tune(ddh.DDH_TUNE_REFINED_WAITS, 1 - refined)
+    g.plan.set_mode(ddh.DDH_MODE_FUSED)
+    check_steps(g, ref, 90 + refined, steps=2, fused_step=True)
+    check_steps(g, ref, 92 + refined, steps=1)
+    g.close()
+
+
 CELL_CASES = [((2, 2, 2), (4.0, 4.0, 4.0), 1.0, 4000, 11),
               ((3, 2, 1), (6.0, 3.0, 2.5), 0.75, 5000, 12),
               ((4, 1, 2), (5.0, 2.0, 4.0), 1.5, 3000, 13)]
