@@ -627,26 +627,14 @@ __global__ void home_start_kernel(const uint32_t* __restrict__ start, const int*
 
 // ---- per-pulse selection
 
+struct STile;  // one slot tile of a pulse's selection (below)
+
 struct SArgs {
-    int p, d, P;
+    int d;
     float L_d, rc;
-    const int* tile_s;    // [b] sender of selection tile b
-    const float* xhome;   // home positions in slot order (float3)
-    const int* home_gid;
-    const int* home_start;
-    const int* nhome;
-    const int* roff_at;   // [S * P + q] first slot of S's region q
-    const int* rsize_at;  // [S * P + q] size of S's region q
-    const int* rstart;    // [S * P + q] index of S's region q in pulse q's storage
-    int* const* rgid;     // per pulse q: global ids of received records
-    float* const* rxyz;   // per pulse q: positions of received records (float3,
-                          // periodic shifts applied)
+    const STile* tiles;   // [b] selection tile b
     const float* lo;      // per S: lower boundary along d
-    const int* first;     // per S: candidate slot range
-    const int* last;
     const int* shiftbit;  // per S: 1 if S sits at index 0 of d
-    int* cnt_send;        // per S outputs of the counting kernel
-    int* cnt_split;
     const int* map_pos;   // per S: first entry of its map in the pulse buffer
     int* map_out;
     const int* out_pos;   // per S: first record of its region at R
@@ -668,30 +656,6 @@ struct SArgs {
 __device__ __forceinline__ int home_units(const SArgs& a, int S)
 {
     return a.hcprefix ? a.hcprefix[S + 1] - a.hcprefix[S] : 0;
-}
-
-// Candidate slot j of sender S: its global id and its coordinates. Home
-// slots read the slot-ordered home positions, received slots the records of
-// the pulse that delivered them, where the periodic shift is already applied
-// (the value the coordinate pass leaves in the slot).
-__device__ const float* resolve(const SArgs& a, int S, int j, int& gid)
-{
-    if (j < a.nhome[S]) {
-        const int r = a.home_start[S] + j;
-        gid = a.home_gid[r];
-        return a.xhome + 3ll * r;
-    }
-    for (int q = 0; q < a.p; q++) {
-        const int o = a.roff_at[S * a.P + q];
-        const int n = a.rsize_at[S * a.P + q];
-        if (j >= o && j < o + n) {
-            const int idx = a.rstart[S * a.P + q] + (j - o);
-            gid = a.rgid[q][idx];
-            return a.rxyz[q] + 3ll * idx;
-        }
-    }
-    gid = -1;
-    return nullptr;
 }
 
 // slot_gid and home_slot of the home atoms: work item b (of ndom * cpd,
@@ -733,20 +697,25 @@ __global__ __launch_bounds__(256) void fill_home_kernel(const int* __restrict__ 
 }
 
 // Slab selection of pulse p in tiles (the slab test of the pulse's dimension
-// d: fl(x_d - lo_d(S)) < rc): sender S's candidate slots
-// [first[S], last[S]) are cut into tiles of kSelTile slots, and tile b of the
-// pulse (tiles of S numbered from tprefix[S]) is one block. Counting and
-// writing by tile fills the GPU whatever the number of domains; an exclusive
-// scan of the tile counts (in S order, then slot order) gives every tile its
-// first entry in the pulse's map buffer, so the compaction stays in slot
-// order.
-__device__ __forceinline__ void tile_of(const SArgs& a, const int* tprefix, int b, int& S,
-                                        int& j0, int& j1)
-{
-    S = a.tile_s[b];  // one load, not a search of tprefix per block
-    j0 = a.first[S] + (b - tprefix[S]) * kSelTile;
-    j1 = min(j0 + kSelTile, a.last[S]);
-}
+// d: fl(x_d - lo_d(S)) < rc): each tile of the pulse (tiles of S numbered
+// from tprefix[S], in slot order) is one block. Counting and writing by tile
+// fills the GPU whatever the number of domains; an exclusive scan of the
+// tile counts (in S order, then slot order) gives every tile its first entry
+// in the pulse's map buffer, so the compaction stays in slot order.
+//
+// One slot tile of a pulse's selection: sender S's candidate slots
+// [j0, j1), all from one source (its home slots, home = 1, or the records
+// one earlier pulse delivered to it), whose global ids and positions (float3,
+// the periodic shift of the delivering pulse already applied: the value the
+// coordinate pass leaves in the slot) start at gid and xyz for slot j0. The
+// host cuts each sender's candidate range at its sources' bounds and then
+// into tiles of at most kSelTile slots, so a block reads its tile's source
+// once instead of resolving every slot.
+struct STile {
+    const int* gid;
+    const float* xyz;
+    int S, j0, j1, home;
+};
 
 // ---- slab selection of the home slots by cells (a dimension's first pulse)
 //
@@ -952,41 +921,31 @@ __global__ __launch_bounds__(256) void select_count_kernel(SArgs a, CArgs ca,
         return;
     }
     const int tb = (int)blockIdx.x - ca.nblocks;
-    __shared__ int s_send, s_split;
-    int S, j0, j1;
-    tile_of(a, tprefix, tb, S, j0, j1);
-    if (threadIdx.x == 0) {
+    __shared__ int s_send;
+    const STile t = a.tiles[tb];
+    const int S = t.S, n = t.j1 - t.j0;
+    if (threadIdx.x == 0)
         s_send = 0;
-        s_split = 0;
-    }
     __syncthreads();
-    int c = 0, bl = 0;
-    const int nh = a.nhome[S];
+    int c = 0;
+    const float lo = a.lo[S];
     // the tile's kSelTile / 256 slots per thread: every position load is
     // issued before the first test, so the loads are in flight together
     constexpr int U = kSelTile / 256;
     float v[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        const int j = j0 + (int)threadIdx.x + u * 256;
-        int gid;
-        const float* pos = j < j1 ? resolve(a, S, j, gid) : nullptr;
-        v[u] = pos ? pos[a.d] : __builtin_nanf("");
+        const int i = (int)threadIdx.x + u * 256;
+        v[u] = i < n ? t.xyz[3ll * i + a.d] : __builtin_nanf("");
     }
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int j = j0 + (int)threadIdx.x + u * 256;
-        if ((v[u] - a.lo[S]) < a.rc) {  // false for the NaN of a slot out of range
-            c++;
-            bl += j < nh;
-        }
-    }
+    for (int u = 0; u < U; u++)
+        c += (v[u] - lo) < a.rc;  // false for the NaN of a slot out of range
     atomicAdd(&s_send, c);
-    atomicAdd(&s_split, bl);
     __syncthreads();
     if (threadIdx.x == 0) {
         ucnt[a.ubase[S] + home_units(a, S) + (tb - tprefix[S])] = (uint32_t)s_send;
-        below[tb] = (uint32_t)s_split;
+        below[tb] = t.home ? (uint32_t)s_send : 0u;
     }
 }
 
@@ -1070,32 +1029,28 @@ __global__ __launch_bounds__(256) void select_write_kernel(SArgs a, CArgs ca,
     const int tb = (int)blockIdx.x - ca.nblocks;
     __shared__ int wave_tot[4];
     __shared__ int s_run;
-    int S, j0, j1;
-    tile_of(a, tprefix, tb, S, j0, j1);
+    const STile t = a.tiles[tb];
+    const int S = t.S, n = t.j1 - t.j0;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (threadIdx.x == 0)  // S's entries of the units before this tile
         s_run = (int)(scan[a.ubase[S] + home_units(a, S) + (tb - tprefix[S])] - scan[a.ubase[S]]);
     __syncthreads();
     const bool shift = a.shiftbit[S] != 0;
+    const float lo = a.lo[S];
     // as in the count: every slot's position load is issued before the
     // first test
     constexpr int U = kSelTile / 256;
-    const float* pp[U];
-    int gg[U];
     float v[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        const int j = j0 + (int)threadIdx.x + u * 256;
-        gg[u] = -1;
-        pp[u] = j < j1 ? resolve(a, S, j, gg[u]) : nullptr;
-        v[u] = pp[u] ? pp[u][a.d] : __builtin_nanf("");
+        const int i = (int)threadIdx.x + u * 256;
+        v[u] = i < n ? t.xyz[3ll * i + a.d] : __builtin_nanf("");
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        const int j = j0 + (int)threadIdx.x + u * 256;
-        const int gid = gg[u];
-        const float* pos = pp[u];
-        const bool pred = (v[u] - a.lo[S]) < a.rc;  // false for the NaN of a slot out of range
+        const int i = (int)threadIdx.x + u * 256;
+        const int j = t.j0 + i;
+        const bool pred = (v[u] - lo) < a.rc;  // false for the NaN of a slot out of range
         const unsigned long long bal = __ballot(pred);
         const int pre = __popcll(bal & ((1ull << lane) - 1ull));
         if (lane == 0)
@@ -1110,9 +1065,10 @@ __global__ __launch_bounds__(256) void select_write_kernel(SArgs a, CArgs ca,
         if (pred) {
             const int idx = off + pre;
             a.map_out[a.map_pos[S] + idx] = j;
-            a.out_gid[a.out_pos[S] + idx] = gid;
+            a.out_gid[a.out_pos[S] + idx] = t.gid[i];
             // the record as the receiver gets it: + L_d on component d when
             // the sender sits at index 0 of d
+            const float* pos = t.xyz + 3ll * i;
             float* o = a.out_xyz + 3ll * (a.out_pos[S] + idx);
             for (int c = 0; c < 3; c++) {
                 float r = pos[c];
@@ -2272,23 +2228,40 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
                 last[S] = first[S] + rsize_at[S * P + q - 1];
             }
         }
-        // tiles of kSelTile candidate slots, numbered sender by sender
+        // slot tiles, numbered sender by sender in slot order: each sender's
+        // candidate range cut at its sources' bounds (home slots, then the
+        // region of each earlier pulse), then into tiles of kSelTile slots
+        std::vector<STile> tiles;
         std::vector<int> tprefix((size_t)D + 1, 0);
-        for (int S = 0; S < D; S++)
-            tprefix[S + 1] = tprefix[S] + (last[S] - first[S] + kSelTile - 1) / kSelTile;
+        for (int S = 0; S < D; S++) {
+            tprefix[S] = (int)tiles.size();
+            auto add = [&](int s0, int s1, const int* gid0, const float* xyz0, int home) {
+                const int j_lo = std::max(s0, first[S]), j_hi = std::min(s1, last[S]);
+                for (int j0 = j_lo; j0 < j_hi; j0 += kSelTile) {
+                    STile t;
+                    t.S = S;
+                    t.j0 = j0;
+                    t.j1 = std::min(j0 + kSelTile, j_hi);
+                    t.home = home;
+                    t.gid = gid0 + (j0 - s0);
+                    t.xyz = xyz0 + 3ll * (j0 - s0);
+                    tiles.push_back(t);
+                }
+            };
+            add(0, p->nhome[S], p->d_home_gid + hs[S], d_xhome + 3ll * hs[S], 1);
+            for (int qq = 0; qq < q; qq++) {
+                const size_t it = (size_t)S * P + qq;
+                add(roff_at[it], roff_at[it] + rsize_at[it], rgid[qq] + rstart[it],
+                    rxyz[qq] + 3ll * rstart[it], 0);
+            }
+        }
+        tprefix[D] = (int)tiles.size();
         const int T = tprefix[D];
         // the pulse's small tables in one copy
         blobs.emplace_back();
         Blob& in = blobs.back();
-        const size_t o_lo = in.add(lo), o_first = in.add(first), o_last = in.add(last);
-        const size_t o_sbit = in.add(sbit), o_roff = in.add(roff_at), o_rsize = in.add(rsize_at);
-        const size_t o_rstart = in.add(rstart), o_rgid = in.add(rgid), o_rxyz = in.add(rxyz);
-        const size_t o_tprefix = in.add(tprefix);
-        std::vector<int> tile_s((size_t)std::max(T, 1), 0);
-        for (int S = 0; S < D; S++)
-            for (int b = tprefix[S]; b < tprefix[S + 1]; b++)
-                tile_s[b] = S;
-        const size_t o_tile_s = in.add(tile_s);
+        const size_t o_lo = in.add(lo), o_sbit = in.add(sbit), o_tprefix = in.add(tprefix);
+        const size_t o_tiles = in.add(tiles);
         const int CT = by_cells ? ctprefix[D] : 0;
         std::vector<int> ctile_s((size_t)std::max(CT, 1), 0);
         for (int S = 0; by_cells && S < D; S++)
@@ -2305,44 +2278,21 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         std::vector<int> snd(D);  // the sender of each receiver
         for (int S = 0; S < D; S++)
             snd[rcv[S]] = S;
-        const size_t o_ubase = in.add(ubase), o_nhome = in.add(p->nhome);
+        const size_t o_ubase = in.add(ubase);
         const size_t o_rcv = in.add(rcv), o_snd = in.add(snd);
         char* d_in;
         DDH_HIP(in.send(sc, &d_in, s));
         const float* d_lo = (const float*)(d_in + o_lo);
-        const int* d_first = (const int*)(d_in + o_first);
-        const int* d_last = (const int*)(d_in + o_last);
         const int* d_shiftbit = (const int*)(d_in + o_sbit);
-        const int* d_roff_at = (const int*)(d_in + o_roff);
-        const int* d_rsize_at = (const int*)(d_in + o_rsize);
-        const int* d_rstart = (const int*)(d_in + o_rstart);
-        int* const* d_rgid = (int* const*)(d_in + o_rgid);
-        float* const* d_rxyz = (float* const*)(d_in + o_rxyz);
         const int* d_tprefix = (const int*)(d_in + o_tprefix);
-        const int* d_tile_s = (const int*)(d_in + o_tile_s);
 
         SArgs a{};
-        a.p = q;
         a.d = d;
-        a.P = P;
         a.L_d = g.L[d];
         a.rc = g.rc;
-        a.tile_s = d_tile_s;
-        a.xhome = d_xhome;
-        a.home_gid = p->d_home_gid;
-        a.home_start = d_hs;
-        a.nhome = (const int*)(d_in + o_nhome);
-        a.roff_at = d_roff_at;
-        a.rsize_at = d_rsize_at;
-        a.rstart = d_rstart;
-        a.rgid = d_rgid;
-        a.rxyz = d_rxyz;
+        a.tiles = (const STile*)(d_in + o_tiles);
         a.lo = d_lo;
-        a.first = d_first;
-        a.last = d_last;
         a.shiftbit = d_shiftbit;
-        a.cnt_send = d_cnt_send;
-        a.cnt_split = d_cnt_split;
         a.ubase = (const int*)(d_in + o_ubase);
         CArgs ca{};
         if (by_cells) {
