@@ -190,12 +190,25 @@ constexpr uint32_t kPartNone = 0xFFFFFFFFu;  // code of an atom outside the box
 constexpr int kKeyBits = 12;                 // cell key bits of a code
 static_assert((1 << kKeyBits) >= kPartMaxCells, "cell keys must fit their bits");
 
-// Partition, pass 1: block b takes atoms [b T, (b + 1) T), T = 256 * ITEMS,
+// The partition's tile of work-group b of n. The hardware deals
+// work-groups to the eight XCDs in turn, so work-group b runs on XCD b % 8;
+// XCD k takes the k-th contiguous eighth of the tiles instead, so the
+// per-(domain, tile) counts of neighbouring tiles, which share cache lines,
+// are written and read back through one XCD's L2. A permutation of the
+// tiles: the results do not depend on it.
+__device__ __forceinline__ int xcd_tile(int b, int n)
+{
+    const int per = n / 8, rem = n % 8;  // XCD k takes per + (k < rem) tiles
+    const int k = b % 8;
+    return k * per + min(k, rem) + b / 8;
+}
+
+// Partition, pass 1: tile b takes atoms [b T, (b + 1) T), T = 256 * ITEMS,
 // with the geometry tables copied to LDS; stores each atom's code (domain <<
 // kKeyBits | cell key, kPartNone outside the box, reported on the error word) and
-// counts its atoms per domain in LDS. hist[d * nblk + b] receives block b's
+// counts its atoms per domain in LDS. hist[d * nblk + b] receives tile b's
 // count of domain d (domain-major, so one exclusive scan gives every
-// (domain, block) its first position).
+// (domain, tile) its first position).
 template <int ITEMS>
 __global__ __launch_bounds__(256) void part_count_kernel(const float* __restrict__ xg, int n_atoms,
                                                          AGeom g, int ndom, int nblk,
@@ -215,7 +228,8 @@ __global__ __launch_bounds__(256) void part_count_kernel(const float* __restrict
         const float* bd = g.b + g.boff[d];
         tab[k] = make_float4(bd[i], bd[i + 1], __int_as_float(g.ncell[k]), 0.0f);
     }
-    const int64_t a0 = (int64_t)blockIdx.x * (256 * ITEMS);
+    const int blk = xcd_tile((int)blockIdx.x, (int)gridDim.x);
+    const int64_t a0 = (int64_t)blk * (256 * ITEMS);
     // every position load of the thread is issued before the first test
     float v[ITEMS][3];
 #pragma unroll
@@ -247,7 +261,7 @@ __global__ __launch_bounds__(256) void part_count_kernel(const float* __restrict
         atomicOr(err, 1u);
     __syncthreads();
     for (int d = tid; d < ndom; d += 256)
-        hist[(int64_t)d * nblk + blockIdx.x] = cnt[d];
+        hist[(int64_t)d * nblk + blk] = cnt[d];
 }
 
 // Partition, pass 2: the block's atoms grouped by domain in LDS (at an LDS
@@ -268,7 +282,7 @@ __global__ __launch_bounds__(256) void part_scatter_kernel(const uint32_t* __res
     uint2* stage = (uint2*)sh;
     int* off = (int*)(sh + 2 * (256 * ITEMS));
     uint32_t* rnk = sh + 2 * (256 * ITEMS) + ndom;
-    const int tid = (int)threadIdx.x, blk = (int)blockIdx.x;
+    const int tid = (int)threadIdx.x, blk = xcd_tile((int)blockIdx.x, (int)gridDim.x);
     const int64_t a0 = (int64_t)blk * (256 * ITEMS);
     uint32_t c[ITEMS];
 #pragma unroll
