@@ -190,19 +190,6 @@ constexpr uint32_t kPartNone = 0xFFFFFFFFu;  // code of an atom outside the box
 constexpr int kKeyBits = 12;                 // cell key bits of a code
 static_assert((1 << kKeyBits) >= kPartMaxCells, "cell keys must fit their bits");
 
-// The partition's tile of work-group b of n. The hardware deals
-// work-groups to the eight XCDs in turn, so work-group b runs on XCD b % 8;
-// XCD k takes the k-th contiguous eighth of the tiles instead, so the
-// per-(domain, tile) counts of neighbouring tiles, which share cache lines,
-// are written and read back through one XCD's L2. A permutation of the
-// tiles: the results do not depend on it.
-__device__ __forceinline__ int xcd_tile(int b, int n)
-{
-    const int per = n / 8, rem = n % 8;  // XCD k takes per + (k < rem) tiles
-    const int k = b % 8;
-    return k * per + min(k, rem) + b / 8;
-}
-
 // Partition, pass 1: tile b takes atoms [b T, (b + 1) T), T = 256 * ITEMS,
 // with the geometry tables copied to LDS; stores each atom's code (domain <<
 // kKeyBits | cell key, kPartNone outside the box, reported on the error word) and
@@ -228,7 +215,7 @@ __global__ __launch_bounds__(256) void part_count_kernel(const float* __restrict
         const float* bd = g.b + g.boff[d];
         tab[k] = make_float4(bd[i], bd[i + 1], __int_as_float(g.ncell[k]), 0.0f);
     }
-    const int blk = xcd_tile((int)blockIdx.x, (int)gridDim.x);
+    const int blk = xcd_tile((int)blockIdx.x, (int)gridDim.x);  // neighbours share an L2
     const int64_t a0 = (int64_t)blk * (256 * ITEMS);
     // every position load of the thread is issued before the first test
     float v[ITEMS][3];
@@ -1792,7 +1779,7 @@ static int pulse_chunk(const Plan* p, bool step)
         return step ? 2048 : 1024;
     if (a >= 256)
         return 768;
-    return 256;
+    return kSmallChunk;
 }
 
 // A per-pulse launches' table of chunk size t.chunk, made on the device.

@@ -765,6 +765,8 @@ struct PArgs {
     const DChunk* fchunks;
     int32_t xbegin, nxb, fbegin;
     int32_t nb;       // chunks of the launch (blocks loop over them)
+    int32_t xgroup;   // neighbouring chunks per XCD turn (0: a contiguous
+                      // eighth of the chunks per XCD)
     float* stage;     // null, or the staging buffer of the host-orchestrated mode
     uint32_t* ctrl;
     uint32_t* flags;
@@ -864,7 +866,10 @@ __global__ __launch_bounds__(B) void pulse_kernel(PArgs a)
     // block's next chunk, then chunk b's stores, so the next chunk's first
     // loads are in flight while this one's records arrive.
     const int grid = (int)gridDim.x;
-    int b = (int)blockIdx.x;
+    // neighbouring chunks share an XCD: a contiguous eighth of them per XCD
+    // where launches are latency-bound (small chunks), else groups of four
+    // dealt in turn, so every XCD takes coordinate and force chunks alike
+    int b = a.xgroup ? xcd_group<4>((int)blockIdx.x, grid) : xcd_tile((int)blockIdx.x, grid);
     DChunk c;
     int jr[E];
     const I* m = nullptr;
@@ -1175,6 +1180,7 @@ int launch_pulse(const Plan* p, float* x, float* f, const WorkTable& t, int xb, 
     a.pad = !use_pad_maps(p) ? nullptr : narrow ? (const void*)t.d_pad16 : (const void*)t.d_pad;
     a.maps = narrow ? (const void*)p->d_maps16 : (const void*)p->d_maps;
     a.chunk = t.chunk;
+    a.xgroup = t.chunk > kSmallChunk ? 4 : 0;
     // pad slots: coordinate chunk k owns slot k; a force chunk uses the slot
     // of the coordinate chunk of the same map slice (the tables slice every
     // map alike, and list a pulse's chunks in the same order in both passes)

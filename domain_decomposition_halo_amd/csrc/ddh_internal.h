@@ -150,6 +150,7 @@ struct WorkTable {
     int32_t* d_pad = nullptr;
     uint16_t* d_pad16 = nullptr;
 };
+constexpr int kSmallChunk = 256;   // per-pulse chunk where launches are latency-bound
 constexpr int kPadTail = 4096;      // >= entries per round of any block
 
 // The passes an exchange call runs.
@@ -266,6 +267,32 @@ struct Plan {
     hipStream_t capture_stream = nullptr;
     std::map<std::tuple<int, void*, void*, int>, hipGraphExec_t> graphs;
 };
+
+// Work item of work-group b of n, dealt so that neighbouring items share an
+// XCD: the hardware deals work-groups to the eight XCDs in turn (work-group b
+// runs on XCD b % 8), and XCD k takes the k-th contiguous eighth of the
+// items instead, so items whose data share cache lines go through one L2. A
+// permutation of [0, n): results do not depend on it.
+__device__ __forceinline__ int xcd_tile(int b, int n)
+{
+    const int per = n / 8, rem = n % 8;  // XCD k takes per + (k < rem) items
+    const int k = b % 8;
+    return k * per + (k < rem ? k : rem) + b / 8;
+}
+
+// Work item of work-group b of n when groups of G neighbouring items should
+// share an XCD but every XCD should still see items from the whole range:
+// the XCDs take groups of G items in turn (work-groups in whole rounds of
+// 8 * G; the rest keep their own index). A permutation of [0, n).
+template <int G>
+__device__ __forceinline__ int xcd_group(int b, int n)
+{
+    constexpr int span = 8 * G;
+    if (b >= n / span * span)
+        return b;
+    const int i = b / 8;  // the i-th work-group of XCD b % 8
+    return i / G * span + b % 8 * G + i % G;
+}
 
 // error reporting (thread-local text)
 int fail(int code, const std::string& msg);
