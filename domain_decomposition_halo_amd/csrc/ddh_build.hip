@@ -1766,15 +1766,39 @@ static int fused_chunk(const Plan* p) { return p->wave_chunks ? 1024 : 8192; }
 //     768 (1M: 17.15, 512: 17.15, 1024: 17.44; 384k: 22.85, 1024: 22.82, 512:
 //     23.46, the former one chunk per map of up to 2752 entries: 27.4);
 //   - smaller (96k atoms on 2x2x2, a = 93): 256 (8.95; 128: 9.32, 512: 9.18).
+// But first, for the table of step calls, where some chunk size of at most
+// 4096 entries keeps every launch at one chunk per compute unit or fewer,
+// the smallest such multiple of 256: a launch then takes as long as its
+// largest chunk (maps are split into equal parts). 1M: 2816 (16.1 us per
+// step; 768: 17.1; 2560, whose launch of the Z coordinates and X forces has
+// 320 chunks: 19.9; 3584, which leaves maps of 3499 entries whole: 18.5).
+// 12M and 384k have more maps than compute units per launch and keep the
+// rule below. Single-pass launches carry half the work and keep it too
+// (the same rule for them: 1M coordinates 10.9 -> 11.4 us at 1536, 384k
+// 15.7 -> 16.2 at 2816).
 // step: the table of step calls (both passes share each launch), else the
 // one of single-pass calls.
 static int pulse_chunk(const Plan* p, bool step)
 {
-    const int P = p->g.P;
+    const int P = p->g.P, D = p->g.ndom;
+    const int ncu = std::max(1, p->n_cu);
+    auto chunks = [&](int q, int ch) {  // chunks of pulse q's maps (one at least each)
+        int64_t c = 0;
+        for (int S = 0; S < D; S++)
+            c += std::max(1, (p->send[(size_t)S * P + q] + ch - 1) / ch);
+        return c;
+    };
+    for (int ch = kSmallChunk; step && ch <= 4096 && P > 0; ch += 256) {
+        int64_t most = 0;  // chunks of the table's largest launch
+        for (int q = 0; q < P; q++)
+            most = std::max(most, chunks(q, ch) + chunks(P - 1 - q, ch));
+        if (most <= ncu)
+            return ch;
+    }
     int64_t total = 0;
     for (int32_t n : p->send)
         total += n;
-    const int64_t a = P > 0 ? total / P / std::max(1, p->n_cu) : 0;
+    const int64_t a = P > 0 ? total / P / ncu : 0;
     if (a >= 4096)
         return step ? 2048 : 1024;
     if (a >= 256)
