@@ -1759,9 +1759,11 @@ static int fused_chunk(const Plan* p) { return p->wave_chunks ? 1024 : 8192; }
 // entries per lane and round), from the average entries of a pulse per
 // compute unit, a. Measured on MI355X (graph replay, us per step; each pass
 // alone in brackets):
-//   - a >= 4096 (12M atoms on 8x8x8 domains, a = 11000): steps 2048 (111.0;
-//     1024: 118.0, 1536: 114.7, 2560: 117.8, 3072: 115.4); a pass alone 1024
-//     (coordinates 47.8 against 49.0 at 2048; forces 68.0 against 67.9);
+//   - a >= 4096 (12M atoms on 8x8x8 domains, a = 11000): 2048, for steps
+//     (111.0; 1024: 118.0, 1536: 114.7, 2560: 117.8, 3072: 115.4) and, since
+//     neighbouring chunks are dealt to one XCD, for a pass alone too (one
+//     table for both: coordinates 48.3 against 48.9 at 1024, forces 68.1
+//     against 68.9);
 //   - a >= 256 (1M atoms on 4x4x4, a = 1080; 384k atoms on 16x4x4, a = 1050):
 //     768 (1M: 17.15, 512: 17.15, 1024: 17.44; 384k: 22.85, 1024: 22.82, 512:
 //     23.46, the former one chunk per map of up to 2752 entries: 27.4);
@@ -1800,7 +1802,7 @@ static int pulse_chunk(const Plan* p, bool step)
         total += n;
     const int64_t a = P > 0 ? total / P / ncu : 0;
     if (a >= 4096)
-        return step ? 2048 : 1024;
+        return 2048;
     if (a >= 256)
         return 768;
     return kSmallChunk;
