@@ -42,9 +42,17 @@
  *    n_d - 1 pulses, is rejected (the halo would wrap onto itself);
  *  - boundaries b_d[i] = fl32(L_d * i / n_d) evaluated in double, intervals
  *    half-open [b_d[i], b_d[i+1]);
- *  - home atoms are ordered by sort cell, then by global id; the cell index
- *    in a dimension is floor(fl(fl(x - lo) * fl32(1/c))) clamped to
- *    [0, ceil((hi - lo) / c) - 1], key = cx + ncx * (cy + ncy * cz);
+ *  - home atoms are ordered by sort cell, then by class, then by global id;
+ *    the cell index in a dimension is floor(fl(fl(x - lo) * fl32(1/c)))
+ *    clamped to [0, ceil((hi - lo) / c) - 1], key = cx + ncx * (cy + ncy * cz)
+ *    (c <= 0: one cell per domain, index 0);
+ *  - the class orders a cell's atoms by the first pulses that send them:
+ *    m = sum over d of 2^d [fl(x_d - lo_d) < rc], the slab test of the first
+ *    pulse of d; class = 7 - m (atoms that pass first) when cx - px is even,
+ *    px = floor(fl(rc * fl32(1/c))) the x index of the cell holding the cut,
+ *    else class = m (atoms that pass last). So a cell that a slab cuts keeps
+ *    the atoms that pulse sends together, and along x such runs meet across
+ *    neighbouring cells, also with the wholly selected cells below the cut;
  *  - force add order: pulses in reverse global order, plain fp32 adds in place.
  *
  * Layout: domain D = ix + nx * (iy + ny * iz) owns the slots
@@ -76,7 +84,7 @@ typedef struct {
     int n[3];            /* domains per dimension; 0 = X, 1 = Y, 2 = Z */
     float L[3];          /* box edges (fp32) */
     float rc;            /* cutoff */
-    float cell;          /* sort-cell edge; <= 0 sorts by global id only */
+    float cell;          /* sort-cell edge; <= 0: one cell per domain */
     float *b[3];         /* boundaries, n[d] + 1 values per dimension */
     int ndom;
     int P;               /* total number of pulses */
@@ -142,6 +150,7 @@ static int grow(void **p, size_t nbytes)
 
 typedef struct {
     int64_t key;
+    int cls;
     int gid;
 } keyed;
 
@@ -150,6 +159,8 @@ static int cmp_keyed(const void *a, const void *b)
     const keyed *p = (const keyed *)a, *q = (const keyed *)b;
     if (p->key != q->key)
         return p->key < q->key ? -1 : 1;
+    if (p->cls != q->cls)
+        return p->cls < q->cls ? -1 : 1;
     return p->gid < q->gid ? -1 : (p->gid > q->gid ? 1 : 0);
 }
 
@@ -338,6 +349,7 @@ static int assign_home(oplan *o, const float *xg, int n_atoms)
         members[dom_of[a]][fill[dom_of[a]]++] = a;
 
     float inv_c = o->cell > 0.0f ? (float)(1.0 / (double)o->cell) : 0.0f;
+    const int px = (int)floorf(o->rc * inv_c);
     for (int D = 0; D < o->ndom; D++) {
         int c[3];
         dom_coords(o, D, c);
@@ -368,6 +380,11 @@ static int assign_home(oplan *o, const float *xg, int n_atoms)
             for (int d = 0; d < 3; d++)
                 ci[d] = cell_of(xg[3 * (size_t)a + d], lo[d], inv_c, nc[d]);
             list[j].key = (int64_t)ci[0] + (int64_t)nc[0] * ((int64_t)ci[1] + (int64_t)nc[1] * ci[2]);
+            int m = 0;
+            for (int d = 0; d < 3; d++)
+                if (xg[3 * (size_t)a + d] - lo[d] < o->rc)
+                    m |= 1 << d;
+            list[j].cls = ((ci[0] - px) % 2 == 0) ? 7 - m : m;
             list[j].gid = a;
         }
         qsort(list, (size_t)m, sizeof(keyed), cmp_keyed);

@@ -82,24 +82,66 @@ def test_bruteforce_halo_exact(grid, box, rc, n):
 
 
 @pytest.mark.parametrize("grid,box,rc,n", DYADIC)
-def test_home_order_is_cell_then_id(grid, box, rc, n):
+def test_home_order_is_cell_class_then_id(grid, box, rc, n):
+    """Home order from its definition, in exact arithmetic (dyadic box, lattice
+    positions): sort cell, then the class of the first pulses that send the
+    atom (the cells' selected atoms together, first or last by the parity of
+    the x index counted from the cell that holds the cut), then global id."""
     x = W.lattice_positions(n, box, seed=3 + n)
     plan = oracle.OraclePlan(x, grid, box, rc, cell=0.5)
     bounds = _bounds(grid, box)
+    px = math.floor(rc / 0.5)
     for D in range(plan.n_domains):
         c = (D % grid[0], (D // grid[0]) % grid[1], D // (grid[0] * grid[1]))
         b, nh = int(plan.base[D]), int(plan.nhome[D])
         ids = plan.slot_ids[b:b + nh]
         xs = x[ids].astype(np.float64)
         ci, nc = [], []
+        sent = np.zeros(nh, dtype=np.int64)
         for d in range(3):
             lo, hi = bounds[d][c[d]], bounds[d][c[d] + 1]
             ncd = max(1, math.ceil((hi - lo) / 0.5))
             ci.append(np.minimum(np.floor((xs[:, d] - lo) / 0.5), ncd - 1).astype(np.int64))
             nc.append(ncd)
+            sent |= (xs[:, d] - lo < rc).astype(np.int64) << d
         key = ci[0] + nc[0] * (ci[1] + nc[1] * ci[2])
-        order = np.lexsort((ids, key))
+        cls = np.where((ci[0] - px) % 2 == 0, 7 - sent, sent)
+        order = np.lexsort((ids, cls, key))
         assert np.array_equal(order, np.arange(nh))
+
+
+def test_cut_cells_keep_each_pulse_contiguous():
+    """In every cell that one slab cuts, the atoms that dimension's first pulse
+    sends form one run, at the cell's start when the cell's x index has the parity of the
+    cut's cell and at its end otherwise, so a cell below the cut along x runs
+    straight into the sent part of the next."""
+    grid, box, rc = (2, 2, 2), (8.0, 8.0, 8.0), 1.25
+    x = W.lattice_positions(4000, box, seed=41)
+    plan = oracle.OraclePlan(x, grid, box, rc, cell=0.5)
+    cut_cells = 0
+    for D in range(plan.n_domains):
+        c = (D % 2, (D // 2) % 2, D // 4)
+        lo = [4.0 * c[d] for d in range(3)]
+        b, nh = int(plan.base[D]), int(plan.nhome[D])
+        xs = x[plan.slot_ids[b:b + nh]].astype(np.float64)
+        cell = np.floor((xs - np.array(lo)) / 0.5).astype(np.int64)
+        key = cell[:, 0] + 8 * (cell[:, 1] + 8 * cell[:, 2])
+        starts = np.flatnonzero(np.r_[True, key[1:] != key[:-1]])
+        ends = np.r_[starts[1:], nh]
+        for s, e in zip(starts, ends):
+            cx = cell[s, 0]
+            sent = [xs[s:e, d] - lo[d] < rc for d in range(3)]
+            cut = [d for d in range(3) if sent[d].any() and not sent[d].all()]
+            if len(cut) != 1:
+                continue  # where two slabs cut a cell only the higher dimension's run is whole
+            cut_cells += 1
+            hit = np.flatnonzero(sent[cut[0]])
+            assert hit[-1] - hit[0] + 1 == len(hit), "a pulse's atoms split inside a cell"
+            if (cx - 2) % 2 == 0:
+                assert hit[0] == 0
+            else:
+                assert hit[-1] == e - s - 1
+    assert cut_cells > 100
 
 
 @pytest.mark.parametrize("grid,box,rc,n", DYADIC)
