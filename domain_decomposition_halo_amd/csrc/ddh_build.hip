@@ -11,12 +11,14 @@
 //   1. every atom goes to the domain whose half-open interval [b_d[i],
 //      b_d[i+1]) holds it in each dimension (fp32 compares decide);
 //   2. home atoms of a domain are ordered by sort cell (key cx + ncx * (cy +
-//      ncy * cz)) and then by global id: a partition of the atoms by domain
+//      ncy * cz)), then by class (the first pulses' slab tests, see
+//      home_class: a cell that a slab cuts keeps the atoms that pulse sends
+//      together), then by global id: a partition of the atoms by domain
 //      (block histograms in LDS, one scan, a scatter with LDS counters), a
 //      counting sort of each domain's atoms by cell in LDS, then each cell
-//      sorted by id; or, where a domain or a cell table is too large for
-//      LDS, a counting sort over all cells of all domains with device
-//      atomics, made deterministic the same way;
+//      sorted by class and id; or, where a domain or a cell table is too
+//      large for LDS, a counting sort over all cells of all domains with
+//      device atomics, made deterministic the same way;
 //   3. pulse p along d, sender S: candidates are S's home slots and every
 //      slot it received in earlier pulses (first pulse of d), or the slots it
 //      received in the previous pulse of d (later pulses); slot j is selected
@@ -34,6 +36,7 @@
 #pragma clang fp contract(off)
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 
 #include "ddh_internal.h"
@@ -61,6 +64,8 @@ struct AGeom {
     int n[3];
     float L[3];
     float inv_c;
+    float rc;
+    int px;               // x index of the cell holding the cut, floor(fl(rc * inv_c))
     const float* b;       // boundaries, dimension d at boff[d]
     int boff[3];
     const int* ncell;     // cells across domain index i of d, at noff[d]
@@ -68,14 +73,30 @@ struct AGeom {
     const int* cellbase;  // first bucket of each domain
 };
 
-// Domain and sort cell of one position from the boundary and cell-count
-// tables b and nc (laid out as in AGeom: dimension d at boff[d] and noff[d]);
-// false when a coordinate lies outside [0, L) or is not a number. key is the
-// cell's index inside the domain, x fastest.
+// An atom's class inside its sort cell, from the slab tests of the first
+// pulses (bit d: fl(x_d - lo_d) < rc, the selection's own compare): 7 - m in
+// cells whose x index has the parity of px (the atoms the slabs send first),
+// m in the others (last). Home atoms are ordered by cell, class, global id,
+// so a cell that one slab cuts keeps that pulse's atoms in one run, and the
+// runs of neighbouring cells along x meet.
+__device__ __forceinline__ int home_class(const float u[3], int cx, const AGeom& g)
+{
+    int m = 0;
+#pragma unroll
+    for (int d = 0; d < 3; d++)
+        m |= (u[d] < g.rc ? 1 : 0) << d;
+    return ((cx - g.px) & 1) == 0 ? 7 - m : m;
+}
+
+// Domain, sort cell and class of one position from the boundary and
+// cell-count tables b and nc (laid out as in AGeom: dimension d at boff[d]
+// and noff[d]); false when a coordinate lies outside [0, L) or is not a
+// number. key is the cell's index inside the domain, x fastest.
 __device__ __forceinline__ bool locate(const float v[3], const AGeom& g, const float* b,
-                                       const int* nc, int& dom, int& key)
+                                       const int* nc, int& dom, int& key, int& cls)
 {
     int ci[3], cc[3], ncd[3];
+    float u[3];
 #pragma unroll
     for (int d = 0; d < 3; d++) {
         if (!(v[d] >= 0.0f && v[d] < g.L[d]))
@@ -90,9 +111,10 @@ __device__ __forceinline__ bool locate(const float v[3], const AGeom& g, const f
             i++;
         ci[d] = i;
         ncd[d] = nc[g.noff[d] + i];
+        u[d] = v[d] - bd[i];
         int c = 0;
         if (ncd[d] > 1) {
-            const float t = (v[d] - bd[i]) * g.inv_c;
+            const float t = u[d] * g.inv_c;
             c = (int)floorf(t);
             c = c < 0 ? 0 : (c > ncd[d] - 1 ? ncd[d] - 1 : c);
         }
@@ -100,6 +122,7 @@ __device__ __forceinline__ bool locate(const float v[3], const AGeom& g, const f
     }
     dom = ci[0] + g.n[0] * (ci[1] + g.n[1] * ci[2]);
     key = cc[0] + ncd[0] * (cc[1] + ncd[1] * cc[2]);
+    cls = home_class(u, cc[0], g);
     return true;
 }
 
@@ -109,7 +132,7 @@ __device__ __forceinline__ bool locate(const float v[3], const AGeom& g, const f
 // one LDS read per dimension decides it (the three issued together); the
 // search steps run only when it does not. Same results as locate().
 __device__ __forceinline__ bool locate_tab(const float v[3], const AGeom& g, const float4* tab,
-                                           int& dom, int& key)
+                                           int& dom, int& key, int& cls)
 {
     int est[3];
     float4 e[3];
@@ -123,6 +146,7 @@ __device__ __forceinline__ bool locate_tab(const float v[3], const AGeom& g, con
         e[d] = tab[g.noff[d] + i];
     }
     int ci[3], cc[3], ncd[3];
+    float u[3];
 #pragma unroll
     for (int d = 0; d < 3; d++) {
         if (!(v[d] >= 0.0f && v[d] < g.L[d]))
@@ -143,23 +167,31 @@ __device__ __forceinline__ bool locate_tab(const float v[3], const AGeom& g, con
         }
         ci[d] = i;
         ncd[d] = __float_as_int(t.z);
+        u[d] = v[d] - t.x;
         int c = 0;
         if (ncd[d] > 1) {
-            const float u = (v[d] - t.x) * g.inv_c;
-            c = (int)floorf(u);
+            c = (int)floorf(u[d] * g.inv_c);
             c = c < 0 ? 0 : (c > ncd[d] - 1 ? ncd[d] - 1 : c);
         }
         cc[d] = c;
     }
     dom = ci[0] + g.n[0] * (ci[1] + g.n[1] * ci[2]);
     key = cc[0] + ncd[0] * (cc[1] + ncd[1] * cc[2]);
+    cls = home_class(u, cc[0], g);
     return true;
 }
+
+// A home atom's sort value inside its cell: class in the top bits, global id
+// below (at most 2^29 atoms), so one unsigned compare orders by class, then
+// id; the per-cell sort stores the id alone.
+constexpr int kClassShift = 29;
+constexpr uint32_t kIdMask = (1u << kClassShift) - 1u;
 
 // Counting form of the assignment: each atom's bucket (its domain's first
 // bucket plus its cell key, -1 outside the box) and its arrival rank in the
 // bucket from the count's atomic add (an arbitrary order inside the bucket,
-// which the per-cell sort by global id then fixes).
+// which the per-cell sort by class and global id then fixes), with its class
+// in the rank's top bits.
 __global__ __launch_bounds__(256) void assign_count_kernel(const float* __restrict__ xg,
                                                            int n_atoms, AGeom g,
                                                            int* __restrict__ bucket,
@@ -171,15 +203,15 @@ __global__ __launch_bounds__(256) void assign_count_kernel(const float* __restri
     if (a >= n_atoms)
         return;
     const float v[3] = {xg[3ll * a], xg[3ll * a + 1], xg[3ll * a + 2]};
-    int dom, key;
-    if (!locate(v, g, g.b, g.ncell, dom, key)) {
+    int dom, key, cls;
+    if (!locate(v, g, g.b, g.ncell, dom, key, cls)) {
         bucket[a] = -1;
         atomicOr(err, 1u);
         return;
     }
     const int bk = g.cellbase[dom] + key;
     bucket[a] = bk;
-    rank[a] = atomicAdd(count + bk, 1u);
+    rank[a] = atomicAdd(count + bk, 1u) | ((uint32_t)cls << kClassShift);
 }
 
 // ---- partition sort of the home atoms (LDS counters only)
@@ -188,11 +220,17 @@ __device__ uint32_t block_scan_excl(uint32_t v, uint32_t* sh, uint32_t& total);
 
 constexpr uint32_t kPartNone = 0xFFFFFFFFu;  // code of an atom outside the box
 constexpr int kKeyBits = 12;                 // cell key bits of a code
+constexpr int kDomBits = 11;                 // domain bits of a code, above the key
+constexpr uint32_t kKeyMask = (1u << kKeyBits) - 1u;
+constexpr uint32_t kDomMask = (1u << kDomBits) - 1u;
 static_assert((1 << kKeyBits) >= kPartMaxCells, "cell keys must fit their bits");
+static_assert((1 << kDomBits) >= kPartMaxDomains, "domains must fit their bits");
+static_assert(kKeyBits + kDomBits + 3 < 32, "a code must differ from kPartNone");
 
 // Partition, pass 1: tile b takes atoms [b T, (b + 1) T), T = 256 * ITEMS,
-// with the geometry tables copied to LDS; stores each atom's code (domain <<
-// kKeyBits | cell key, kPartNone outside the box, reported on the error word) and
+// with the geometry tables copied to LDS; stores each atom's code (class,
+// domain, cell key from the top; kPartNone outside the box, reported on the
+// error word) and
 // counts its atoms per domain in LDS. hist[d * nblk + b] receives tile b's
 // count of domain d (domain-major, so one exclusive scan gives every
 // (domain, tile) its first position).
@@ -233,10 +271,11 @@ __global__ __launch_bounds__(256) void part_count_kernel(const float* __restrict
     for (int i = 0; i < ITEMS; i++) {
         const int64_t a = a0 + (int64_t)i * 256 + tid;
         if (a < n_atoms) {
-            int dom, key;
+            int dom, key, cls;
             uint32_t c = kPartNone;
-            if (locate_tab(v[i], g, tab, dom, key)) {
-                c = ((uint32_t)dom << kKeyBits) | (uint32_t)key;
+            if (locate_tab(v[i], g, tab, dom, key, cls)) {
+                c = ((uint32_t)cls << (kKeyBits + kDomBits)) | ((uint32_t)dom << kKeyBits) |
+                    (uint32_t)key;
                 atomicAdd(&cnt[dom], 1u);
             } else {
                 bad = 1u;
@@ -253,10 +292,10 @@ __global__ __launch_bounds__(256) void part_count_kernel(const float* __restrict
 
 // Partition, pass 2: the block's atoms grouped by domain in LDS (at an LDS
 // counter's rank: any order inside a domain's share, which the per-domain
-// cell sort and the per-cell sort by id then fix), then written out in that
-// order, so each domain's share leaves as one contiguous run. rec[pos] gets
-// (cell key inside the domain, global id) at the (domain, block)'s first
-// position from hscan plus the rank.
+// cell sort and the per-cell sort by class and id then fix), then written out
+// in that order, so each domain's share leaves as one contiguous run.
+// rec[pos] gets (cell key inside the domain, class << kClassShift | global
+// id) at the (domain, block)'s first position from hscan plus the rank.
 template <int ITEMS>
 __global__ __launch_bounds__(256) void part_scatter_kernel(const uint32_t* __restrict__ code,
                                                            int n_atoms,
@@ -298,15 +337,16 @@ __global__ __launch_bounds__(256) void part_scatter_kernel(const uint32_t* __res
 #pragma unroll
     for (int i = 0; i < ITEMS; i++) {
         if (c[i] != kPartNone) {
-            const uint32_t r = atomicAdd(&rnk[c[i] >> kKeyBits], 1u);
+            const uint32_t r = atomicAdd(&rnk[(c[i] >> kKeyBits) & kDomMask], 1u);
             stage[r] = make_uint2(c[i], (uint32_t)(a0 + (int64_t)i * 256 + tid));
         }
     }
     __syncthreads();
     for (uint32_t r = tid; r < total; r += 256) {
         const uint2 e = stage[r];
-        const int d = (int)(e.x >> kKeyBits);
-        rec[(int64_t)off[d] + r] = make_uint2(e.x & ((1u << kKeyBits) - 1u), e.y);
+        const int d = (int)((e.x >> kKeyBits) & kDomMask);
+        const uint32_t cls = e.x >> (kKeyBits + kDomBits);
+        rec[(int64_t)off[d] + r] = make_uint2(e.x & kKeyMask, (cls << kClassShift) | e.y);
     }
 }
 
@@ -332,24 +372,25 @@ __device__ uint32_t scan1024_excl(uint32_t v, uint32_t* wsum)
     return before + x - v;
 }
 
-// Order the n = e - s global ids at out[s, e) (one cell, ~10 atoms):
-// insertion sort in registers for up to kCellRegs ids, loaded and stored
-// once, else in place.
+// Order the n = e - s sort values (class << kClassShift | global id) at
+// out[s, e) (one cell, ~10 atoms) and leave the global ids there: insertion
+// sort in registers for up to kCellRegs values, loaded and stored once, else
+// in place, then the classes cleared.
 constexpr int kCellRegs = 32;
 __device__ __forceinline__ void sort_cell(int* __restrict__ out, uint32_t s, uint32_t e)
 {
     const int n = (int)(e - s);
     if (n <= kCellRegs) {
-        int v[kCellRegs];
+        uint32_t v[kCellRegs];
 #pragma unroll
         for (int i = 0; i < kCellRegs; i++)
-            v[i] = i < n ? out[s + i] : INT32_MAX;
+            v[i] = i < n ? (uint32_t)out[s + i] : 0xFFFFFFFFu;
         // fixed trip counts keep v[] in registers
 #pragma unroll
         for (int i = 1; i < kCellRegs; i++) {
 #pragma unroll
             for (int j = i; j > 0; j--) {
-                const int lo = min(v[j - 1], v[j]), hi = max(v[j - 1], v[j]);
+                const uint32_t lo = min(v[j - 1], v[j]), hi = max(v[j - 1], v[j]);
                 v[j - 1] = lo;
                 v[j] = hi;
             }
@@ -357,23 +398,25 @@ __device__ __forceinline__ void sort_cell(int* __restrict__ out, uint32_t s, uin
 #pragma unroll
         for (int i = 0; i < kCellRegs; i++)
             if (i < n)
-                out[s + i] = v[i];
+                out[s + i] = (int)(v[i] & kIdMask);
         return;
     }
     for (uint32_t i = s + 1; i < e; i++) {
-        const int v = out[i];
+        const uint32_t v = (uint32_t)out[i];
         uint32_t j = i;
-        while (j > s && out[j - 1] > v) {
+        while (j > s && (uint32_t)out[j - 1] > v) {
             out[j] = out[j - 1];
             j--;
         }
-        out[j] = v;
+        out[j] = (int)v;
     }
+    for (uint32_t i = s; i < e; i++)
+        out[i] = (int)((uint32_t)out[i] & kIdMask);
 }
 
-// Place every id of rec[h0, h1) at its cell's next position in out (c[k]
-// holds cell k's first position and ends as its end), then order each cell
-// by global id. out is the block's LDS copy of the domain or the domain's
+// Place every sort value of rec[h0, h1) at its cell's next position in out
+// (c[k] holds cell k's first position and ends as its end), then order each
+// cell by class and global id, leaving the ids. out is the block's LDS copy of the domain or the domain's
 // part of home_gid.
 template <typename Out>
 __device__ __forceinline__ void place_and_sort(const uint2* __restrict__ rec, uint32_t h0,
@@ -454,10 +497,10 @@ __device__ __forceinline__ void gather_home_positions(const Ids* ids, uint32_t n
 // One block per domain D, whose atoms are rec[h0, h1): count them per cell
 // in LDS, scan, store the buckets' first positions (start[cellbase[D] + k],
 // and start[nb] = every atom inside the box from the last domain), place
-// every id at its cell's position and order each cell by global id, then
-// gather the home positions the selection reads into xhome. A domain of at
-// most kDomCap atoms is placed and sorted in LDS and leaves in one coalesced
-// copy; a larger one is placed and sorted in home_gid.
+// every atom at its cell's position and order each cell by class and global
+// id, then gather the home positions the selection reads into xhome. A
+// domain of at most kDomCap atoms is placed and sorted in LDS and leaves in
+// one coalesced copy; a larger one is placed and sorted in home_gid.
 __global__ __launch_bounds__(1024) void domain_sort_kernel(const uint2* __restrict__ rec,
                                                            const uint32_t* __restrict__ hscan,
                                                            int nblk, const int* __restrict__ cellbase,
@@ -592,8 +635,9 @@ __global__ __launch_bounds__(256) void scan_apply_kernel(const uint32_t* __restr
         out[n] = pre + total;
 }
 
-// Every atom to its bucket's range, at its arrival rank (an arbitrary order
-// inside the bucket: the per-cell sort by global id fixes it).
+// Every atom's sort value (class << kClassShift | global id) to its bucket's
+// range, at its arrival rank (an arbitrary order inside the bucket: the
+// per-cell sort by class and global id fixes it).
 __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ bucket,
                                                       const uint32_t* __restrict__ rank,
                                                       int n_atoms,
@@ -606,10 +650,11 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ bu
     const int bk = bucket[a];
     if (bk < 0)
         return;  // a position outside the box: reported by the build
-    sorted[start[bk] + rank[a]] = a;
+    const uint32_t r = rank[a];
+    sorted[start[bk] + (r & kIdMask)] = (int)((r & ~kIdMask) | (uint32_t)a);
 }
 
-// Order each cell's atoms by global id (one thread per cell).
+// Order each cell's atoms by class and global id (one thread per cell).
 __global__ __launch_bounds__(256) void sort_cells_kernel(const uint32_t* __restrict__ start, int nb,
                                                          int* __restrict__ sorted)
 {
@@ -1996,6 +2041,8 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     const int D = g.ndom, P = g.P;
     if (n_atoms < 0 || (n_atoms > 0 && !xg))
         return fail(DDH_EINVAL, "ddh_build_maps: bad positions pointer or count");
+    if ((int64_t)n_atoms > (int64_t)kIdMask + 1)
+        return fail(DDH_EINVAL, "ddh_build_maps: at most 2^29 atoms");
     if (p->build_failed)
         DDH_HIP(hipDeviceSynchronize());  // kernels of the failed build may still run
     p->build_failed = true;
@@ -2015,6 +2062,8 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
         ncat.insert(ncat.end(), g.ncell[d].begin(), g.ncell[d].end());
     }
     ag.inv_c = g.inv_c;
+    ag.rc = g.rc;
+    ag.px = (int)std::floor(g.rc * g.inv_c);
     std::vector<int> cellbase((size_t)D + 1, 0);
     {
         int64_t acc = 0;
@@ -2092,7 +2141,7 @@ int build_maps(Plan* p, const float* xg, int32_t n_atoms, hipStream_t s)
     // domain counting its atoms per cell in LDS and placing them; no device
     // atomic on any atom. Counting (any size): a device atomic count per
     // bucket gives each atom its arrival rank, a scan the bucket starts, a
-    // scatter the positions. Both then sort each cell by global id.
+    // scatter the positions. Both then sort each cell by class and global id.
     int max_cells = 0;
     for (int Dm = 0; Dm < D; Dm++)
         max_cells = std::max(max_cells, cellbase[Dm + 1] - cellbase[Dm]);

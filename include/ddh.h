@@ -35,8 +35,10 @@
  * GPU-native halo exchange": received coordinates land at the receiver's
  * offset and are used in place). Domain D = ix + nx * (iy + ny * iz) owns
  * slots [base_D, base_D + n_total_D): first its n_home_D home atoms, ordered
- * by sort cell and then by global id, then one contiguous received region per
- * pulse in global pulse order.
+ * by sort cell, then by class, then by global id (the class, at
+ * ddh_build_maps, keeps together the atoms of a cell that each dimension's
+ * first pulse sends), then one contiguous received region per pulse in global
+ * pulse order.
  */
 #ifndef DDH_H
 #define DDH_H
@@ -69,7 +71,7 @@ typedef struct ddh_params {
     float box[3];    /* periodic box edges L_x, L_y, L_z (nm) */
     float rc;        /* halo cutoff (nm), > 0 */
     float cell;      /* edge of the cells home atoms are sorted by (nm);
-                        <= 0 orders home atoms by global id only */
+                        <= 0: one cell per domain */
     int32_t flags;   /* reserved, pass 0 */
 } ddh_params;
 
@@ -134,8 +136,14 @@ const char *ddh_last_error(void);
  * Build the halo maps from global positions x_global_dev[n_atoms][3]
  * (device, float32, every coordinate in [0, L)). Runs on `stream` and waits
  * for it. Steps: assign each atom to the domain whose half-open interval
- * holds it in every dimension; order each domain's home atoms by sort cell
- * and global id; then for every pulse p (dimension d) and sender S choose the
+ * holds it in every dimension; order each domain's home atoms by sort cell,
+ * class and global id, where an atom's class comes from the slab tests of
+ * the first pulses, bit d = [fl(x_d - lo_d) < rc] (m), and is 7 - m in cells
+ * whose x index differs by an even number from px = floor(fl(rc * fl(1 /
+ * cell))), else m (the guide fixes no order inside a cell; this one keeps
+ * each pulse's atoms of a cell that its slab cuts in one run, and the runs of
+ * neighbouring cells along x adjacent, so the pulses' gathers touch fewer
+ * memory lines); then for every pulse p (dimension d) and sender S choose the
  * candidate slots (k == 0: home plus all slots received in earlier pulses;
  * k >= 1: the slots received in the previous pulse of d), keep those with
  * fl(x_d - lo_d(S)) < rc in increasing slot order, and deliver them to the
@@ -150,8 +158,8 @@ const char *ddh_last_error(void);
  * but exchange calls captured into a caller's graph keep the launch shapes
  * and the tables of the build they were captured after: recapture them
  * after every ddh_build_maps.
- * Errors: DDH_EINVAL (bad pointer or position), DDH_ECAPACITY (layout too
- * large), DDH_EHIP.
+ * Errors: DDH_EINVAL (bad pointer or position, more than 2^29 atoms),
+ * DDH_ECAPACITY (layout too large), DDH_EHIP.
  */
 int ddh_build_maps(ddh_plan *plan, const float *x_global_dev, int32_t n_atoms, void *stream);
 
@@ -402,8 +410,8 @@ int ddh_check(ddh_plan *plan, void *stream);
                                     at the next build. */
 
 #define DDH_TUNE_HOME_SORT 12      /* how the build orders the home atoms (by
-                                    domain, cell, then global id; the result
-                                    is the same): 0 (default) automatic, the
+                                    domain, cell, class, then global id; the
+                                    result is the same): 0 (default) automatic, the
                                     partition sort where its tables fit (at
                                     most 2048 domains and 4096 sort cells per
                                     domain), else the counting sort; 1 the

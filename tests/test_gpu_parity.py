@@ -18,6 +18,8 @@ one-sided inputs, many domains with short or empty maps, error paths and the
 bounded-wait timeout paths.
 """
 
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -810,7 +812,7 @@ def test_empty_and_one_sided_inputs():
     check_layout(g, ref)
     check_steps(g, ref, 5)
     g.close()
-    # cell <= 0: home atoms ordered by global id only
+    # cell <= 0: one cell per domain (home atoms by class, then global id)
     x = W.lattice_positions(900, box, seed=4)
     ref = oracle.OraclePlan(x, (2, 2, 2), box, 1.25, cell=0.0)
     g = GpuPlan(x, (2, 2, 2), box, 1.25, cell=0.0)
@@ -998,6 +1000,10 @@ def test_error_paths():
     with pytest.raises(ddh.DDHError) as e:
         plan.exchange_step(full, full)
     assert e.value.code == ddh.DDH_EINVAL
+    # more atoms than a home sort value's 29 id bits hold: refused before
+    # any position is read
+    rc = ddh._lib.ddh_build_maps(plan._h, ctypes.c_void_p(full.data_ptr()), (1 << 29) + 1, None)
+    assert rc == ddh.DDH_EINVAL
     plan.close()
 
 
