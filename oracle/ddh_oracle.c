@@ -44,15 +44,19 @@
  *    half-open [b_d[i], b_d[i+1]);
  *  - home atoms are ordered by sort cell, then by class, then by global id;
  *    the cell index in a dimension is floor(fl(fl(x - lo) * fl32(1/c)))
- *    clamped to [0, ceil((hi - lo) / c) - 1], key = cx + ncx * (cy + ncy * cz)
- *    (c <= 0: one cell per domain, index 0);
+ *    clamped to [0, ceil((hi - lo) / c) - 1] (c <= 0: one cell per domain,
+ *    index 0); cells go row by row, row = cy + ncy * cz, and along x within
+ *    a row, upward in even rows and downward in odd ones (a serpentine), key
+ *    = x' + ncx * row with x' = cx or ncx - 1 - cx. The rows' cells below
+ *    the x cut then meet those of the next row;
  *  - the class orders a cell's atoms by the first pulses that send them:
  *    m = sum over d of 2^d [fl(x_d - lo_d) < rc], the slab test of the first
- *    pulse of d; class = 7 - m (atoms that pass first) when cx - px is even,
- *    px = floor(fl(rc * fl32(1/c))) the x index of the cell holding the cut,
- *    else class = m (atoms that pass last). So a cell that a slab cuts keeps
- *    the atoms that pulse sends together, and along x such runs meet across
- *    neighbouring cells, also with the wholly selected cells below the cut;
+ *    pulse of d; px = floor(fl(rc * fl32(1/c))) is the x index of the cell
+ *    holding the cut; class = 7 - m (atoms that pass first) when cx - px is
+ *    even in an even row or odd in an odd row, else class = m (atoms that
+ *    pass last). So a cell that a slab cuts keeps the atoms that pulse sends
+ *    together, and along a row such runs meet across neighbouring cells, and
+ *    the cut cell's run meets the wholly selected cells below the cut;
  *  - force add order: pulses in reverse global order, plain fp32 adds in place.
  *
  * Layout: domain D = ix + nx * (iy + ny * iz) owns the slots
@@ -379,12 +383,15 @@ static int assign_home(oplan *o, const float *xg, int n_atoms)
             int ci[3];
             for (int d = 0; d < 3; d++)
                 ci[d] = cell_of(xg[3 * (size_t)a + d], lo[d], inv_c, nc[d]);
-            list[j].key = (int64_t)ci[0] + (int64_t)nc[0] * ((int64_t)ci[1] + (int64_t)nc[1] * ci[2]);
+            const int64_t row = (int64_t)ci[1] + (int64_t)nc[1] * ci[2];
+            const int odd = (int)(row % 2);
+            list[j].key = (int64_t)(odd ? nc[0] - 1 - ci[0] : ci[0]) + (int64_t)nc[0] * row;
             int m = 0;
             for (int d = 0; d < 3; d++)
                 if (xg[3 * (size_t)a + d] - lo[d] < o->rc)
                     m |= 1 << d;
-            list[j].cls = ((ci[0] - px) % 2 == 0) ? 7 - m : m;
+            const int even_from_cut = (ci[0] - px) % 2 == 0;
+            list[j].cls = even_from_cut != odd ? 7 - m : m;
             list[j].gid = a;
         }
         qsort(list, (size_t)m, sizeof(keyed), cmp_keyed);

@@ -84,9 +84,11 @@ def test_bruteforce_halo_exact(grid, box, rc, n):
 @pytest.mark.parametrize("grid,box,rc,n", DYADIC)
 def test_home_order_is_cell_class_then_id(grid, box, rc, n):
     """Home order from its definition, in exact arithmetic (dyadic box, lattice
-    positions): sort cell, then the class of the first pulses that send the
+    positions): sort cell (rows cy + ncy cz in turn, x upward in even rows and
+    downward in odd ones), then the class of the first pulses that send the
     atom (the cells' selected atoms together, first or last by the parity of
-    the x index counted from the cell that holds the cut), then global id."""
+    the x index counted from the cell that holds the cut, flipped in odd
+    rows), then global id."""
     x = W.lattice_positions(n, box, seed=3 + n)
     plan = oracle.OraclePlan(x, grid, box, rc, cell=0.5)
     bounds = _bounds(grid, box)
@@ -104,21 +106,26 @@ def test_home_order_is_cell_class_then_id(grid, box, rc, n):
             ci.append(np.minimum(np.floor((xs[:, d] - lo) / 0.5), ncd - 1).astype(np.int64))
             nc.append(ncd)
             sent |= (xs[:, d] - lo < rc).astype(np.int64) << d
-        key = ci[0] + nc[0] * (ci[1] + nc[1] * ci[2])
-        cls = np.where((ci[0] - px) % 2 == 0, 7 - sent, sent)
+        row = ci[1] + nc[1] * ci[2]
+        odd = row % 2 == 1
+        key = np.where(odd, nc[0] - 1 - ci[0], ci[0]) + nc[0] * row
+        first = ((ci[0] - px) % 2 == 0) != odd
+        cls = np.where(first, 7 - sent, sent)
         order = np.lexsort((ids, cls, key))
         assert np.array_equal(order, np.arange(nh))
 
 
 def test_cut_cells_keep_each_pulse_contiguous():
     """In every cell that one slab cuts, the atoms that dimension's first pulse
-    sends form one run, at the cell's start when the cell's x index has the parity of the
-    cut's cell and at its end otherwise, so a cell below the cut along x runs
-    straight into the sent part of the next."""
+    sends form one run, at the cell's start when the cell's x index has the
+    parity of the cut's cell (the other parity in odd rows, which run
+    downward in x) and at its end otherwise, so a cell below the cut along x
+    runs straight into the sent part of the next. And the X pulse's home
+    atoms of an odd row end where those of the next row begin."""
     grid, box, rc = (2, 2, 2), (8.0, 8.0, 8.0), 1.25
-    x = W.lattice_positions(4000, box, seed=41)
+    x = W.lattice_positions(30000, box, seed=41)
     plan = oracle.OraclePlan(x, grid, box, rc, cell=0.5)
-    cut_cells = 0
+    cut_cells = joined = 0
     for D in range(plan.n_domains):
         c = (D % 2, (D // 2) % 2, D // 4)
         lo = [4.0 * c[d] for d in range(3)]
@@ -137,11 +144,26 @@ def test_cut_cells_keep_each_pulse_contiguous():
             cut_cells += 1
             hit = np.flatnonzero(sent[cut[0]])
             assert hit[-1] - hit[0] + 1 == len(hit), "a pulse's atoms split inside a cell"
-            if (cx - 2) % 2 == 0:
+            odd = (cell[s, 1] + 8 * cell[s, 2]) % 2 == 1
+            if ((cx - 2) % 2 == 0) != odd:
                 assert hit[0] == 0
             else:
                 assert hit[-1] == e - s - 1
-    assert cut_cells > 100
+        # serpentine: odd row r ends with its x-sent cells and row r + 1
+        # starts with them, so both rows' X pulse atoms form one run (rows
+        # that the y or z slab also cuts excepted: there a cell cut twice
+        # keeps only its z or y run whole)
+        row = cell[:, 1] + 8 * cell[:, 2]
+        xsent = xs[:, 0] - lo[0] < rc
+        for r in range(1, 63, 2):
+            if 2 in (r % 8, r // 8, (r + 1) % 8, (r + 1) // 8):
+                continue
+            a, b = np.flatnonzero(row == r), np.flatnonzero(row == r + 1)
+            assert b[0] == a[-1] + 1
+            hit = np.flatnonzero(xsent[a[0]:b[-1] + 1])
+            assert hit[-1] - hit[0] + 1 == len(hit), "rows r and r + 1 split the X pulse's run"
+            joined += 1
+    assert cut_cells > 100 and joined > 100
 
 
 @pytest.mark.parametrize("grid,box,rc,n", DYADIC)
