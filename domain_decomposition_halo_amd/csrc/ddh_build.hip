@@ -10,10 +10,11 @@
 //
 //   1. every atom goes to the domain whose half-open interval [b_d[i],
 //      b_d[i+1]) holds it in each dimension (fp32 compares decide);
-//   2. home atoms of a domain are ordered by sort cell (key cx + ncx * (cy +
-//      ncy * cz)), then by class (the first pulses' slab tests, see
-//      home_class: a cell that a slab cuts keeps the atoms that pulse sends
-//      together), then by global id: a partition of the atoms by domain
+//   2. home atoms of a domain are ordered by sort cell (rows cy + ncy * cz in
+//      turn, each a serpentine along x: cell_key), then by class (the first
+//      pulses' slab tests, see home_class: a cell that a slab cuts keeps the
+//      atoms that pulse sends together), then by global id: a partition of
+//      the atoms by domain
 //      (block histograms in LDS, one scan, a scatter with LDS counters), a
 //      counting sort of each domain's atoms by cell in LDS, then each cell
 //      sorted by class and id; or, where a domain or a cell table is too
@@ -73,25 +74,37 @@ struct AGeom {
     const int* cellbase;  // first bucket of each domain
 };
 
+// Cells of a domain go row by row (row = cy + ncy * cz), along x upward in
+// even rows and downward in odd ones, so the cells below the x cut at the
+// end of an odd row meet those at the start of the next: the cell's key.
+__device__ __forceinline__ int cell_key(const int cc[3], const int ncd[3])
+{
+    const int row = cc[1] + ncd[1] * cc[2];
+    return ((row & 1) ? ncd[0] - 1 - cc[0] : cc[0]) + ncd[0] * row;
+}
+
 // An atom's class inside its sort cell, from the slab tests of the first
-// pulses (bit d: fl(x_d - lo_d) < rc, the selection's own compare): 7 - m in
-// cells whose x index has the parity of px (the atoms the slabs send first),
-// m in the others (last). Home atoms are ordered by cell, class, global id,
-// so a cell that one slab cuts keeps that pulse's atoms in one run, and the
-// runs of neighbouring cells along x meet.
-__device__ __forceinline__ int home_class(const float u[3], int cx, const AGeom& g)
+// pulses (bit d: fl(x_d - lo_d) < rc, the selection's own compare): 7 - m
+// (the atoms the slabs send first) in cells whose x index differs from px by
+// an even number in an even row, or by an odd one in an odd row; m (last)
+// in the others. Home atoms are ordered by cell, class, global id, so a cell
+// that one slab cuts keeps that pulse's atoms in one run, which meets the
+// next cell's run along the row's walk.
+__device__ __forceinline__ int home_class(const float u[3], const int cc[3], const int ncd[3],
+                                          const AGeom& g)
 {
     int m = 0;
 #pragma unroll
     for (int d = 0; d < 3; d++)
         m |= (u[d] < g.rc ? 1 : 0) << d;
-    return ((cx - g.px) & 1) == 0 ? 7 - m : m;
+    const int odd = (cc[1] + ncd[1] * cc[2]) & 1;
+    return (((cc[0] - g.px) ^ odd) & 1) == 0 ? 7 - m : m;
 }
 
 // Domain, sort cell and class of one position from the boundary and
 // cell-count tables b and nc (laid out as in AGeom: dimension d at boff[d]
 // and noff[d]); false when a coordinate lies outside [0, L) or is not a
-// number. key is the cell's index inside the domain, x fastest.
+// number. key is the cell's index inside the domain (cell_key).
 __device__ __forceinline__ bool locate(const float v[3], const AGeom& g, const float* b,
                                        const int* nc, int& dom, int& key, int& cls)
 {
@@ -121,8 +134,8 @@ __device__ __forceinline__ bool locate(const float v[3], const AGeom& g, const f
         cc[d] = c;
     }
     dom = ci[0] + g.n[0] * (ci[1] + g.n[1] * ci[2]);
-    key = cc[0] + ncd[0] * (cc[1] + ncd[1] * cc[2]);
-    cls = home_class(u, cc[0], g);
+    key = cell_key(cc, ncd);
+    cls = home_class(u, cc, ncd, g);
     return true;
 }
 
@@ -176,8 +189,8 @@ __device__ __forceinline__ bool locate_tab(const float v[3], const AGeom& g, con
         cc[d] = c;
     }
     dom = ci[0] + g.n[0] * (ci[1] + g.n[1] * ci[2]);
-    key = cc[0] + ncd[0] * (cc[1] + ncd[1] * cc[2]);
-    cls = home_class(u, cc[0], g);
+    key = cell_key(cc, ncd);
+    cls = home_class(u, cc, ncd, g);
     return true;
 }
 
@@ -469,7 +482,8 @@ __device__ __forceinline__ void gather_home_positions(const Ids* ids, uint32_t n
                     else
                         lo = mid + 1;
                 }
-                const int cx = lo % g.x, cy = (lo / g.x) % g.y, cz = lo / (g.x * g.y);
+                const int row = lo / g.x, w = lo - row * g.x;  // key = w + ncx * row
+                const int cx = (row & 1) ? g.x - 1 - w : w, cy = row % g.y, cz = row / g.y;
                 if (cx < cfx || cy < cfy || cz < cfz)
                     id[j] = (int)ids[i];
             }
@@ -797,9 +811,10 @@ struct CArgs {
     float* out_xyz;
 };
 
-// Candidate cell m of a sender: its key (cx + ncx (cy + ncy cz)) and its
-// coordinate along d. Along z the candidates are the layers cz < cf, along
-// y the rows cy < cf of every layer, along x the first cf cells of every row.
+// Candidate cell m of a sender: its key (cell_key) and its coordinate along
+// d. Along z the candidates are the layers cz < cf, along y the rows cy < cf
+// of every layer, along x the cells cx < cf of every row: the first cf keys
+// of an even row and the last cf, cx descending, of an odd one.
 __device__ __forceinline__ int cand_cell(int m, int d, int ncx, int ncy, int cf, int& cd)
 {
     if (d == 2) {
@@ -811,9 +826,13 @@ __device__ __forceinline__ int cand_cell(int m, int d, int ncx, int ncy, int cf,
         cd = r / ncx;
         return r + cz * ncx * ncy;
     }
-    const int row = m / cf, cx = m - row * cf;
-    cd = cx;
-    return cx + ncx * row;
+    const int row = m / cf, i = m - row * cf;
+    if (row & 1) {
+        cd = cf - 1 - i;
+        return ncx - cf + i + ncx * row;
+    }
+    cd = i;
+    return i + ncx * row;
 }
 
 constexpr int kCellBatch = 16;  // positions of a cell a thread loads together

@@ -137,17 +137,19 @@ const char *ddh_last_error(void);
  * (device, float32, every coordinate in [0, L)). Runs on `stream` and waits
  * for it. Steps: assign each atom to the domain whose half-open interval
  * holds it in every dimension; order each domain's home atoms by sort cell,
- * class and global id, where an atom's class comes from the slab tests of
- * the first pulses, bit d = [fl(x_d - lo_d) < rc] (m), and is 7 - m in cells
- * whose x index differs by an even number from px = floor(fl(rc * fl(1 /
- * cell))), else m (the guide fixes no order inside a cell; this one keeps
- * each pulse's atoms of a cell that its slab cuts in one run, and the runs of
- * neighbouring cells along x adjacent, so the pulses' gathers touch fewer
- * memory lines); then for every pulse p (dimension d) and sender S choose the
- * candidate slots (k == 0: home plus all slots received in earlier pulses;
- * k >= 1: the slots received in the previous pulse of d), keep those with
- * fl(x_d - lo_d(S)) < rc in increasing slot order, and deliver them to the
- * -d neighbour. Cell-sorted home atoms, slab selection and multi-pulse relay
+ * class and global id. Cells go row by row (row = cy + ncy * cz), along x
+ * upward in even rows and downward in odd ones. An atom's class comes from
+ * the slab tests of the first pulses, bit d = [fl(x_d - lo_d) < rc] (m): 7 -
+ * m in cells whose x index differs from px = floor(fl(rc * fl(1 / cell))) by
+ * an even number in an even row or an odd number in an odd row, else m. The
+ * guide fixes neither order; these keep each pulse's atoms of a cell that
+ * its slab cuts in one run, adjacent to the next cell's run along the walk,
+ * and join the x pulse's cells of neighbouring rows, so the pulses' gathers
+ * touch fewer memory lines. Then for every pulse p (dimension d) and sender
+ * S choose the candidate slots (k == 0: home plus all slots received in
+ * earlier pulses; k >= 1: the slots received in the previous pulse of d),
+ * keep those with fl(x_d - lo_d(S)) < rc in increasing slot order, and
+ * deliver them to the -d neighbour. Cell-sorted home atoms, slab selection and multi-pulse relay
  * follow "Accelerating GROMACS using Device-initiated Remote Memory Access"
  * and "Enabling parallelism across pulses through kernel fusion" (the
  * dependency offset of each map is the sender's home count).
